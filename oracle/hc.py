@@ -1,0 +1,47 @@
+"""Fused RMSNorm + Q8_0 hyper-connection down read, and the Q8_0 up read (oracle; test infrastructure).
+
+HC-Q8 page, "What changed": the down read works on R' * w_norm, unscaled, and
+keeps the sums of squares; the RMSNorm factor rs is applied after the dot
+product, when the partial sums are combined. The up read multiplies the Q8_0
+up projection (its rows are K = 320 long) by the down read's output.
+
+Readings taken where the page is not explicit:
+  * rs is one value per token row over the whole row: rs = 1/sqrt(mean(R^2) + eps),
+    eps = 1e-6, with the mean over the K columns of R (not of R * w_norm);
+  * R' is R itself (no pending write is modelled);
+  * the down output lo is rs * dot, stored as bf16; rs is also returned;
+  * the up read's own epilogue (pending write, gate, stream mean) is not
+    defined on the page and is left out: the up output is the plain product,
+    stored as bf16.
+All arithmetic is float64; R * w_norm is exact there.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .numerics import bf16_to_f32
+from .q8 import dequantize, q8_0_gemv
+
+
+def hc_down(R_bits, wnorm_bits, blocks, eps=1e-6):
+    """Down read.  R_bits bf16 [T, K], wnorm_bits bf16 [K], blocks: Q8_0 of W_down [N, K].
+
+    Returns (lo [T, N], rs [T], S [T, N]) in float64, where S = rs * sum_k |d q u_k|
+    is the scale of the pass rule.
+    """
+    R = bf16_to_f32(R_bits).astype(np.float64)
+    wn = bf16_to_f32(wnorm_bits).astype(np.float64)
+    K = R.shape[1]
+    u = R * wn[None, :]
+    ss = np.sum(R * R, axis=1)
+    rs = 1.0 / np.sqrt(ss / K + eps)
+    W = dequantize(blocks)
+    dot = u @ W.T
+    lo = rs[:, None] * dot
+    S = rs[:, None] * (np.abs(u) @ np.abs(W).T)
+    return lo, rs, S
+
+
+def hc_up(lo_bits, blocks):
+    """Up read.  lo_bits bf16 [T, K_lr], blocks: Q8_0 of W_up [N, K_lr].  Returns (out, S) float64."""
+    return q8_0_gemv(blocks, bf16_to_f32(lo_bits))

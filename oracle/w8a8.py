@@ -1,0 +1,42 @@
+"""W8A8 decode product (oracle; test infrastructure).
+
+W8A8 page, operator statement at the top: int8 x_q[M, K] times int8 W[K, N]
+accumulates into int32; the int32 result is multiplied by the per-row
+activation scale x_scale[M] and the per-column weight scale w_scale[N] and
+written as bf16[M, N].
+
+Readings:
+  * the epilogue is read left to right in fp32: bf16( (fp32(acc) * x_scale[m]) * w_scale[n] ),
+    two separately rounded fp32 products (no fused multiply-add), every rounding
+    to nearest even;
+  * int32 addition is exact here (|acc| <= 127*127*K < 2**31 for K <= 133,143),
+    so the accumulator has exactly one correct value whatever the summation
+    order (the page's "exact int32 order" matters only for determinism).
+The accumulator is computed in int64 and checked to fit int32.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .numerics import bf16_bits, f32
+
+
+def w8a8_acc(xq, W):
+    """acc[m, n] = sum_k xq[m, k] * W[k, n], exact (int64, asserted to fit int32)."""
+    acc = np.asarray(xq, dtype=np.int64) @ np.asarray(W, dtype=np.int64)
+    assert np.all(np.abs(acc) < 2 ** 31), "accumulator leaves int32"
+    return acc
+
+
+def w8a8_epilogue(acc, x_scale, w_scale):
+    """bf16 bits of (fp32(acc) * x_scale[m]) * w_scale[n], each product rounded in fp32."""
+    a = np.asarray(acc, dtype=np.int64).astype(np.float32)      # int -> fp32, nearest even
+    v = (a * f32(x_scale)[:, None]).astype(np.float32)
+    v = (v * f32(w_scale)[None, :]).astype(np.float32)
+    return bf16_bits(v)
+
+
+def w8a8_gemm(xq, x_scale, W, w_scale):
+    """Returns (acc int64 [M, N], out bf16 bits [M, N])."""
+    acc = w8a8_acc(xq, W)
+    return acc, w8a8_epilogue(acc, x_scale, w_scale)

@@ -1,0 +1,94 @@
+"""Pins for the oracle's fused RMSNorm + Q8_0 down read and the up read.
+
+Closed forms (constant R), invariances that fix where rs and w_norm enter
+(R scaled by a power of two leaves lo unchanged; w_norm scaled scales lo),
+and exact rational brute force on a tiny shape.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+
+from gemm_q8_amd import synth
+from oracle.hc import hc_down, hc_up
+from oracle.numerics import bf16_bits, bf16_to_f32, fp16_to_f32
+from oracle.q8 import q8_0_gemv, quantize_q8_0
+
+EPS = 1e-6
+
+
+def _down_blocks(N=6, K=128, seed=0):
+    return quantize_q8_0(synth.normal_f32(seed, "pin.hc.w", (N, K), 0.0, 0.02))
+
+
+def test_down_constant_rows_closed_form():
+    K = 128
+    b = _down_blocks(K=K)
+    c = 1.5
+    R = np.full((2, K), bf16_bits(np.float32(c)), np.uint16)
+    R[1] = bf16_bits(np.float32(-0.25))
+    ones = np.full(K, bf16_bits(np.float32(1.0)), np.uint16)
+    lo, rs, _ = hc_down(R, ones, b, EPS)
+    d = fp16_to_f32(b.d).astype(np.float64)
+    rowsum = (d * b.q.astype(np.int64).sum(axis=2)).sum(axis=1)       # sum_k d q
+    for t, v in enumerate((c, -0.25)):
+        want_rs = 1.0 / math.sqrt(v * v + EPS)
+        assert abs(rs[t] - want_rs) <= 1e-15 * want_rs
+        assert np.allclose(lo[t], want_rs * v * rowsum, rtol=1e-13, atol=0)
+
+
+def test_down_rs_uses_R_and_is_applied_after_the_dot():
+    b = _down_blocks()
+    R = synth.bf16_normal(3, "pin.hc.R", (3, 128))
+    wn = synth.bf16_normal(3, "pin.hc.wn", (128,), 1.0, 0.1)
+    lo, rs, _ = hc_down(R, wn, b, EPS)
+    R4 = bf16_bits(bf16_to_f32(R) * np.float32(4.0))          # exact power-of-two scaling
+    lo4, rs4, _ = hc_down(R4, wn, b, EPS)
+    assert np.allclose(rs4 * 4.0, rs, rtol=1e-6)               # eps is negligible here
+    assert np.allclose(lo4, lo, rtol=1e-6, atol=0)
+    wn2 = bf16_bits(bf16_to_f32(wn) * np.float32(2.0))
+    lo2, rs2, _ = hc_down(R, wn2, b, EPS)
+    assert np.array_equal(rs2, rs)                            # w_norm does not enter rs
+    assert np.allclose(lo2, 2.0 * lo, rtol=1e-13, atol=0)
+
+
+def test_down_with_unit_norm_weight_is_rmsnorm_then_gemv():
+    b = _down_blocks()
+    R = synth.bf16_normal(4, "pin.hc.R1", (2, 128))
+    ones = np.full(128, bf16_bits(np.float32(1.0)), np.uint16)
+    lo, rs, _ = hc_down(R, ones, b, EPS)
+    y, _ = q8_0_gemv(b, bf16_to_f32(R))
+    Rf = bf16_to_f32(R).astype(np.float64)
+    want_rs = 1.0 / np.sqrt((Rf * Rf).mean(axis=1) + EPS)
+    assert np.allclose(rs, want_rs, rtol=1e-14)
+    assert np.allclose(lo, want_rs[:, None] * y, rtol=1e-12, atol=1e-15)
+
+
+def test_down_brute_force_rational():
+    N, K = 3, 64
+    b = _down_blocks(N=N, K=K, seed=5)
+    R = synth.bf16_normal(5, "pin.hc.Rb", (2, K))
+    wn = synth.bf16_normal(5, "pin.hc.wnb", (K,), 1.0, 0.1)
+    lo, rs, S = hc_down(R, wn, b, EPS)
+    Rf, wf = bf16_to_f32(R), bf16_to_f32(wn)
+    for t in range(2):
+        ss = sum(Fraction(float(r)) ** 2 for r in Rf[t])
+        r_t = 1.0 / math.sqrt(float(ss / K) + EPS)
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                acc += (Fraction(float(fp16_to_f32(b.d[n, k // 32]))) * int(b.q[n, k // 32, k % 32])
+                        * Fraction(float(Rf[t, k])) * Fraction(float(wf[k])))
+            assert abs(r_t * float(acc) - lo[t, n]) <= 1e-12 * S[t, n]
+
+
+def test_up_is_gemv_of_bf16_input():
+    b = quantize_q8_0(synth.normal_f32(6, "pin.hc.up", (40, 64), 0.0, 0.02))
+    lo = synth.bf16_normal(6, "pin.hc.lo", (3, 64))
+    out, S = hc_up(lo, b)
+    for k in (0, 33):
+        e = np.zeros((1, 64), np.uint16)
+        e[0, k] = bf16_bits(np.float32(1.0))
+        o, _ = hc_up(e, b)
+        assert np.array_equal(o[0], fp16_to_f32(b.d[:, k // 32]).astype(np.float64) * b.q[:, k // 32, k % 32])
+    assert out.shape == (3, 40) and np.all(S >= np.abs(out))

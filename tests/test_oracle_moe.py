@@ -1,0 +1,76 @@
+"""Pins for the oracle's routing, expert plan and routed-expert forward."""
+import math
+
+import numpy as np
+
+from gemm_q8_amd import synth
+from oracle.moe import expert_rows, moe_forward, plan, route
+from oracle.q8 import dequantize, quantize_q8_0, quantize_q8_1_bf16
+
+
+def test_route_closed_forms():
+    ids, p = route(np.zeros((2, 16), np.float32), 4)
+    assert ids.tolist() == [[0, 1, 2, 3]] * 2                  # ties go to the lower id
+    assert np.allclose(p, 1 / 16, rtol=1e-15)
+    l = np.log(np.array([[1.0, 2.0, 3.0, 0.5]], np.float64)).astype(np.float32)
+    ids, p = route(l, 2)
+    assert ids.tolist() == [[2, 1]]
+    tot = 6.5
+    assert abs(p[0, 0] - 3 / tot) < 1e-7 and abs(p[0, 1] - 2 / tot) < 1e-7
+
+
+def test_route_matches_brute_force_sort():
+    logits = synth.moe_inputs(T=4, E=512)["logits"]
+    ids, p = route(logits, 8)
+    for t in range(4):
+        order = sorted(range(512), key=lambda e: (-float(logits[t, e]), e))[:8]
+        assert ids[t].tolist() == order
+        z = sum(math.exp(float(v) - float(logits[t].max())) for v in logits[t])
+        for j in range(8):
+            assert abs(p[t, j] - math.exp(float(logits[t, ids[t, j]]) - float(logits[t].max())) / z) < 1e-12
+
+
+def test_plan_covers_every_entry_once():
+    ids = np.array([[5, 1, 9], [1, 7, 5], [3, 2, 1]])
+    pl = plan(ids)
+    assert [e for e, _ in pl] == [1, 2, 3, 5, 7, 9]
+    seen = sorted(i for _, es in pl for i in es)
+    assert seen == list(range(9))
+    for e, es in pl:
+        assert es == sorted(es) and all(ids.flat[i] == e for i in es)
+
+
+def _tiny_expert(e, D=64, F=32):
+    w = synth.moe_expert_weights(e, D=D, F=F, seed=7)
+    return quantize_q8_0(w["gate_up"]), quantize_q8_0(w["down"])
+
+
+def test_expert_rows_match_dequantized_math():
+    D, F = 64, 32
+    x81 = quantize_q8_1_bf16(synth.bf16_normal(7, "pin.moe.x", (2, D)))
+    gu, dn = _tiny_expert(3)
+    xd = dequantize(x81)                                        # d_x * q_x as float64
+    gu_v = dequantize(gu) @ xd[1]
+    g, u = gu_v[:F], gu_v[F:]
+    h = g * u / (1.0 + np.exp(-g))
+    want = dequantize(dn) @ h
+    r, S = expert_rows(x81, 1, gu, dn)
+    assert np.allclose(r, want, rtol=1e-12, atol=1e-15)
+    assert np.all(S >= np.abs(r))
+
+
+def test_forward_is_weighted_sum_and_linear_in_weights():
+    D, F = 64, 32
+    x81 = quantize_q8_1_bf16(synth.bf16_normal(8, "pin.moe.x2", (2, D)))
+    ids = np.array([[3, 1], [1, 4]])
+    p = np.array([[0.6, 0.4], [0.25, 0.75]])
+    blocks = lambda e: _tiny_expert(e, D, F)  # noqa: E731
+    y, S = moe_forward(x81, ids, p, blocks)
+    for t in range(2):
+        want = sum(p[t, j] * expert_rows(x81, t, *blocks(ids[t, j]))[0] for j in range(2))
+        assert np.allclose(y[t], want, rtol=1e-13, atol=1e-16)
+    y2, _ = moe_forward(x81, ids, 2 * p, blocks)
+    assert np.allclose(y2, 2 * y, rtol=1e-13, atol=1e-16)
+    # one expert with weight one is that expert's rows
+    y1, _ = moe_forward(x81, np.array([[4], [4]]), np.ones((2, 1)), blocks)
+    assert np.allclose(y1[0], expert_rows(x81, 0, *blocks(4))[0], rtol=0, atol=0)

@@ -1,0 +1,51 @@
+"""Pins for the oracle's W8A8 product: integer brute force, closed forms, and rounding ties."""
+import numpy as np
+
+from gemm_q8_amd import synth
+from oracle.numerics import bf16_to_f32
+from oracle.w8a8 import w8a8_acc, w8a8_epilogue, w8a8_gemm
+
+
+def test_acc_brute_force_python_ints():
+    M, K, N = 3, 40, 5
+    x = synth.int8_uniform(0, "pin.w8.x", (M, K))
+    W = synth.int8_uniform(0, "pin.w8.W", (K, N))
+    acc = w8a8_acc(x, W)
+    for m in range(M):
+        for n in range(N):
+            assert acc[m, n] == sum(int(x[m, k]) * int(W[k, n]) for k in range(K))
+
+
+def test_acc_closed_forms():
+    K = 4096
+    assert np.all(w8a8_acc(np.ones((2, K), np.int8), np.ones((K, 3), np.int8)) == K)
+    big = np.full((1, K), 127, np.int8)
+    assert w8a8_acc(big, np.full((K, 1), -127, np.int8))[0, 0] == -127 * 127 * K
+    x = synth.int8_uniform(1, "pin.w8.neg", (4, 64))
+    W = synth.int8_uniform(1, "pin.w8.negW", (64, 7))
+    assert np.array_equal(w8a8_acc(-x.astype(np.int16), W), -w8a8_acc(x, W))
+    # one-hot row / column pick single entries of W / x
+    e = np.zeros((1, 64), np.int8)
+    e[0, 17] = 1
+    assert np.array_equal(w8a8_acc(e, W)[0], W[17].astype(np.int64))
+
+
+def test_epilogue_ties_to_even():
+    one = np.ones(1, np.float32)
+    acc = np.array([[257, 259, 258, -257]])
+    out = w8a8_epilogue(acc, one, np.ones(4, np.float32))
+    assert out[0].tolist() == [0x4380, 0x4382, 0x4381, 0xC380]    # 256, 260, 258, -256
+
+
+def test_epilogue_scales_rows_and_columns():
+    acc = np.array([[1000, -2000], [3000, 4]])
+    xs = np.array([0.5, 0.25], np.float32)
+    ws = np.array([2.0, 4.0], np.float32)
+    out = bf16_to_f32(w8a8_epilogue(acc, xs, ws))
+    assert out.tolist() == [[1000.0, -4000.0], [1504.0, 4.0]]      # 1500 rounds to bf16 1504
+
+
+def test_gemm_shapes_and_int32_range():
+    d = synth.w8a8_inputs(16, 48, 256)
+    acc, out = w8a8_gemm(d["xq"], d["x_scale"], d["W"], d["w_scale"])
+    assert acc.shape == (16, 48) and out.shape == (16, 48) and out.dtype == np.uint16
