@@ -1,0 +1,411 @@
+#!/usr/bin/env python3
+"""Benchmark of the decode-time Q8_0 read on one MI355X.
+
+Workload (one "step"): the fused RMSNorm + Q8_0 hyper-connection down read (W_down Q8_0
+[320, 16384], R bf16 [T, 16384]) followed by the Q8_0 up read (W_up Q8_0 [16384, 320]) for each
+T in {1, 4, 6}: six kernels' worth of calls, 3 x 11,141,120 weight bytes. Every pair reads its
+own copy of the weights; the copies rotate through a working set larger than twice the
+Infinity Cache (MALL) plus the L2s, so the weight bytes come from HBM. Inputs are seeded and
+synthetic (gemm_q8_amd.synth), resident in HBM before the timed region. Calls are captured
+serially on one stream into hipGraphs and replayed.
+
+Output: one JSON line on stdout (metric = weight bytes / time in GB/s), with
+  roofline      the dominant kernel's algorithmic bytes per launch / its average launch
+                duration, from HIP events on the launch stream, against 8 TB/s;
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload.
+--all-configs also times the other workloads (Q8_0 GEMV T sweep, W8A8 sweep, routed MoE)
+and writes their lines to --report (default gpurun_out/bench_all.jsonl) and stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+WS_TARGET = 640 << 20          # working set per rotation: > 2 x (256 MB MALL + 8 x 4 MB L2)
+TS = (1, 4, 6)
+K_HC, N_LR = 16384, 320
+# the HC-Q8 page's kernel-level times on an Arc Pro B70 (us per down+up read, Q8_0), for context
+PAGE_US = {1: 24.7, 4: 29.3, 6: 34.4}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------------------------ helpers
+
+class GraphSteps:
+    """Captures steps (each a list of launch callables) into hipGraphs on `stream` and replays
+    them on that same stream so that exactly K steps run: replays of a full-rotation graph plus
+    one remainder graph, all captured before any timed region (prepare)."""
+
+    def __init__(self, torch, stream, step_fns, steps_per_graph):
+        self.torch, self.stream = torch, stream
+        self.step_fns = step_fns
+        self.steps_per_graph = steps_per_graph
+        self.g_full = self._capture(steps_per_graph)
+        self.rem = {}
+
+    def _capture(self, n):
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(self.stream):
+            for i in range(n):                      # eager pass first (lazy init outside capture)
+                for f in self.step_fns(i):
+                    f(self.stream)
+            self.stream.synchronize()
+            with torch.cuda.graph(g, stream=self.stream):
+                for i in range(n):
+                    for f in self.step_fns(i):
+                        f(self.stream)
+        self.stream.synchronize()
+        return g
+
+    def prepare(self, K):
+        r = K % self.steps_per_graph
+        if r and r not in self.rem:
+            self.rem[r] = self._capture(r)
+        return self
+
+    def run(self, K):
+        full, r = divmod(K, self.steps_per_graph)
+        assert r == 0 or r in self.rem, "prepare(K) before run(K)"
+        with self.torch.cuda.stream(self.stream):   # replay() launches on the current stream
+            for _ in range(full):
+                self.g_full.replay()
+            if r:
+                self.rem[r].replay()
+
+
+def time_region(torch, stream, fn):
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    fn()
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1e-3       # seconds
+
+
+def n_sets_for(nbytes, multiple=1):
+    n = int(np.ceil(WS_TARGET / nbytes))
+    return int(np.ceil(n / multiple) * multiple)
+
+
+# ------------------------------------------------------------------------------------ HC workload
+
+def setup_hc(torch, gq8, synth, dev):
+    from gemm_q8_amd.device import q8_0_from_f32, to_dev, workspace
+    base = synth.hc_inputs(6)
+    wd0 = q8_0_from_f32(to_dev(base["w_down"]))
+    wu0 = q8_0_from_f32(to_dev(base["w_up"]))
+    pair_bytes = wd0.numel() + wu0.numel()
+    n_sets = n_sets_for(pair_bytes, len(TS))
+    wds = [wd0] + [wd0.clone() for _ in range(n_sets - 1)]
+    wus = [wu0] + [wu0.clone() for _ in range(n_sets - 1)]
+    per_t = {}
+    for T in TS:
+        d = synth.hc_inputs(T)
+        nbd = gq8.gq8_workspace_bytes(gq8.OP_HC_DOWN, T, N_LR, K_HC)
+        nbu = gq8.gq8_workspace_bytes(gq8.OP_HC_UP, T, K_HC, N_LR)
+        per_t[T] = dict(
+            R=to_dev(d["R"]), wn=to_dev(d["w_norm"]),
+            lo=torch.empty((T, N_LR), dtype=torch.int16, device=dev),
+            rs=torch.empty((T,), dtype=torch.float32, device=dev),
+            out=torch.empty((T, K_HC), dtype=torch.int16, device=dev),
+            wsd=workspace(nbd), nbd=nbd, wsu=workspace(nbu), nbu=nbu)
+    return dict(wds=wds, wus=wus, n_sets=n_sets, per_t=per_t, pair_bytes=pair_bytes)
+
+
+def hc_down_fn(gq8, h, T, i):
+    p = h["per_t"][T]
+    w = h["wds"][i % h["n_sets"]]
+    return lambda s: gq8.gq8_hc_q8_down(w, p["R"], p["wn"], 1e-6, p["lo"], p["rs"], T, N_LR, K_HC,
+                                        p["wsd"], p["nbd"], s)
+
+
+def hc_up_fn(gq8, h, T, i):
+    p = h["per_t"][T]
+    w = h["wus"][i % h["n_sets"]]
+    return lambda s: gq8.gq8_hc_q8_up(w, p["lo"], p["out"], T, K_HC, N_LR, p["wsu"], p["nbu"], s)
+
+
+def hc_step_fns(gq8, h):
+    def fns(step):
+        out = []
+        for j, T in enumerate(TS):
+            i = step * len(TS) + j
+            out += [hc_down_fn(gq8, h, T, i), hc_up_fn(gq8, h, T, i)]
+        return out
+    return fns
+
+
+def hc_kernel_bytes(kind, T):
+    """Algorithmic bytes of one launch: weights + activations read + outputs written."""
+    w = K_HC * N_LR + K_HC * N_LR // 32 * 2
+    if kind == "down":
+        return w + T * K_HC * 2 + K_HC * 2 + T * N_LR * 2 + T * 4
+    return w + T * N_LR * 2 + T * K_HC * 2
+
+
+# ------------------------------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(synth, budget_s):
+    """The oracle (test infrastructure) on the same workload: down + up for T = 1, 4, 6 per
+    step, repeated until about `budget_s` seconds have been spent."""
+    import oracle
+    from oracle.q8 import quantize_q8_0
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        cores = 1
+    base = synth.hc_inputs(6)
+    bd, bu = quantize_q8_0(base["w_down"]), quantize_q8_0(base["w_up"])
+    from oracle.numerics import bf16_bits
+    ins = {T: synth.hc_inputs(T) for T in TS}
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        for T in TS:
+            lo, _, _ = oracle.hc.hc_down(ins[T]["R"], ins[T]["w_norm"], bd)
+            oracle.hc.hc_up(bf16_bits(lo.astype(np.float32)), bu)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    wbytes = steps * len(TS) * 2 * (K_HC * N_LR + K_HC * N_LR // 32 * 2)
+    return {"value": round(wbytes / el / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{steps} oracle steps (down+up read at T=1,4,6 each, full size) in {el:.1f} s; "
+                      f"numpy float64 on the host, BLAS threads={cores}"}
+
+
+# ------------------------------------------------------------------------------------ other configs
+
+def bench_other_configs(torch, gq8, synth, dev, stream, report):
+    from gemm_q8_amd.device import q8_0_from_f32, to_dev, workspace
+    lines = []
+
+    def emit(d):
+        lines.append(d)
+        log(json.dumps(d))
+
+    def timed(fn_for_set, n_sets, reps=30):
+        fns = lambda step: [fn_for_set(step)]  # noqa: E731
+        gs = GraphSteps(torch, stream, fns, n_sets)
+        gs.run(n_sets)
+        t = time_region(torch, stream, lambda: gs.run(n_sets * reps))
+        return t / (n_sets * reps) * 1e6
+
+    # read-bandwidth probe at the same byte counts
+    for nbytes in (4_456_448, 5_570_560, 6_291_456, 8_388_608, 10_485_760):
+        n = n_sets_for(nbytes)
+        bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(n)]
+        sink = torch.empty(gq8.gq8_read_probe_sink_floats(nbytes), dtype=torch.float32, device=dev)
+        us = timed(lambda i: (lambda s, b=bufs[i % n]: gq8.gq8_read_probe(b, nbytes, sink, s)), n)
+        emit({"workload": "read probe", "bytes": nbytes, "us_per_call": round(us, 3),
+              "GBps": round(nbytes / us / 1e3, 1)})
+        del bufs
+
+    # Q8_0 GEMV N=1024 K=4096, T sweep
+    d = synth.q8_0_gemv_inputs(T=16)
+    w0 = q8_0_from_f32(to_dev(d["w"]))
+    n = n_sets_for(w0.numel())
+    ws_ = [w0] + [w0.clone() for _ in range(n - 1)]
+    for T in (1, 2, 4, 8, 16):
+        x = to_dev(np.ascontiguousarray(d["x"][:T]))
+        y = torch.empty((T, 1024), dtype=torch.float32, device=dev)
+        nb = gq8.gq8_workspace_bytes(gq8.OP_Q8_0_GEMV, T, 1024, 4096)
+        wsp = workspace(nb)
+        us = timed(lambda i, T=T, x=x, y=y, nb=nb, wsp=wsp: (
+            lambda s, w=ws_[i % n]: gq8.gq8_q8_0_gemv(w, x, y, T, 1024, 4096, wsp, nb, s)), n)
+        emit({"workload": "Q8_0 GEMV N=1024 K=4096", "T": T, "us_per_call": round(us, 3),
+              "weight_GBps": round(w0.numel() / us / 1e3, 1)})
+    del ws_
+
+    # W8A8
+    for (M, N, K) in [(16, 1536, 4096)] + [(m, 2560, 4096) for m in (1, 4, 8, 16, 32)] + \
+                     [(m, 4096, 2048) for m in (1, 4, 8, 16, 32)]:
+        dd = synth.w8a8_inputs(M, N, K)
+        wp0 = torch.empty(gq8.gq8_w8a8_packed_bytes(K, N), dtype=torch.int8, device=dev)
+        gq8.gq8_w8a8_pack(to_dev(dd["W"]), K, N, wp0)
+        n = n_sets_for(wp0.numel())
+        wps = [wp0] + [wp0.clone() for _ in range(n - 1)]
+        xq, xs, wsc = to_dev(dd["xq"]), to_dev(dd["x_scale"]), to_dev(dd["w_scale"])
+        out = torch.empty((M, N), dtype=torch.int16, device=dev)
+        nb = gq8.gq8_workspace_bytes(gq8.OP_W8A8, M, N, K)
+        wsp = workspace(nb)
+        us = timed(lambda i: (lambda s, w=wps[i % n]: gq8.gq8_w8a8_gemm(xq, xs, w, wsc, out, M, N, K, wsp, nb, s)), n)
+        emit({"workload": "W8A8", "M": M, "N": N, "K": K, "us_per_call": round(us, 3),
+              "weight_GBps": round(N * K / us / 1e3, 1)})
+        del wps
+
+    # routed MoE: 512 experts, T=4, top-8, D=2048, F=512
+    T, E, topk, D, F = 4, 512, 8, 2048, 512
+    gu_b, dn_b = gq8.gq8_q8_0_bytes(2 * F, D), gq8.gq8_q8_0_bytes(D, F)
+    agu = torch.empty(E * gu_b, dtype=torch.uint8, device=dev)
+    adn = torch.empty(E * dn_b, dtype=torch.uint8, device=dev)
+    for e in range(E):
+        w = synth.moe_expert_weights(e, D=D, F=F)
+        gq8.gq8_q8_0_quantize(to_dev(w["gate_up"]), 2 * F, D, agu[e * gu_b:(e + 1) * gu_b])
+        gq8.gq8_q8_0_quantize(to_dev(w["down"]), D, F, adn[e * dn_b:(e + 1) * dn_b])
+    n = 8
+    agus = [agu] + [agu.clone() for _ in range(n - 1)]
+    adns = [adn] + [adn.clone() for _ in range(n - 1)]
+    inp = synth.moe_inputs(T=T, E=E, D=D)
+    ids = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, topk), dtype=torch.float32, device=dev)
+    gq8.gq8_moe_route(to_dev(inp["logits"]), T, E, topk, ids, wts)
+    xq = torch.empty((T, D), dtype=torch.int8, device=dev)
+    xd = torch.empty((T, D // 32), dtype=torch.int16, device=dev)
+    gq8.gq8_q8_1_quantize(to_dev(inp["x"]), T, D, xq, xd, None)
+    nb = gq8.gq8_moe_workspace_bytes(T, topk, D, F)
+    wsp = torch.empty(nb, dtype=torch.uint8, device=dev)
+    out = torch.empty((T, D), dtype=torch.int16, device=dev)
+    U = len(set(to_host_ids(ids)))
+    us = timed(lambda i: (lambda s, a=agus[i % n], b=adns[i % n]: gq8.gq8_moe_q8_0_routed(
+        xq, xd, ids, wts, a, b, out, T, topk, E, D, F, wsp, nb, s)), n, reps=50)
+    emit({"workload": "routed MoE T=4 E=512 top-8 D=2048 F=512", "unique_experts": U,
+          "us_per_call": round(us, 3), "weight_GBps": round(U * (gu_b + dn_b) / us / 1e3, 1)})
+
+    if report:
+        os.makedirs(os.path.dirname(report) or ".", exist_ok=True)
+        with open(report, "w") as f:
+            for d in lines:
+                f.write(json.dumps(d) + "\n")
+
+
+def to_host_ids(ids):
+    return ids.cpu().numpy().ravel().tolist()
+
+
+# ------------------------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=42)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all-configs", action="store_true")
+    ap.add_argument("--report", default="gpurun_out/bench_all.jsonl")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also launch one device copy of this many MiB (for scaling PMC byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU sharding is described, not run", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gemm_q8_amd import gq8, synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    log(f"[bench] device {torch.cuda.get_device_name(0)}, {gq8.gq8_device_cus()} CUs; lib {gq8.LIB_PATH}")
+
+    h = setup_hc(torch, gq8, synth, dev)
+    steps_per_graph = h["n_sets"] // len(TS)
+    log(f"[bench] HC workload: {h['n_sets']} weight sets x {h['pair_bytes']} B, {steps_per_graph} steps per graph")
+    gs = GraphSteps(torch, stream, hc_step_fns(gq8, h), steps_per_graph)
+    gs.prepare(args.warmup).prepare(args.steps)
+
+    # warmup, then exactly K timed steps bracketed by synchronizations
+    gs.run(args.warmup)
+    torch.cuda.synchronize()
+    t = time_region(torch, stream, lambda: gs.run(args.steps))
+    torch.cuda.synchronize()
+    step_bytes = len(TS) * h["pair_bytes"]
+    value = step_bytes * args.steps / t / 1e9
+    ms_per_step = t / args.steps * 1e3
+    log(f"[bench] {args.steps} steps in {t * 1e3:.3f} ms: {ms_per_step * 1e3:.2f} us/step, {value:.1f} GB/s")
+
+    # per-T pair time and per-kernel launch durations (same launches, isolated graphs)
+    n = h["n_sets"]
+    per_call = {}
+    kern = {}
+    reps = 20
+    for T in TS:
+        pair = GraphSteps(torch, stream, lambda i, T=T: [hc_down_fn(gq8, h, T, i), hc_up_fn(gq8, h, T, i)], n)
+        pair.run(n)
+        tp = time_region(torch, stream, lambda: pair.run(n * reps))
+        per_call[f"T{T}"] = round(tp / (n * reps) * 1e6, 3)
+        for kind, mk in (("down", hc_down_fn), ("up", hc_up_fn)):
+            g = GraphSteps(torch, stream, lambda i, T=T, mk=mk: [mk(gq8, h, T, i)], n)
+            g.run(n)
+            tk = time_region(torch, stream, lambda: g.run(n * reps))
+            k = kern.setdefault(kind, {"t": 0.0, "bytes": 0, "launches": 0})
+            k["t"] += tk
+            k["bytes"] += hc_kernel_bytes(kind, T) * n * reps
+            k["launches"] += n * reps
+    dom = max(kern, key=lambda k: kern[k]["t"] / kern[k]["launches"])
+    kd = kern[dom]
+    avg_us = kd["t"] / kd["launches"] * 1e6
+    achieved = kd["bytes"] / kd["t"] / 1e9
+    log(f"[bench] per-call pair us {per_call}; kernels: " + ", ".join(
+        f"{k} {v['t'] / v['launches'] * 1e6:.3f} us/launch" for k, v in kern.items()))
+
+    if args.copy_probe_mib:
+        nbytes = args.copy_probe_mib << 20
+        a = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        with torch.cuda.stream(stream):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {nbytes} bytes read + {nbytes} written")
+
+    page_pair = sum(PAGE_US[T] for T in TS)
+    page_gbs = step_bytes / (page_pair * 1e-6) / 1e9
+    result = {
+        "metric": "achieved HBM GB/s (weight bytes/us) and us/call, Q8_0 & W8A8 decode, T=1..16",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / page_gbs, 3),
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "fused RMSNorm + Q8_0 hyper-connection down read [320 x 16384] and Q8_0 up "
+                        "read [16384 x 320], T in {1,4,6}",
+            "T": list(TS),
+            "weight_bytes_per_step": step_bytes,
+            "weight_sets_rotated": h["n_sets"],
+            "hipgraph": True,
+            "us_per_pair": per_call,
+            "baseline_note": "vs_baseline divides by the HC-Q8 page's Arc Pro B70 Q8_0 read times "
+                             "(24.7/29.3/34.4 us at T=1/4/6): another machine, context only",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": f"hc_{dom}",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(avg_us, 3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(synth, args.cpu_seconds)
+    if args.all_configs:
+        bench_other_configs(torch, gq8, synth, dev, stream, args.report)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,301 @@
+// C ABI of libgq8.so: argument checks, dispatch to the kernel launchers, workspace sizing.
+// Every entry point validates before enqueueing anything and never allocates or synchronizes.
+#include <string.h>
+
+#include "gq8_internal.h"
+
+using namespace gq8;
+
+namespace gq8 {
+
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return 0;
+    if (dev < 64) cached[dev] = prop.multiProcessorCount;
+    return prop.multiProcessorCount;
+}
+
+}  // namespace gq8
+
+static inline hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
+
+static int check_ws(void* ws, size_t ws_bytes, size_t need) {
+    if (need == 0) return GQ8_OK;
+    if (ws == nullptr || ws_bytes < need) return GQ8_EWORKSPACE;
+    if (!aligned16(ws)) return GQ8_EALIGN;
+    return GQ8_OK;
+}
+
+GQ8_EXPORT const char* gq8_status_str(int st) {
+    switch (st) {
+        case GQ8_OK: return "ok";
+        case GQ8_EINVAL: return "invalid argument";
+        case GQ8_ESHAPE: return "unsupported shape";
+        case GQ8_EALIGN: return "misaligned pointer";
+        case GQ8_EWORKSPACE: return "workspace missing or too small";
+        case GQ8_ECAPTURE: return "stream is capturing";
+        case GQ8_EHIP: return "HIP error";
+        case GQ8_ENODEV: return "no gfx950 device";
+        default: return "unknown status";
+    }
+}
+
+GQ8_EXPORT int gq8_abi_version(void) { return GQ8_ABI_VERSION; }
+
+GQ8_EXPORT int gq8_device_cus(int* cus_out) {
+    if (cus_out == nullptr) return GQ8_EINVAL;
+    const int c = device_cus();
+    *cus_out = c;
+    return c > 0 ? GQ8_OK : GQ8_ENODEV;
+}
+
+// ---------------------------------------------------------------------------------- Q8_0 layout
+
+GQ8_EXPORT size_t gq8_q8_0_bytes(int64_t rows, int64_t K) {
+    if (rows < 0 || K < 0 || K % 32 != 0) return 0;
+    return (size_t)rows * (size_t)K + (size_t)rows * (size_t)(K / 32) * 2;
+}
+
+GQ8_EXPORT int gq8_q8_0_quantize(const float* w, int rows, int K, void* w_split, void* stream) {
+    if (rows < 0 || K < 0) return GQ8_EINVAL;
+    if (K % 32 != 0) return GQ8_ESHAPE;
+    if (rows == 0 || K == 0) return GQ8_OK;
+    if (w == nullptr || w_split == nullptr) return GQ8_EINVAL;
+    if (!aligned16(w) || !aligned16(w_split)) return GQ8_EALIGN;
+    if (device_cus() == 0) return GQ8_ENODEV;
+    return launch_q8_0_quantize(w, rows, K, w_split, S(stream));
+}
+
+GQ8_EXPORT int gq8_q8_0_split_from_blocks(const void* blocks34, int rows, int K, void* w_split,
+                                          void* stream) {
+    if (rows < 0 || K < 0) return GQ8_EINVAL;
+    if (K % 32 != 0) return GQ8_ESHAPE;
+    if (rows == 0 || K == 0) return GQ8_OK;
+    if (blocks34 == nullptr || w_split == nullptr) return GQ8_EINVAL;
+    if (!aligned16(w_split)) return GQ8_EALIGN;
+    if (device_cus() == 0) return GQ8_ENODEV;
+    return launch_q8_0_split_from_blocks(blocks34, rows, K, w_split, S(stream));
+}
+
+GQ8_EXPORT int gq8_q8_1_quantize(const uint16_t* x_bf16, int rows, int K, int8_t* q, uint16_t* d,
+                                 uint16_t* s, void* stream) {
+    if (rows < 0 || K < 0) return GQ8_EINVAL;
+    if (K % 32 != 0) return GQ8_ESHAPE;
+    if (rows == 0 || K == 0) return GQ8_OK;
+    if (x_bf16 == nullptr || q == nullptr || d == nullptr) return GQ8_EINVAL;
+    if (device_cus() == 0) return GQ8_ENODEV;
+    return launch_q8_1_quantize(x_bf16, rows, K, q, d, s, S(stream));
+}
+
+// ---------------------------------------------------------------------------------- workspace
+
+static bool q8_shape_ok(int T, int N, int K) {
+    return T >= 0 && T <= kMaxT && N >= 0 && K >= 0 && K % 32 == 0;
+}
+
+GQ8_EXPORT size_t gq8_workspace_counter_bytes(int op, int rows, int N, int K) {
+    (void)op; (void)rows; (void)N; (void)K;
+    return 0;   // no operation keeps arrival counters: split sums are combined by a second kernel
+}
+
+GQ8_EXPORT size_t gq8_workspace_bytes(int op, int rows, int N, int K) {
+    switch (op) {
+        case GQ8_OP_HC_DOWN:
+            if (!q8_shape_ok(rows, N, K) || rows == 0 || N == 0 || K == 0) return 0;
+            return hc_down_workspace_bytes(rows, N, K);
+        case GQ8_OP_Q8_0_GEMV:
+        case GQ8_OP_HC_UP:
+        case GQ8_OP_W8A8:
+        default:
+            return 0;
+    }
+}
+
+GQ8_EXPORT int gq8_workspace_init(void* ws, size_t bytes, void* stream) {
+    if (bytes == 0) return GQ8_OK;
+    if (ws == nullptr) return GQ8_EINVAL;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(S(stream), &cs) != hipSuccess) return GQ8_EHIP;
+    if (cs != hipStreamCaptureStatusNone) return GQ8_ECAPTURE;
+    if (device_cus() == 0) return GQ8_ENODEV;
+    return launch_fill_zero(ws, bytes, S(stream));
+}
+
+// ---------------------------------------------------------------------------------- Q8_0 reads
+
+GQ8_EXPORT int gq8_q8_0_gemv(const void* w_split, const float* x, float* y, int T, int N, int K,
+                             void* ws, size_t ws_bytes, void* stream) {
+    (void)ws; (void)ws_bytes;
+    if (T < 0 || N < 0 || K < 0) return GQ8_EINVAL;
+    if (!q8_shape_ok(T, N, K)) return GQ8_ESHAPE;
+    if (T == 0 || N == 0) return GQ8_OK;
+    if (y == nullptr) return GQ8_EINVAL;
+    if (K == 0) {
+        if (device_cus() == 0) return GQ8_ENODEV;
+        return launch_fill_zero(y, (size_t)T * N * sizeof(float), S(stream));
+    }
+    if (w_split == nullptr || x == nullptr) return GQ8_EINVAL;
+    if (!aligned16(w_split) || !aligned16(x)) return GQ8_EALIGN;
+    if (device_cus() == 0) return GQ8_ENODEV;
+    GemvArgs a{};
+    a.q = static_cast<const int8_t*>(w_split);
+    a.d = reinterpret_cast<const uint16_t*>(a.q + (size_t)N * K);
+    a.x = x; a.T = T; a.N = N; a.K = K; a.out = y;
+    return launch_q8_0_gemv(a, S(stream));
+}
+
+GQ8_EXPORT int gq8_hc_q8_down(const void* w_split, const uint16_t* R, const uint16_t* w_norm,
+                              float eps, uint16_t* lo, float* rs_out, int T, int N, int K,
+                              void* ws, size_t ws_bytes, void* stream) {
+    if (T < 0 || N < 0 || K < 0) return GQ8_EINVAL;
+    if (!q8_shape_ok(T, N, K) || K == 0) return GQ8_ESHAPE;
+    if (T == 0 || N == 0) return GQ8_OK;
+    if (w_split == nullptr || R == nullptr || w_norm == nullptr || lo == nullptr) return GQ8_EINVAL;
+    if (!aligned16(R) || !aligned16(w_norm) || !aligned16(w_split)) return GQ8_EALIGN;
+    if (!(eps >= 0.f)) return GQ8_EINVAL;
+    int rc = check_ws(ws, ws_bytes, hc_down_workspace_bytes(T, N, K));
+    if (rc != GQ8_OK) return rc;
+    if (device_cus() == 0) return GQ8_ENODEV;
+    GemvArgs a{};
+    a.q = static_cast<const int8_t*>(w_split);
+    a.d = reinterpret_cast<const uint16_t*>(a.q + (size_t)N * K);
+    a.x = R; a.wnorm = w_norm; a.T = T; a.N = N; a.K = K; a.out = lo; a.rs_out = rs_out; a.eps = eps;
+    return launch_hc_down(a, ws, S(stream));
+}
+
+GQ8_EXPORT int gq8_hc_q8_up(const void* w_split, const uint16_t* lo, uint16_t* out, int T, int N,
+                            int K, void* ws, size_t ws_bytes, void* stream) {
+    (void)ws; (void)ws_bytes;
+    if (T < 0 || N < 0 || K < 0) return GQ8_EINVAL;
+    if (!q8_shape_ok(T, N, K) || K > 1024) return GQ8_ESHAPE;
+    if (T == 0 || N == 0) return GQ8_OK;
+    if (out == nullptr) return GQ8_EINVAL;
+    if (K == 0) {
+        if (device_cus() == 0) return GQ8_ENODEV;
+        return launch_fill_zero(out, (size_t)T * N * sizeof(uint16_t), S(stream));
+    }
+    if (w_split == nullptr || lo == nullptr) return GQ8_EINVAL;
+    if (!aligned16(w_split) || !aligned16(lo)) return GQ8_EALIGN;
+    if (device_cus() == 0) return GQ8_ENODEV;
+    GemvArgs a{};
+    a.q = static_cast<const int8_t*>(w_split);
+    a.d = reinterpret_cast<const uint16_t*>(a.q + (size_t)N * K);
+    a.x = lo; a.T = T; a.N = N; a.K = K; a.out = out;
+    return launch_hc_up(a, S(stream));
+}
+
+// ---------------------------------------------------------------------------------- W8A8
+
+GQ8_EXPORT size_t gq8_w8a8_packed_bytes(int K, int N) {
+    if (K < 0 || N < 0) return 0;
+    return (size_t)((N + 15) / 16) * 16 * (size_t)((K + 63) / 64) * 64;
+}
+
+GQ8_EXPORT int gq8_w8a8_pack(const int8_t* W, int K, int N, int8_t* W_packed, void* stream) {
+    if (K < 0 || N < 0) return GQ8_EINVAL;
+    if (K % 16 != 0) return GQ8_ESHAPE;
+    if (K == 0 || N == 0) return GQ8_OK;
+    if (W == nullptr || W_packed == nullptr) return GQ8_EINVAL;
+    if (!aligned16(W_packed)) return GQ8_EALIGN;
+    if (device_cus() == 0) return GQ8_ENODEV;
+    return launch_w8a8_pack(W, K, N, W_packed, S(stream));
+}
+
+static int w8a8_common(const int8_t* xq, const float* xs, const int8_t* wp, const float* wsc,
+                       void* out, bool i32, int M, int N, int K, void* stream) {
+    if (M < 0 || N < 0 || K < 0) return GQ8_EINVAL;
+    if (M > kMaxM || K % 16 != 0 || K > kW8MaxK) return GQ8_ESHAPE;
+    if (M == 0 || N == 0) return GQ8_OK;
+    if (out == nullptr) return GQ8_EINVAL;
+    if (K == 0) {
+        if (device_cus() == 0) return GQ8_ENODEV;
+        return launch_fill_zero(out, (size_t)M * N * (i32 ? 4 : 2), S(stream));
+    }
+    if (xq == nullptr || wp == nullptr || (!i32 && (xs == nullptr || wsc == nullptr))) return GQ8_EINVAL;
+    if (!aligned16(xq) || !aligned16(wp)) return GQ8_EALIGN;
+    if (device_cus() == 0) return GQ8_ENODEV;
+    return launch_w8a8(plan_w8a8(M, N, K), xq, xs, wp, wsc, out, i32, M, N, K, S(stream));
+}
+
+GQ8_EXPORT int gq8_w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* W_packed,
+                             const float* w_scale, uint16_t* out, int M, int N, int K, void* ws,
+                             size_t ws_bytes, void* stream) {
+    (void)ws; (void)ws_bytes;
+    return w8a8_common(xq, x_scale, W_packed, w_scale, out, false, M, N, K, stream);
+}
+
+GQ8_EXPORT int gq8_w8a8_gemm_i32(const int8_t* xq, const int8_t* W_packed, int32_t* acc, int M,
+                                 int N, int K, void* ws, size_t ws_bytes, void* stream) {
+    (void)ws; (void)ws_bytes;
+    return w8a8_common(xq, nullptr, W_packed, nullptr, acc, true, M, N, K, stream);
+}
+
+// ---------------------------------------------------------------------------------- MoE
+
+GQ8_EXPORT int gq8_moe_route(const float* logits, int T, int E, int topk, int32_t* ids,
+                             float* weights, void* stream) {
+    if (T < 0 || E < 0 || topk < 0) return GQ8_EINVAL;
+    if (T == 0) return GQ8_OK;
+    if (topk < 1 || topk > 16 || E < topk || E > 4096) return GQ8_ESHAPE;
+    if (logits == nullptr || ids == nullptr || weights == nullptr) return GQ8_EINVAL;
+    if (device_cus() == 0) return GQ8_ENODEV;
+    return launch_moe_route(logits, T, E, topk, ids, weights, S(stream));
+}
+
+GQ8_EXPORT size_t gq8_moe_plan_words(int T, int topk) {
+    if (T < 0 || topk < 0) return 0;
+    return 1 + 4 * (size_t)T * topk;
+}
+
+GQ8_EXPORT int gq8_moe_plan(const int32_t* ids, int T, int topk, int E, int32_t* plan,
+                            void* stream) {
+    if (T < 0 || topk < 0 || E < 0) return GQ8_EINVAL;
+    if (T * topk > 256 || (T > 0 && topk < 1)) return GQ8_ESHAPE;
+    if (T == 0) return GQ8_OK;
+    if (ids == nullptr || plan == nullptr) return GQ8_EINVAL;
+    if (device_cus() == 0) return GQ8_ENODEV;
+    return launch_moe_plan(ids, T, topk, E, plan, S(stream));
+}
+
+GQ8_EXPORT size_t gq8_moe_workspace_bytes(int T, int topk, int D, int F) {
+    if (T < 1 || topk < 1 || D < 1 || F < 1) return 0;
+    return moe_workspace_bytes(T, topk, D, F);
+}
+
+GQ8_EXPORT int gq8_moe_q8_0_routed(const int8_t* xq, const uint16_t* xd, const int32_t* ids,
+                                   const float* weights, const void* w_gate_up, const void* w_down,
+                                   uint16_t* out, int T, int topk, int E, int D, int F, void* ws,
+                                   size_t ws_bytes, void* stream) {
+    if (T < 0 || topk < 0 || E < 0 || D < 0 || F < 0) return GQ8_EINVAL;
+    if (T == 0) return GQ8_OK;
+    if (T > kMaxT || topk < 1 || T * topk > 256 || E < 1 || D < 32 || D % 32 != 0 || F < 32 ||
+        F % 32 != 0 || F > 1024)
+        return GQ8_ESHAPE;
+    if (xq == nullptr || xd == nullptr || ids == nullptr || weights == nullptr ||
+        w_gate_up == nullptr || w_down == nullptr || out == nullptr)
+        return GQ8_EINVAL;
+    if (!aligned16(xq) || !aligned16(w_gate_up) || !aligned16(w_down)) return GQ8_EALIGN;
+    int rc = check_ws(ws, ws_bytes, moe_workspace_bytes(T, topk, D, F));
+    if (rc != GQ8_OK) return rc;
+    if (device_cus() == 0) return GQ8_ENODEV;
+    return launch_moe_routed(xq, xd, ids, weights, w_gate_up, w_down, out, T, topk, E, D, F, ws,
+                             S(stream));
+}
+
+// ---------------------------------------------------------------------------------- probe
+
+GQ8_EXPORT size_t gq8_read_probe_sink_floats(size_t bytes) { return read_probe_blocks(bytes); }
+
+GQ8_EXPORT int gq8_read_probe(const void* src, size_t bytes, float* sink, void* stream) {
+    if (bytes % 16 != 0) return GQ8_ESHAPE;
+    if (bytes == 0) return GQ8_OK;
+    if (src == nullptr || sink == nullptr) return GQ8_EINVAL;
+    if (!aligned16(src)) return GQ8_EALIGN;
+    if (device_cus() == 0) return GQ8_ENODEV;
+    return launch_read_probe(src, bytes, sink, S(stream));
+}

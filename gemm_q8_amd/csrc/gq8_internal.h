@@ -1,0 +1,90 @@
+// Host-side internals shared by the gq8 translation units (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/gq8.h"
+
+#define GQ8_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace gq8 {
+
+constexpr int kMaxT = 16;        // token rows of the Q8_0 reads
+constexpr int kMaxM = 32;        // rows of the W8A8 product
+constexpr int kW8MaxK = 8192;    // W8A8 depth: 16 waves x 8 k-steps of 64
+constexpr size_t kCounterAlign = 256;
+
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Launch status -> gq8 status (clears the sticky launch error).
+inline int launch_status() { return hipGetLastError() == hipSuccess ? GQ8_OK : GQ8_EHIP; }
+
+// CU count of the current device (cached per device id). 0 when there is no device.
+int device_cus();
+
+// ---------------------------------------------------------------- Q8_0 read family
+
+struct GemvArgs {
+    const int8_t* q;        // split layout: quants [N][K]
+    const uint16_t* d;      //               scales [N][K/32] (fp16 bits)
+    const void* x;          // fp32 [T][K] (GEMV), bf16 R [T][K] (down), bf16 lo [T][K] (up)
+    const uint16_t* wnorm;  // bf16 [K] (down)
+    int T, N, K;
+    int S;                  // down: K slabs
+    float* part;            // down: [S][T][N] fp32 partial sums
+    float* ssq;             // down: [S][T] partial sums of squares
+    void* out;              // fp32 y [T][N] or bf16 [T][N]
+    float* rs_out;          // fp32 [T] (down, nullable)
+    float eps;
+};
+
+// Q8_0 GEMV (fp32 x): one work-group per RW rows, all of K, no workspace.
+int launch_q8_0_gemv(GemvArgs a, hipStream_t st);
+
+// fused RMSNorm + Q8_0 down read: MFMA partial kernel over K slabs, then a combine kernel.
+constexpr int kDownSlab = 128;                 // columns per slab (4 Q8_0 blocks)
+inline int hc_down_slabs(int K) { return (K + kDownSlab - 1) / kDownSlab; }
+size_t hc_down_workspace_bytes(int T, int N, int K);
+int launch_hc_down(GemvArgs a, void* ws, hipStream_t st);
+
+// Q8_0 up read (bf16 x, K <= 1024): MFMA, one wave per 32 output rows, no workspace.
+int launch_hc_up(GemvArgs a, hipStream_t st);
+
+// ---------------------------------------------------------------- W8A8
+
+struct W8Plan {
+    bool mfma;         // int8 MFMA path (M >= 16) or VALU dot4 path
+    int ntiles;        // N rounded up to 16, / 16: one work-group each
+    int ksteps;        // K rounded up to 64, / 64
+    int nw;            // waves per work-group (<= 16)
+    int kpw;           // k-steps per wave
+};
+W8Plan plan_w8a8(int M, int N, int K);
+int launch_w8a8(const W8Plan& p, const int8_t* xq, const float* xs, const int8_t* wp,
+                const float* ws_scale, void* out, bool i32_out, int M, int N, int K, hipStream_t st);
+
+// ---------------------------------------------------------------- small kernels
+
+int launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+int launch_q8_0_quantize(const float* w, int rows, int K, void* w_split, hipStream_t st);
+int launch_q8_0_split_from_blocks(const void* b34, int rows, int K, void* w_split, hipStream_t st);
+int launch_q8_1_quantize(const uint16_t* x, int rows, int K, int8_t* q, uint16_t* d, uint16_t* s,
+                         hipStream_t st);
+int launch_w8a8_pack(const int8_t* W, int K, int N, int8_t* Wp, hipStream_t st);
+int launch_read_probe(const void* src, size_t bytes, float* sink, hipStream_t st);
+size_t read_probe_blocks(size_t bytes);
+
+// ---------------------------------------------------------------- MoE
+
+int launch_moe_route(const float* logits, int T, int E, int topk, int32_t* ids, float* w,
+                     hipStream_t st);
+int launch_moe_plan(const int32_t* ids, int T, int topk, int E, int32_t* plan, hipStream_t st);
+size_t moe_workspace_bytes(int T, int topk, int D, int F);
+int launch_moe_routed(const int8_t* xq, const uint16_t* xd, const int32_t* ids, const float* w,
+                      const void* wgu, const void* wdn, uint16_t* out, int T, int topk, int E,
+                      int D, int F, void* ws, hipStream_t st);
+
+}  // namespace gq8

@@ -1,0 +1,425 @@
+// Routed experts with Q8_0 weights and a q8_1 input (EP page, "What changed": the q8_1 MoE input,
+// a device plan grouping the routed entries by expert, one row per entry written into a rows
+// buffer, then the single-card combine; defer page, "What it changes": rows combined weighted by
+// their routing weight).
+//
+// Kernels, in stream order:
+//   plan     one work-group: entries sorted by (expert, entry); distinct experts -> slots
+//   gate/up  grid (row pairs, slots): each slot's expert weights are read once for all of its
+//            tokens; per 32-block integer dots (v_dot4_i32_i8) of weight quants with the q8_1
+//            quants, scaled by both block scales; h = SiLU(gate) * up -> h[entry][F] fp32
+//   down     grid (row tiles, slots): rows of K = F bytes, lane groups per row as in the short
+//            Q8_0 read; h in registers; rows[entry][D] fp32
+//   combine  out[t] = bf16( sum_j w[t][j] * rows[t*topk + j] ), slots j in order
+// Experts that no token routes to are never read.
+#include "gq8_device.h"
+#include "gq8_internal.h"
+
+namespace gq8 {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------------------------ routing
+
+GQ8_DEV float block_sum_256(float v, float* red) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    return ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+GQ8_DEV float block_max_256(float v, float* red) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// better = larger value, then lower index
+GQ8_DEV bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
+
+__global__ void __launch_bounds__(256) moe_route_kernel(const float* __restrict__ logits, int E,
+                                                        int topk, int32_t* __restrict__ ids,
+                                                        float* __restrict__ wout) {
+    extern __shared__ float sl[];                       // E logits, then E selection flags
+    int* sel = reinterpret_cast<int*>(sl + E);
+    __shared__ float red[4];
+    __shared__ float rv[4];
+    __shared__ int ri[4];
+    const int t = blockIdx.x;
+    const float* l = logits + (size_t)t * E;
+    for (int i = threadIdx.x; i < E; i += 256) {
+        sl[i] = l[i];
+        sel[i] = 0;
+    }
+    __syncthreads();
+    float mx = -INFINITY;
+    for (int i = threadIdx.x; i < E; i += 256) mx = fmaxf(mx, sl[i]);
+    mx = block_max_256(mx, red);
+    float sum = 0.f;
+    for (int i = threadIdx.x; i < E; i += 256) sum += expf(sl[i] - mx);
+    sum = block_sum_256(sum, red);
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int j = 0; j < topk; ++j) {
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+        for (int i = threadIdx.x; i < E; i += 256)
+            if (!sel[i] && better(sl[i], i, bv, bi)) { bv = sl[i]; bi = i; }
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float ov = __shfl_xor(bv, o, 64);
+            const int oi = __shfl_xor(bi, o, 64);
+            if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+        }
+        if (lane == 0) { rv[wave] = bv; ri[wave] = bi; }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float b = rv[0];
+            int bidx = ri[0];
+            for (int w = 1; w < 4; ++w)
+                if (better(rv[w], ri[w], b, bidx)) { b = rv[w]; bidx = ri[w]; }
+            const bool ok = bidx >= 0 && bidx < E;          // false only for NaN logits
+            ids[(size_t)t * topk + j] = ok ? bidx : -1;
+            wout[(size_t)t * topk + j] = ok ? expf(b - mx) / sum : 0.f;
+            if (ok) sel[bidx] = 1;
+        }
+        __syncthreads();
+    }
+}
+
+int launch_moe_route(const float* logits, int T, int E, int topk, int32_t* ids, float* w,
+                     hipStream_t st) {
+    const size_t lds = (size_t)E * (sizeof(float) + sizeof(int));
+    hipLaunchKernelGGL(moe_route_kernel, dim3(T), dim3(256), lds, st, logits, E, topk, ids, w);
+    return launch_status();
+}
+
+// ------------------------------------------------------------------------------------ plan
+
+// Device plan (layout documented with gq8_moe_plan). P = T*topk <= 256 entries.
+GQ8_DEV void build_plan(const int32_t* ids, int P, int E, int32_t* plan) {
+    __shared__ int sid[256];
+    __shared__ int sorted[256];
+    __shared__ int first[256];
+    __shared__ int s_bad, s_u;
+    const int tid = threadIdx.x;
+    if (tid == 0) { s_bad = 0; s_u = 0; }
+    __syncthreads();
+    if (tid < P) {
+        const int e = ids[tid];
+        sid[tid] = e;
+        if (e < 0 || e >= E) atomicOr(&s_bad, 1);
+    }
+    __syncthreads();
+    if (s_bad) {
+        if (tid == 0) plan[0] = -1;
+        if (tid < P) {
+            plan[1 + tid] = -1;
+            plan[1 + P + tid] = 0;
+            plan[1 + 2 * P + tid] = P;
+            plan[1 + 3 * P + tid] = -1;
+        }
+        return;
+    }
+    if (tid < P) {
+        const int key = sid[tid];
+        int rank = 0;
+        for (int j = 0; j < P; ++j) rank += (sid[j] < key) || (sid[j] == key && j < tid);
+        sorted[rank] = tid;
+    }
+    __syncthreads();
+    if (tid < P) {
+        first[tid] = (tid == 0) || (sid[sorted[tid]] != sid[sorted[tid - 1]]);
+        if (first[tid]) atomicAdd(&s_u, 1);
+    }
+    __syncthreads();
+    const int U = s_u;
+    if (tid == 0) plan[0] = U;
+    if (tid < P) {
+        int u = -1;
+        for (int j = 0; j <= tid; ++j) u += first[j];
+        plan[1 + 3 * P + tid] = sorted[tid];
+        if (first[tid]) {
+            int c = 1;
+            while (tid + c < P && !first[tid + c]) ++c;
+            plan[1 + u] = sid[sorted[tid]];
+            plan[1 + P + u] = c;
+            plan[1 + 2 * P + u] = tid;
+        }
+        if (tid >= U) {
+            plan[1 + tid] = -1;
+            plan[1 + P + tid] = 0;
+            plan[1 + 2 * P + tid] = P;
+        }
+    }
+}
+
+__global__ void __launch_bounds__(256) moe_plan_kernel(const int32_t* ids, int P, int E, int32_t* plan) {
+    build_plan(ids, P, E, plan);
+}
+
+int launch_moe_plan(const int32_t* ids, int T, int topk, int E, int32_t* plan, hipStream_t st) {
+    hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(256), 0, st, ids, T * topk, E, plan);
+    return launch_status();
+}
+
+// ------------------------------------------------------------------------------------ experts
+
+struct MoeArgs {
+    const int8_t* xq;       // [T][D]
+    const uint16_t* xd;     // [T][D/32]
+    const float* w;         // routing weights [T][topk]
+    const int8_t* wgu;      // gate/up arena
+    const int8_t* wdn;      // down arena
+    size_t gu_bytes, dn_bytes;
+    uint16_t* out;          // [T][D]
+    int T, topk, P, E, D, F;
+    const int32_t* plan;
+    float* h;               // [P][F]
+    float* rows;            // [P][D]
+};
+
+constexpr int kGuRpw = 2;    // gate/up row pairs per wave
+
+// Gate/up: each wave owns kGuRpw row pairs (gate row n, up row F + n) of one routed expert and
+// all of D; a lane reads 16 columns per 1024-column chunk. Loads of a chunk batch (weights,
+// scales and the entries' q8_1 quants) are issued together, clamped, before any arithmetic.
+template <int CMAX>
+__global__ void __launch_bounds__(256) moe_gate_up_kernel(MoeArgs a) {
+    constexpr int KB = CMAX <= 4 ? 2 : 1;          // 1024-column chunks per load batch
+    const int slot = blockIdx.y;
+    const int U = a.plan[0];
+    if (slot >= U) return;
+    const int P = a.P, D = a.D, F = a.F;
+    const int e = a.plan[1 + slot];
+    const int c = a.plan[1 + P + slot];
+    const int st = a.plan[1 + 2 * P + slot];
+    const int8_t* q = a.wgu + (size_t)e * a.gu_bytes;
+    const uint16_t* d = reinterpret_cast<const uint16_t*>(q + (size_t)2 * F * D);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int pr0 = (blockIdx.x * 4 + wave) * kGuRpw;
+    const int nblk = D >> 5;
+
+    // entries in chunks of CMAX (an expert has at most T entries when each token routes to
+    // distinct experts, so one chunk in practice; more chunks re-read the weights)
+    for (int cb = 0; cb < c; cb += CMAX) {
+        const int cn = c - cb < CMAX ? c - cb : CMAX;
+        int ent[CMAX], tok[CMAX];
+#pragma unroll
+        for (int ci = 0; ci < CMAX; ++ci) {
+            ent[ci] = a.plan[1 + 3 * P + st + cb + (ci < cn ? ci : 0)];
+            tok[ci] = ent[ci] / a.topk;
+        }
+        float ag[kGuRpw][CMAX], au[kGuRpw][CMAX];
+#pragma unroll
+        for (int r = 0; r < kGuRpw; ++r)
+#pragma unroll
+            for (int ci = 0; ci < CMAX; ++ci) { ag[r][ci] = 0.f; au[r][ci] = 0.f; }
+
+        for (int k0 = 0; k0 < D; k0 += 1024 * KB) {
+            v4i qg[kGuRpw][KB], qu[kGuRpw][KB], xv[CMAX][KB];
+            uint16_t dg[kGuRpw][KB], du[kGuRpw][KB], dx[CMAX][KB];
+#pragma unroll
+            for (int j = 0; j < KB; ++j) {
+                const int k = k0 + j * 1024 + lane * 16;
+                const int kc = k < D ? k : D - 16;
+#pragma unroll
+                for (int r = 0; r < kGuRpw; ++r) {
+                    const int n = pr0 + r < F ? pr0 + r : F - 1;
+                    qg[r][j] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(q + (size_t)n * D + kc));
+                    qu[r][j] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(q + (size_t)(F + n) * D + kc));
+                    dg[r][j] = d[(size_t)n * nblk + (kc >> 5)];
+                    du[r][j] = d[(size_t)(F + n) * nblk + (kc >> 5)];
+                }
+#pragma unroll
+                for (int ci = 0; ci < CMAX; ++ci) {
+                    xv[ci][j] = *reinterpret_cast<const v4i*>(a.xq + (size_t)tok[ci] * D + kc);
+                    dx[ci][j] = a.xd[(size_t)tok[ci] * nblk + (kc >> 5)];
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < KB; ++j) {
+                if (k0 + j * 1024 + lane * 16 >= D) continue;
+#pragma unroll
+                for (int ci = 0; ci < CMAX; ++ci) {
+                    if (ci >= cn) continue;
+                    const v4i x = xv[ci][j];
+                    const float dxf = h2f(dx[ci][j]);
+#pragma unroll
+                    for (int r = 0; r < kGuRpw; ++r) {
+                        int sg = 0, su = 0;
+                        sg = __builtin_amdgcn_sdot4(qg[r][j].x, x.x, sg, false);
+                        sg = __builtin_amdgcn_sdot4(qg[r][j].y, x.y, sg, false);
+                        sg = __builtin_amdgcn_sdot4(qg[r][j].z, x.z, sg, false);
+                        sg = __builtin_amdgcn_sdot4(qg[r][j].w, x.w, sg, false);
+                        su = __builtin_amdgcn_sdot4(qu[r][j].x, x.x, su, false);
+                        su = __builtin_amdgcn_sdot4(qu[r][j].y, x.y, su, false);
+                        su = __builtin_amdgcn_sdot4(qu[r][j].z, x.z, su, false);
+                        su = __builtin_amdgcn_sdot4(qu[r][j].w, x.w, su, false);
+                        // d_w * d_x is exact in fp32 (11-bit x 11-bit significands)
+                        ag[r][ci] = fmaf((float)sg, h2f(dg[r][j]) * dxf, ag[r][ci]);
+                        au[r][ci] = fmaf((float)su, h2f(du[r][j]) * dxf, au[r][ci]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kGuRpw; ++r) {
+#pragma unroll
+            for (int ci = 0; ci < CMAX; ++ci) {
+                if (ci < cn) {
+                    const float g = wave_sum(ag[r][ci]);
+                    const float u = wave_sum(au[r][ci]);
+                    const int n = pr0 + r;
+                    if (lane == 0 && n < F) a.h[(size_t)ent[ci] * F + n] = g / (1.0f + expf(-g)) * u;
+                }
+            }
+        }
+    }
+}
+
+// Down projection: rows of F quants, F/16 lanes per row (F <= 1024), h in registers; each row's
+// lane partials are summed in a fixed order through LDS.
+constexpr int kDnNrs = 2;
+
+template <int CMAX>
+__global__ void __launch_bounds__(256) moe_down_kernel(MoeArgs a) {
+    extern __shared__ float smem[];
+    const int slot = blockIdx.y;
+    const int U = a.plan[0];
+    if (slot >= U) return;
+    const int P = a.P, D = a.D, F = a.F;
+    const int e = a.plan[1 + slot];
+    const int c = a.plan[1 + P + slot];
+    const int st = a.plan[1 + 2 * P + slot];
+    const int8_t* q = a.wdn + (size_t)e * a.dn_bytes;
+    const uint16_t* d = reinterpret_cast<const uint16_t*>(q + (size_t)D * F);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int LPR = F >> 4, RPS = 64 / LPR;
+    const int rsub = lane / LPR, cl = lane - rsub * LPR;
+    const bool lane_ok = rsub < RPS;
+    const int k = lane_ok ? cl * 16 : 0;
+    const int nblk = F >> 5;
+    const int base = (blockIdx.x * 4 + wave) * kDnNrs * RPS;
+
+    v4i wq[kDnNrs];
+    uint16_t wd[kDnNrs];
+#pragma unroll
+    for (int i = 0; i < kDnNrs; ++i) {
+        int row = base + i * RPS + (lane_ok ? rsub : 0);
+        row = row < D ? row : D - 1;
+        wq[i] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(q + (size_t)row * F + k));
+        wd[i] = d[(size_t)row * nblk + (k >> 5)];
+    }
+    float* red = smem + wave * (kDnNrs * 64 * CMAX);
+    const int rows_w = kDnNrs * RPS;
+
+    for (int cb = 0; cb < c; cb += CMAX) {
+        const int cn = c - cb < CMAX ? c - cb : CMAX;
+        int ent[CMAX];
+        float hv[CMAX][16];
+#pragma unroll
+        for (int ci = 0; ci < CMAX; ++ci) {
+            ent[ci] = a.plan[1 + 3 * P + st + cb + (ci < cn ? ci : 0)];
+            const float* hp = a.h + (size_t)ent[ci] * F + k;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float4 f = reinterpret_cast<const float4*>(hp)[i];
+                hv[ci][4 * i] = f.x; hv[ci][4 * i + 1] = f.y; hv[ci][4 * i + 2] = f.z; hv[ci][4 * i + 3] = f.w;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ci = 0; ci < CMAX; ++ci) {
+            if (ci >= cn) continue;
+#pragma unroll
+            for (int i = 0; i < kDnNrs; ++i) {
+                const float v = h2f(wd[i]) * dot16_i8_f32(__builtin_bit_cast(u32x4, wq[i]), hv[ci]);
+                if (lane_ok) red[((i * RPS + rsub) * CMAX + ci) * LPR + cl] = v;
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        for (int o = lane; o < rows_w * cn; o += 64) {
+            const int ci = o / rows_w;
+            const int rl = o - ci * rows_w;
+            const int row = base + rl;
+            if (row >= D) continue;
+            const float* p = red + (rl * CMAX + ci) * LPR;
+            float v = 0.f;
+            for (int c2 = 0; c2 < LPR; ++c2) v += p[c2];
+            int en = 0;
+#pragma unroll
+            for (int cc = 0; cc < CMAX; ++cc) if (cc == ci) en = ent[cc];
+            a.rows[(size_t)en * D + row] = v;
+        }
+        // the next chunk overwrites red: every lane's reads of this chunk come first
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+}
+
+__global__ void __launch_bounds__(256) moe_combine_kernel(MoeArgs a) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= a.T * a.D) return;
+    const int t = i / a.D, m = i - t * a.D;
+    float v = 0.f;
+    if (a.plan[0] >= 0) {
+        for (int j = 0; j < a.topk; ++j)
+            v = fmaf(a.w[t * a.topk + j], a.rows[(size_t)(t * a.topk + j) * a.D + m], v);
+    }
+    a.out[i] = f2bf_bits(v);
+}
+
+size_t moe_workspace_bytes(int T, int topk, int D, int F) {
+    const size_t P = (size_t)T * topk;
+    return round_up((1 + 4 * P) * sizeof(int32_t), kCounterAlign) +
+           round_up(P * F * sizeof(float), kCounterAlign) + round_up(P * D * sizeof(float), kCounterAlign);
+}
+
+int launch_moe_routed(const int8_t* xq, const uint16_t* xd, const int32_t* ids, const float* w,
+                      const void* wgu, const void* wdn, uint16_t* out, int T, int topk, int E,
+                      int D, int F, void* ws, hipStream_t st) {
+    MoeArgs a{};
+    a.xq = xq; a.xd = xd; a.w = w;
+    a.wgu = static_cast<const int8_t*>(wgu);
+    a.wdn = static_cast<const int8_t*>(wdn);
+    a.gu_bytes = (size_t)2 * F * D + (size_t)2 * F * (D / 32) * 2;
+    a.dn_bytes = (size_t)D * F + (size_t)D * (F / 32) * 2;
+    a.out = out; a.T = T; a.topk = topk; a.P = T * topk; a.E = E; a.D = D; a.F = F;
+    const size_t P = (size_t)a.P;
+    char* p = static_cast<char*>(ws);
+    int32_t* plan = reinterpret_cast<int32_t*>(p);
+    a.plan = plan;
+    p += round_up((1 + 4 * P) * sizeof(int32_t), kCounterAlign);
+    a.h = reinterpret_cast<float*>(p);
+    p += round_up(P * F * sizeof(float), kCounterAlign);
+    a.rows = reinterpret_cast<float*>(p);
+
+    hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(256), 0, st, ids, a.P, E, plan);
+    int rc = launch_status();
+    if (rc != GQ8_OK) return rc;
+    const int cmax4 = T <= 4;
+    const dim3 ggu((F + 4 * kGuRpw - 1) / (4 * kGuRpw), a.P);
+    if (cmax4) hipLaunchKernelGGL((moe_gate_up_kernel<4>), ggu, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((moe_gate_up_kernel<16>), ggu, dim3(256), 0, st, a);
+    if ((rc = launch_status()) != GQ8_OK) return rc;
+    const int rps = 64 / (F / 16);
+    const dim3 gdn((D + 4 * kDnNrs * rps - 1) / (4 * kDnNrs * rps), a.P);
+    hipLaunchKernelGGL((moe_down_kernel<4>), gdn, dim3(256), (size_t)4 * kDnNrs * 64 * 4 * sizeof(float), st, a);
+    if ((rc = launch_status()) != GQ8_OK) return rc;
+    hipLaunchKernelGGL(moe_combine_kernel, dim3((T * D + 255) / 256), dim3(256), 0, st, a);
+    return launch_status();
+}
+
+}  // namespace gq8

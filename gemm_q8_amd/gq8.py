@@ -1,0 +1,207 @@
+"""Thin Python binding of libgq8.so (include/gq8.h), same names and argument order as the C ABI.
+
+Argument marshalling only: device-pointer arguments accept a torch tensor (its data_ptr()), an
+int address, or None (NULL); `stream` defaults to torch's current stream on the current device.
+A negative status raises GQ8Error. Every computation happens in the library's HIP kernels.
+
+Importing this module loads libgq8.so and fails loudly if it has not been built
+(python -m gemm_q8_amd.build) -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgq8.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"gemm_q8_amd: {_LIB_PATH} is missing; build it with `python -m gemm_q8_amd.build`")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+LIB_PATH = _LIB_PATH
+
+OK, EINVAL, ESHAPE, EALIGN, EWORKSPACE, ECAPTURE, EHIP, ENODEV = 0, -1, -2, -3, -4, -5, -6, -7
+OP_Q8_0_GEMV, OP_HC_DOWN, OP_HC_UP, OP_W8A8 = 1, 2, 3, 4
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_F = ctypes.c_float
+
+# name -> (restype, argtypes), in include/gq8.h order
+_SIGS = {
+    "gq8_status_str": (ctypes.c_char_p, [_I]),
+    "gq8_abi_version": (_I, []),
+    "gq8_device_cus": (_I, [ctypes.POINTER(_I)]),
+    "gq8_q8_0_bytes": (_SZ, [_I64, _I64]),
+    "gq8_q8_0_quantize": (_I, [_P, _I, _I, _P, _P]),
+    "gq8_q8_0_split_from_blocks": (_I, [_P, _I, _I, _P, _P]),
+    "gq8_q8_1_quantize": (_I, [_P, _I, _I, _P, _P, _P, _P]),
+    "gq8_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
+    "gq8_workspace_counter_bytes": (_SZ, [_I, _I, _I, _I]),
+    "gq8_workspace_init": (_I, [_P, _SZ, _P]),
+    "gq8_q8_0_gemv": (_I, [_P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "gq8_hc_q8_down": (_I, [_P, _P, _P, _F, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "gq8_hc_q8_up": (_I, [_P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "gq8_w8a8_packed_bytes": (_SZ, [_I, _I]),
+    "gq8_w8a8_pack": (_I, [_P, _I, _I, _P, _P]),
+    "gq8_w8a8_gemm": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "gq8_w8a8_gemm_i32": (_I, [_P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "gq8_moe_route": (_I, [_P, _I, _I, _I, _P, _P, _P]),
+    "gq8_moe_plan_words": (_SZ, [_I, _I]),
+    "gq8_moe_plan": (_I, [_P, _I, _I, _I, _P, _P]),
+    "gq8_moe_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
+    "gq8_moe_q8_0_routed": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P]),
+    "gq8_read_probe_sink_floats": (_SZ, [_SZ]),
+    "gq8_read_probe": (_I, [_P, _SZ, _P, _P]),
+}
+
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class GQ8Error(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: status {status} ({gq8_status_str(status)})")
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(name, st):
+    if st != OK:
+        raise GQ8Error(name, st)
+    return st
+
+
+def gq8_status_str(status):
+    return _lib.gq8_status_str(status).decode()
+
+
+def gq8_abi_version():
+    return _lib.gq8_abi_version()
+
+
+def gq8_device_cus():
+    c = _I(0)
+    _check("gq8_device_cus", _lib.gq8_device_cus(ctypes.byref(c)))
+    return c.value
+
+
+def gq8_q8_0_bytes(rows, K):
+    return _lib.gq8_q8_0_bytes(rows, K)
+
+
+def gq8_q8_0_quantize(w, rows, K, w_split, stream=None):
+    return _check("gq8_q8_0_quantize", _lib.gq8_q8_0_quantize(_ptr(w), rows, K, _ptr(w_split), _stream(stream)))
+
+
+def gq8_q8_0_split_from_blocks(blocks34, rows, K, w_split, stream=None):
+    return _check("gq8_q8_0_split_from_blocks",
+                  _lib.gq8_q8_0_split_from_blocks(_ptr(blocks34), rows, K, _ptr(w_split), _stream(stream)))
+
+
+def gq8_q8_1_quantize(x_bf16, rows, K, q, d, s, stream=None):
+    return _check("gq8_q8_1_quantize", _lib.gq8_q8_1_quantize(
+        _ptr(x_bf16), rows, K, _ptr(q), _ptr(d), _ptr(s), _stream(stream)))
+
+
+def gq8_workspace_bytes(op, rows, N, K):
+    return _lib.gq8_workspace_bytes(op, rows, N, K)
+
+
+def gq8_workspace_counter_bytes(op, rows, N, K):
+    return _lib.gq8_workspace_counter_bytes(op, rows, N, K)
+
+
+def gq8_workspace_init(ws, nbytes, stream=None):
+    return _check("gq8_workspace_init", _lib.gq8_workspace_init(_ptr(ws), nbytes, _stream(stream)))
+
+
+def gq8_q8_0_gemv(w_split, x, y, T, N, K, ws, ws_bytes, stream=None):
+    return _check("gq8_q8_0_gemv", _lib.gq8_q8_0_gemv(
+        _ptr(w_split), _ptr(x), _ptr(y), T, N, K, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def gq8_hc_q8_down(w_split, R, w_norm, eps, lo, rs_out, T, N, K, ws, ws_bytes, stream=None):
+    return _check("gq8_hc_q8_down", _lib.gq8_hc_q8_down(
+        _ptr(w_split), _ptr(R), _ptr(w_norm), eps, _ptr(lo), _ptr(rs_out), T, N, K, _ptr(ws), ws_bytes,
+        _stream(stream)))
+
+
+def gq8_hc_q8_up(w_split, lo, out, T, N, K, ws, ws_bytes, stream=None):
+    return _check("gq8_hc_q8_up", _lib.gq8_hc_q8_up(
+        _ptr(w_split), _ptr(lo), _ptr(out), T, N, K, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def gq8_w8a8_packed_bytes(K, N):
+    return _lib.gq8_w8a8_packed_bytes(K, N)
+
+
+def gq8_w8a8_pack(W, K, N, W_packed, stream=None):
+    return _check("gq8_w8a8_pack", _lib.gq8_w8a8_pack(_ptr(W), K, N, _ptr(W_packed), _stream(stream)))
+
+
+def gq8_w8a8_gemm(xq, x_scale, W_packed, w_scale, out, M, N, K, ws, ws_bytes, stream=None):
+    return _check("gq8_w8a8_gemm", _lib.gq8_w8a8_gemm(
+        _ptr(xq), _ptr(x_scale), _ptr(W_packed), _ptr(w_scale), _ptr(out), M, N, K, _ptr(ws), ws_bytes,
+        _stream(stream)))
+
+
+def gq8_w8a8_gemm_i32(xq, W_packed, acc, M, N, K, ws, ws_bytes, stream=None):
+    return _check("gq8_w8a8_gemm_i32", _lib.gq8_w8a8_gemm_i32(
+        _ptr(xq), _ptr(W_packed), _ptr(acc), M, N, K, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def gq8_moe_route(logits, T, E, topk, ids, weights, stream=None):
+    return _check("gq8_moe_route", _lib.gq8_moe_route(
+        _ptr(logits), T, E, topk, _ptr(ids), _ptr(weights), _stream(stream)))
+
+
+def gq8_moe_plan_words(T, topk):
+    return _lib.gq8_moe_plan_words(T, topk)
+
+
+def gq8_moe_plan(ids, T, topk, E, plan, stream=None):
+    return _check("gq8_moe_plan", _lib.gq8_moe_plan(_ptr(ids), T, topk, E, _ptr(plan), _stream(stream)))
+
+
+def gq8_moe_workspace_bytes(T, topk, D, F):
+    return _lib.gq8_moe_workspace_bytes(T, topk, D, F)
+
+
+def gq8_moe_q8_0_routed(xq, xd, ids, weights, w_gate_up, w_down, out, T, topk, E, D, F, ws, ws_bytes,
+                        stream=None):
+    return _check("gq8_moe_q8_0_routed", _lib.gq8_moe_q8_0_routed(
+        _ptr(xq), _ptr(xd), _ptr(ids), _ptr(weights), _ptr(w_gate_up), _ptr(w_down), _ptr(out),
+        T, topk, E, D, F, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def gq8_read_probe_sink_floats(nbytes):
+    return _lib.gq8_read_probe_sink_floats(nbytes)
+
+
+def gq8_read_probe(src, nbytes, sink, stream=None):
+    return _check("gq8_read_probe", _lib.gq8_read_probe(_ptr(src), nbytes, _ptr(sink), _stream(stream)))
+
+
+def raw():
+    """The ctypes library handle (for tests that check status codes without raising)."""
+    return _lib

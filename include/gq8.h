@@ -1,0 +1,212 @@
+/*
+ * gq8 -- decode-time skinny quantized matrix products on MI355X (gfx950).
+ *
+ * C ABI of libgq8.so. Plain pointers and sizes only. Unless a parameter says
+ * otherwise, every pointer is DEVICE memory owned by the caller (for example
+ * a torch tensor's data_ptr()); the library never keeps a pointer past the
+ * call, never allocates, and never synchronizes. `stream` is a hipStream_t
+ * (0 = the legacy null stream); every call only enqueues work on it, so the
+ * compute entry points can be captured into a hipGraph.
+ *
+ * Return value: GQ8_OK (0) or a negative gq8_status. Arguments are checked
+ * before anything is enqueued; on an error nothing has been launched and the
+ * outputs are untouched. A HIP launch failure is reported as GQ8_EHIP.
+ *
+ * Pages cited (by title and section):
+ *   HC-Q8 page  "sycl: STRATA_HC_Q8=1 reads the Q8_0 hyper-connection projections" (PR #2810)
+ *   EP page     "sycl: --expert-parallel-device N, two Arc cards compute each layer's experts together" (PR #1798)
+ *   defer page  "verify: STRATA_VERIFY_DEFER_CPU_BELOW=<w>" (PR #2690)
+ *   W8A8 page   "INT8 W8A8 GEMM -- Decode (M <= 32) -- gfx928 / SGLang TP4"
+ */
+#ifndef GQ8_H
+#define GQ8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GQ8_ABI_VERSION 1
+
+enum gq8_status {
+    GQ8_OK = 0,
+    GQ8_EINVAL = -1,     /* null pointer, negative size, unknown op                     */
+    GQ8_ESHAPE = -2,     /* a size outside what the operation supports                   */
+    GQ8_EALIGN = -3,     /* a pointer not aligned as the operation requires (16 bytes)   */
+    GQ8_EWORKSPACE = -4, /* workspace null or smaller than gq8_workspace_bytes()         */
+    GQ8_ECAPTURE = -5,   /* gq8_workspace_init() called on a capturing stream            */
+    GQ8_EHIP = -6,       /* a HIP call or kernel launch failed                           */
+    GQ8_ENODEV = -7      /* no usable gfx950 device is current                           */
+};
+
+/* Operations that take a workspace (the `op` argument of the workspace functions). */
+enum gq8_op {
+    GQ8_OP_Q8_0_GEMV = 1,
+    GQ8_OP_HC_DOWN = 2,
+    GQ8_OP_HC_UP = 3,
+    GQ8_OP_W8A8 = 4
+};
+
+/* Static string for a status code. Host only. */
+const char* gq8_status_str(int status);
+
+/* GQ8_ABI_VERSION of the built library. Host only. */
+int gq8_abi_version(void);
+
+/* Compute units of the current device (the split-K sizing uses it); GQ8_ENODEV without one. */
+int gq8_device_cus(int* cus_out);
+
+/* ------------------------------------------------------------------------------------------
+ * Q8_0 weights (HC-Q8 page, "What changed": blocks of 32 int8 quants with one fp16 scale,
+ * ggml's 34-byte blocks, and the "split" order the read uses).
+ *
+ * Split layout of a [rows, K] Q8_0 matrix (K % 32 == 0), gq8_q8_0_bytes(rows, K) bytes:
+ *   int8 q[rows][K]            every row's quants, row-major
+ *   fp16 d[rows][K/32]         then every row's block scales, row-major
+ * The scales start at byte offset rows*K. The buffer must be 16-byte aligned.
+ * ------------------------------------------------------------------------------------------ */
+size_t gq8_q8_0_bytes(int64_t rows, int64_t K);
+
+/* Quantize fp32 rows w[rows][K] into the split layout (HC-Q8 page, "What changed": ggml's
+ * rounding). Per block: d = fp16(amax / 127) (fp32 quotient, round to nearest even);
+ * q = round(w / d) with the fp32 quotient by the stored fp16 d, ties away from zero, clamped to
+ * [-127, 127]; a block whose fp16 d is 0 gets zero quants. Weight preparation, not a hot-path
+ * call. w: 16-byte aligned; K % 32 == 0. */
+int gq8_q8_0_quantize(const float* w, int rows, int K, void* w_split, void* stream);
+
+/* Reorder ggml 34-byte blocks {fp16 d; int8 q[32]} (row-major blocks, [rows][K/32]) into the
+ * split layout: the same bytes, reordered (HC-Q8 page, "What changed"). */
+int gq8_q8_0_split_from_blocks(const void* blocks34, int rows, int K, void* w_split, void* stream);
+
+/* q8_1 quantization of bf16 rows x[rows][K] (EP page, "What changed": the q8_1 MoE input).
+ * Per 32-block, the Q8_0 rule above plus s = fp16(d * sum(q)).
+ * Outputs: q int8 [rows][K], d fp16 [rows][K/32], s fp16 [rows][K/32] (s may be null). */
+int gq8_q8_1_quantize(const uint16_t* x_bf16, int rows, int K, int8_t* q, uint16_t* d,
+                      uint16_t* s, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Workspace: split-K partial sums and arrival counters for the compute calls.
+ *   - size it with gq8_workspace_bytes() for the exact (op, rows, N, K) of the call;
+ *   - zero it once with gq8_workspace_init(), outside any stream capture;
+ *   - a call leaves every counter at zero again (the last-arriving work-group resets it), so a
+ *     workspace can be reused by any later call on the SAME stream without re-initialising;
+ *     calls that may run concurrently (different streams, or a graph replayed concurrently
+ *     with itself) need separate workspaces (HC-Q8 page, "What changed": one scratch per queue,
+ *     zeroed outside any capture);
+ *   - the counters occupy the first gq8_workspace_counter_bytes() bytes; the partial sums after
+ *     them are fully rewritten by every call before they are read (no clearing needed;
+ *     W8A8 page, "Split-K requirements").
+ * rows = T for the Q8_0 calls, M for W8A8. A size of 0 means the call needs no workspace.
+ * ------------------------------------------------------------------------------------------ */
+size_t gq8_workspace_bytes(int op, int rows, int N, int K);
+size_t gq8_workspace_counter_bytes(int op, int rows, int N, int K);
+int gq8_workspace_init(void* ws, size_t bytes, void* stream);
+
+/* Q8_0 matrix-vector product for T = 1..16 token rows (HC-Q8 page, "What changed": w = d*q,
+ * exact in fp32):
+ *   y[t][n] = sum_k d[n][k/32] * q[n][k] * x[t][k]
+ * w_split: split-layout Q8_0 [N][K]; x fp32 [T][K]; y fp32 [T][N] (written, not accumulated).
+ * K % 32 == 0. Accumulation is fp32 in a fixed order: the result is deterministic for a given
+ * device and shape (replays are bitwise identical). T == 0 or N == 0: nothing to do.
+ * K == 0: y is zero-filled. */
+int gq8_q8_0_gemv(const void* w_split, const float* x, float* y, int T, int N, int K,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/* Fused RMSNorm + Q8_0 hyper-connection down read (HC-Q8 page, "What changed": the down kernel
+ * works on R * w_norm unscaled plus the sums of squares, and the last work-group of a row group
+ * applies the RMSNorm factor when it combines the partial sums):
+ *   rs[t]    = 1 / sqrt(mean_k R[t][k]^2 + eps)
+ *   lo[t][n] = bf16( rs[t] * sum_k d[n][k/32] * q[n][k] * (R[t][k] * w_norm[k]) )
+ * w_split: Q8_0 [N][K]; R bf16 [T][K]; w_norm bf16 [K]; lo bf16 [T][N]; rs_out fp32 [T]
+ * (nullable). T = 1..16, K % 32 == 0, K > 0. */
+int gq8_hc_q8_down(const void* w_split, const uint16_t* R, const uint16_t* w_norm, float eps,
+                   uint16_t* lo, float* rs_out, int T, int N, int K,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* Q8_0 hyper-connection up read (HC-Q8 page, "What changed": rows of K = 320, the fifths of each
+ * row summed in a fixed order). The page's own epilogue (pending write, gate, stream mean) is
+ * not defined there and is not part of this call:
+ *   out[t][n] = bf16( sum_k d[n][k/32] * q[n][k] * lo[t][k] )
+ * w_split: Q8_0 [N][K]; lo bf16 [T][K]; out bf16 [T][N]. T = 1..16, K % 32 == 0, K <= 1024. */
+int gq8_hc_q8_up(const void* w_split, const uint16_t* lo, uint16_t* out, int T, int N, int K,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * W8A8 (W8A8 page, operator statement): int8 x_q[M][K] @ int8 W[K][N] -> int32, then
+ * * x_scale[M] * w_scale[N] -> bf16[M][N], M = 1..32.
+ * The weight is packed once, outside the timed path (W8A8 page, "Cross-shape rules": pack the
+ * cold weight into the fragment layout): gq8_w8a8_pack() turns the logical row-major W[K][N]
+ * into an opaque layout of gq8_w8a8_packed_bytes(K, N) bytes (N rounded up to 16 and K to 64,
+ * padding zero-filled). K % 16 == 0; x_q rows are K bytes, 16-byte aligned.
+ * ------------------------------------------------------------------------------------------ */
+size_t gq8_w8a8_packed_bytes(int K, int N);
+int gq8_w8a8_pack(const int8_t* W, int K, int N, int8_t* W_packed, void* stream);
+
+/* out[m][n] = bf16( (fp32(acc[m][n]) * x_scale[m]) * w_scale[n] ), acc = exact int32 sum,
+ * two separately rounded fp32 products, round to nearest even. Exactly one correct output. */
+int gq8_w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* W_packed,
+                  const float* w_scale, uint16_t* out, int M, int N, int K,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/* Same kernels, int32 accumulators written instead of the bf16 epilogue (acc int32 [M][N]). */
+int gq8_w8a8_gemm_i32(const int8_t* xq, const int8_t* W_packed, int32_t* acc, int M, int N,
+                      int K, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Routed experts (EP page, "What changed": q8_1 MoE input, a device plan grouping the routed
+ * entries by expert, one row per entry into a rows buffer, then the single-card combine;
+ * defer page, "What it changes": rows combined by routing weight).
+ * ------------------------------------------------------------------------------------------ */
+
+/* Softmax over E router logits per token, then the top-k experts by probability, descending
+ * (ties to the lower id); weights are those probabilities (not renormalised).
+ * logits fp32 [T][E]; ids int32 [T][topk]; weights fp32 [T][topk]. T >= 1, 1 <= topk <= 16,
+ * topk <= E <= 4096. */
+int gq8_moe_route(const float* logits, int T, int E, int topk, int32_t* ids, float* weights,
+                  void* stream);
+
+/* Device plan (EP page, "What changed" and "How it was checked": every routed entry exactly
+ * once). With P = T*topk entries, entry i = t*topk + j, the plan is int32 [gq8_moe_plan_words]:
+ *   plan[0]               U, the number of distinct experts routed
+ *   plan[1 + u]           expert of slot u (u < U), ascending
+ *   plan[1 + P + u]       number of entries of slot u
+ *   plan[1 + 2P + u]      index of slot u's first entry in the entry list
+ *   plan[1 + 3P + i]      entry list: the entries grouped by slot, ascending within a slot
+ * Slots u >= U are written as -1 / 0 / P. An id outside [0, E) makes U = -1 (plan error). */
+size_t gq8_moe_plan_words(int T, int topk);
+int gq8_moe_plan(const int32_t* ids, int T, int topk, int E, int32_t* plan, void* stream);
+
+/* Routed Q8_0 experts on a q8_1 input. Expert e's gate/up weight, Q8_0 [2F][D] in split
+ * layout (rows 0..F-1 gate, F..2F-1 up), starts at w_gate_up + e * gq8_q8_0_bytes(2F, D);
+ * its down weight, Q8_0 [D][F], at w_down + e * gq8_q8_0_bytes(D, F). For each entry (t, j):
+ *   g, u = gate/up rows . x[t]   (per 32-block: d_w * d_x * sum q_w q_x)
+ *   h    = SiLU(g) * u            (fp32, not re-quantized)
+ *   r    = down . h
+ * and out[t] = bf16( sum_{j=0..topk-1} weights[t][j] * r_{t,j} ), in slot order.
+ * xq int8 [T][D], xd fp16 [T][D/32] (the q8_1 quants and scales); ids int32 [T][topk];
+ * weights fp32 [T][topk]; out bf16 [T][D]. D % 32 == 0, F % 32 == 0, F <= 1024,
+ * T*topk <= 256. Only the routed experts' bytes are read. */
+size_t gq8_moe_workspace_bytes(int T, int topk, int D, int F);
+int gq8_moe_q8_0_routed(const int8_t* xq, const uint16_t* xd, const int32_t* ids,
+                        const float* weights, const void* w_gate_up, const void* w_down,
+                        uint16_t* out, int T, int topk, int E, int D, int F,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Diagnostics
+ * ------------------------------------------------------------------------------------------ */
+
+/* Streaming read of `bytes` (multiple of 16) from src, 4 KiB per work-group; sink holds
+ * gq8_read_probe_sink_floats(bytes) floats, written only for a bit pattern that keeps the loads
+ * from being elided (its contents are unspecified). Measures the read bandwidth reachable for a
+ * given byte count in one launch. */
+size_t gq8_read_probe_sink_floats(size_t bytes);
+int gq8_read_probe(const void* src, size_t bytes, float* sink, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQ8_H */

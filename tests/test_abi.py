@@ -1,0 +1,96 @@
+"""CPU checks of the C ABI library: it loads, exports every symbol include/gq8.h declares, and
+its host-only functions (sizes, status strings, argument checks that return before any device
+work) behave as documented. No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gq8.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gq8_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from gemm_q8_amd import gq8
+    return gq8
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) >= 20
+    raw = ctypes.CDLL(lib.LIB_PATH)
+    missing = [n for n in names if not hasattr(raw, n)]
+    assert not missing, missing
+    # the binding wraps each one under the same name
+    assert not [n for n in names if not hasattr(lib, n)]
+
+
+def test_status_strings_and_version(lib):
+    assert lib.gq8_abi_version() == 1
+    assert lib.gq8_status_str(0) == "ok"
+    assert lib.gq8_status_str(-4).startswith("workspace")
+    assert lib.gq8_status_str(12345) == "unknown status"
+
+
+def test_q8_0_bytes(lib):
+    assert lib.gq8_q8_0_bytes(1024, 4096) == 4_456_448
+    assert lib.gq8_q8_0_bytes(320, 16384) == 5_570_560
+    assert lib.gq8_q8_0_bytes(16384, 320) == 5_570_560
+    assert lib.gq8_q8_0_bytes(3, 33) == 0            # K not a multiple of 32
+
+
+def test_w8a8_packed_bytes_pads_to_fragments(lib):
+    assert lib.gq8_w8a8_packed_bytes(4096, 1536) == 4096 * 1536
+    assert lib.gq8_w8a8_packed_bytes(80, 17) == 128 * 32
+
+
+def test_workspace_sizes(lib):
+    # only the down read (split over K slabs) and the routed experts need a workspace
+    assert lib.gq8_workspace_bytes(lib.OP_HC_DOWN, 1, 320, 16384) >= 128 * 320 * 4
+    assert lib.gq8_workspace_bytes(lib.OP_HC_DOWN, 6, 320, 16384) > \
+        lib.gq8_workspace_bytes(lib.OP_HC_DOWN, 1, 320, 16384)
+    for op, rows, n, k in [(lib.OP_Q8_0_GEMV, 1, 1024, 4096), (lib.OP_HC_UP, 4, 16384, 320),
+                           (lib.OP_W8A8, 16, 1536, 4096), (99, 1, 1, 32)]:
+        assert lib.gq8_workspace_bytes(op, rows, n, k) == 0
+        assert lib.gq8_workspace_counter_bytes(op, rows, n, k) == 0
+    assert lib.gq8_moe_plan_words(4, 8) == 1 + 4 * 32
+    assert lib.gq8_moe_workspace_bytes(4, 8, 2048, 512) > 32 * (2048 + 512) * 4
+
+
+def test_argument_checks_return_before_device_work(lib):
+    raw = lib.raw()
+    dummy = 1 << 20  # never dereferenced: every case below fails validation first
+    # K not a multiple of 32
+    assert raw.gq8_q8_0_gemv(dummy, dummy, dummy, 1, 8, 48, None, 0, None) == lib.ESHAPE
+    # T above 16
+    assert raw.gq8_q8_0_gemv(dummy, dummy, dummy, 17, 8, 64, None, 0, None) == lib.ESHAPE
+    # negative size
+    assert raw.gq8_hc_q8_down(dummy, dummy, dummy, 1e-6, dummy, None, -1, 8, 64, None, 0, None) == lib.EINVAL
+    # up read with K above 1024
+    assert raw.gq8_hc_q8_up(dummy, dummy, dummy, 1, 8, 2048, None, 0, None) == lib.ESHAPE
+    # W8A8 M above 32, K not a multiple of 16
+    assert raw.gq8_w8a8_gemm(dummy, dummy, dummy, dummy, dummy, 33, 16, 64, None, 0, None) == lib.ESHAPE
+    assert raw.gq8_w8a8_gemm(dummy, dummy, dummy, dummy, dummy, 4, 16, 40, None, 0, None) == lib.ESHAPE
+    # misaligned weight pointer
+    assert raw.gq8_q8_0_gemv(dummy + 4, dummy, dummy, 1, 8, 64, None, 0, None) == lib.EALIGN
+    # missing / short workspace for the split down read
+    assert raw.gq8_hc_q8_down(dummy, dummy, dummy, 1e-6, dummy, None, 1, 320, 16384, None, 0, None) == lib.EWORKSPACE
+    assert raw.gq8_hc_q8_down(dummy, dummy, dummy, 1e-6, dummy, None, 1, 320, 16384, dummy, 64, None) == lib.EWORKSPACE
+    # W8A8 depth limit
+    assert raw.gq8_w8a8_gemm(dummy, dummy, dummy, dummy, dummy, 4, 16, 8192 + 16, None, 0, None) == lib.ESHAPE
+    # empty calls are no-ops
+    assert raw.gq8_q8_0_gemv(None, None, None, 0, 8, 64, None, 0, None) == lib.OK
+    assert raw.gq8_w8a8_gemm(None, None, None, None, None, 0, 16, 64, None, 0, None) == lib.OK
+    # null output
+    assert raw.gq8_q8_0_gemv(dummy, dummy, None, 1, 8, 64, None, 0, None) == lib.EINVAL
+    # MoE limits
+    assert raw.gq8_moe_q8_0_routed(dummy, dummy, dummy, dummy, dummy, dummy, dummy,
+                                   4, 8, 512, 2048, 2048, None, 0, None) == lib.ESHAPE

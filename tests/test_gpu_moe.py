@@ -1,0 +1,117 @@
+"""GPU parity of the routed-expert path: routing (ids exact, weights to fp32 rounding), the
+device plan (word for word against the oracle's grouping), and the routed Q8_0 forward against
+the oracle at small shapes and at the full 512-expert workload."""
+import numpy as np
+import pytest
+import torch
+
+from gemm_q8_amd import synth
+from gemm_q8_amd.device import to_dev, to_host
+from oracle.moe import moe_forward, plan, route
+from oracle.q8 import quantize_q8_0, quantize_q8_1_bf16
+from tests.helpers import check_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _route(gpu, logits, topk):
+    T, E = logits.shape
+    ids = torch.empty((T, topk), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, topk), dtype=torch.float32, device="cuda")
+    gpu.gq8_moe_route(to_dev(logits), T, E, topk, ids, w)
+    return to_host(ids), to_host(w)
+
+
+@pytest.mark.parametrize("T,E,topk", [(4, 512, 8), (1, 16, 1), (7, 300, 5), (16, 4096, 16)])
+def test_route_matches_oracle(gpu, T, E, topk):
+    logits = synth.normal_f32(40, "gpu.moe.logits", (T, E))
+    ids, w = _route(gpu, logits, topk)
+    ids_ref, p_ref = route(logits, topk)
+    assert np.array_equal(ids, ids_ref)
+    assert np.allclose(w, p_ref, rtol=1e-5, atol=0)
+
+
+def _decode_plan(words, P):
+    U = int(words[0])
+    slots = []
+    for u in range(U):
+        e, c, st = int(words[1 + u]), int(words[1 + P + u]), int(words[1 + 2 * P + u])
+        slots.append((e, [int(v) for v in words[1 + 3 * P + st: 1 + 3 * P + st + c]]))
+    return U, slots
+
+
+@pytest.mark.parametrize("T,topk,E", [(4, 8, 512), (3, 3, 6), (16, 16, 64), (1, 1, 1)])
+def test_plan_word_for_word(gpu, T, topk, E):
+    g = np.random.default_rng(T * 100 + topk)
+    ids = np.stack([g.choice(E, size=topk, replace=False) for _ in range(T)]).astype(np.int32)
+    P = T * topk
+    out = torch.empty(gpu.gq8_moe_plan_words(T, topk), dtype=torch.int32, device="cuda")
+    gpu.gq8_moe_plan(to_dev(ids), T, topk, E, out)
+    words = to_host(out)
+    U, slots = _decode_plan(words, P)
+    assert slots == plan(ids)
+    assert sorted(i for _, es in slots for i in es) == list(range(P))   # every entry once
+    assert all(words[1 + u] == -1 for u in range(U, P))
+
+
+def test_plan_error_on_bad_id(gpu):
+    ids = np.array([[0, 5], [1, 9]], np.int32)
+    out = torch.empty(gpu.gq8_moe_plan_words(2, 2), dtype=torch.int32, device="cuda")
+    gpu.gq8_moe_plan(to_dev(ids), 2, 2, 8, out)
+    assert int(to_host(out)[0]) == -1
+
+
+def _arena(gpu, experts, E, D, F, routed, seed, fill_unrouted=0x7F):
+    """Device arenas with the routed experts quantized in place; the others hold junk bytes
+    (so reading them would show)."""
+    gu_b, dn_b = gpu.gq8_q8_0_bytes(2 * F, D), gpu.gq8_q8_0_bytes(D, F)
+    agu = torch.full((E * gu_b,), fill_unrouted, dtype=torch.uint8, device="cuda")
+    adn = torch.full((E * dn_b,), fill_unrouted, dtype=torch.uint8, device="cuda")
+    for e in routed:
+        w = experts(e)
+        gpu.gq8_q8_0_quantize(to_dev(w["gate_up"]), 2 * F, D, agu[e * gu_b:(e + 1) * gu_b])
+        gpu.gq8_q8_0_quantize(to_dev(w["down"]), D, F, adn[e * dn_b:(e + 1) * dn_b])
+    return agu, adn
+
+
+def _moe_case(gpu, T, E, topk, D, F, seed):
+    inp = synth.moe_inputs(T=T, E=E, D=D, seed=seed)
+    ids_ref, p_ref = route(inp["logits"], topk)
+    experts = lambda e: synth.moe_expert_weights(e, D=D, F=F, seed=seed)  # noqa: E731
+    routed = sorted(set(ids_ref.ravel().tolist()))
+    agu, adn = _arena(gpu, experts, E, D, F, routed, seed)
+    # device routing and q8_1 quantization (the product path's own)
+    ids = torch.empty((T, topk), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, topk), dtype=torch.float32, device="cuda")
+    gpu.gq8_moe_route(to_dev(inp["logits"]), T, E, topk, ids, w)
+    xq = torch.empty((T, D), dtype=torch.int8, device="cuda")
+    xd = torch.empty((T, D // 32), dtype=torch.int16, device="cuda")
+    gpu.gq8_q8_1_quantize(to_dev(inp["x"]), T, D, xq, xd, None)
+    nb = gpu.gq8_moe_workspace_bytes(T, topk, D, F)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, D), dtype=torch.int16, device="cuda")
+    gpu.gq8_moe_q8_0_routed(xq, xd, ids, w, agu, adn, out, T, topk, E, D, F, ws, nb)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(ids), ids_ref)
+    x81 = quantize_q8_1_bf16(inp["x"])
+    blocks = lambda e: (quantize_q8_0(experts(e)["gate_up"]), quantize_q8_0(experts(e)["down"]))  # noqa: E731
+    y_ref, S = moe_forward(x81, ids_ref, p_ref, blocks)
+    check_bf16(to_host(out, np.uint16), y_ref, S, f"moe T={T} E={E} topk={topk} D={D} F={F}")
+    return out, (xq, xd, ids, w, agu, adn, ws, nb)
+
+
+@pytest.mark.parametrize("T,E,topk,D,F", [(1, 8, 2, 64, 32), (3, 20, 4, 128, 64), (6, 40, 6, 1056, 96),
+                                          (16, 64, 4, 256, 128)])
+def test_moe_small(gpu, T, E, topk, D, F):
+    _moe_case(gpu, T, E, topk, D, F, seed=41)
+
+
+def test_moe_full_size(gpu):
+    T, E, topk, D, F = 4, 512, 8, 2048, 512
+    out, (xq, xd, ids, w, agu, adn, ws, nb) = _moe_case(gpu, T, E, topk, D, F, seed=0)
+    # replay determinism with the workspace poisoned
+    out2 = torch.empty_like(out)
+    ws.fill_(0xFF)
+    gpu.gq8_moe_q8_0_routed(xq, xd, ids, w, agu, adn, out2, T, topk, E, D, F, ws, nb)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)

@@ -1,0 +1,222 @@
+"""GPU parity of the Q8_0 reads against the oracle: the Q8_0 matrix-vector product (T = 1..16),
+the fused RMSNorm + Q8_0 down read and the up read, at small ragged shapes and at the full
+workload sizes, plus exactness, determinism, graph-replay and workspace invariants."""
+import numpy as np
+import pytest
+import torch
+
+from gemm_q8_amd import synth
+from gemm_q8_amd.device import q8_0_from_f32, to_dev, to_host, workspace
+from oracle.hc import hc_down, hc_up
+from oracle.numerics import bf16_to_f32, fp16_to_f32
+from oracle.q8 import q8_0_gemv, quantize_q8_0
+from tests.helpers import check_bf16, check_f32
+
+pytestmark = pytest.mark.gpu
+
+
+def _gemv(gpu, wbuf, x, T, N, K):
+    nb = gpu.gq8_workspace_bytes(gpu.OP_Q8_0_GEMV, T, N, K)
+    ws = workspace(nb)
+    y = torch.empty((T, N), dtype=torch.float32, device="cuda")
+    gpu.gq8_q8_0_gemv(wbuf, x, y, T, N, K, ws, nb)
+    return y, ws, nb
+
+
+@pytest.mark.parametrize("T,N,K", [(1, 96, 4096), (3, 37, 1056), (5, 130, 2080), (8, 64, 96),
+                                   (11, 33, 320), (16, 70, 4096), (2, 5, 32), (4, 300, 1024)])
+def test_gemv_matches_oracle(gpu, T, N, K):
+    w = synth.normal_f32(10, "gpu.gemv.w", (N, K), 0.0, 0.02)
+    x = synth.normal_f32(10, "gpu.gemv.x", (T, K))
+    y, _, _ = _gemv(gpu, q8_0_from_f32(to_dev(w)), to_dev(x), T, N, K)
+    y_ref, S = q8_0_gemv(quantize_q8_0(w), x)
+    check_f32(to_host(y), y_ref, S, f"gemv T={T} N={N} K={K}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 8, 16])
+def test_gemv_full_size(gpu, T):
+    d = synth.q8_0_gemv_inputs(T=T)
+    y, _, _ = _gemv(gpu, q8_0_from_f32(to_dev(d["w"])), to_dev(d["x"]), T, 1024, 4096)
+    y_ref, S = q8_0_gemv(quantize_q8_0(d["w"]), d["x"])
+    check_f32(to_host(y), y_ref, S, f"gemv full T={T}")
+
+
+def test_gemv_one_hot_is_exact(gpu):
+    N, K = 50, 2048
+    w = synth.normal_f32(11, "gpu.gemv.oh", (N, K), 0.0, 0.02)
+    ks = [0, 31, 32, 1023, 1024, 2047]
+    x = np.zeros((len(ks), K), np.float32)
+    for t, k in enumerate(ks):
+        x[t, k] = 1.0
+    b = quantize_q8_0(w)
+    y, _, _ = _gemv(gpu, q8_0_from_f32(to_dev(w)), to_dev(x), len(ks), N, K)
+    y = to_host(y)
+    for t, k in enumerate(ks):
+        want = fp16_to_f32(b.d[:, k // 32]) * b.q[:, k // 32, k % 32].astype(np.float32)
+        assert np.array_equal(y[t], want)
+
+
+def test_gemv_reads_the_scales(gpu):
+    """Perturbing one block scale changes exactly that row's outputs (the Q8_0 bytes are read)."""
+    N, K, T = 40, 1024, 2
+    w = synth.normal_f32(12, "gpu.gemv.sc", (N, K), 0.0, 0.02)
+    x = to_dev(synth.normal_f32(12, "gpu.gemv.scx", (T, K)))
+    wbuf = q8_0_from_f32(to_dev(w))
+    y0, _, _ = _gemv(gpu, wbuf, x, T, N, K)
+    sc = wbuf[N * K:].view(torch.float16)
+    sc[7 * (K // 32) + 3] *= 2
+    y1, _, _ = _gemv(gpu, wbuf, x, T, N, K)
+    diff = (to_host(y0) != to_host(y1)).any(axis=0)
+    assert diff.tolist() == [n == 7 for n in range(N)]
+
+
+def test_gemv_repeat_calls_bitwise(gpu):
+    T, N, K = 4, 1024, 4096
+    d = synth.q8_0_gemv_inputs(T=T)
+    wbuf, x = q8_0_from_f32(to_dev(d["w"])), to_dev(d["x"])
+    y0, _, _ = _gemv(gpu, wbuf, x, T, N, K)
+    for _ in range(3):
+        y1, _, _ = _gemv(gpu, wbuf, x, T, N, K)
+        torch.cuda.synchronize()
+        assert torch.equal(y0, y1)
+
+
+def test_down_workspace_poison_and_replay(gpu):
+    """Every call rewrites every partial sum it reads: poisoning the workspace between calls
+    (NaN bit patterns) changes nothing, and a captured graph replays bitwise."""
+    T, N, K = 6, 320, 16384
+    d = synth.hc_inputs(T)
+    wd = q8_0_from_f32(to_dev(d["w_down"]))
+    R, wn = to_dev(d["R"]), to_dev(d["w_norm"])
+    nb = gpu.gq8_workspace_bytes(gpu.OP_HC_DOWN, T, N, K)
+    ws = workspace(nb)
+    lo0 = torch.empty((T, N), dtype=torch.int16, device="cuda")
+    rs0 = torch.empty((T,), dtype=torch.float32, device="cuda")
+    gpu.gq8_hc_q8_down(wd, R, wn, 1e-6, lo0, rs0, T, N, K, ws, nb)
+    torch.cuda.synchronize()
+    lo, rs = torch.zeros_like(lo0), torch.zeros_like(rs0)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            gpu.gq8_hc_q8_down(wd, R, wn, 1e-6, lo, rs, T, N, K, ws, nb, s)
+    for _ in range(3):
+        ws.fill_(0xFF)
+        lo.zero_()
+        rs.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(lo, lo0) and torch.equal(rs, rs0)
+
+
+def test_gemv_graph_replay_bitwise(gpu):
+    T, N, K = 6, 512, 4096
+    w = synth.normal_f32(13, "gpu.gemv.g", (N, K), 0.0, 0.02)
+    x = to_dev(synth.normal_f32(13, "gpu.gemv.gx", (T, K)))
+    wbuf = q8_0_from_f32(to_dev(w))
+    y_direct, ws, nb = _gemv(gpu, wbuf, x, T, N, K)
+    torch.cuda.synchronize()
+    y = torch.zeros_like(y_direct)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            gpu.gq8_q8_0_gemv(wbuf, x, y, T, N, K, ws, nb, s)
+    for _ in range(3):
+        y.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_direct)
+
+
+def test_gemv_empty_and_zero_k(gpu):
+    y = torch.full((2, 8), 7.0, device="cuda")
+    gpu.gq8_q8_0_gemv(None, None, y, 2, 8, 0, None, 0)
+    torch.cuda.synchronize()
+    assert int(y.count_nonzero()) == 0
+    gpu.gq8_q8_0_gemv(None, None, None, 0, 8, 64, None, 0)   # T = 0: nothing to do
+
+
+# ------------------------------------------------------------------------------ hyper-connection
+
+def _down(gpu, wbuf, R, wn, T, N, K, eps=1e-6):
+    nb = gpu.gq8_workspace_bytes(gpu.OP_HC_DOWN, T, N, K)
+    ws = workspace(nb)
+    lo = torch.empty((T, N), dtype=torch.int16, device="cuda")
+    rs = torch.empty((T,), dtype=torch.float32, device="cuda")
+    gpu.gq8_hc_q8_down(wbuf, R, wn, eps, lo, rs, T, N, K, ws, nb)
+    return lo, rs
+
+
+def _up(gpu, wbuf, lo, T, N, K):
+    nb = gpu.gq8_workspace_bytes(gpu.OP_HC_UP, T, N, K)
+    ws = workspace(nb)
+    out = torch.empty((T, N), dtype=torch.int16, device="cuda")
+    gpu.gq8_hc_q8_up(wbuf, lo, out, T, N, K, ws, nb)
+    return out
+
+
+@pytest.mark.parametrize("T,N,K", [(1, 37, 2048), (4, 10, 1056), (6, 64, 96), (16, 9, 4096)])
+def test_down_matches_oracle_small(gpu, T, N, K):
+    d = synth.hc_inputs(T, K=K, N=N, seed=20)
+    lo, rs = _down(gpu, q8_0_from_f32(to_dev(d["w_down"])), to_dev(d["R"]), to_dev(d["w_norm"]), T, N, K)
+    lo_ref, rs_ref, S = hc_down(d["R"], d["w_norm"], quantize_q8_0(d["w_down"]))
+    check_bf16(to_host(lo, np.uint16), lo_ref, S, f"down T={T} N={N} K={K}")
+    assert np.allclose(to_host(rs), rs_ref, rtol=1e-5, atol=0)
+
+
+@pytest.mark.parametrize("T", [1, 4, 6])
+def test_hc_pair_full_size(gpu, T):
+    d = synth.hc_inputs(T)
+    bd, bu = quantize_q8_0(d["w_down"]), quantize_q8_0(d["w_up"])
+    wd, wu = q8_0_from_f32(to_dev(d["w_down"])), q8_0_from_f32(to_dev(d["w_up"]))
+    lo, rs = _down(gpu, wd, to_dev(d["R"]), to_dev(d["w_norm"]), T, 320, 16384)
+    lo_ref, rs_ref, S = hc_down(d["R"], d["w_norm"], bd)
+    lo_h = to_host(lo, np.uint16)
+    check_bf16(lo_h, lo_ref, S, f"down full T={T}")
+    assert np.allclose(to_host(rs), rs_ref, rtol=1e-5, atol=0)
+
+    # up read on its own: the same bf16 input on both sides (the oracle's own rounding of lo)
+    from oracle.numerics import bf16_bits
+    lo_in = bf16_bits(lo_ref.astype(np.float32))
+    out = _up(gpu, wu, to_dev(lo_in), T, 16384, 320)
+    out_ref, S_up = hc_up(lo_in, bu)
+    check_bf16(to_host(out, np.uint16), out_ref, S_up, f"up full T={T}")
+
+    # chained: GPU down -> GPU up against oracle down -> oracle up, tolerance widened by the
+    # bf16 rounding of lo (one spacing either way) and the down read's own tolerance
+    out2 = _up(gpu, wu, lo, T, 16384, 320)
+    ref_chain, _ = hc_up(lo_in, bu)
+    from oracle.q8 import dequantize
+    from oracle.numerics import bf16_ulp
+    Wu = np.abs(dequantize(bu))
+    dlo = 2e-3 * S + bf16_ulp(np.abs(lo_ref) + 2e-3 * S)
+    S_chain = S_up + dlo @ Wu.T / 2e-3
+    check_bf16(to_host(out2, np.uint16), ref_chain, S_chain, f"hc chain T={T}")
+
+
+@pytest.mark.parametrize("T,N,K", [(1, 100, 320), (4, 77, 320), (6, 5, 64), (9, 40, 1024), (16, 33, 320)])
+def test_up_matches_oracle_small(gpu, T, N, K):
+    w = synth.normal_f32(21, "gpu.up.w", (N, K), 0.0, 0.02)
+    lo = synth.bf16_normal(21, "gpu.up.lo", (T, K))
+    out = _up(gpu, q8_0_from_f32(to_dev(w)), to_dev(lo), T, N, K)
+    ref, S = hc_up(lo, quantize_q8_0(w))
+    check_bf16(to_host(out, np.uint16), ref, S, f"up T={T} N={N} K={K}")
+
+
+def test_down_scale_invariance_on_gpu(gpu):
+    """R scaled by 4 leaves lo unchanged up to rounding: rs is applied after the dot."""
+    T, N, K = 2, 64, 4096
+    d = synth.hc_inputs(T, K=K, N=N, seed=22)
+    wd = q8_0_from_f32(to_dev(d["w_down"]))
+    R4 = (bf16_to_f32(d["R"]) * np.float32(4.0)).view(np.uint32) >> np.uint32(16)
+    lo1, rs1 = _down(gpu, wd, to_dev(d["R"]), to_dev(d["w_norm"]), T, N, K)
+    lo4, rs4 = _down(gpu, wd, to_dev(R4.astype(np.uint16)), to_dev(d["w_norm"]), T, N, K)
+    a = bf16_to_f32(to_host(lo1, np.uint16))
+    b = bf16_to_f32(to_host(lo4, np.uint16))
+    assert np.allclose(a, b, rtol=2 ** -7, atol=1e-6)
+    assert np.allclose(to_host(rs1), 4 * to_host(rs4), rtol=1e-5)
