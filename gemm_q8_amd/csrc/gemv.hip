@@ -106,7 +106,7 @@ __global__ void __launch_bounds__(64 * MAXW) gemv_rows_kernel(GemvArgs a) {
     }
 }
 
-template <int T> constexpr int gemv_rw() { return T <= 2 ? 8 : (T <= 4 ? 4 : (T <= 8 ? 2 : 1)); }
+template <int T> constexpr int gemv_rw() { return T <= 4 ? 2 : 1; }
 
 template <int T>
 static int launch_gemv_t(GemvArgs a, hipStream_t st) {
@@ -140,95 +140,117 @@ int launch_q8_0_gemv(GemvArgs a, hipStream_t st) { GQ8_T_SWITCH(launch_gemv_t, a
 // ------------------------------------------------------------------------------ down read
 
 constexpr int kDnNB = kDownSlab / 32;     // Q8_0 blocks per slab
+constexpr int kDnStride = kDownSlab + 16; // padded LDS row stride of a wave's weight tile (bytes)
 
-template <int T> constexpr int vmax_for() { return T <= 8 ? 4 : (T <= 16 ? 8 : 16); }
-
-// One work-group: slab blockIdx.x (128 columns) x up to 16 row tiles of 32 (one per wave).
+// One work-group: slab blockIdx.x (128 columns) x up to 16 waves of 32 rows (two 16-row MFMA
+// tiles each). Each wave reads its 32 x 128-byte weight tile with four coalesced 1 KiB loads
+// (eight 128-byte row segments per load) into LDS and takes the MFMA operands from there.
 template <int T>
 __global__ void __launch_bounds__(1024) hc_down_partial_kernel(GemvArgs a) {
-    constexpr int VMAX = vmax_for<T>();
-    __shared__ u32x4 ua[2][kDnNB][2][64];           // u hi / lo pieces in MFMA A layout
-    __shared__ float sq[kDnNB][2][2][32];           // sum of R^2 of each staged 8-column piece
+    __shared__ u32x4 ua[2][kDnNB][64];                            // u hi / lo, 16x16x32 A layout
+    __shared__ float sq[kDnNB][4][16];                            // sums of R^2 per 8-column piece
+    __shared__ __attribute__((aligned(16))) uint8_t wt[16][32 * kDnStride];   // weight tiles
+    __shared__ uint16_t ws[16][32][kDnNB];                        // their block scales
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int N = a.N, K = a.K, nblk = K >> 5;
     const int s = blockIdx.x;
     const int k0 = s * kDownSlab;
-    const int rt = blockIdx.y * 16 + wave;
-    const int g = lane >> 5;
-    const int n = rt * 32 + (lane & 31);
-    const int nc = imin(n, N - 1);
+    const int r0 = (blockIdx.y * 16 + wave) * 32;                 // first row of this wave
     const uint16_t* R = reinterpret_cast<const uint16_t*>(a.x);
 
-    // 1. weight quants and scales of this wave's 32 rows x 4 blocks (clamped, masked later)
-    u32x4 wq[kDnNB];
-    uint16_t wd[kDnNB];
+    // 1. coalesced weight loads: load i covers rows 8i..8i+7 of the tile, 16 bytes per lane
+    u32x4 wv[4];
 #pragma unroll
-    for (int b = 0; b < kDnNB; ++b) {
-        const int kb = imin(k0 + 32 * b, K - 32);
-        wq[b] = ld_nt16(a.q + (size_t)nc * K + kb + 16 * g);
-        wd[b] = a.d[(size_t)nc * nblk + (kb >> 5)];
+    for (int i = 0; i < 4; ++i) {
+        const int row = imin(r0 + 8 * i + (lane >> 3), N - 1);
+        const int kb = imin(k0 + 16 * (lane & 7), K - 16);
+        wv[i] = ld_nt16(a.q + (size_t)row * K + kb);
+    }
+    uint16_t sc[kDnNB];
+    {
+        const int row = imin(r0 + (lane & 31), N - 1);
+#pragma unroll
+        for (int b = 0; b < kDnNB; ++b) sc[b] = a.d[(size_t)row * nblk + imin((k0 >> 5) + b, nblk - 1)];
     }
 
-    // 2. stage u = R * w_norm for the slab as exact bf16 hi + lo, and R^2 sums
-    for (int it = threadIdx.x; it < kDnNB * 2 * 64; it += blockDim.x) {
-        const int b = it >> 7, m = (it >> 6) & 1, l = it & 63;
-        const int t = l & 31, gg = l >> 5;
-        const int k = k0 + 32 * b + 16 * gg + 8 * m;
-        const bool ok = t < a.T && k < K;
+    // 2. stage u = R * w_norm for the slab as exact bf16 hi + lo (A operand: lane l holds row
+    //    t = l % 16, columns 32b + 8(l/16) .. +8), and the R^2 sums
+    for (int it = threadIdx.x; it < kDnNB * 64; it += blockDim.x) {
+        const int b = it >> 6, l = it & 63;
+        const int t = l & 15, gg = l >> 4;
+        const int k = k0 + 32 * b + 8 * gg;
+        const bool ok = t < T && k < K;
         const int kc = ok ? k : 0, tc = ok ? t : 0;
         const uint4 rv = *reinterpret_cast<const uint4*>(R + (size_t)tc * K + kc);
-        const uint4 wv = *reinterpret_cast<const uint4*>(a.wnorm + kc);
-        const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w}, ww[4] = {wv.x, wv.y, wv.z, wv.w};
+        const uint4 nv = *reinterpret_cast<const uint4*>(a.wnorm + kc);
+        const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w}, ww[4] = {nv.x, nv.y, nv.z, nv.w};
         uint32_t hi[4], lo[4];
         float r2 = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float r0 = __uint_as_float(rw[i] << 16), r1 = __uint_as_float(rw[i] & 0xffff0000u);
+            const float q0 = __uint_as_float(rw[i] << 16), q1 = __uint_as_float(rw[i] & 0xffff0000u);
             const float w0 = __uint_as_float(ww[i] << 16), w1 = __uint_as_float(ww[i] & 0xffff0000u);
-            const float u0 = ok ? r0 * w0 : 0.f, u1 = ok ? r1 * w1 : 0.f;   // exact products
+            const float u0 = ok ? q0 * w0 : 0.f, u1 = ok ? q1 * w1 : 0.f;   // exact products
             const uint16_t h0 = f2bf_bits(u0), h1 = f2bf_bits(u1);
             const float l0 = u0 - bf2f(h0), l1 = u1 - bf2f(h1);             // exact residuals
             hi[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
             lo[i] = pack_bf16_trunc(l0, l1);                                // exact in bf16
-            r2 = fmaf(r0, r0, r2);
-            r2 = fmaf(r1, r1, r2);
+            r2 = fmaf(q0, q0, r2);
+            r2 = fmaf(q1, q1, r2);
         }
-        ua[0][b][m][l] = u32x4{hi[0], hi[1], hi[2], hi[3]};
-        ua[1][b][m][l] = u32x4{lo[0], lo[1], lo[2], lo[3]};
-        sq[b][m][gg][t] = ok ? r2 : 0.f;
+        ua[0][b][l] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+        ua[1][b][l] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+        sq[b][gg][t] = ok ? r2 : 0.f;
+    }
+    // 3. the wave's weight tile and scales into LDS
+    uint8_t* tile = wt[wave];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4*>(tile + (8 * i + (lane >> 3)) * kDnStride + 16 * (lane & 7)) = wv[i];
+    if (lane < 32) {
+#pragma unroll
+        for (int b = 0; b < kDnNB; ++b) ws[wave][lane][b] = sc[b];
     }
     __syncthreads();
 
-    // 3. per block: four exact-product MFMAs, then the block scale
-    f32x16 acc = {};
+    // 4. per block and 16-row half: two exact-product MFMAs (hi, lo), then the block scale
+    const int j = lane & 15, g = lane >> 4;
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int b = 0; b < kDnNB; ++b) {
         const bool bok = k0 + 32 * b < K;
-        const float dsc = bok ? h2f(wd[b]) : 0.f;
-        const bf16x8 b0 = i8x8_to_bf16x8(wq[b].x, wq[b].y);
-        const bf16x8 b1 = i8x8_to_bf16x8(wq[b].z, wq[b].w);
-        f32x16 D = {};
-        D = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, ua[0][b][0][lane]), b0, D);
-        D = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, ua[1][b][0][lane]), b0, D);
-        D = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, ua[0][b][1][lane]), b1, D);
-        D = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, ua[1][b][1][lane]), b1, D);
+        const bf16x8 ahi = __builtin_bit_cast(bf16x8, ua[0][b][lane]);
+        const bf16x8 alo = __builtin_bit_cast(bf16x8, ua[1][b][lane]);
 #pragma unroll
-        for (int v = 0; v < VMAX; ++v) acc[v] = fmaf(dsc, D[v], acc[v]);
+        for (int h = 0; h < 2; ++h) {
+            const int row = 16 * h + j;
+            const uint2 q = *reinterpret_cast<const uint2*>(tile + row * kDnStride + 32 * b + 8 * g);
+            const bf16x8 w = i8x8_to_bf16x8(q.x, q.y);
+            f32x4 D = {0.f, 0.f, 0.f, 0.f};
+            D = mfma_bf16_16x16x32(ahi, w, D);
+            D = mfma_bf16_16x16x32(alo, w, D);
+            const float dsc = bok ? h2f(ws[wave][row][b]) : 0.f;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[h][v] = fmaf(dsc, D[v], acc[h][v]);
+        }
     }
 
-    // 4. partial sums of this slab: part[s][t][n], and the slab's sum of R^2 per row t
+    // 5. partial sums of this slab: part[s][t][n], and the slab's sum of R^2 per row t
 #pragma unroll
-    for (int v = 0; v < VMAX; ++v) {
-        const int t = mfma32_row(v, lane);
-        if (t < a.T && n < N) a.part[((size_t)s * a.T + t) * N + n] = acc[v];
+    for (int h = 0; h < 2; ++h) {
+        const int n = r0 + 16 * h + j;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int t = 4 * g + v;
+            if (t < T && n < N) a.part[((size_t)s * T + t) * N + n] = acc[h][v];
+        }
     }
-    if (blockIdx.y == 0 && threadIdx.x < a.T) {
+    if (blockIdx.y == 0 && threadIdx.x < T) {
         const int t = threadIdx.x;
         float v = 0.f;
         for (int b = 0; b < kDnNB; ++b)
-            for (int m = 0; m < 2; ++m)
-                for (int gg = 0; gg < 2; ++gg) v += sq[b][m][gg][t];
-        a.ssq[(size_t)s * a.T + t] = v;
+            for (int gg = 0; gg < 4; ++gg) v += sq[b][gg][t];
+        a.ssq[(size_t)s * T + t] = v;
     }
 }
 
@@ -300,62 +322,137 @@ int launch_hc_down(GemvArgs a, void* ws, hipStream_t st) { GQ8_T_SWITCH(launch_d
 
 // ------------------------------------------------------------------------------ up read
 
-constexpr int kUpCB = 10;                 // Q8_0 blocks per register batch (K = 320 in one)
+constexpr int kUpCW = 320;                  // columns per chunk (the K = 320 read is one chunk)
+constexpr int kUpCB = kUpCW / 32;           // Q8_0 blocks per chunk
+constexpr int kUpStride = kUpCW + 16;       // padded LDS row stride of a weight tile (bytes)
+constexpr int kUpLoStride = 2 * kUpCW + 16; // padded LDS row stride of the bf16 input (bytes)
+constexpr int kUpLoads = 16 * kUpCW / 1024; // coalesced 1 KiB loads per 16-row tile chunk
 
-template <int T>
+// One wave per 16 output rows (one 16x16x32 MFMA per Q8_0 block); a work-group of 4 waves
+// shares the staged input chunk. A wave's 16 rows x 320 bytes are one contiguous 5 KiB range:
+// five coalesced 1 KiB loads into LDS, then MFMA operands (row = lane % 16) out of LDS.
+// FULL: every chunk is 320 columns wide (K % 320 == 0), so every load, LDS access and MFMA of a
+// chunk is unconditional and the three phases (LDS reads, MFMAs, scale FMAs) issue back to back.
+template <int T, bool FULL>
 __global__ void __launch_bounds__(256) hc_up_kernel(GemvArgs a) {
-    constexpr int VMAX = vmax_for<T>();
+    __shared__ __attribute__((aligned(16))) uint8_t wt[4][16 * kUpStride];
+    __shared__ uint16_t wsc[4][16][kUpCB];
+    __shared__ __attribute__((aligned(16))) uint8_t xl[kMaxT][kUpLoStride];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int N = a.N, K = a.K, nblk = K >> 5;
-    const int rt = blockIdx.x * 4 + wave;
-    const int g = lane >> 5, t = lane & 31;
-    const int n = rt * 32 + t;
-    const int nc = imin(n, N - 1);
-    const int tc = t < T ? t : 0;
+    const int r0 = (blockIdx.x * 4 + wave) * 16;
+    const int j = lane & 15, g = lane >> 4;
     const uint16_t* lo = reinterpret_cast<const uint16_t*>(a.x);
+    const u32x4 z = {0u, 0u, 0u, 0u};
 
-    f32x16 acc = {};
-    for (int cb = 0; cb < nblk; cb += kUpCB) {
-        u32x4 wq[kUpCB];
-        uint16_t wd[kUpCB];
-        u32x4 xa[kUpCB][2];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < K; c0 += kUpCW) {
+        const int cw = FULL ? kUpCW : (K - c0 < kUpCW ? K - c0 : kUpCW);   // multiple of 32
+        const int np = cw >> 4;                             // 16-byte pieces per weight row
+        const int cb = cw >> 5;
+        const int npx = cw >> 3;                            // 16-byte pieces per input row
+        // weights: piece e = i*64 + lane of the tile -> (row e/np, piece e%np)
+        u32x4 wv[kUpLoads];
 #pragma unroll
-        for (int b = 0; b < kUpCB; ++b) {
-            const int bb = imin(cb + b, nblk - 1);
-            wq[b] = ld_nt16(a.q + (size_t)nc * K + 32 * bb + 16 * g);
-            wd[b] = a.d[(size_t)nc * nblk + bb];
+        for (int i = 0; i < kUpLoads; ++i) {
+            const int e = imin(i * 64 + lane, 16 * np - 1);
+            const int row = e / np, pc = e - row * np;
+            wv[i] = ld_nt16(a.q + (size_t)imin(r0 + row, N - 1) * K + c0 + 16 * pc);
+        }
+        uint16_t sv[3];
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
-                xa[b][m] = *reinterpret_cast<const u32x4*>(lo + (size_t)tc * K + 32 * bb + 16 * g + 8 * m);
+        for (int i = 0; i < 3; ++i) {
+            const int e = imin(i * 64 + lane, 16 * cb - 1);
+            const int row = e / cb, b = e - row * cb;
+            sv[i] = a.d[(size_t)imin(r0 + row, N - 1) * nblk + (c0 >> 5) + b];
+        }
+        // the input chunk, shared by the work-group: T rows x npx pieces of 8 bf16
+        u32x4 xv[3];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int e = imin(i * 256 + (int)threadIdx.x, T * npx - 1);
+            const int t = e / npx, pc = e - t * npx;
+            xv[i] = *reinterpret_cast<const u32x4*>(lo + (size_t)t * K + c0 + 8 * pc);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int b = 0; b < kUpCB; ++b) {
-            if (cb + b < nblk) {
-                const float dsc = h2f(wd[b]);
-                const u32x4 z = {0u, 0u, 0u, 0u};
-                const bf16x8 a0 = __builtin_bit_cast(bf16x8, t < T ? xa[b][0] : z);
-                const bf16x8 a1 = __builtin_bit_cast(bf16x8, t < T ? xa[b][1] : z);
-                f32x16 D = {};
-                D = mfma_bf16_32x32x16(a0, i8x8_to_bf16x8(wq[b].x, wq[b].y), D);
-                D = mfma_bf16_32x32x16(a1, i8x8_to_bf16x8(wq[b].z, wq[b].w), D);
-#pragma unroll
-                for (int v = 0; v < VMAX; ++v) acc[v] = fmaf(dsc, D[v], acc[v]);
+        for (int i = 0; i < kUpLoads; ++i) {
+            const int e = i * 64 + lane;
+            if (FULL || e < 16 * np) {
+                const int row = e / np, pc = e - row * np;
+                *reinterpret_cast<u32x4*>(&wt[wave][row * kUpStride + 16 * pc]) = wv[i];
             }
         }
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int e = i * 64 + lane;
+            if (e < 16 * cb) wsc[wave][e / cb][e % cb] = sv[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int e = i * 256 + (int)threadIdx.x;
+            if (e < T * npx) {
+                const int t = e / npx, pc = e - t * npx;
+                *reinterpret_cast<u32x4*>(&xl[t][16 * pc]) = xv[i];
+            }
+        }
+        __syncthreads();
+        const int tj = j < T ? j : 0;
+        if (FULL) {
+            uint2 q[kUpCB];
+            u32x4 x[kUpCB];
+            uint16_t sc[kUpCB];
+#pragma unroll
+            for (int b = 0; b < kUpCB; ++b) {
+                q[b] = *reinterpret_cast<const uint2*>(&wt[wave][j * kUpStride + 32 * b + 8 * g]);
+                x[b] = *reinterpret_cast<const u32x4*>(&xl[tj][2 * (32 * b + 8 * g)]);
+                sc[b] = wsc[wave][j][b];
+            }
+            f32x4 D[kUpCB];
+#pragma unroll
+            for (int b = 0; b < kUpCB; ++b) {
+                const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
+                D[b] = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8, j < T ? x[b] : z),
+                                          i8x8_to_bf16x8(q[b].x, q[b].y), zf);
+            }
+#pragma unroll
+            for (int b = 0; b < kUpCB; ++b) {
+                const float dsc = h2f(sc[b]);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[v] = fmaf(dsc, D[b][v], acc[v]);
+            }
+        } else {
+#pragma unroll
+            for (int b = 0; b < kUpCB; ++b) {
+                if (b < cb) {
+                    const uint2 q = *reinterpret_cast<const uint2*>(&wt[wave][j * kUpStride + 32 * b + 8 * g]);
+                    const u32x4 x = *reinterpret_cast<const u32x4*>(&xl[tj][2 * (32 * b + 8 * g)]);
+                    f32x4 D = {0.f, 0.f, 0.f, 0.f};
+                    D = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8, j < T ? x : z), i8x8_to_bf16x8(q.x, q.y), D);
+                    const float dsc = h2f(wsc[wave][j][b]);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[v] = fmaf(dsc, D[v], acc[v]);
+                }
+            }
+        }
+        if (c0 + kUpCW < K) __syncthreads();                // the next chunk overwrites LDS
     }
     uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+    const int n = r0 + j;
 #pragma unroll
-    for (int v = 0; v < VMAX; ++v) {
-        const int tt = mfma32_row(v, lane);
-        if (tt < T && n < N) out[(size_t)tt * N + n] = f2bf_bits(acc[v]);
+    for (int v = 0; v < 4; ++v) {
+        const int t = 4 * g + v;
+        if (t < T && n < N) out[(size_t)t * N + n] = f2bf_bits(acc[v]);
     }
 }
 
 template <int T>
 static int launch_up_t(GemvArgs a, hipStream_t st) {
-    const int ntile = (a.N + 31) / 32;
-    hipLaunchKernelGGL((hc_up_kernel<T>), dim3((ntile + 3) / 4), dim3(256), 0, st, a);
+    const int ntile = (a.N + 15) / 16;
+    if (a.K % kUpCW == 0)
+        hipLaunchKernelGGL((hc_up_kernel<T, true>), dim3((ntile + 3) / 4), dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((hc_up_kernel<T, false>), dim3((ntile + 3) / 4), dim3(256), 0, st, a);
     return launch_status();
 }
 
