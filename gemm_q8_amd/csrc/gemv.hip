@@ -139,132 +139,207 @@ int launch_q8_0_gemv(GemvArgs a, hipStream_t st) { GQ8_T_SWITCH(launch_gemv_t, a
 
 // ------------------------------------------------------------------------------ down read
 
-constexpr int kDnNB = kDownSlab / 32;     // Q8_0 blocks per slab
-constexpr int kDnStride = kDownSlab + 16; // padded LDS row stride of a wave's weight tile (bytes)
+constexpr int kDnNB = kDownSlab / 32;      // Q8_0 blocks per slab
+constexpr int kDnStride = kDownSlab + 16;  // padded LDS row stride of a wave's weight tile (bytes)
+constexpr int kDnRows = 64;                // rows per work-group: four waves of 16
 
-// One work-group: slab blockIdx.x (128 columns) x up to 16 waves of 32 rows (two 16-row MFMA
-// tiles each). Each wave reads its 32 x 128-byte weight tile with four coalesced 1 KiB loads
-// (eight 128-byte row segments per load) into LDS and takes the MFMA operands from there.
+// One work-group: slab blockIdx.x (512 columns) x 64 rows (blockIdx.y), one 16-row MFMA tile per
+// wave. The A operand is u = R * w_norm for the slab, staged once per work-group as exact bf16
+// hi and lo parts; for T <= 8 the two parts share one A operand (rows 0..7 hi, rows 8..15 lo of
+// token t), so one MFMA per block does both, and the hi and lo results are added at the end
+// (the block scale multiplies both). A wave reads its 16 x 512-byte weight tile in two column
+// halves of four coalesced 1 KiB loads (four rows x 256 bytes each), in the order the work
+// consumes them: activations first, then half 0, then half 1, so that the LDS transpose and
+// MFMAs of half 0 run while half 1 is still in flight. The weight tile is private to its wave.
 template <int T>
-__global__ void __launch_bounds__(1024) hc_down_partial_kernel(GemvArgs a) {
-    __shared__ u32x4 ua[2][kDnNB][64];                            // u hi / lo, 16x16x32 A layout
-    __shared__ float sq[kDnNB][4][16];                            // sums of R^2 per 8-column piece
-    __shared__ __attribute__((aligned(16))) uint8_t wt[16][32 * kDnStride];   // weight tiles
-    __shared__ uint16_t ws[16][32][kDnNB];                        // their block scales
+__global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
+    constexpr bool PACK = T <= 8;
+    constexpr int NPL = PACK ? 1 : 2;                              // A planes (hi, lo)
+    constexpr int TR = PACK ? 8 : 16;                              // token rows per plane
+    constexpr int NI = kDnNB * 4 * TR / 256;                       // staging items per thread
+    __shared__ u32x4 ua[NPL][kDnNB][64];                           // A operands, lane order
+    __shared__ float sqw[4][TR];                                   // per-wave sums of R^2
+    __shared__ __attribute__((aligned(16))) uint8_t wt[4][16 * kDnStride];
+    __shared__ __attribute__((aligned(16))) uint16_t wsc[4][16][kDnNB];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int N = a.N, K = a.K, nblk = K >> 5;
     const int s = blockIdx.x;
     const int k0 = s * kDownSlab;
-    const int r0 = (blockIdx.y * 16 + wave) * 32;                 // first row of this wave
+    const int cw = imin(kDownSlab, K - k0);                        // multiple of 32
+    const int cb = cw >> 5;
+    const int r0 = blockIdx.y * kDnRows + 16 * wave;               // first row of this wave
     const uint16_t* R = reinterpret_cast<const uint16_t*>(a.x);
 
-    // 1. coalesced weight loads: load i covers rows 8i..8i+7 of the tile, 16 bytes per lane
-    u32x4 wv[4];
+    // 0. activations: item it = 256 j + thread covers token t = it % TR (the same t for every
+    //    j), columns 32b + 8g .. +8 with b = it / (4 TR), g = (it / TR) % 4
+    const int t = (int)threadIdx.x % TR;
+    uint4 rv[NI], nv[NI];
+    bool okv[NI];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = imin(r0 + 8 * i + (lane >> 3), N - 1);
-        const int kb = imin(k0 + 16 * (lane & 7), K - 16);
-        wv[i] = ld_nt16(a.q + (size_t)row * K + kb);
+    for (int i = 0; i < NI; ++i) {
+        const int it = 256 * i + (int)threadIdx.x;
+        const int b = it / (4 * TR), g = (it / TR) & 3;
+        const int k = k0 + 32 * b + 8 * g;
+        okv[i] = t < T && 32 * b < cw;
+        const int kc = okv[i] ? k : 0, tc = okv[i] ? t : 0;
+        rv[i] = *reinterpret_cast<const uint4*>(R + (size_t)tc * K + kc);
+        nv[i] = *reinterpret_cast<const uint4*>(a.wnorm + kc);
     }
-    uint16_t sc[kDnNB];
+    // block scales: lane l holds row l/4, blocks 4(l%4) .. +3
+    uint16_t sc[4];
     {
-        const int row = imin(r0 + (lane & 31), N - 1);
+        const int row = imin(r0 + (lane >> 2), N - 1);
 #pragma unroll
-        for (int b = 0; b < kDnNB; ++b) sc[b] = a.d[(size_t)row * nblk + imin((k0 >> 5) + b, nblk - 1)];
+        for (int j = 0; j < 4; ++j)
+            sc[j] = a.d[(size_t)row * nblk + imin((k0 >> 5) + 4 * (lane & 3) + j, nblk - 1)];
     }
+    // 1. weights: half h, load i covers rows 4i .. 4i+3, columns 256h .. +256 (16 lanes a row)
+    u32x4 wv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int h = i >> 2;
+        const int row = imin(r0 + 4 * (i & 3) + (lane >> 4), N - 1);
+        const int col = k0 + imin(256 * h + 16 * (lane & 15), cw - 16);
+        wv[i] = ld_nt16(a.q + (size_t)row * K + col);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
-    // 2. stage u = R * w_norm for the slab as exact bf16 hi + lo (A operand: lane l holds row
-    //    t = l % 16, columns 32b + 8(l/16) .. +8), and the R^2 sums
-    for (int it = threadIdx.x; it < kDnNB * 64; it += blockDim.x) {
-        const int b = it >> 6, l = it & 63;
-        const int t = l & 15, gg = l >> 4;
-        const int k = k0 + 32 * b + 8 * gg;
-        const bool ok = t < T && k < K;
-        const int kc = ok ? k : 0, tc = ok ? t : 0;
-        const uint4 rv = *reinterpret_cast<const uint4*>(R + (size_t)tc * K + kc);
-        const uint4 nv = *reinterpret_cast<const uint4*>(a.wnorm + kc);
-        const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w}, ww[4] = {nv.x, nv.y, nv.z, nv.w};
+    // 2. u = R * w_norm, exact in fp32, split exactly into bf16 hi + lo, written as A operands:
+    //    lane l of block b holds row l%16, columns 32b + 8(l/16) .. +8
+    float r2acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int it = 256 * i + (int)threadIdx.x;
+        const int b = it / (4 * TR), g = (it / TR) & 3;
+        const bool ok = okv[i];
+        const uint32_t rw[4] = {rv[i].x, rv[i].y, rv[i].z, rv[i].w};
+        const uint32_t ww[4] = {nv[i].x, nv[i].y, nv[i].z, nv[i].w};
         uint32_t hi[4], lo[4];
         float r2 = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float q0 = __uint_as_float(rw[i] << 16), q1 = __uint_as_float(rw[i] & 0xffff0000u);
-            const float w0 = __uint_as_float(ww[i] << 16), w1 = __uint_as_float(ww[i] & 0xffff0000u);
+        for (int e = 0; e < 4; ++e) {
+            const float q0 = __uint_as_float(rw[e] << 16), q1 = __uint_as_float(rw[e] & 0xffff0000u);
+            const float w0 = __uint_as_float(ww[e] << 16), w1 = __uint_as_float(ww[e] & 0xffff0000u);
             const float u0 = ok ? q0 * w0 : 0.f, u1 = ok ? q1 * w1 : 0.f;   // exact products
             const uint16_t h0 = f2bf_bits(u0), h1 = f2bf_bits(u1);
             const float l0 = u0 - bf2f(h0), l1 = u1 - bf2f(h1);             // exact residuals
-            hi[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-            lo[i] = pack_bf16_trunc(l0, l1);                                // exact in bf16
+            hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            lo[e] = pack_bf16_trunc(l0, l1);                                // exact in bf16
             r2 = fmaf(q0, q0, r2);
             r2 = fmaf(q1, q1, r2);
         }
-        ua[0][b][l] = u32x4{hi[0], hi[1], hi[2], hi[3]};
-        ua[1][b][l] = u32x4{lo[0], lo[1], lo[2], lo[3]};
-        sq[b][gg][t] = ok ? r2 : 0.f;
+        if (PACK) {
+            ua[0][b][16 * g + t] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+            ua[0][b][16 * g + 8 + t] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+        } else {
+            ua[0][b][16 * g + t] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+            ua[NPL - 1][b][16 * g + t] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+        }
+        r2acc += ok ? r2 : 0.f;
     }
-    // 3. the wave's weight tile and scales into LDS
-    uint8_t* tile = wt[wave];
+    // sums of R^2 of token t: over the lanes of the wave holding t (lane bits above TR), then
+    // over the waves (in the epilogue), in a fixed order
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4*>(tile + (8 * i + (lane >> 3)) * kDnStride + 16 * (lane & 7)) = wv[i];
-    if (lane < 32) {
-#pragma unroll
-        for (int b = 0; b < kDnNB; ++b) ws[wave][lane][b] = sc[b];
+    for (int m = TR; m < 64; m <<= 1) r2acc += __shfl_xor(r2acc, m, 64);
+    if (lane < TR) sqw[wave][lane] = r2acc;
+    {
+        uint2 sv;
+        sv.x = (uint32_t)sc[0] | ((uint32_t)sc[1] << 16);
+        sv.y = (uint32_t)sc[2] | ((uint32_t)sc[3] << 16);
+        *reinterpret_cast<uint2*>(&wsc[wave][lane >> 2][4 * (lane & 3)]) = sv;
     }
     __syncthreads();
 
-    // 4. per block and 16-row half: two exact-product MFMAs (hi, lo), then the block scale
+    // 3. per half: weight tile into LDS (this wave only), then per block one MFMA (two for
+    //    T > 8) on the exact operands and the block scale (0 past the slab end)
     const int j = lane & 15, g = lane >> 4;
-    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    uint8_t* tile = wt[wave];
+    const u32x4 s01 = *reinterpret_cast<const u32x4*>(&wsc[wave][j][0]);
+    const u32x4 s23 = *reinterpret_cast<const u32x4*>(&wsc[wave][j][8]);
+    const uint32_t sw[8] = {s01.x, s01.y, s01.z, s01.w, s23.x, s23.y, s23.z, s23.w};
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int b = 0; b < kDnNB; ++b) {
-        const bool bok = k0 + 32 * b < K;
-        const bf16x8 ahi = __builtin_bit_cast(bf16x8, ua[0][b][lane]);
-        const bf16x8 alo = __builtin_bit_cast(bf16x8, ua[1][b][lane]);
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int row = 16 * h + j;
-            const uint2 q = *reinterpret_cast<const uint2*>(tile + row * kDnStride + 32 * b + 8 * g);
-            const bf16x8 w = i8x8_to_bf16x8(q.x, q.y);
-            f32x4 D = {0.f, 0.f, 0.f, 0.f};
-            D = mfma_bf16_16x16x32(ahi, w, D);
-            D = mfma_bf16_16x16x32(alo, w, D);
-            const float dsc = bok ? h2f(ws[wave][row][b]) : 0.f;
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<u32x4*>(tile + (4 * i + (lane >> 4)) * kDnStride + 256 * h + 16 * (lane & 15)) =
+                wv[4 * h + i];
+        __builtin_amdgcn_wave_barrier();       // LDS accesses of one wave complete in order
+        uint2 q[8];
+        u32x4 x0[8], x1[8];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[h][v] = fmaf(dsc, D[v], acc[h][v]);
+        for (int i = 0; i < 8; ++i) {
+            const int b = 8 * h + i;
+            q[i] = *reinterpret_cast<const uint2*>(tile + j * kDnStride + 32 * b + 8 * g);
+            x0[i] = ua[0][b][lane];
+            if (!PACK) x1[i] = ua[NPL - 1][b][lane];
+        }
+        f32x4 D[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const bf16x8 w = i8x8_to_bf16x8(q[i].x, q[i].y);
+            const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
+            D[i] = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8, x0[i]), w, zf);
+            if (!PACK) D[i] = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8, x1[i]), w, D[i]);
+        }
+        __builtin_amdgcn_sched_barrier(0);     // eight MFMAs in flight, then their scales
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int b = 8 * h + i;
+            const uint32_t sp = sw[b >> 1];
+            const float dsc = b < cb ? h2f((uint16_t)((b & 1) ? (sp >> 16) : (sp & 0xffffu))) : 0.f;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[v] = fmaf(dsc, D[i][v], acc[v]);
         }
     }
 
-    // 5. partial sums of this slab: part[s][t][n], and the slab's sum of R^2 per row t
+    // 4. partial sums of this slab, part[s][t][n] (D lane l: column n = r0 + l%16, rows 4(l/16)+v)
+    const int n = r0 + j;
+    if (PACK) {
+        // rows 8..15 (lanes 32..63) hold the lo parts of tokens 0..7: add them to rows 0..7
+        float tot[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int n = r0 + 16 * h + j;
+        for (int v = 0; v < 4; ++v) tot[v] = acc[v] + __shfl_down(acc[v], 32, 64);
+        if (lane < 32) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int tt = 4 * g + v;
+                if (tt < T && n < N) a.part[((size_t)s * T + tt) * N + n] = tot[v];
+            }
+        }
+    } else {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int t = 4 * g + v;
-            if (t < T && n < N) a.part[((size_t)s * T + t) * N + n] = acc[h][v];
+            const int tt = 4 * g + v;
+            if (tt < T && n < N) a.part[((size_t)s * T + tt) * N + n] = acc[v];
         }
     }
     if (blockIdx.y == 0 && threadIdx.x < T) {
-        const int t = threadIdx.x;
-        float v = 0.f;
-        for (int b = 0; b < kDnNB; ++b)
-            for (int gg = 0; gg < 4; ++gg) v += sq[b][gg][t];
-        a.ssq[(size_t)s * T + t] = v;
+        const int tt = threadIdx.x;
+        a.ssq[(size_t)s * T + tt] = ((sqw[0][tt] + sqw[1][tt]) + sqw[2][tt]) + sqw[3][tt];
     }
 }
 
-// lo[t][n] = bf16(rs[t] * sum_s part[s][t][n]); one work-group per (32 rows, t). The S slab sums
-// are added in ascending order within each of 8 contiguous slab groups, then the groups in order.
+// lo[t][n] = bf16(rs[t] * sum_s part[s][t][n]); one work-group per (64 rows, t). Four slab groups
+// of ceil(S/4) consecutive slabs are each added in ascending order, then the groups in order.
 __global__ void __launch_bounds__(256) hc_down_combine_kernel(GemvArgs a) {
-    __shared__ float red[8][32];
+    __shared__ float red[4][64];
     __shared__ float s_rs;
     const int t = blockIdx.y;
-    const int sg = threadIdx.x >> 5, nl = threadIdx.x & 31;
-    const int n = blockIdx.x * 32 + nl;
+    const int sg = threadIdx.x >> 6, nl = threadIdx.x & 63;
+    const int n = blockIdx.x * 64 + nl;
     const int S = a.S, N = a.N;
-    const int per = (S + 7) / 8;
+    const int per = (S + 3) / 4;
     const int s0 = sg * per, s1 = imin(S, s0 + per);
+    const int nc = imin(n, N - 1);
+    float v = 0.f;
+    for (int s = s0; s < s1; s += 8) {
+        float p[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = a.part[((size_t)imin(s + i, S - 1) * a.T + t) * N + nc];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v += s + i < s1 ? p[i] : 0.f;
+    }
     if (threadIdx.x < 64) {            // rs[t]: lane-strided sums, then the wave sum
         float ss = 0.f;
         for (int s = threadIdx.x; s < S; s += 64) ss += a.ssq[(size_t)s * a.T + t];
@@ -275,23 +350,10 @@ __global__ void __launch_bounds__(256) hc_down_combine_kernel(GemvArgs a) {
             if (blockIdx.x == 0 && a.rs_out != nullptr) a.rs_out[t] = rs;
         }
     }
-    float v = 0.f;
-    if (n < N) {
-        for (int s = s0; s < s1; s += 16) {
-            float p[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                p[i] = s + i < s1 ? a.part[((size_t)(s + i) * a.T + t) * N + n] : 0.f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) v += p[i];
-        }
-    }
     red[sg][nl] = v;
     __syncthreads();
-    if (threadIdx.x < 32 && n < N && a.out != nullptr) {
-        float tot = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) tot += red[i][nl];
+    if (threadIdx.x < 64 && n < N && a.out != nullptr) {
+        const float tot = ((red[0][nl] + red[1][nl]) + red[2][nl]) + red[3][nl];
         reinterpret_cast<uint16_t*>(a.out)[(size_t)t * N + n] = f2bf_bits(s_rs * tot);
     }
 }
@@ -305,16 +367,14 @@ size_t hc_down_workspace_bytes(int T, int N, int K) {
 template <int T>
 static int launch_down_t(GemvArgs a, void* ws, hipStream_t st) {
     const int S = hc_down_slabs(a.K);
-    const int ntile = (a.N + 31) / 32;
     char* w = static_cast<char*>(ws);
     a.S = S;
     a.part = reinterpret_cast<float*>(w);
     a.ssq = reinterpret_cast<float*>(w + round_up((size_t)S * T * a.N * sizeof(float), kCounterAlign));
-    const int waves = ntile < 16 ? ntile : 16;
-    hipLaunchKernelGGL((hc_down_partial_kernel<T>), dim3(S, (ntile + 15) / 16), dim3(64 * waves), 0, st, a);
+    hipLaunchKernelGGL((hc_down_partial_kernel<T>), dim3(S, (a.N + kDnRows - 1) / kDnRows), dim3(256), 0, st, a);
     int rc = launch_status();
     if (rc != GQ8_OK) return rc;
-    hipLaunchKernelGGL(hc_down_combine_kernel, dim3(ntile, T), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(hc_down_combine_kernel, dim3((a.N + 63) / 64, T), dim3(256), 0, st, a);
     return launch_status();
 }
 

@@ -45,7 +45,7 @@ struct GemvArgs {
 int launch_q8_0_gemv(GemvArgs a, hipStream_t st);
 
 // fused RMSNorm + Q8_0 down read: MFMA partial kernel over K slabs, then a combine kernel.
-constexpr int kDownSlab = 128;                 // columns per slab (4 Q8_0 blocks)
+constexpr int kDownSlab = 512;                 // columns per slab (16 Q8_0 blocks)
 inline int hc_down_slabs(int K) { return (K + kDownSlab - 1) / kDownSlab; }
 size_t hc_down_workspace_bytes(int T, int N, int K);
 int launch_hc_down(GemvArgs a, void* ws, hipStream_t st);
