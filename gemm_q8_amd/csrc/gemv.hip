@@ -393,7 +393,7 @@ constexpr int kUpLoads = 16 * kUpCW / 1024; // coalesced 1 KiB loads per 16-row 
 // five coalesced 1 KiB loads into LDS, then MFMA operands (row = lane % 16) out of LDS.
 // FULL: every chunk is 320 columns wide (K % 320 == 0), so every load, LDS access and MFMA of a
 // chunk is unconditional and the three phases (LDS reads, MFMAs, scale FMAs) issue back to back.
-template <int T, bool FULL>
+template <int T>
 __global__ void __launch_bounds__(256) hc_up_kernel(GemvArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t wt[4][16 * kUpStride];
     __shared__ uint16_t wsc[4][16][kUpCB];
@@ -407,7 +407,7 @@ __global__ void __launch_bounds__(256) hc_up_kernel(GemvArgs a) {
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int c0 = 0; c0 < K; c0 += kUpCW) {
-        const int cw = FULL ? kUpCW : (K - c0 < kUpCW ? K - c0 : kUpCW);   // multiple of 32
+        const int cw = K - c0 < kUpCW ? K - c0 : kUpCW;   // multiple of 32
         const int np = cw >> 4;                             // 16-byte pieces per weight row
         const int cb = cw >> 5;
         const int npx = cw >> 3;                            // 16-byte pieces per input row
@@ -438,7 +438,7 @@ __global__ void __launch_bounds__(256) hc_up_kernel(GemvArgs a) {
 #pragma unroll
         for (int i = 0; i < kUpLoads; ++i) {
             const int e = i * 64 + lane;
-            if (FULL || e < 16 * np) {
+            if (e < 16 * np) {
                 const int row = e / np, pc = e - row * np;
                 *reinterpret_cast<u32x4*>(&wt[wave][row * kUpStride + 16 * pc]) = wv[i];
             }
@@ -458,41 +458,93 @@ __global__ void __launch_bounds__(256) hc_up_kernel(GemvArgs a) {
         }
         __syncthreads();
         const int tj = j < T ? j : 0;
-        if (FULL) {
-            uint2 q[kUpCB];
-            u32x4 x[kUpCB];
-            uint16_t sc[kUpCB];
 #pragma unroll
-            for (int b = 0; b < kUpCB; ++b) {
-                q[b] = *reinterpret_cast<const uint2*>(&wt[wave][j * kUpStride + 32 * b + 8 * g]);
-                x[b] = *reinterpret_cast<const u32x4*>(&xl[tj][2 * (32 * b + 8 * g)]);
-                sc[b] = wsc[wave][j][b];
+        for (int b = 0; b < kUpCB; ++b) {
+            if (b < cb) {
+                const uint2 q = *reinterpret_cast<const uint2*>(&wt[wave][j * kUpStride + 32 * b + 8 * g]);
+                const u32x4 x = *reinterpret_cast<const u32x4*>(&xl[tj][2 * (32 * b + 8 * g)]);
+                f32x4 D = {0.f, 0.f, 0.f, 0.f};
+                D = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8, j < T ? x : z), i8x8_to_bf16x8(q.x, q.y), D);
+                const float dsc = h2f(wsc[wave][j][b]);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[v] = fmaf(dsc, D[v], acc[v]);
             }
-            f32x4 D[kUpCB];
+        }
+        if (c0 + kUpCW < K) __syncthreads();                // the next chunk overwrites LDS
+    }
+    uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+    const int n = r0 + j;
 #pragma unroll
-            for (int b = 0; b < kUpCB; ++b) {
+    for (int v = 0; v < 4; ++v) {
+        const int t = 4 * g + v;
+        if (t < T && n < N) out[(size_t)t * N + n] = f2bf_bits(acc[v]);
+    }
+}
+
+// K % 320 == 0: the weight tile goes straight from the loads into MFMA operands. Load i gives lane
+// l the 16 bytes of row l%16 at column 64i + 16(l/16) of the chunk: Q8_0 block 2i in lanes 0..31,
+// block 2i+1 in lanes 32..63. One v_permlane32_swap per dword pair (lanes l and l+32 trade a dword)
+// leaves lane (row j, k-group g) holding, for each of the two blocks, the 8 bytes at block offset
+// {0, 16, 8, 24}[g]; the input operand takes its k-groups at the same offsets. Each block's MFMA
+// waits only for its own load, so the work of early loads overlaps the arrival of later ones.
+GQ8_DEV int up_koff(int g) { return 16 * (g & 1) + 8 * (g >> 1); }
+
+template <int T>
+__global__ void __launch_bounds__(256) hc_up_direct_kernel(GemvArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t xl[kMaxT][kUpLoStride];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int N = a.N, K = a.K, nblk = K >> 5;
+    const int r0 = (blockIdx.x * 4 + wave) * 16;
+    const int j = lane & 15, g = lane >> 4;
+    const int row = imin(r0 + j, N - 1);
+    const uint16_t* lo = reinterpret_cast<const uint16_t*>(a.x);
+    constexpr int npx = kUpCW / 8;                                  // 16-byte pieces per input row
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const int tj = j < T ? j : 0;
+    const int ko = 2 * up_koff(g);                                  // byte offset in a bf16 row
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < K; c0 += kUpCW) {
+        // the input chunk (T rows x 40 pieces), the row's 10 block scales, the 5 weight loads
+        u32x4 xv[3];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int e = imin(i * 256 + (int)threadIdx.x, T * npx - 1);
+            const int t = e / npx, pc = e - t * npx;
+            xv[i] = *reinterpret_cast<const u32x4*>(lo + (size_t)t * K + c0 + 8 * pc);
+        }
+        uint32_t sc[kUpCB / 2];
+        const uint32_t* dp = reinterpret_cast<const uint32_t*>(a.d + (size_t)row * nblk + (c0 >> 5));
+#pragma unroll
+        for (int i = 0; i < kUpCB / 2; ++i) sc[i] = dp[i];
+        u32x4 wv[kUpLoads];
+        const int8_t* wp = a.q + (size_t)row * K + c0 + 16 * g;
+#pragma unroll
+        for (int i = 0; i < kUpLoads; ++i) wv[i] = ld_nt16(wp + 64 * i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int e = i * 256 + (int)threadIdx.x;
+            if (e < T * npx) {
+                const int t = e / npx, pc = e - t * npx;
+                *reinterpret_cast<u32x4*>(&xl[t][16 * pc]) = xv[i];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kUpLoads; ++i) {
+            const auto s02 = __builtin_amdgcn_permlane32_swap(wv[i].x, wv[i].z, false, false);
+            const auto s13 = __builtin_amdgcn_permlane32_swap(wv[i].y, wv[i].w, false, false);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int b = 2 * i + h;
+                const u32x4 x = *reinterpret_cast<const u32x4*>(&xl[tj][64 * b + ko]);
                 const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
-                D[b] = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8, j < T ? x[b] : z),
-                                          i8x8_to_bf16x8(q[b].x, q[b].y), zf);
-            }
+                const f32x4 D = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8, j < T ? x : z),
+                                                   i8x8_to_bf16x8(s02[h], s13[h]), zf);
+                const float dsc = h2f((uint16_t)(h ? (sc[i] >> 16) : (sc[i] & 0xffffu)));
 #pragma unroll
-            for (int b = 0; b < kUpCB; ++b) {
-                const float dsc = h2f(sc[b]);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) acc[v] = fmaf(dsc, D[b][v], acc[v]);
-            }
-        } else {
-#pragma unroll
-            for (int b = 0; b < kUpCB; ++b) {
-                if (b < cb) {
-                    const uint2 q = *reinterpret_cast<const uint2*>(&wt[wave][j * kUpStride + 32 * b + 8 * g]);
-                    const u32x4 x = *reinterpret_cast<const u32x4*>(&xl[tj][2 * (32 * b + 8 * g)]);
-                    f32x4 D = {0.f, 0.f, 0.f, 0.f};
-                    D = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8, j < T ? x : z), i8x8_to_bf16x8(q.x, q.y), D);
-                    const float dsc = h2f(wsc[wave][j][b]);
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) acc[v] = fmaf(dsc, D[v], acc[v]);
-                }
+                for (int v = 0; v < 4; ++v) acc[v] = fmaf(dsc, D[v], acc[v]);
             }
         }
         if (c0 + kUpCW < K) __syncthreads();                // the next chunk overwrites LDS
@@ -510,9 +562,9 @@ template <int T>
 static int launch_up_t(GemvArgs a, hipStream_t st) {
     const int ntile = (a.N + 15) / 16;
     if (a.K % kUpCW == 0)
-        hipLaunchKernelGGL((hc_up_kernel<T, true>), dim3((ntile + 3) / 4), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((hc_up_direct_kernel<T>), dim3((ntile + 3) / 4), dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL((hc_up_kernel<T, false>), dim3((ntile + 3) / 4), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((hc_up_kernel<T>), dim3((ntile + 3) / 4), dim3(256), 0, st, a);
     return launch_status();
 }
 

@@ -160,7 +160,8 @@ def _up(gpu, wbuf, lo, T, N, K):
     return out
 
 
-@pytest.mark.parametrize("T,N,K", [(1, 37, 2048), (4, 10, 1056), (6, 64, 96), (16, 9, 4096)])
+@pytest.mark.parametrize("T,N,K", [(1, 37, 2048), (4, 10, 1056), (6, 64, 96), (16, 9, 4096),
+                                   (8, 70, 1536), (9, 33, 544)])
 def test_down_matches_oracle_small(gpu, T, N, K):
     d = synth.hc_inputs(T, K=K, N=N, seed=20)
     lo, rs = _down(gpu, q8_0_from_f32(to_dev(d["w_down"])), to_dev(d["R"]), to_dev(d["w_norm"]), T, N, K)
@@ -199,7 +200,8 @@ def test_hc_pair_full_size(gpu, T):
     check_bf16(to_host(out2, np.uint16), ref_chain, S_chain, f"hc chain T={T}")
 
 
-@pytest.mark.parametrize("T,N,K", [(1, 100, 320), (4, 77, 320), (6, 5, 64), (9, 40, 1024), (16, 33, 320)])
+@pytest.mark.parametrize("T,N,K", [(1, 100, 320), (4, 77, 320), (6, 5, 64), (9, 40, 1024), (16, 33, 320),
+                                   (2, 50, 640), (7, 70, 960), (3, 21, 352)])
 def test_up_matches_oracle_small(gpu, T, N, K):
     w = synth.normal_f32(21, "gpu.up.w", (N, K), 0.0, 0.02)
     lo = synth.bf16_normal(21, "gpu.up.lo", (T, K))
