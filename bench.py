@@ -2,16 +2,18 @@
 """Benchmark of the decode-time Q8_0 read on one MI355X.
 
 Workload (one "step"): the fused RMSNorm + Q8_0 hyper-connection down read (W_down Q8_0
-[320, 16384], R bf16 [T, 16384]) followed by the Q8_0 up read (W_up Q8_0 [16384, 320]) for each
-T in {1, 4, 6}: six kernels' worth of calls, 3 x 11,141,120 weight bytes. Every pair reads its
+[320, 16384], R bf16 [T, 16384]) followed by the Q8_0 up read (W_up Q8_0 [16384, 320]) on its
+output, one gq8_hc_q8_pair call for each T in {1, 4, 6}: 3 x 11,141,120 weight bytes. Every pair reads its
 own copy of the weights; the copies rotate through a working set larger than twice the
 Infinity Cache (MALL) plus the L2s, so the weight bytes come from HBM. Inputs are seeded and
 synthetic (gemm_q8_amd.synth), resident in HBM before the timed region. Calls are captured
 serially on one stream into hipGraphs and replayed.
 
 Output: one JSON line on stdout (metric = weight bytes / time in GB/s), with
-  roofline      the dominant kernel's algorithmic bytes per launch / its average launch
-                duration, from HIP events on the launch stream, against 8 TB/s;
+  roofline      the pair call's algorithmic bytes / its average duration (HIP events on the
+                launch stream, graphs of back-to-back calls), against 8 TB/s; the call is two
+                kernels (the down read's partial sums, then the up read with the down's
+                combine inside), whose separate durations the rocprofv3 summary gives;
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload.
 --all-configs also times the other workloads (Q8_0 GEMV T sweep, W8A8 sweep, routed MoE)
 and writes their lines to --report (default gpurun_out/bench_all.jsonl) and stderr.
@@ -113,7 +115,7 @@ def setup_hc(torch, gq8, synth, dev):
     per_t = {}
     for T in TS:
         d = synth.hc_inputs(T)
-        nbd = gq8.gq8_workspace_bytes(gq8.OP_HC_DOWN, T, N_LR, K_HC)
+        nbd = gq8.gq8_workspace_bytes(gq8.OP_HC_PAIR, T, N_LR, K_HC)
         nbu = gq8.gq8_workspace_bytes(gq8.OP_HC_UP, T, K_HC, N_LR)
         per_t[T] = dict(
             R=to_dev(d["R"]), wn=to_dev(d["w_norm"]),
@@ -137,22 +139,26 @@ def hc_up_fn(gq8, h, T, i):
     return lambda s: gq8.gq8_hc_q8_up(w, p["lo"], p["out"], T, K_HC, N_LR, p["wsu"], p["nbu"], s)
 
 
+def hc_pair_fn(gq8, h, T, i):
+    p = h["per_t"][T]
+    wd = h["wds"][i % h["n_sets"]]
+    wu = h["wus"][i % h["n_sets"]]
+    return lambda s: gq8.gq8_hc_q8_pair(wd, p["R"], p["wn"], 1e-6, wu, p["lo"], p["rs"], p["out"],
+                                        T, N_LR, K_HC, p["wsd"], p["nbd"], s)
+
+
 def hc_step_fns(gq8, h):
     def fns(step):
-        out = []
-        for j, T in enumerate(TS):
-            i = step * len(TS) + j
-            out += [hc_down_fn(gq8, h, T, i), hc_up_fn(gq8, h, T, i)]
-        return out
+        return [hc_pair_fn(gq8, h, T, step * len(TS) + j) for j, T in enumerate(TS)]
     return fns
 
 
 def hc_kernel_bytes(kind, T):
-    """Algorithmic bytes of one launch: weights + activations read + outputs written."""
+    """Algorithmic bytes of one call: weights + activations read + outputs written."""
     w = K_HC * N_LR + K_HC * N_LR // 32 * 2
-    if kind == "down":
-        return w + T * K_HC * 2 + K_HC * 2 + T * N_LR * 2 + T * 4
-    return w + T * N_LR * 2 + T * K_HC * 2
+    down = w + T * K_HC * 2 + K_HC * 2 + T * N_LR * 2 + T * 4
+    up = w + T * N_LR * 2 + T * K_HC * 2
+    return {"down": down, "up": up, "pair": down + up}[kind]
 
 
 # ------------------------------------------------------------------------------------ CPU baseline
@@ -329,17 +335,14 @@ def main():
     ms_per_step = t / args.steps * 1e3
     log(f"[bench] {args.steps} steps in {t * 1e3:.3f} ms: {ms_per_step * 1e3:.2f} us/step, {value:.1f} GB/s")
 
-    # per-T pair time and per-kernel launch durations (same launches, isolated graphs)
+    # per-T pair time (the step's own calls) and the separate down / up calls, each in graphs of
+    # back-to-back calls over the rotated weight sets
     n = h["n_sets"]
     per_call = {}
     kern = {}
     reps = 20
     for T in TS:
-        pair = GraphSteps(torch, stream, lambda i, T=T: [hc_down_fn(gq8, h, T, i), hc_up_fn(gq8, h, T, i)], n)
-        pair.run(n)
-        tp = time_region(torch, stream, lambda: pair.run(n * reps))
-        per_call[f"T{T}"] = round(tp / (n * reps) * 1e6, 3)
-        for kind, mk in (("down", hc_down_fn), ("up", hc_up_fn)):
+        for kind, mk in (("pair", hc_pair_fn), ("down", hc_down_fn), ("up", hc_up_fn)):
             g = GraphSteps(torch, stream, lambda i, T=T, mk=mk: [mk(gq8, h, T, i)], n)
             g.run(n)
             tk = time_region(torch, stream, lambda: g.run(n * reps))
@@ -347,12 +350,14 @@ def main():
             k["t"] += tk
             k["bytes"] += hc_kernel_bytes(kind, T) * n * reps
             k["launches"] += n * reps
-    dom = max(kern, key=lambda k: kern[k]["t"] / kern[k]["launches"])
+            if kind == "pair":
+                per_call[f"T{T}"] = round(tk / (n * reps) * 1e6, 3)
+    dom = "pair"
     kd = kern[dom]
     avg_us = kd["t"] / kd["launches"] * 1e6
     achieved = kd["bytes"] / kd["t"] / 1e9
-    log(f"[bench] per-call pair us {per_call}; kernels: " + ", ".join(
-        f"{k} {v['t'] / v['launches'] * 1e6:.3f} us/launch" for k, v in kern.items()))
+    log(f"[bench] per-call pair us {per_call}; calls: " + ", ".join(
+        f"{k} {v['t'] / v['launches'] * 1e6:.3f} us" for k, v in kern.items()))
 
     if args.copy_probe_mib:
         nbytes = args.copy_probe_mib << 20
@@ -391,13 +396,13 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": f"hc_{dom}",
+            "kernel": "gq8_hc_q8_pair: hc_down_partial_kernel + hc_pair_up_kernel",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None,
-            "avg_launch_us": round(avg_us, 3),
+            "avg_call_us": round(avg_us, 3),
         },
     }
     if not args.no_cpu_baseline:

@@ -106,6 +106,7 @@ GQ8_EXPORT size_t gq8_workspace_counter_bytes(int op, int rows, int N, int K) {
 GQ8_EXPORT size_t gq8_workspace_bytes(int op, int rows, int N, int K) {
     switch (op) {
         case GQ8_OP_HC_DOWN:
+        case GQ8_OP_HC_PAIR:
             if (!q8_shape_ok(rows, N, K) || rows == 0 || N == 0 || K == 0) return 0;
             return hc_down_workspace_bytes(rows, N, K);
         case GQ8_OP_Q8_0_GEMV:
@@ -187,6 +188,36 @@ GQ8_EXPORT int gq8_hc_q8_up(const void* w_split, const uint16_t* lo, uint16_t* o
     a.d = reinterpret_cast<const uint16_t*>(a.q + (size_t)N * K);
     a.x = lo; a.T = T; a.N = N; a.K = K; a.out = out;
     return launch_hc_up(a, S(stream));
+}
+
+GQ8_EXPORT int gq8_hc_q8_pair(const void* w_down, const uint16_t* R, const uint16_t* w_norm,
+                              float eps, const void* w_up, uint16_t* lo, float* rs_out,
+                              uint16_t* out, int T, int Nlr, int Khc, void* ws, size_t ws_bytes,
+                              void* stream) {
+    if (T < 0 || Nlr < 0 || Khc < 0) return GQ8_EINVAL;
+    if (!q8_shape_ok(T, Nlr, Khc) || Nlr % 32 != 0 || Nlr > 1024 || Khc == 0 || Nlr == 0)
+        return GQ8_ESHAPE;
+    if (T == 0) return GQ8_OK;
+    if (w_down == nullptr || R == nullptr || w_norm == nullptr || w_up == nullptr ||
+        lo == nullptr || out == nullptr)
+        return GQ8_EINVAL;
+    if (!aligned16(w_down) || !aligned16(R) || !aligned16(w_norm) || !aligned16(w_up) ||
+        !aligned16(lo))
+        return GQ8_EALIGN;
+    if (!(eps >= 0.f)) return GQ8_EINVAL;
+    int rc = check_ws(ws, ws_bytes, hc_down_workspace_bytes(T, Nlr, Khc));
+    if (rc != GQ8_OK) return rc;
+    if (device_cus() == 0) return GQ8_ENODEV;
+    GemvArgs dn{};
+    dn.q = static_cast<const int8_t*>(w_down);
+    dn.d = reinterpret_cast<const uint16_t*>(dn.q + (size_t)Nlr * Khc);
+    dn.x = R; dn.wnorm = w_norm; dn.T = T; dn.N = Nlr; dn.K = Khc; dn.out = lo;
+    dn.rs_out = rs_out; dn.eps = eps;
+    GemvArgs up{};
+    up.q = static_cast<const int8_t*>(w_up);
+    up.d = reinterpret_cast<const uint16_t*>(up.q + (size_t)Khc * Nlr);
+    up.x = lo; up.T = T; up.N = Khc; up.K = Nlr; up.out = out;
+    return launch_hc_pair(dn, up, ws, S(stream));
 }
 
 // ---------------------------------------------------------------------------------- W8A8

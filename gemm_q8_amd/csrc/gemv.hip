@@ -570,4 +570,175 @@ static int launch_up_t(GemvArgs a, hipStream_t st) {
 
 int launch_hc_up(GemvArgs a, hipStream_t st) { GQ8_T_SWITCH(launch_up_t, a, st) }
 
+// ------------------------------------------------------------------------------ fused pair
+
+// The up read of the down/up pair for K == 320 and small T with the down's combine folded in:
+// waves 4..7 of the work-group add the down's slab partial sums for all T x 320 inputs (the same
+// order as hc_down_combine_kernel, so lo is bitwise the down read's output), apply rs and round
+// to bf16 into LDS, while waves 0..3 have their weight loads in flight; after one barrier waves
+// 0..3 run the up read's MFMAs as hc_up_direct_kernel does. Every work-group computes the same
+// lo; work-group 0 also writes lo and rs out. Separate waves keep the partial-sum loads (L2)
+// from waiting behind the weight loads (HBM): a wave's loads complete in issue order.
+constexpr int kPairQuads = kUpCW / 4;       // float4 quads of a 320-wide row
+
+template <int T>
+__global__ void __launch_bounds__(512) hc_pair_up_kernel(GemvArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t xl[kMaxT][kUpLoStride];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int N = a.N, K = a.K;                                   // up rows, up depth (== 320)
+    const int j = lane & 15, g = lane >> 4;
+    if (wave < 4) {
+        // weights and scales of this wave's 16 rows, in flight across the combine
+        const int r0 = (blockIdx.x * 4 + wave) * 16;
+        const int row = imin(r0 + j, N - 1);
+        uint32_t sc[kUpCB / 2];
+        const uint32_t* dp = reinterpret_cast<const uint32_t*>(a.d + (size_t)row * (K >> 5));
+#pragma unroll
+        for (int i = 0; i < kUpCB / 2; ++i) sc[i] = dp[i];
+        u32x4 wv[kUpLoads];
+        const int8_t* wp = a.q + (size_t)row * K + 16 * g;
+#pragma unroll
+        for (int i = 0; i < kUpLoads; ++i) wv[i] = ld_nt16(wp + 64 * i);
+        __syncthreads();
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const int tj = j < T ? j : 0;
+        const int ko = 2 * up_koff(g);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < kUpLoads; ++i) {
+            const auto s02 = __builtin_amdgcn_permlane32_swap(wv[i].x, wv[i].z, false, false);
+            const auto s13 = __builtin_amdgcn_permlane32_swap(wv[i].y, wv[i].w, false, false);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int b = 2 * i + h;
+                const u32x4 x = *reinterpret_cast<const u32x4*>(&xl[tj][64 * b + ko]);
+                const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
+                const f32x4 D = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8, j < T ? x : z),
+                                                   i8x8_to_bf16x8(s02[h], s13[h]), zf);
+                const float dsc = h2f((uint16_t)(h ? (sc[i] >> 16) : (sc[i] & 0xffffu)));
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[v] = fmaf(dsc, D[v], acc[v]);
+            }
+        }
+        uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+        const int n = r0 + j;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int t = 4 * g + v;
+            if (t < T && n < N) out[(size_t)t * N + n] = f2bf_bits(acc[v]);
+        }
+        return;
+    }
+    // combine waves: rs[t] from the slab sums of squares (lane-strided, then the wave sum, as
+    // hc_down_combine_kernel does), then lo for quads (t, 4 consecutive inputs)
+    const int S = a.S;
+    const int ct = (int)threadIdx.x - 256;
+    float rs[T];
+    {
+        float ss[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) ss[t] = 0.f;
+        for (int s = lane; s < S; s += 64) {
+#pragma unroll
+            for (int t = 0; t < T; ++t) ss[t] += a.ssq[(size_t)s * T + t];
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t) rs[t] = 1.0f / sqrtf(wave_sum(ss[t]) / (float)a.kd + a.eps);
+    }
+    if (blockIdx.x == 0 && ct < T && a.rs_out != nullptr) {
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+            if (t == ct) a.rs_out[t] = rs[t];
+    }
+    const int per = (S + 3) / 4;
+    for (int qd = ct; qd < T * kPairQuads; qd += 256) {
+        const int t = qd / kPairQuads, n = 4 * (qd - t * kPairQuads);
+        const float4* p = reinterpret_cast<const float4*>(a.part + (size_t)t * K + n);
+        const size_t plane = (size_t)T * K / 4;                     // float4s per slab plane
+        float4 vg[4];
+        if (S == 32) {                      // per == 8: all 32 loads in flight at once
+            float4 pv[32];
+#pragma unroll
+            for (int i = 0; i < 32; ++i) pv[i] = p[(size_t)i * plane];
+#pragma unroll
+            for (int sg = 0; sg < 4; ++sg) {
+                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    v.x += pv[8 * sg + i].x; v.y += pv[8 * sg + i].y;
+                    v.z += pv[8 * sg + i].z; v.w += pv[8 * sg + i].w;
+                }
+                vg[sg] = v;
+            }
+        } else
+#pragma unroll
+        for (int sg = 0; sg < 4; ++sg) {
+            const int s0 = sg * per, s1 = imin(S, s0 + per);
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int s = s0; s < s1; s += 8) {
+                float4 pv[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pv[i] = p[(size_t)imin(s + i, S - 1) * plane];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const bool in = s + i < s1;
+                    v.x += in ? pv[i].x : 0.f; v.y += in ? pv[i].y : 0.f;
+                    v.z += in ? pv[i].z : 0.f; v.w += in ? pv[i].w : 0.f;
+                }
+            }
+            vg[sg] = v;
+        }
+        float r = rs[0];
+#pragma unroll
+        for (int tt = 1; tt < T; ++tt) r = tt == t ? rs[tt] : r;
+        const float tx = ((vg[0].x + vg[1].x) + vg[2].x) + vg[3].x;
+        const float ty = ((vg[0].y + vg[1].y) + vg[2].y) + vg[3].y;
+        const float tz = ((vg[0].z + vg[1].z) + vg[2].z) + vg[3].z;
+        const float tw = ((vg[0].w + vg[1].w) + vg[2].w) + vg[3].w;
+        uint2 lv;
+        lv.x = (uint32_t)f2bf_bits(r * tx) | ((uint32_t)f2bf_bits(r * ty) << 16);
+        lv.y = (uint32_t)f2bf_bits(r * tz) | ((uint32_t)f2bf_bits(r * tw) << 16);
+        *reinterpret_cast<uint2*>(&xl[t][2 * n]) = lv;
+        if (blockIdx.x == 0 && a.lo_out != nullptr)
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.lo_out) + (size_t)t * K + n) = lv;
+    }
+    __syncthreads();
+}
+
+// The in-kernel combine reads all S x T x 320 partial sums in every up work-group (L2 traffic
+// that grows with T), the separate combine kernel costs one more launch: measured on MI355X at
+// K = 16384 (S = 32), folding wins for T <= 2 and loses from T = 3 on.
+constexpr int kPairMaxT = 2;
+
+template <int T>
+static int launch_pair_t(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st) {
+    if constexpr (T > kPairMaxT) {
+        const int rc = launch_down_t<T>(dn, ws, st);
+        return rc != GQ8_OK ? rc : launch_up_t<T>(up, st);
+    } else {
+        const int S = hc_down_slabs(dn.K);
+        char* w = static_cast<char*>(ws);
+        dn.S = S;
+        dn.part = reinterpret_cast<float*>(w);
+        dn.ssq = reinterpret_cast<float*>(w + round_up((size_t)S * T * dn.N * sizeof(float), kCounterAlign));
+        hipLaunchKernelGGL((hc_down_partial_kernel<T>), dim3(S, (dn.N + kDnRows - 1) / kDnRows), dim3(256), 0, st, dn);
+        int rc = launch_status();
+        if (rc != GQ8_OK) return rc;
+        up.S = S; up.part = dn.part; up.ssq = dn.ssq; up.eps = dn.eps; up.kd = dn.K;
+        up.rs_out = dn.rs_out; up.lo_out = dn.out;
+        const int ntile = (up.N + 15) / 16;
+        hipLaunchKernelGGL((hc_pair_up_kernel<T>), dim3((ntile + 3) / 4), dim3(512), 0, st, up);
+        return launch_status();
+    }
+}
+
+int launch_hc_pair(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st) {
+    if (up.K != kUpCW) {                   // no fused variant: the down read, then the up read
+        const int rc = launch_hc_down(dn, ws, st);
+        return rc != GQ8_OK ? rc : launch_hc_up(up, st);
+    }
+    GemvArgs& a = dn;
+    GQ8_T_SWITCH(launch_pair_t, dn, up, ws, st)
+}
+
 }  // namespace gq8

@@ -39,6 +39,8 @@ struct GemvArgs {
     void* out;              // fp32 y [T][N] or bf16 [T][N]
     float* rs_out;          // fp32 [T] (down, nullable)
     float eps;
+    void* lo_out;           // fused pair: bf16 [T][K] down output written by work-group 0
+    int kd;                 // fused pair: depth of the down read (the RMS mean's divisor)
 };
 
 // Q8_0 GEMV (fp32 x): one work-group per RW rows, all of K, no workspace.
@@ -50,8 +52,12 @@ inline int hc_down_slabs(int K) { return (K + kDownSlab - 1) / kDownSlab; }
 size_t hc_down_workspace_bytes(int T, int N, int K);
 int launch_hc_down(GemvArgs a, void* ws, hipStream_t st);
 
-// Q8_0 up read (bf16 x, K <= 1024): MFMA, one wave per 32 output rows, no workspace.
+// Q8_0 up read (bf16 x, K <= 1024): MFMA, one wave per 16 output rows, no workspace.
 int launch_hc_up(GemvArgs a, hipStream_t st);
+
+// the down read then the up read on its output; for an up depth of 320 and T <= 2 the down's
+// combine runs inside the up kernel (two launches instead of three). dn.out = lo (bf16 [T][dn.N]).
+int launch_hc_pair(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st);
 
 // ---------------------------------------------------------------- W8A8
 

@@ -20,7 +20,7 @@ _lib = ctypes.CDLL(_LIB_PATH)
 LIB_PATH = _LIB_PATH
 
 OK, EINVAL, ESHAPE, EALIGN, EWORKSPACE, ECAPTURE, EHIP, ENODEV = 0, -1, -2, -3, -4, -5, -6, -7
-OP_Q8_0_GEMV, OP_HC_DOWN, OP_HC_UP, OP_W8A8 = 1, 2, 3, 4
+OP_Q8_0_GEMV, OP_HC_DOWN, OP_HC_UP, OP_W8A8, OP_HC_PAIR = 1, 2, 3, 4, 5
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -43,6 +43,7 @@ _SIGS = {
     "gq8_q8_0_gemv": (_I, [_P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_hc_q8_down": (_I, [_P, _P, _P, _F, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_hc_q8_up": (_I, [_P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "gq8_hc_q8_pair": (_I, [_P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_w8a8_packed_bytes": (_SZ, [_I, _I]),
     "gq8_w8a8_pack": (_I, [_P, _I, _I, _P, _P]),
     "gq8_w8a8_gemm": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
@@ -149,6 +150,13 @@ def gq8_hc_q8_down(w_split, R, w_norm, eps, lo, rs_out, T, N, K, ws, ws_bytes, s
 def gq8_hc_q8_up(w_split, lo, out, T, N, K, ws, ws_bytes, stream=None):
     return _check("gq8_hc_q8_up", _lib.gq8_hc_q8_up(
         _ptr(w_split), _ptr(lo), _ptr(out), T, N, K, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def gq8_hc_q8_pair(w_down, R, w_norm, eps, w_up, lo, rs_out, out, T, Nlr, Khc, ws, ws_bytes,
+                   stream=None):
+    return _check("gq8_hc_q8_pair", _lib.gq8_hc_q8_pair(
+        _ptr(w_down), _ptr(R), _ptr(w_norm), eps, _ptr(w_up), _ptr(lo), _ptr(rs_out), _ptr(out),
+        T, Nlr, Khc, _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def gq8_w8a8_packed_bytes(K, N):

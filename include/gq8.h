@@ -46,7 +46,8 @@ enum gq8_op {
     GQ8_OP_Q8_0_GEMV = 1,
     GQ8_OP_HC_DOWN = 2,
     GQ8_OP_HC_UP = 3,
-    GQ8_OP_W8A8 = 4
+    GQ8_OP_W8A8 = 4,
+    GQ8_OP_HC_PAIR = 5     /* rows = T, N = Nlr, K = Khc of gq8_hc_q8_pair */
 };
 
 /* Static string for a status code. Host only. */
@@ -132,6 +133,19 @@ int gq8_hc_q8_down(const void* w_split, const uint16_t* R, const uint16_t* w_nor
  * w_split: Q8_0 [N][K]; lo bf16 [T][K]; out bf16 [T][N]. T = 1..16, K % 32 == 0, K <= 1024. */
 int gq8_hc_q8_up(const void* w_split, const uint16_t* lo, uint16_t* out, int T, int N, int K,
                  void* ws, size_t ws_bytes, void* stream);
+
+/* The down read followed by the up read on its output (HC-Q8 page, "What changed": the down and
+ * up projections of one hyper-connection read), in one call:
+ *   lo  = gq8_hc_q8_down(w_down [Nlr][Khc], R [T][Khc], w_norm [Khc])     bf16 [T][Nlr]
+ *   out = gq8_hc_q8_up(w_up [Khc][Nlr], lo)                                bf16 [T][Khc]
+ * lo, rs_out and out are bitwise what the two separate calls produce. For Nlr == 320 and
+ * T <= 2 the down read's combine of its split partial sums runs inside the up kernel (two kernel
+ * launches instead of three); otherwise the two calls' kernels run in sequence. lo is written (bf16
+ * [T][Nlr], 16-byte aligned, required); rs_out fp32 [T] is nullable. T = 1..16, Khc % 32 == 0,
+ * Nlr % 32 == 0, 0 < Nlr <= 1024. Workspace: gq8_workspace_bytes(GQ8_OP_HC_PAIR, T, Nlr, Khc). */
+int gq8_hc_q8_pair(const void* w_down, const uint16_t* R, const uint16_t* w_norm, float eps,
+                   const void* w_up, uint16_t* lo, float* rs_out, uint16_t* out,
+                   int T, int Nlr, int Khc, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * W8A8 (W8A8 page, operator statement): int8 x_q[M][K] @ int8 W[K][N] -> int32, then

@@ -91,6 +91,17 @@ def test_argument_checks_return_before_device_work(lib):
     assert raw.gq8_w8a8_gemm(None, None, None, None, None, 0, 16, 64, None, 0, None) == lib.OK
     # null output
     assert raw.gq8_q8_0_gemv(dummy, dummy, None, 1, 8, 64, None, 0, None) == lib.EINVAL
+    # down/up pair: depth above 1024, depth not a multiple of 32, missing lo, short workspace
+    assert raw.gq8_hc_q8_pair(dummy, dummy, dummy, 1e-6, dummy, dummy, None, dummy, 1, 2048, 4096,
+                              None, 0, None) == lib.ESHAPE
+    assert raw.gq8_hc_q8_pair(dummy, dummy, dummy, 1e-6, dummy, dummy, None, dummy, 1, 48, 4096,
+                              None, 0, None) == lib.ESHAPE
+    assert raw.gq8_hc_q8_pair(dummy, dummy, dummy, 1e-6, dummy, None, None, dummy, 1, 320, 4096,
+                              None, 0, None) == lib.EINVAL
+    assert raw.gq8_hc_q8_pair(dummy, dummy, dummy, 1e-6, dummy, dummy, None, dummy, 1, 320, 4096,
+                              dummy, 64, None) == lib.EWORKSPACE
+    assert lib.gq8_workspace_bytes(lib.OP_HC_PAIR, 6, 320, 16384) == \
+        lib.gq8_workspace_bytes(lib.OP_HC_DOWN, 6, 320, 16384)
     # MoE limits
     assert raw.gq8_moe_q8_0_routed(dummy, dummy, dummy, dummy, dummy, dummy, dummy,
                                    4, 8, 512, 2048, 2048, None, 0, None) == lib.ESHAPE

@@ -222,3 +222,60 @@ def test_down_scale_invariance_on_gpu(gpu):
     b = bf16_to_f32(to_host(lo4, np.uint16))
     assert np.allclose(a, b, rtol=2 ** -7, atol=1e-6)
     assert np.allclose(to_host(rs1), 4 * to_host(rs4), rtol=1e-5)
+
+
+def _pair(gpu, wd, R, wn, wu, T, Nlr, Khc, ws=None, stream=None, lo=None, rs=None, out=None):
+    nb = gpu.gq8_workspace_bytes(gpu.OP_HC_PAIR, T, Nlr, Khc)
+    ws = workspace(nb) if ws is None else ws
+    lo = torch.empty((T, Nlr), dtype=torch.int16, device="cuda") if lo is None else lo
+    rs = torch.empty((T,), dtype=torch.float32, device="cuda") if rs is None else rs
+    out = torch.empty((T, Khc), dtype=torch.int16, device="cuda") if out is None else out
+    gpu.gq8_hc_q8_pair(wd, R, wn, 1e-6, wu, lo, rs, out, T, Nlr, Khc, ws, nb, stream)
+    return lo, rs, out
+
+
+@pytest.mark.parametrize("T,Nlr,Khc", [(1, 320, 16384), (4, 320, 16384), (6, 320, 16384),
+                                       (16, 320, 16384), (3, 320, 1056), (8, 64, 2048),
+                                       (5, 96, 544)])
+def test_pair_is_the_two_calls(gpu, T, Nlr, Khc):
+    """The pair entry (two kernels for Nlr = 320, the combine inside the up read) gives bitwise the
+    down call's lo and rs and the up call's output on that lo."""
+    d = synth.hc_inputs(T, K=Khc, N=Nlr, seed=40)
+    wd, wu = q8_0_from_f32(to_dev(d["w_down"])), q8_0_from_f32(to_dev(d["w_up"]))
+    R, wn = to_dev(d["R"]), to_dev(d["w_norm"])
+    lo_p, rs_p, out_p = _pair(gpu, wd, R, wn, wu, T, Nlr, Khc)
+    lo_s, rs_s = _down(gpu, wd, R, wn, T, Nlr, Khc)
+    out_s = _up(gpu, wu, lo_s, T, Khc, Nlr)
+    torch.cuda.synchronize()
+    assert torch.equal(lo_p, lo_s)
+    assert torch.equal(rs_p, rs_s)
+    assert torch.equal(out_p, out_s)
+    # and the pair's up output against the oracle's up read of the pair's own lo
+    out_ref, S_up = hc_up(to_host(lo_p, np.uint16), quantize_q8_0(d["w_up"]))
+    check_bf16(to_host(out_p, np.uint16), out_ref, S_up, f"pair up T={T} Nlr={Nlr} Khc={Khc}")
+
+
+def test_pair_graph_replay_and_poison(gpu):
+    T, Nlr, Khc = 6, 320, 16384
+    d = synth.hc_inputs(T, seed=41)
+    wd, wu = q8_0_from_f32(to_dev(d["w_down"])), q8_0_from_f32(to_dev(d["w_up"]))
+    R, wn = to_dev(d["R"]), to_dev(d["w_norm"])
+    nb = gpu.gq8_workspace_bytes(gpu.OP_HC_PAIR, T, Nlr, Khc)
+    ws = workspace(nb)
+    lo0, rs0, out0 = _pair(gpu, wd, R, wn, wu, T, Nlr, Khc, ws=ws)
+    torch.cuda.synchronize()
+    lo, rs = torch.empty_like(lo0), torch.empty_like(rs0)
+    out = torch.empty_like(out0)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            _pair(gpu, wd, R, wn, wu, T, Nlr, Khc, ws=ws, stream=s, lo=lo, rs=rs, out=out)
+    for _ in range(3):
+        lo.zero_(); rs.zero_(); out.zero_()
+        ws.fill_(0x7F)                     # partial planes and sums of squares poisoned
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(lo, lo0) and torch.equal(rs, rs0) and torch.equal(out, out0)
