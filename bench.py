@@ -302,6 +302,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all-configs", action="store_true")
     ap.add_argument("--report", default="gpurun_out/bench_all.jsonl")
+    ap.add_argument("--reps", type=int, default=20,
+                    help="replays of each per-call timing graph (per-T pair, down, up)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also launch one device copy of this many MiB (for scaling PMC byte counters)")
     args = ap.parse_args()
@@ -340,7 +342,7 @@ def main():
     n = h["n_sets"]
     per_call = {}
     kern = {}
-    reps = 20
+    reps = max(1, args.reps)
     for T in TS:
         for kind, mk in (("pair", hc_pair_fn), ("down", hc_down_fn), ("up", hc_up_fn)):
             g = GraphSteps(torch, stream, lambda i, T=T, mk=mk: [mk(gq8, h, T, i)], n)

@@ -143,8 +143,11 @@ constexpr int kDnNB = kDownSlab / 32;      // Q8_0 blocks per slab
 constexpr int kDnStride = kDownSlab + 16;  // padded LDS row stride of a wave's weight tile (bytes)
 constexpr int kDnRows = 64;                // rows per work-group: four waves of 16
 
-// One work-group: slab blockIdx.x (512 columns) x 64 rows (blockIdx.y), one 16-row MFMA tile per
-// wave. The A operand is u = R * w_norm for the slab, staged once per work-group as exact bf16
+// One work-group: a slab of 512 columns x 64 rows, one 16-row MFMA tile per wave. Work-groups
+// are dealt round-robin to the 8 XCDs (work-group i to XCD i % 8), each with its own L2; when the
+// slab count is a multiple of 8, XCD x gets slabs [x S/8, (x+1) S/8) for every row group, so the
+// activation columns and the 128-byte scale lines a slab group shares are fetched into one L2
+// only. The A operand is u = R * w_norm for the slab, staged once per work-group as exact bf16
 // hi and lo parts; for T <= 8 the two parts share one A operand (rows 0..7 hi, rows 8..15 lo of
 // token t), so one MFMA per block does both, and the hi and lo results are added at the end
 // (the block scale multiplies both). A wave reads its 16 x 512-byte weight tile in two column
@@ -163,11 +166,20 @@ __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t wsc[4][16][kDnNB];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int N = a.N, K = a.K, nblk = K >> 5;
-    const int s = blockIdx.x;
+    const int S = a.S;
+    int s, y;
+    if ((S & 7) == 0) {
+        const int x = blockIdx.x & 7, k = blockIdx.x >> 3, per = S >> 3;
+        s = x * per + k % per;
+        y = k / per;
+    } else {
+        s = blockIdx.x % S;
+        y = blockIdx.x / S;
+    }
     const int k0 = s * kDownSlab;
     const int cw = imin(kDownSlab, K - k0);                        // multiple of 32
     const int cb = cw >> 5;
-    const int r0 = blockIdx.y * kDnRows + 16 * wave;               // first row of this wave
+    const int r0 = y * kDnRows + 16 * wave;                        // first row of this wave
     const uint16_t* R = reinterpret_cast<const uint16_t*>(a.x);
 
     // 0. activations: item it = 256 j + thread covers token t = it % TR (the same t for every
@@ -314,7 +326,7 @@ __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
             if (tt < T && n < N) a.part[((size_t)s * T + tt) * N + n] = acc[v];
         }
     }
-    if (blockIdx.y == 0 && threadIdx.x < T) {
+    if (y == 0 && threadIdx.x < T) {
         const int tt = threadIdx.x;
         a.ssq[(size_t)s * T + tt] = ((sqw[0][tt] + sqw[1][tt]) + sqw[2][tt]) + sqw[3][tt];
     }
@@ -371,7 +383,7 @@ static int launch_down_t(GemvArgs a, void* ws, hipStream_t st) {
     a.S = S;
     a.part = reinterpret_cast<float*>(w);
     a.ssq = reinterpret_cast<float*>(w + round_up((size_t)S * T * a.N * sizeof(float), kCounterAlign));
-    hipLaunchKernelGGL((hc_down_partial_kernel<T>), dim3(S, (a.N + kDnRows - 1) / kDnRows), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((hc_down_partial_kernel<T>), dim3(S * ((a.N + kDnRows - 1) / kDnRows)), dim3(256), 0, st, a);
     int rc = launch_status();
     if (rc != GQ8_OK) return rc;
     hipLaunchKernelGGL(hc_down_combine_kernel, dim3((a.N + 63) / 64, T), dim3(256), 0, st, a);
@@ -721,7 +733,7 @@ static int launch_pair_t(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st) {
         dn.S = S;
         dn.part = reinterpret_cast<float*>(w);
         dn.ssq = reinterpret_cast<float*>(w + round_up((size_t)S * T * dn.N * sizeof(float), kCounterAlign));
-        hipLaunchKernelGGL((hc_down_partial_kernel<T>), dim3(S, (dn.N + kDnRows - 1) / kDnRows), dim3(256), 0, st, dn);
+        hipLaunchKernelGGL((hc_down_partial_kernel<T>), dim3(S * ((dn.N + kDnRows - 1) / kDnRows)), dim3(256), 0, st, dn);
         int rc = launch_status();
         if (rc != GQ8_OK) return rc;
         up.S = S; up.part = dn.part; up.ssq = dn.ssq; up.eps = dn.eps; up.kd = dn.K;
