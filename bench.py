@@ -96,6 +96,21 @@ def time_region(torch, stream, fn):
     return e0.elapsed_time(e1) * 1e-3       # seconds
 
 
+def recorded_traffic():
+    """HBM bytes per pair call from the committed FETCH_SIZE / WRITE_SIZE summary, or None when
+    the kernel sources have changed since those counters were taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", "hc_pair_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        h.update(open(os.path.join(root, f), "rb").read())
+    return rec["traffic_bytes_per_pair_call"] if h.hexdigest() == rec["kernel_sources_sha256"] else None
+
+
 def n_sets_for(nbytes, multiple=1):
     n = int(np.ceil(WS_TARGET / nbytes))
     return int(np.ceil(n / multiple) * multiple)
@@ -403,7 +418,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(),
+            "traffic_unit": "bytes per pair call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
             "avg_call_us": round(avg_us, 3),
         },
     }

@@ -88,18 +88,19 @@ int gq8_q8_1_quantize(const uint16_t* x_bf16, int rows, int K, int8_t* q, uint16
                       uint16_t* s, void* stream);
 
 /* ------------------------------------------------------------------------------------------
- * Workspace: split-K partial sums and arrival counters for the compute calls.
- *   - size it with gq8_workspace_bytes() for the exact (op, rows, N, K) of the call;
- *   - zero it once with gq8_workspace_init(), outside any stream capture;
- *   - a call leaves every counter at zero again (the last-arriving work-group resets it), so a
- *     workspace can be reused by any later call on the SAME stream without re-initialising;
- *     calls that may run concurrently (different streams, or a graph replayed concurrently
- *     with itself) need separate workspaces (HC-Q8 page, "What changed": one scratch per queue,
- *     zeroed outside any capture);
- *   - the counters occupy the first gq8_workspace_counter_bytes() bytes; the partial sums after
- *     them are fully rewritten by every call before they are read (no clearing needed;
- *     W8A8 page, "Split-K requirements").
- * rows = T for the Q8_0 calls, M for W8A8. A size of 0 means the call needs no workspace.
+ * Workspace: device scratch that a compute call needs beyond its inputs and outputs.
+ *   - size it with gq8_workspace_bytes() for the exact (op, rows, N, K) of the call; 0 means the
+ *     call needs none (pass NULL, 0). Today only the down read and the down/up pair use one: fp32
+ *     partial sums of the K slabs [S][T][N] and the slabs' sums of squares [S][T] (HC-Q8 page,
+ *     "What changed": one scratch per queue, allocated outside any capture);
+ *   - every call rewrites every workspace value it later reads, so a workspace needs no clearing
+ *     and can be reused by any later call on the same stream (W8A8 page, "Split-K requirements":
+ *     planes fully rewritten, no memset in the timed region); calls that may run concurrently
+ *     (different streams, or a graph replayed concurrently with itself) need separate workspaces;
+ *   - gq8_workspace_counter_bytes() is 0 for every operation (no call keeps arrival counters: the
+ *     partial sums are combined by a kernel of their own, or inside the up read's kernel);
+ *     gq8_workspace_init() zero-fills a workspace (harmless, never required).
+ * rows = T for the Q8_0 calls, M for W8A8.
  * ------------------------------------------------------------------------------------------ */
 size_t gq8_workspace_bytes(int op, int rows, int N, int K);
 size_t gq8_workspace_counter_bytes(int op, int rows, int N, int K);
@@ -116,12 +117,14 @@ int gq8_q8_0_gemv(const void* w_split, const float* x, float* y, int T, int N, i
                   void* ws, size_t ws_bytes, void* stream);
 
 /* Fused RMSNorm + Q8_0 hyper-connection down read (HC-Q8 page, "What changed": the down kernel
- * works on R * w_norm unscaled plus the sums of squares, and the last work-group of a row group
- * applies the RMSNorm factor when it combines the partial sums):
+ * works on R * w_norm unscaled plus the slab's sums of squares, and the RMSNorm factor is applied
+ * when the slabs' partial sums are combined, in a fixed order):
  *   rs[t]    = 1 / sqrt(mean_k R[t][k]^2 + eps)
  *   lo[t][n] = bf16( rs[t] * sum_k d[n][k/32] * q[n][k] * (R[t][k] * w_norm[k]) )
  * w_split: Q8_0 [N][K]; R bf16 [T][K]; w_norm bf16 [K]; lo bf16 [T][N]; rs_out fp32 [T]
- * (nullable). T = 1..16, K % 32 == 0, K > 0. */
+ * (nullable). T = 1..16, K % 32 == 0, K > 0. Workspace: gq8_workspace_bytes(GQ8_OP_HC_DOWN, T,
+ * N, K). Two kernels: per 512-column slab partial sums (bf16 MFMA on exact hi/lo operands), then
+ * the combine (slab groups in ascending order) with rs and the bf16 rounding. */
 int gq8_hc_q8_down(const void* w_split, const uint16_t* R, const uint16_t* w_norm, float eps,
                    uint16_t* lo, float* rs_out, int T, int N, int K,
                    void* ws, size_t ws_bytes, void* stream);
@@ -164,7 +167,8 @@ int gq8_w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* W_packed
                   const float* w_scale, uint16_t* out, int M, int N, int K,
                   void* ws, size_t ws_bytes, void* stream);
 
-/* Same kernels, int32 accumulators written instead of the bf16 epilogue (acc int32 [M][N]). */
+/* Same kernels, int32 accumulators written instead of the bf16 epilogue (acc int32 [M][N]).
+ * Both W8A8 calls: M = 0..32, K % 16 == 0, K <= 8192 (GQ8_ESHAPE above), no workspace. */
 int gq8_w8a8_gemm_i32(const int8_t* xq, const int8_t* W_packed, int32_t* acc, int M, int N,
                       int K, void* ws, size_t ws_bytes, void* stream);
 
