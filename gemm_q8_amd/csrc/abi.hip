@@ -110,6 +110,8 @@ GQ8_EXPORT size_t gq8_workspace_bytes(int op, int rows, int N, int K) {
             if (!q8_shape_ok(rows, N, K) || rows == 0 || N == 0 || K == 0) return 0;
             return hc_down_workspace_bytes(rows, N, K);
         case GQ8_OP_Q8_0_GEMV:
+            if (!q8_shape_ok(rows, N, K)) return 0;
+            return gemv_workspace_bytes(rows, N, K);
         case GQ8_OP_HC_UP:
         case GQ8_OP_W8A8:
         default:
@@ -131,7 +133,6 @@ GQ8_EXPORT int gq8_workspace_init(void* ws, size_t bytes, void* stream) {
 
 GQ8_EXPORT int gq8_q8_0_gemv(const void* w_split, const float* x, float* y, int T, int N, int K,
                              void* ws, size_t ws_bytes, void* stream) {
-    (void)ws; (void)ws_bytes;
     if (T < 0 || N < 0 || K < 0) return GQ8_EINVAL;
     if (!q8_shape_ok(T, N, K)) return GQ8_ESHAPE;
     if (T == 0 || N == 0) return GQ8_OK;
@@ -142,12 +143,14 @@ GQ8_EXPORT int gq8_q8_0_gemv(const void* w_split, const float* x, float* y, int 
     }
     if (w_split == nullptr || x == nullptr) return GQ8_EINVAL;
     if (!aligned16(w_split) || !aligned16(x)) return GQ8_EALIGN;
+    const int rc = check_ws(ws, ws_bytes, gemv_workspace_bytes(T, N, K));
+    if (rc != GQ8_OK) return rc;
     if (device_cus() == 0) return GQ8_ENODEV;
     GemvArgs a{};
     a.q = static_cast<const int8_t*>(w_split);
     a.d = reinterpret_cast<const uint16_t*>(a.q + (size_t)N * K);
     a.x = x; a.T = T; a.N = N; a.K = K; a.out = y;
-    return launch_q8_0_gemv(a, S(stream));
+    return launch_q8_0_gemv(a, ws, S(stream));
 }
 
 GQ8_EXPORT int gq8_hc_q8_down(const void* w_split, const uint16_t* R, const uint16_t* w_norm,

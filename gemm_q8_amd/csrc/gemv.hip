@@ -108,8 +108,19 @@ __global__ void __launch_bounds__(64 * MAXW) gemv_rows_kernel(GemvArgs a) {
 
 template <int T> constexpr int gemv_rw() { return T <= 4 ? 2 : 1; }
 
+// From this many token rows on, the GEMV runs on MFMA (the down read's slab kernel with x as the
+// A operand, then its combine): the VALU dot re-reads x from cache for every 16 weight bytes,
+// which binds once T grows.
+constexpr int kGemvMfmaT = 5;
+
 template <int T>
-static int launch_gemv_t(GemvArgs a, hipStream_t st) {
+static int launch_gemv_mfma_t(GemvArgs a, void* ws, hipStream_t st);
+
+template <int T>
+static int launch_gemv_t(GemvArgs a, void* ws, hipStream_t st) {
+    if constexpr (T >= kGemvMfmaT) {
+        if (a.K > 0) return launch_gemv_mfma_t<T>(a, ws, st);
+    }
     constexpr int RW = gemv_rw<T>();
     int nw = (a.K + 1023) / 1024;
     if (nw <= 4) {
@@ -135,7 +146,7 @@ static int launch_gemv_t(GemvArgs a, hipStream_t st) {
         default: return GQ8_ESHAPE;                                                               \
     }
 
-int launch_q8_0_gemv(GemvArgs a, hipStream_t st) { GQ8_T_SWITCH(launch_gemv_t, a, st) }
+int launch_q8_0_gemv(GemvArgs a, void* ws, hipStream_t st) { GQ8_T_SWITCH(launch_gemv_t, a, ws, st) }
 
 // ------------------------------------------------------------------------------ down read
 
@@ -154,7 +165,11 @@ constexpr int kDnRows = 64;                // rows per work-group: four waves of
 // halves of four coalesced 1 KiB loads (four rows x 256 bytes each), in the order the work
 // consumes them: activations first, then half 0, then half 1, so that the LDS transpose and
 // MFMAs of half 0 run while half 1 is still in flight. The weight tile is private to its wave.
-template <int T>
+//
+// XF (the Q8_0 GEMV at larger T): the A operand is x itself (fp32 [T][K]) instead of R * w_norm;
+// hi = bf16(x) and lo = bf16(x - hi), both rounded to nearest, leave |x - hi - lo| <= 2^-17 |x|,
+// far inside the read's tolerance; no sums of squares.
+template <int T, bool XF = false>
 __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
     constexpr bool PACK = T <= 8;
     constexpr int NPL = PACK ? 1 : 2;                              // A planes (hi, lo)
@@ -194,8 +209,14 @@ __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
         const int k = k0 + 32 * b + 8 * g;
         okv[i] = t < T && 32 * b < cw;
         const int kc = okv[i] ? k : 0, tc = okv[i] ? t : 0;
-        rv[i] = *reinterpret_cast<const uint4*>(R + (size_t)tc * K + kc);
-        nv[i] = *reinterpret_cast<const uint4*>(a.wnorm + kc);
+        if (XF) {                                  // eight fp32 x values
+            const float* xf = reinterpret_cast<const float*>(a.x) + (size_t)tc * K + kc;
+            rv[i] = *reinterpret_cast<const uint4*>(xf);
+            nv[i] = *reinterpret_cast<const uint4*>(xf + 4);
+        } else {
+            rv[i] = *reinterpret_cast<const uint4*>(R + (size_t)tc * K + kc);
+            nv[i] = *reinterpret_cast<const uint4*>(a.wnorm + kc);
+        }
     }
     // block scales: lane l holds row l/4, blocks 4(l%4) .. +3
     uint16_t sc[4];
@@ -228,17 +249,29 @@ __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
         const uint32_t ww[4] = {nv[i].x, nv[i].y, nv[i].z, nv[i].w};
         uint32_t hi[4], lo[4];
         float r2 = 0.f;
+        if (XF) {
+            const uint32_t xw[8] = {rw[0], rw[1], rw[2], rw[3], ww[0], ww[1], ww[2], ww[3]};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float q0 = __uint_as_float(rw[e] << 16), q1 = __uint_as_float(rw[e] & 0xffff0000u);
-            const float w0 = __uint_as_float(ww[e] << 16), w1 = __uint_as_float(ww[e] & 0xffff0000u);
-            const float u0 = ok ? q0 * w0 : 0.f, u1 = ok ? q1 * w1 : 0.f;   // exact products
-            const uint16_t h0 = f2bf_bits(u0), h1 = f2bf_bits(u1);
-            const float l0 = u0 - bf2f(h0), l1 = u1 - bf2f(h1);             // exact residuals
-            hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-            lo[e] = pack_bf16_trunc(l0, l1);                                // exact in bf16
-            r2 = fmaf(q0, q0, r2);
-            r2 = fmaf(q1, q1, r2);
+            for (int e = 0; e < 4; ++e) {
+                const float u0 = ok ? __uint_as_float(xw[2 * e]) : 0.f;
+                const float u1 = ok ? __uint_as_float(xw[2 * e + 1]) : 0.f;
+                const uint16_t h0 = f2bf_bits(u0), h1 = f2bf_bits(u1);
+                hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                lo[e] = (uint32_t)f2bf_bits(u0 - bf2f(h0)) | ((uint32_t)f2bf_bits(u1 - bf2f(h1)) << 16);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float q0 = __uint_as_float(rw[e] << 16), q1 = __uint_as_float(rw[e] & 0xffff0000u);
+                const float w0 = __uint_as_float(ww[e] << 16), w1 = __uint_as_float(ww[e] & 0xffff0000u);
+                const float u0 = ok ? q0 * w0 : 0.f, u1 = ok ? q1 * w1 : 0.f;   // exact products
+                const uint16_t h0 = f2bf_bits(u0), h1 = f2bf_bits(u1);
+                const float l0 = u0 - bf2f(h0), l1 = u1 - bf2f(h1);             // exact residuals
+                hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                lo[e] = pack_bf16_trunc(l0, l1);                                // exact in bf16
+                r2 = fmaf(q0, q0, r2);
+                r2 = fmaf(q1, q1, r2);
+            }
         }
         if (PACK) {
             ua[0][b][16 * g + t] = u32x4{hi[0], hi[1], hi[2], hi[3]};
@@ -326,7 +359,7 @@ __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
             if (tt < T && n < N) a.part[((size_t)s * T + tt) * N + n] = acc[v];
         }
     }
-    if (y == 0 && threadIdx.x < T) {
+    if (!XF && y == 0 && threadIdx.x < T) {
         const int tt = threadIdx.x;
         a.ssq[(size_t)s * T + tt] = ((sqw[0][tt] + sqw[1][tt]) + sqw[2][tt]) + sqw[3][tt];
     }
@@ -334,6 +367,8 @@ __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
 
 // lo[t][n] = bf16(rs[t] * sum_s part[s][t][n]); one work-group per (64 rows, t). Four slab groups
 // of ceil(S/4) consecutive slabs are each added in ascending order, then the groups in order.
+// XF: the GEMV's y[t][n] = sum_s part[s][t][n] in fp32, same order, no rs.
+template <bool XF = false>
 __global__ void __launch_bounds__(256) hc_down_combine_kernel(GemvArgs a) {
     __shared__ float red[4][64];
     __shared__ float s_rs;
@@ -352,7 +387,7 @@ __global__ void __launch_bounds__(256) hc_down_combine_kernel(GemvArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) v += s + i < s1 ? p[i] : 0.f;
     }
-    if (threadIdx.x < 64) {            // rs[t]: lane-strided sums, then the wave sum
+    if (!XF && threadIdx.x < 64) {     // rs[t]: lane-strided sums, then the wave sum
         float ss = 0.f;
         for (int s = threadIdx.x; s < S; s += 64) ss += a.ssq[(size_t)s * a.T + t];
         ss = wave_sum(ss);
@@ -366,7 +401,10 @@ __global__ void __launch_bounds__(256) hc_down_combine_kernel(GemvArgs a) {
     __syncthreads();
     if (threadIdx.x < 64 && n < N && a.out != nullptr) {
         const float tot = ((red[0][nl] + red[1][nl]) + red[2][nl]) + red[3][nl];
-        reinterpret_cast<uint16_t*>(a.out)[(size_t)t * N + n] = f2bf_bits(s_rs * tot);
+        if (XF)
+            reinterpret_cast<float*>(a.out)[(size_t)t * N + n] = tot;
+        else
+            reinterpret_cast<uint16_t*>(a.out)[(size_t)t * N + n] = f2bf_bits(s_rs * tot);
     }
 }
 
@@ -386,11 +424,30 @@ static int launch_down_t(GemvArgs a, void* ws, hipStream_t st) {
     hipLaunchKernelGGL((hc_down_partial_kernel<T>), dim3(S * ((a.N + kDnRows - 1) / kDnRows)), dim3(256), 0, st, a);
     int rc = launch_status();
     if (rc != GQ8_OK) return rc;
-    hipLaunchKernelGGL(hc_down_combine_kernel, dim3((a.N + 63) / 64, T), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(hc_down_combine_kernel<false>, dim3((a.N + 63) / 64, T), dim3(256), 0, st, a);
     return launch_status();
 }
 
 int launch_hc_down(GemvArgs a, void* ws, hipStream_t st) { GQ8_T_SWITCH(launch_down_t, a, ws, st) }
+
+size_t gemv_workspace_bytes(int T, int N, int K) {
+    if (T < kGemvMfmaT || N == 0 || K == 0) return 0;
+    const size_t S = hc_down_slabs(K);
+    return round_up(S * T * N * sizeof(float), kCounterAlign);
+}
+
+template <int T>
+static int launch_gemv_mfma_t(GemvArgs a, void* ws, hipStream_t st) {
+    const int S = hc_down_slabs(a.K);
+    a.S = S;
+    a.part = static_cast<float*>(ws);
+    a.ssq = nullptr;
+    hipLaunchKernelGGL((hc_down_partial_kernel<T, true>), dim3(S * ((a.N + kDnRows - 1) / kDnRows)), dim3(256), 0, st, a);
+    int rc = launch_status();
+    if (rc != GQ8_OK) return rc;
+    hipLaunchKernelGGL(hc_down_combine_kernel<true>, dim3((a.N + 63) / 64, T), dim3(256), 0, st, a);
+    return launch_status();
+}
 
 // ------------------------------------------------------------------------------ up read
 

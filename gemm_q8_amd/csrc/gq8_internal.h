@@ -43,8 +43,11 @@ struct GemvArgs {
     int kd;                 // fused pair: depth of the down read (the RMS mean's divisor)
 };
 
-// Q8_0 GEMV (fp32 x): one work-group per RW rows, all of K, no workspace.
-int launch_q8_0_gemv(GemvArgs a, hipStream_t st);
+// Q8_0 GEMV (fp32 x): T < 5 one work-group per RW rows and all of K on the VALU, no workspace;
+// T >= 5 MFMA over 512-column slabs into S partial planes [S][T][N] (the workspace), then a
+// combine kernel.
+int launch_q8_0_gemv(GemvArgs a, void* ws, hipStream_t st);
+size_t gemv_workspace_bytes(int T, int N, int K);
 
 // fused RMSNorm + Q8_0 down read: MFMA partial kernel over K slabs, then a combine kernel.
 constexpr int kDownSlab = 512;                 // columns per slab (16 Q8_0 blocks)

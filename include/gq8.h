@@ -90,9 +90,10 @@ int gq8_q8_1_quantize(const uint16_t* x_bf16, int rows, int K, int8_t* q, uint16
 /* ------------------------------------------------------------------------------------------
  * Workspace: device scratch that a compute call needs beyond its inputs and outputs.
  *   - size it with gq8_workspace_bytes() for the exact (op, rows, N, K) of the call; 0 means the
- *     call needs none (pass NULL, 0). Today only the down read and the down/up pair use one: fp32
- *     partial sums of the K slabs [S][T][N] and the slabs' sums of squares [S][T] (HC-Q8 page,
- *     "What changed": one scratch per queue, allocated outside any capture);
+ *     call needs none (pass NULL, 0). The down read and the down/up pair use one (fp32 partial
+ *     sums of the K slabs [S][T][N], then the slabs' sums of squares [S][T]), and so does the
+ *     GEMV at T >= 5 (the partial sums only) (HC-Q8 page, "What changed": one scratch per queue,
+ *     allocated outside any capture);
  *   - every call rewrites every workspace value it later reads, so a workspace needs no clearing
  *     and can be reused by any later call on the same stream (W8A8 page, "Split-K requirements":
  *     planes fully rewritten, no memset in the timed region); calls that may run concurrently
@@ -112,7 +113,9 @@ int gq8_workspace_init(void* ws, size_t bytes, void* stream);
  * w_split: split-layout Q8_0 [N][K]; x fp32 [T][K]; y fp32 [T][N] (written, not accumulated).
  * K % 32 == 0. Accumulation is fp32 in a fixed order: the result is deterministic for a given
  * device and shape (replays are bitwise identical). T == 0 or N == 0: nothing to do.
- * K == 0: y is zero-filled. */
+ * K == 0: y is zero-filled. T <= 4: VALU dots, one kernel, no workspace. T >= 5: bf16 MFMA on
+ * x split into bf16 hi + lo (|x - hi - lo| <= 2^-17 |x|) over 512-column slabs, then a combine
+ * of the slab sums in a fixed order; workspace gq8_workspace_bytes(GQ8_OP_Q8_0_GEMV, T, N, K). */
 int gq8_q8_0_gemv(const void* w_split, const float* x, float* y, int T, int N, int K,
                   void* ws, size_t ws_bytes, void* stream);
 

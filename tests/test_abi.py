@@ -61,6 +61,9 @@ def test_workspace_sizes(lib):
                            (lib.OP_W8A8, 16, 1536, 4096), (99, 1, 1, 32)]:
         assert lib.gq8_workspace_bytes(op, rows, n, k) == 0
         assert lib.gq8_workspace_counter_bytes(op, rows, n, k) == 0
+    # the GEMV takes a workspace from T = 5 on (MFMA over slabs, then a combine)
+    assert lib.gq8_workspace_bytes(lib.OP_Q8_0_GEMV, 4, 1024, 4096) == 0
+    assert lib.gq8_workspace_bytes(lib.OP_Q8_0_GEMV, 8, 1024, 4096) >= 8 * 8 * 1024 * 4
     assert lib.gq8_moe_plan_words(4, 8) == 1 + 4 * 32
     assert lib.gq8_moe_workspace_bytes(4, 8, 2048, 512) > 32 * (2048 + 512) * 4
 
@@ -84,6 +87,8 @@ def test_argument_checks_return_before_device_work(lib):
     # missing / short workspace for the split down read
     assert raw.gq8_hc_q8_down(dummy, dummy, dummy, 1e-6, dummy, None, 1, 320, 16384, None, 0, None) == lib.EWORKSPACE
     assert raw.gq8_hc_q8_down(dummy, dummy, dummy, 1e-6, dummy, None, 1, 320, 16384, dummy, 64, None) == lib.EWORKSPACE
+    # GEMV at T >= 5 without its workspace
+    assert raw.gq8_q8_0_gemv(dummy, dummy, dummy, 8, 64, 4096, None, 0, None) == lib.EWORKSPACE
     # W8A8 depth limit
     assert raw.gq8_w8a8_gemm(dummy, dummy, dummy, dummy, dummy, 4, 16, 8192 + 16, None, 0, None) == lib.ESHAPE
     # empty calls are no-ops
