@@ -8,9 +8,10 @@
 // across blocks because its chip had 120 CUs per 40-160 tiles; here a work-group of 16 waves
 // has the same bytes in flight without the combine round trip). Every load of a wave is issued,
 // clamped to valid addresses, before the first MFMA / dot.
-//   M >= 16: v_mfma_i32_16x16x64_i8, one MFMA row tile for M <= 16 and two (sharing the weight
-//            fragment) for M <= 32.
-//   M <  16: v_dot4_i32_i8 on the VALU over the same fragments.
+//   M >= 2:  v_mfma_i32_16x16x64_i8 (rows past M are zero), one MFMA row tile for M <= 16 and
+//            two (sharing the weight fragment) for M <= 32. One x load per k-step per lane;
+//            the VALU dot needs M of them, which bound it from M = 4 on (measured).
+//   M == 1:  v_dot4_i32_i8 on the VALU over the same fragments.
 // int32 sums are exact, so every order gives the one correct accumulator; the epilogue is
 // bf16( (fp32(acc) * x_scale[m]) * w_scale[n] ), two rounded fp32 products.
 #include "gq8_device.h"
@@ -33,22 +34,41 @@ struct W8Args {
 
 GQ8_DEV int imin8(int a, int b) { return a < b ? a : b; }
 
-// The WG's int32 tiles [NW][32][16] -> sum over waves -> epilogue. M <= 32: a thread handles
-// outputs i and i + 256 of the M x 16 tile... of up to 512 outputs.
-GQ8_DEV void w8a8_finish(const W8Args& a, int nt, int nw, int (*tile)[32][16]) {
+// x_scale[m] * ... of the thread's first output (i = thread of the M x 16 tile), loaded at kernel
+// start so that the epilogue does not wait for a global load after the reduction.
+struct W8Scales {
+    float xs, ws;
+};
+
+GQ8_DEV W8Scales w8a8_prefetch_scales(const W8Args& a, int nt) {
+    const int i = (int)threadIdx.x;
+    const int m = imin8(i >> 4, a.M - 1), n = imin8(nt * 16 + (i & 15), a.N - 1);
+    W8Scales sc;
+    sc.xs = a.i32_out ? 0.f : a.xs[m];
+    sc.ws = a.i32_out ? 0.f : a.wsc[n];
+    return sc;
+}
+
+// The WG's int32 tiles [NW][32][16] -> sum over waves (in wave order) -> epilogue.
+GQ8_DEV void w8a8_finish(const W8Args& a, int nt, int nw, int (*tile)[32][16], W8Scales sc) {
     __syncthreads();
     for (int i = threadIdx.x; i < a.M * 16; i += blockDim.x) {
         const int m = i >> 4, nl = i & 15;
         const int n = nt * 16 + nl;
+        int p[16];
+#pragma unroll
+        for (int w = 0; w < 16; ++w) p[w] = tile[w][m][nl];     // all reads in flight
         int v = 0;
-        for (int w = 0; w < nw; ++w) v += tile[w][m][nl];
+#pragma unroll
+        for (int w = 0; w < 16; ++w) v += w < nw ? p[w] : 0;
         if (n < a.N) {
             if (a.i32_out) {
                 reinterpret_cast<int*>(a.out)[(size_t)m * a.N + n] = v;
             } else {
+                const bool first = i == (int)threadIdx.x;
                 float f = (float)v;
-                f = f * a.xs[m];
-                f = f * a.wsc[n];
+                f = f * (first ? sc.xs : a.xs[m]);
+                f = f * (first ? sc.ws : a.wsc[n]);
                 reinterpret_cast<uint16_t*>(a.out)[(size_t)m * a.N + n] = f2bf_bits(f);
             }
         }
@@ -82,6 +102,7 @@ __global__ void __launch_bounds__(1024) w8a8_mfma_kernel(W8Args a) {
     v4i b[KPW];
     bool ok[KPW];
     load_frags<KPW>(a, nt, wave, nw, lane, b, ok);
+    const W8Scales sc = w8a8_prefetch_scales(a, nt);
     const int mrow = lane & 15;
     v4i x0[KPW], x1[KPW];
 #pragma unroll
@@ -111,7 +132,7 @@ __global__ void __launch_bounds__(1024) w8a8_mfma_kernel(W8Args a) {
         tile[wave][r0 + v][col] = acc0[v];
         if (MT == 2) tile[wave][16 + r0 + v][col] = acc1[v];
     }
-    w8a8_finish(a, nt, nw, tile);
+    w8a8_finish(a, nt, nw, tile, sc);
 }
 
 template <int MC, int KPW>
@@ -123,6 +144,7 @@ __global__ void __launch_bounds__(1024) w8a8_dot_kernel(W8Args a) {
     v4i b[KPW];
     bool ok[KPW];
     load_frags<KPW>(a, nt, wave, nw, lane, b, ok);
+    const W8Scales sc = w8a8_prefetch_scales(a, nt);
     int acc[MC];
 #pragma unroll
     for (int m = 0; m < MC; ++m) acc[m] = 0;
@@ -153,14 +175,14 @@ __global__ void __launch_bounds__(1024) w8a8_dot_kernel(W8Args a) {
         t += __shfl_xor(t, 32, 64);
         if (lane < 16 && m < a.M) tile[wave][m][lane] = t;
     }
-    w8a8_finish(a, nt, nw, tile);
+    w8a8_finish(a, nt, nw, tile, sc);
 }
 
 // ------------------------------------------------------------------------------------ planning
 
 W8Plan plan_w8a8(int M, int N, int K) {
     W8Plan p{};
-    p.mfma = M >= 16;
+    p.mfma = M >= 2;
     p.ntiles = (N + 15) / 16;
     p.ksteps = (K + 63) / 64;
     p.nw = p.ksteps < 16 ? p.ksteps : 16;
