@@ -369,6 +369,105 @@ __global__ void __launch_bounds__(256) moe_down_kernel(MoeArgs a) {
     }
 }
 
+// Down projection on MFMA (F % 64 == 0, F = 64 NL): one 16-row tile of the expert's down weight
+// per wave, 4 waves per work-group, the slot's entries as the A rows. h (fp32) is staged per
+// chunk of 8 entries as bf16 hi + lo (|h - hi - lo| <= 2^-17 |h|) in one packed A operand (rows
+// 0..7 hi, 8..15 lo of entry ci). The weight rows (F bytes each) are read straight into MFMA
+// operands: load i gives lane l the 16 bytes of row l%16 at column 64i + 16(l/16) (Q8_0 block 2i
+// in lanes 0..31, 2i+1 in lanes 32..63), and v_permlane32_swap makes both blocks' operands, so
+// lane (row j, k-group g) holds block offset {0, 16, 8, 24}[g] -- the A operand uses the same.
+GQ8_DEV int dn_koff(int g) { return 16 * (g & 1) + 8 * (g >> 1); }
+
+template <int NL>
+__global__ void __launch_bounds__(256) moe_down_mfma_kernel(MoeArgs a) {
+    constexpr int NB = 2 * NL;                     // Q8_0 blocks per row
+    constexpr int F = 64 * NL;
+    __shared__ u32x4 ua[NB][64];                   // A operands of the current entry chunk
+    const int slot = blockIdx.y;
+    const int U = a.plan[0];
+    if (slot >= U) return;
+    const int P = a.P, D = a.D;
+    const int e = a.plan[1 + slot];
+    const int c = a.plan[1 + P + slot];
+    const int st = a.plan[1 + 2 * P + slot];
+    const int8_t* q = a.wdn + (size_t)e * a.dn_bytes;
+    const uint16_t* d = reinterpret_cast<const uint16_t*>(q + (size_t)D * F);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j = lane & 15, g = lane >> 4;
+    const int r0 = (blockIdx.x * 4 + wave) * 16;
+    const int row = r0 + j < D ? r0 + j : D - 1;
+
+    // the wave's weight tile and its block scales (each row's NB scales, 4-byte pieces)
+    uint32_t sc[NL];
+    const uint32_t* dp = reinterpret_cast<const uint32_t*>(d + (size_t)row * NB);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) sc[i] = dp[i];
+    v4i wv[NL];
+    const int8_t* wp = q + (size_t)row * F + 16 * g;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) wv[i] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wp + 64 * i));
+
+    for (int cb = 0; cb < c; cb += 8) {
+        const int cn = c - cb < 8 ? c - cb : 8;
+        if (cb > 0) __syncthreads();               // the previous chunk's operands are dead
+        // stage: item (b, g2, ci), ci < 8, thread-strided; entry ci's h at columns
+        // 32 b + dn_koff(g2) .. +8 as bf16 hi (row ci) and lo (row 8 + ci)
+        for (int it = threadIdx.x; it < NB * 32; it += 256) {
+            const int ci = it & 7, g2 = (it >> 3) & 3, b = it >> 5;
+            u32x4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
+            if (ci < cn) {
+                const int ent = a.plan[1 + 3 * P + st + cb + ci];
+                const float4* hp = reinterpret_cast<const float4*>(a.h + (size_t)ent * F + 32 * b + dn_koff(g2));
+                const float4 f0 = hp[0], f1 = hp[1];
+                const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+                uint32_t h4[4], l4[4];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const uint16_t h0 = f2bf_bits(f[2 * e2]), h1 = f2bf_bits(f[2 * e2 + 1]);
+                    h4[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                    l4[e2] = (uint32_t)f2bf_bits(f[2 * e2] - bf2f(h0)) |
+                             ((uint32_t)f2bf_bits(f[2 * e2 + 1] - bf2f(h1)) << 16);
+                }
+                hi = u32x4{h4[0], h4[1], h4[2], h4[3]};
+                lo = u32x4{l4[0], l4[1], l4[2], l4[3]};
+            }
+            ua[b][16 * g2 + ci] = hi;
+            ua[b][16 * g2 + 8 + ci] = lo;
+        }
+        __syncthreads();
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const auto s02 = __builtin_amdgcn_permlane32_swap((uint32_t)wv[i].x, (uint32_t)wv[i].z, false, false);
+            const auto s13 = __builtin_amdgcn_permlane32_swap((uint32_t)wv[i].y, (uint32_t)wv[i].w, false, false);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int b = 2 * i + h;
+                const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
+                const f32x4 D4 = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8, ua[b][lane]),
+                                                    i8x8_to_bf16x8(s02[h], s13[h]), zf);
+                const float dsc = h2f((uint16_t)(h ? (sc[i] >> 16) : (sc[i] & 0xffffu)));
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[v] = fmaf(dsc, D4[v], acc[v]);
+            }
+        }
+        // rows 8..15 (lanes 32..63) hold the lo parts: add them to rows 0..7 (entries)
+        float tot[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) tot[v] = acc[v] + __shfl_down(acc[v], 32, 64);
+        if (lane < 32 && r0 + j < D) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int ci = 4 * g + v;
+                if (ci < cn) {
+                    const int ent = a.plan[1 + 3 * P + st + cb + ci];
+                    a.rows[(size_t)ent * D + r0 + j] = tot[v];
+                }
+            }
+        }
+    }
+}
+
 __global__ void __launch_bounds__(256) moe_combine_kernel(MoeArgs a) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= a.T * a.D) return;
@@ -414,9 +513,16 @@ int launch_moe_routed(const int8_t* xq, const uint16_t* xd, const int32_t* ids, 
     if (cmax4) hipLaunchKernelGGL((moe_gate_up_kernel<4>), ggu, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((moe_gate_up_kernel<16>), ggu, dim3(256), 0, st, a);
     if ((rc = launch_status()) != GQ8_OK) return rc;
-    const int rps = 64 / (F / 16);
-    const dim3 gdn((D + 4 * kDnNrs * rps - 1) / (4 * kDnNrs * rps), a.P);
-    hipLaunchKernelGGL((moe_down_kernel<4>), gdn, dim3(256), (size_t)4 * kDnNrs * 64 * 4 * sizeof(float), st, a);
+    if (F == 256 || F == 512 || F == 1024) {
+        const dim3 gm((D + 63) / 64, a.P);
+        if (F == 256) hipLaunchKernelGGL((moe_down_mfma_kernel<4>), gm, dim3(256), 0, st, a);
+        else if (F == 512) hipLaunchKernelGGL((moe_down_mfma_kernel<8>), gm, dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((moe_down_mfma_kernel<16>), gm, dim3(256), 0, st, a);
+    } else {
+        const int rps = 64 / (F / 16);
+        const dim3 gdn((D + 4 * kDnNrs * rps - 1) / (4 * kDnNrs * rps), a.P);
+        hipLaunchKernelGGL((moe_down_kernel<4>), gdn, dim3(256), (size_t)4 * kDnNrs * 64 * 4 * sizeof(float), st, a);
+    }
     if ((rc = launch_status()) != GQ8_OK) return rc;
     hipLaunchKernelGGL(moe_combine_kernel, dim3((T * D + 255) / 256), dim3(256), 0, st, a);
     return launch_status();

@@ -101,7 +101,11 @@ def _moe_case(gpu, T, E, topk, D, F, seed):
 
 
 @pytest.mark.parametrize("T,E,topk,D,F", [(1, 8, 2, 64, 32), (3, 20, 4, 128, 64), (6, 40, 6, 1056, 96),
-                                          (16, 64, 4, 256, 128)])
+                                          (16, 64, 4, 256, 128),
+                                          # MFMA down read (F = 256, 512, 1024): ragged D, an
+                                          # expert with 16 entries (two chunks of 8)
+                                          (16, 1, 1, 160, 256), (2, 10, 2, 96, 512),
+                                          (5, 12, 3, 544, 1024), (16, 3, 2, 64, 512)])
 def test_moe_small(gpu, T, E, topk, D, F):
     _moe_case(gpu, T, E, topk, D, F, seed=41)
 
