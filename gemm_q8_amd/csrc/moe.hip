@@ -382,6 +382,7 @@ template <int NL>
 __global__ void __launch_bounds__(256) moe_down_mfma_kernel(MoeArgs a) {
     constexpr int NB = 2 * NL;                     // Q8_0 blocks per row
     constexpr int F = 64 * NL;
+    constexpr int NIT = NB * 32 / 256;             // staging items per thread
     __shared__ u32x4 ua[NB][64];                   // A operands of the current entry chunk
     const int slot = blockIdx.y;
     const int U = a.plan[0];
@@ -397,7 +398,23 @@ __global__ void __launch_bounds__(256) moe_down_mfma_kernel(MoeArgs a) {
     const int r0 = (blockIdx.x * 4 + wave) * 16;
     const int row = r0 + j < D ? r0 + j : D - 1;
 
-    // the wave's weight tile and its block scales (each row's NB scales, 4-byte pieces)
+    // entries of the first chunk (uniform), then their h pieces, then the weights: the staging
+    // below waits for h only (a wave's loads complete in issue order)
+    int ent8[8];
+#pragma unroll
+    for (int ci = 0; ci < 8; ++ci) ent8[ci] = a.plan[1 + 3 * P + st + (ci < c ? ci : 0)];
+    float4 hv[NIT][2];
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) {
+        const int it = (int)threadIdx.x + 256 * k;
+        const int ci = it & 7, g2 = (it >> 3) & 3, b = it >> 5;
+        int ent = ent8[0];
+#pragma unroll
+        for (int cc = 1; cc < 8; ++cc) ent = ci == cc ? ent8[cc] : ent;
+        const float4* hp = reinterpret_cast<const float4*>(a.h + (size_t)ent * F + 32 * b + dn_koff(g2));
+        hv[k][0] = hp[0];
+        hv[k][1] = hp[1];
+    }
     uint32_t sc[NL];
     const uint32_t* dp = reinterpret_cast<const uint32_t*>(d + (size_t)row * NB);
 #pragma unroll
@@ -406,33 +423,44 @@ __global__ void __launch_bounds__(256) moe_down_mfma_kernel(MoeArgs a) {
     const int8_t* wp = q + (size_t)row * F + 16 * g;
 #pragma unroll
     for (int i = 0; i < NL; ++i) wv[i] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wp + 64 * i));
+    __builtin_amdgcn_sched_barrier(0);
 
     for (int cb = 0; cb < c; cb += 8) {
         const int cn = c - cb < 8 ? c - cb : 8;
-        if (cb > 0) __syncthreads();               // the previous chunk's operands are dead
-        // stage: item (b, g2, ci), ci < 8, thread-strided; entry ci's h at columns
-        // 32 b + dn_koff(g2) .. +8 as bf16 hi (row ci) and lo (row 8 + ci)
-        for (int it = threadIdx.x; it < NB * 32; it += 256) {
-            const int ci = it & 7, g2 = (it >> 3) & 3, b = it >> 5;
-            u32x4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
-            if (ci < cn) {
-                const int ent = a.plan[1 + 3 * P + st + cb + ci];
-                const float4* hp = reinterpret_cast<const float4*>(a.h + (size_t)ent * F + 32 * b + dn_koff(g2));
-                const float4 f0 = hp[0], f1 = hp[1];
-                const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-                uint32_t h4[4], l4[4];
+        if (cb > 0) {                              // later chunks (more than 8 entries): reload
+            __syncthreads();                       // the previous chunk's operands are dead
 #pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    const uint16_t h0 = f2bf_bits(f[2 * e2]), h1 = f2bf_bits(f[2 * e2 + 1]);
-                    h4[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-                    l4[e2] = (uint32_t)f2bf_bits(f[2 * e2] - bf2f(h0)) |
-                             ((uint32_t)f2bf_bits(f[2 * e2 + 1] - bf2f(h1)) << 16);
-                }
-                hi = u32x4{h4[0], h4[1], h4[2], h4[3]};
-                lo = u32x4{l4[0], l4[1], l4[2], l4[3]};
+            for (int ci = 0; ci < 8; ++ci) ent8[ci] = a.plan[1 + 3 * P + st + cb + (ci < cn ? ci : 0)];
+#pragma unroll
+            for (int k = 0; k < NIT; ++k) {
+                const int it = (int)threadIdx.x + 256 * k;
+                const int ci = it & 7, g2 = (it >> 3) & 3, b = it >> 5;
+                int ent = ent8[0];
+#pragma unroll
+                for (int cc = 1; cc < 8; ++cc) ent = ci == cc ? ent8[cc] : ent;
+                const float4* hp = reinterpret_cast<const float4*>(a.h + (size_t)ent * F + 32 * b + dn_koff(g2));
+                hv[k][0] = hp[0];
+                hv[k][1] = hp[1];
             }
-            ua[b][16 * g2 + ci] = hi;
-            ua[b][16 * g2 + 8 + ci] = lo;
+        }
+        // stage: item (b, g2, ci): entry ci's h at columns 32 b + dn_koff(g2) .. +8 as bf16 hi
+        // (row ci) and lo (row 8 + ci); absent entries are zero rows
+#pragma unroll
+        for (int k = 0; k < NIT; ++k) {
+            const int it = (int)threadIdx.x + 256 * k;
+            const int ci = it & 7, g2 = (it >> 3) & 3, b = it >> 5;
+            const float f[8] = {hv[k][0].x, hv[k][0].y, hv[k][0].z, hv[k][0].w,
+                                hv[k][1].x, hv[k][1].y, hv[k][1].z, hv[k][1].w};
+            uint32_t h4[4], l4[4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const float f0 = ci < cn ? f[2 * e2] : 0.f, f1 = ci < cn ? f[2 * e2 + 1] : 0.f;
+                const uint16_t h0 = f2bf_bits(f0), h1 = f2bf_bits(f1);
+                h4[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                l4[e2] = (uint32_t)f2bf_bits(f0 - bf2f(h0)) | ((uint32_t)f2bf_bits(f1 - bf2f(h1)) << 16);
+            }
+            ua[b][16 * g2 + ci] = u32x4{h4[0], h4[1], h4[2], h4[3]};
+            ua[b][16 * g2 + 8 + ci] = u32x4{l4[0], l4[1], l4[2], l4[3]};
         }
         __syncthreads();
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -459,10 +487,10 @@ __global__ void __launch_bounds__(256) moe_down_mfma_kernel(MoeArgs a) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int ci = 4 * g + v;
-                if (ci < cn) {
-                    const int ent = a.plan[1 + 3 * P + st + cb + ci];
-                    a.rows[(size_t)ent * D + r0 + j] = tot[v];
-                }
+                int ent = ent8[0];
+#pragma unroll
+                for (int cc = 1; cc < 8; ++cc) ent = ci == cc ? ent8[cc] : ent;
+                if (ci < cn) a.rows[(size_t)ent * D + r0 + j] = tot[v];
             }
         }
     }
