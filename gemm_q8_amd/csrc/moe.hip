@@ -160,6 +160,20 @@ GQ8_DEV void build_plan(const int32_t* ids, int P, int E, int32_t* plan) {
     }
 }
 
+// The plan (1 + 4P words) copied into LDS with one round of vector loads: the slot's expert,
+// count, start and entries are then LDS reads instead of a chain of dependent global loads.
+constexpr int kPlanWords = 1 + 4 * 256;
+
+GQ8_DEV void plan_to_lds(const int32_t* plan, int P, int32_t* lplan) {
+    const int n = 1 + 4 * P;
+#pragma unroll
+    for (int k = 0; k < kPlanWords / 256 + 1; ++k) {
+        const int i = (int)threadIdx.x + 256 * k;
+        if (i < n) lplan[i] = plan[i];
+    }
+    __syncthreads();
+}
+
 __global__ void __launch_bounds__(256) moe_plan_kernel(const int32_t* ids, int P, int E, int32_t* plan) {
     build_plan(ids, P, E, plan);
 }
@@ -193,13 +207,15 @@ constexpr int kGuRpw = 2;    // gate/up row pairs per wave
 template <int CMAX>
 __global__ void __launch_bounds__(256) moe_gate_up_kernel(MoeArgs a) {
     constexpr int KB = CMAX <= 4 ? 2 : 1;          // 1024-column chunks per load batch
+    __shared__ int32_t lplan[kPlanWords];
+    plan_to_lds(a.plan, a.P, lplan);
     const int slot = blockIdx.y;
-    const int U = a.plan[0];
+    const int U = lplan[0];
     if (slot >= U) return;
     const int P = a.P, D = a.D, F = a.F;
-    const int e = a.plan[1 + slot];
-    const int c = a.plan[1 + P + slot];
-    const int st = a.plan[1 + 2 * P + slot];
+    const int e = lplan[1 + slot];
+    const int c = lplan[1 + P + slot];
+    const int st = lplan[1 + 2 * P + slot];
     const int8_t* q = a.wgu + (size_t)e * a.gu_bytes;
     const uint16_t* d = reinterpret_cast<const uint16_t*>(q + (size_t)2 * F * D);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -213,7 +229,7 @@ __global__ void __launch_bounds__(256) moe_gate_up_kernel(MoeArgs a) {
         int ent[CMAX], tok[CMAX];
 #pragma unroll
         for (int ci = 0; ci < CMAX; ++ci) {
-            ent[ci] = a.plan[1 + 3 * P + st + cb + (ci < cn ? ci : 0)];
+            ent[ci] = lplan[1 + 3 * P + st + cb + (ci < cn ? ci : 0)];
             tok[ci] = ent[ci] / a.topk;
         }
         float ag[kGuRpw][CMAX], au[kGuRpw][CMAX];
@@ -384,13 +400,15 @@ __global__ void __launch_bounds__(256) moe_down_mfma_kernel(MoeArgs a) {
     constexpr int F = 64 * NL;
     constexpr int NIT = NB * 32 / 256;             // staging items per thread
     __shared__ u32x4 ua[NB][64];                   // A operands of the current entry chunk
+    __shared__ int32_t lplan[kPlanWords];
+    plan_to_lds(a.plan, a.P, lplan);
     const int slot = blockIdx.y;
-    const int U = a.plan[0];
+    const int U = lplan[0];
     if (slot >= U) return;
     const int P = a.P, D = a.D;
-    const int e = a.plan[1 + slot];
-    const int c = a.plan[1 + P + slot];
-    const int st = a.plan[1 + 2 * P + slot];
+    const int e = lplan[1 + slot];
+    const int c = lplan[1 + P + slot];
+    const int st = lplan[1 + 2 * P + slot];
     const int8_t* q = a.wdn + (size_t)e * a.dn_bytes;
     const uint16_t* d = reinterpret_cast<const uint16_t*>(q + (size_t)D * F);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -402,7 +420,7 @@ __global__ void __launch_bounds__(256) moe_down_mfma_kernel(MoeArgs a) {
     // below waits for h only (a wave's loads complete in issue order)
     int ent8[8];
 #pragma unroll
-    for (int ci = 0; ci < 8; ++ci) ent8[ci] = a.plan[1 + 3 * P + st + (ci < c ? ci : 0)];
+    for (int ci = 0; ci < 8; ++ci) ent8[ci] = lplan[1 + 3 * P + st + (ci < c ? ci : 0)];
     float4 hv[NIT][2];
 #pragma unroll
     for (int k = 0; k < NIT; ++k) {
@@ -430,7 +448,7 @@ __global__ void __launch_bounds__(256) moe_down_mfma_kernel(MoeArgs a) {
         if (cb > 0) {                              // later chunks (more than 8 entries): reload
             __syncthreads();                       // the previous chunk's operands are dead
 #pragma unroll
-            for (int ci = 0; ci < 8; ++ci) ent8[ci] = a.plan[1 + 3 * P + st + cb + (ci < cn ? ci : 0)];
+            for (int ci = 0; ci < 8; ++ci) ent8[ci] = lplan[1 + 3 * P + st + cb + (ci < cn ? ci : 0)];
 #pragma unroll
             for (int k = 0; k < NIT; ++k) {
                 const int it = (int)threadIdx.x + 256 * k;
