@@ -119,3 +119,31 @@ def test_moe_full_size(gpu):
     gpu.gq8_moe_q8_0_routed(xq, xd, ids, w, agu, adn, out2, T, topk, E, D, F, ws, nb)
     torch.cuda.synchronize()
     assert torch.equal(out, out2)
+
+
+@pytest.mark.parametrize("D,F", [(2048, 512), (160, 96)])
+def test_moe_crowded_expert(gpu, D, F):
+    """ids given directly (the routed call accepts any ids in range): a token may name an expert
+    twice and one expert takes 20 of the 32 entries, more than one 16-entry chunk of the gate/up
+    kernel and one 8-entry chunk of the down kernel."""
+    T, topk, E, seed = 16, 2, 3, 43
+    inp = synth.moe_inputs(T=T, E=E, D=D, seed=seed)
+    ids_ref = np.zeros((T, topk), np.int32)
+    ids_ref[10:, 1] = 1
+    ids_ref[12:, 0] = 2
+    p_ref = synth.uniform_f32(seed, "moe.crowded.w", (T, topk), 0.1, 0.9)
+    experts = lambda e: synth.moe_expert_weights(e, D=D, F=F, seed=seed)  # noqa: E731
+    agu, adn = _arena(gpu, experts, E, D, F, [0, 1, 2], seed)
+    xq = torch.empty((T, D), dtype=torch.int8, device="cuda")
+    xd = torch.empty((T, D // 32), dtype=torch.int16, device="cuda")
+    gpu.gq8_q8_1_quantize(to_dev(inp["x"]), T, D, xq, xd, None)
+    nb = gpu.gq8_moe_workspace_bytes(T, topk, D, F)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, D), dtype=torch.int16, device="cuda")
+    gpu.gq8_moe_q8_0_routed(xq, xd, to_dev(ids_ref), to_dev(p_ref), agu, adn, out, T, topk, E, D, F,
+                            ws, nb)
+    torch.cuda.synchronize()
+    x81 = quantize_q8_1_bf16(inp["x"])
+    blocks = lambda e: (quantize_q8_0(experts(e)["gate_up"]), quantize_q8_0(experts(e)["down"]))  # noqa: E731
+    y_ref, S = moe_forward(x81, ids_ref, p_ref, blocks)
+    check_bf16(to_host(out, np.uint16), y_ref, S, f"moe crowded D={D} F={F}")
