@@ -55,22 +55,30 @@ __global__ void __launch_bounds__(64 * MAXW) gemv_rows_kernel(GemvArgs a) {
         const int k = c * 1024 + lane * 16;
         const bool kok = k < K;                             // K % 32 == 0: k + 16 <= K
         const int kc = kok ? k : K - 16;
+        // all x rows in registers (TG == T): x first, then the weight rows in order, so that
+        // row r's dots wait only for loads up to row r (a wave's loads complete in issue order)
+        float xv[TG][16];
+        if (TG == T) {
+#pragma unroll
+            for (int t = 0; t < TG; ++t) load16_f32(x + (size_t)t * K + kc, xv[t]);
+        }
         u32x4 wq[RW];
         uint16_t wd[RW];
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
             const int row = imin(row0 + r, N - 1);
-            wq[r] = ld_nt16(a.q + (size_t)row * K + kc);
             wd[r] = a.d[(size_t)row * nblk + (kc >> 5)];
+            wq[r] = ld_nt16(a.q + (size_t)row * K + kc);
         }
 #pragma unroll
         for (int t0 = 0; t0 < T; t0 += TG) {
             // rows t0 + t >= T exist only when TG does not divide T: those are skipped at
             // compile time (no load, no accumulator)
-            float xv[TG][16];
+            if (TG != T) {
 #pragma unroll
-            for (int t = 0; t < TG; ++t)
-                if (t0 + t < T) load16_f32(x + (size_t)(t0 + t) * K + kc, xv[t]);
+                for (int t = 0; t < TG; ++t)
+                    if (t0 + t < T) load16_f32(x + (size_t)(t0 + t) * K + kc, xv[t]);
+            }
             __builtin_amdgcn_sched_barrier(0);
             if (!kok) {
 #pragma unroll
