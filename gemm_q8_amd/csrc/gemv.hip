@@ -114,7 +114,7 @@ __global__ void __launch_bounds__(64 * MAXW) gemv_rows_kernel(GemvArgs a) {
     }
 }
 
-template <int T> constexpr int gemv_rw() { return T <= 4 ? 2 : 1; }
+template <int T> constexpr int gemv_rw() { return T == 2 ? 4 : (T <= 4 ? 2 : 1); }
 
 // From this many token rows on, the GEMV runs on MFMA (the down read's slab kernel with x as the
 // A operand, then its combine): the VALU dot re-reads x from cache for every 16 weight bytes,
