@@ -206,7 +206,7 @@ constexpr int kGuRpw = 2;    // gate/up row pairs per wave
 // scales and the entries' q8_1 quants) are issued together, clamped, before any arithmetic.
 template <int CMAX>
 __global__ void __launch_bounds__(256) moe_gate_up_kernel(MoeArgs a) {
-    constexpr int KB = CMAX <= 4 ? 2 : 1;          // 1024-column chunks per load batch
+    constexpr int KB = 1;                          // 1024-column chunks per load batch
     __shared__ int32_t lplan[kPlanWords];
     plan_to_lds(a.plan, a.P, lplan);
     const int slot = blockIdx.y;
