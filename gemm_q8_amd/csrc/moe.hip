@@ -301,6 +301,88 @@ __global__ void __launch_bounds__(256) moe_gate_up_kernel(MoeArgs a) {
     }
 }
 
+// Gate/up with the wave's weight rows for all of D in registers (D <= 1024 NCH): the weight
+// loads of the whole row pairs are issued at once, then the slot's entries are taken one at a
+// time (x loads per entry, L2-resident), so the registers do not grow with the entry count and
+// more work-groups stay resident per CU.
+template <int NCH>
+__global__ void __launch_bounds__(256) moe_gate_up_rows_kernel(MoeArgs a) {
+    __shared__ int32_t lplan[kPlanWords];
+    plan_to_lds(a.plan, a.P, lplan);
+    const int slot = blockIdx.y;
+    const int U = lplan[0];
+    if (slot >= U) return;
+    const int P = a.P, D = a.D, F = a.F;
+    const int e = lplan[1 + slot];
+    const int c = lplan[1 + P + slot];
+    const int st = lplan[1 + 2 * P + slot];
+    const int8_t* q = a.wgu + (size_t)e * a.gu_bytes;
+    const uint16_t* d = reinterpret_cast<const uint16_t*>(q + (size_t)2 * F * D);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int pr0 = (blockIdx.x * 4 + wave) * kGuRpw;
+    const int nblk = D >> 5;
+
+    v4i qg[kGuRpw][NCH], qu[kGuRpw][NCH];
+    uint16_t dg[kGuRpw][NCH], du[kGuRpw][NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        const int k = j * 1024 + lane * 16;
+        const int kc = k < D ? k : D - 16;
+#pragma unroll
+        for (int r = 0; r < kGuRpw; ++r) {
+            const int n = pr0 + r < F ? pr0 + r : F - 1;
+            qg[r][j] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(q + (size_t)n * D + kc));
+            qu[r][j] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(q + (size_t)(F + n) * D + kc));
+            dg[r][j] = d[(size_t)n * nblk + (kc >> 5)];
+            du[r][j] = d[(size_t)(F + n) * nblk + (kc >> 5)];
+        }
+    }
+    for (int ci = 0; ci < c; ++ci) {
+        const int ent = lplan[1 + 3 * P + st + ci];
+        const int tok = ent / a.topk;
+        v4i xv[NCH];
+        uint16_t dx[NCH];
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const int k = j * 1024 + lane * 16;
+            const int kc = k < D ? k : D - 16;
+            xv[j] = *reinterpret_cast<const v4i*>(a.xq + (size_t)tok * D + kc);
+            dx[j] = a.xd[(size_t)tok * nblk + (kc >> 5)];
+        }
+        float ag[kGuRpw], au[kGuRpw];
+#pragma unroll
+        for (int r = 0; r < kGuRpw; ++r) { ag[r] = 0.f; au[r] = 0.f; }
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            if (j * 1024 + lane * 16 >= D) continue;
+            const v4i x = xv[j];
+            const float dxf = h2f(dx[j]);
+#pragma unroll
+            for (int r = 0; r < kGuRpw; ++r) {
+                int sg = 0, su = 0;
+                sg = __builtin_amdgcn_sdot4(qg[r][j].x, x.x, sg, false);
+                sg = __builtin_amdgcn_sdot4(qg[r][j].y, x.y, sg, false);
+                sg = __builtin_amdgcn_sdot4(qg[r][j].z, x.z, sg, false);
+                sg = __builtin_amdgcn_sdot4(qg[r][j].w, x.w, sg, false);
+                su = __builtin_amdgcn_sdot4(qu[r][j].x, x.x, su, false);
+                su = __builtin_amdgcn_sdot4(qu[r][j].y, x.y, su, false);
+                su = __builtin_amdgcn_sdot4(qu[r][j].z, x.z, su, false);
+                su = __builtin_amdgcn_sdot4(qu[r][j].w, x.w, su, false);
+                // d_w * d_x is exact in fp32 (11-bit x 11-bit significands)
+                ag[r] = fmaf((float)sg, h2f(dg[r][j]) * dxf, ag[r]);
+                au[r] = fmaf((float)su, h2f(du[r][j]) * dxf, au[r]);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kGuRpw; ++r) {
+            const float g = wave_sum(ag[r]);
+            const float u = wave_sum(au[r]);
+            const int n = pr0 + r;
+            if (lane == 0 && n < F) a.h[(size_t)ent * F + n] = g / (1.0f + expf(-g)) * u;
+        }
+    }
+}
+
 // Down projection: rows of F quants, F/16 lanes per row (F <= 1024), h in registers; each row's
 // lane partials are summed in a fixed order through LDS.
 constexpr int kDnNrs = 2;
@@ -554,9 +636,11 @@ int launch_moe_routed(const int8_t* xq, const uint16_t* xd, const int32_t* ids, 
     hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(256), 0, st, ids, a.P, E, plan);
     int rc = launch_status();
     if (rc != GQ8_OK) return rc;
-    const int cmax4 = T <= 4;
     const dim3 ggu((F + 4 * kGuRpw - 1) / (4 * kGuRpw), a.P);
-    if (cmax4) hipLaunchKernelGGL((moe_gate_up_kernel<4>), ggu, dim3(256), 0, st, a);
+    if (D <= 1024) hipLaunchKernelGGL((moe_gate_up_rows_kernel<1>), ggu, dim3(256), 0, st, a);
+    else if (D <= 2048) hipLaunchKernelGGL((moe_gate_up_rows_kernel<2>), ggu, dim3(256), 0, st, a);
+    else if (D <= 4096) hipLaunchKernelGGL((moe_gate_up_rows_kernel<4>), ggu, dim3(256), 0, st, a);
+    else if (T <= 4) hipLaunchKernelGGL((moe_gate_up_kernel<4>), ggu, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((moe_gate_up_kernel<16>), ggu, dim3(256), 0, st, a);
     if ((rc = launch_status()) != GQ8_OK) return rc;
     if (F == 256 || F == 512 || F == 1024) {
