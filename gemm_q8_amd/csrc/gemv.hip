@@ -169,10 +169,12 @@ constexpr int kDnRows = 64;                // rows per work-group: four waves of
 // only. The A operand is u = R * w_norm for the slab, staged once per work-group as exact bf16
 // hi and lo parts; for T <= 8 the two parts share one A operand (rows 0..7 hi, rows 8..15 lo of
 // token t), so one MFMA per block does both, and the hi and lo results are added at the end
-// (the block scale multiplies both). A wave reads its 16 x 512-byte weight tile in two column
-// halves of four coalesced 1 KiB loads (four rows x 256 bytes each), in the order the work
-// consumes them: activations first, then half 0, then half 1, so that the LDS transpose and
-// MFMAs of half 0 run while half 1 is still in flight. The weight tile is private to its wave.
+// (the block scale multiplies both). A wave reads its 16 x 512-byte weight tile in four column
+// quarters of two coalesced 1 KiB loads (eight rows x 128 bytes each), in the order the work
+// consumes them: activations and block scales first, then quarter 0, 1, 2, 3, so that the LDS
+// transpose, int8 -> bf16 conversion and MFMAs of one quarter run while the later quarters are
+// still in flight. The weight tile is private to its wave; each lane loads the block scales of
+// its own result row directly.
 //
 // XF (the Q8_0 GEMV at larger T): the A operand is x itself (fp32 [T][K]) instead of R * w_norm;
 // hi = bf16(x) and lo = bf16(x - hi), both rounded to nearest, leave |x - hi - lo| <= 2^-17 |x|,
@@ -186,7 +188,6 @@ __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
     __shared__ u32x4 ua[NPL][kDnNB][64];                           // A operands, lane order
     __shared__ float sqw[4][TR];                                   // per-wave sums of R^2
     __shared__ __attribute__((aligned(16))) uint8_t wt[4][16 * kDnStride];
-    __shared__ __attribute__((aligned(16))) uint16_t wsc[4][16][kDnNB];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int N = a.N, K = a.K, nblk = K >> 5;
     const int S = a.S;
@@ -226,21 +227,34 @@ __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
             nv[i] = *reinterpret_cast<const uint4*>(a.wnorm + kc);
         }
     }
-    // block scales: lane l holds row l/4, blocks 4(l%4) .. +3
-    uint16_t sc[4];
+    // block scales in the MFMA result layout: lane l needs the 16 scales of row r0 + l%16 (32
+    //    contiguous bytes when the slab is whole and scale rows are 16-byte aligned)
+    const int j = lane & 15, g = lane >> 4;
+    uint32_t sw[8];
     {
-        const int row = imin(r0 + (lane >> 2), N - 1);
+        const int row = imin(r0 + j, N - 1);
+        const uint16_t* dr = a.d + (size_t)row * nblk + (k0 >> 5);
+        if (cb == kDnNB && (nblk & 7) == 0) {
+            const u32x4 s01 = *reinterpret_cast<const u32x4*>(dr);
+            const u32x4 s23 = *reinterpret_cast<const u32x4*>(dr + 8);
+            sw[0] = s01.x; sw[1] = s01.y; sw[2] = s01.z; sw[3] = s01.w;
+            sw[4] = s23.x; sw[5] = s23.y; sw[6] = s23.z; sw[7] = s23.w;
+        } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            sc[j] = a.d[(size_t)row * nblk + imin((k0 >> 5) + 4 * (lane & 3) + j, nblk - 1)];
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t lo16 = 2 * i < cb ? dr[2 * i] : 0u;
+                const uint32_t hi16 = 2 * i + 1 < cb ? dr[2 * i + 1] : 0u;
+                sw[i] = lo16 | (hi16 << 16);
+            }
+        }
     }
-    // 1. weights: half h, load i covers rows 4i .. 4i+3, columns 256h .. +256 (16 lanes a row)
+    // 1. weights: quarter q = i / 2 covers columns 128q .. +128; load i covers rows 8(i%2) ..
+    //    +8 of it (8 lanes a row)
     u32x4 wv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int h = i >> 2;
-        const int row = imin(r0 + 4 * (i & 3) + (lane >> 4), N - 1);
-        const int col = k0 + imin(256 * h + 16 * (lane & 15), cw - 16);
+        const int row = imin(r0 + 8 * (i & 1) + (lane >> 3), N - 1);
+        const int col = k0 + imin(128 * (i >> 1) + 16 * (lane & 7), cw - 16);
         wv[i] = ld_nt16(a.q + (size_t)row * K + col);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -295,50 +309,40 @@ __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
 #pragma unroll
     for (int m = TR; m < 64; m <<= 1) r2acc += __shfl_xor(r2acc, m, 64);
     if (lane < TR) sqw[wave][lane] = r2acc;
-    {
-        uint2 sv;
-        sv.x = (uint32_t)sc[0] | ((uint32_t)sc[1] << 16);
-        sv.y = (uint32_t)sc[2] | ((uint32_t)sc[3] << 16);
-        *reinterpret_cast<uint2*>(&wsc[wave][lane >> 2][4 * (lane & 3)]) = sv;
-    }
     __syncthreads();
 
-    // 3. per half: weight tile into LDS (this wave only), then per block one MFMA (two for
+    // 3. per quarter: weight tile into LDS (this wave only), then per block one MFMA (two for
     //    T > 8) on the exact operands and the block scale (0 past the slab end)
-    const int j = lane & 15, g = lane >> 4;
     uint8_t* tile = wt[wave];
-    const u32x4 s01 = *reinterpret_cast<const u32x4*>(&wsc[wave][j][0]);
-    const u32x4 s23 = *reinterpret_cast<const u32x4*>(&wsc[wave][j][8]);
-    const uint32_t sw[8] = {s01.x, s01.y, s01.z, s01.w, s23.x, s23.y, s23.z, s23.w};
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int qq = 0; qq < 4; ++qq) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<u32x4*>(tile + (4 * i + (lane >> 4)) * kDnStride + 256 * h + 16 * (lane & 15)) =
-                wv[4 * h + i];
+        for (int i = 0; i < 2; ++i)
+            *reinterpret_cast<u32x4*>(tile + (8 * i + (lane >> 3)) * kDnStride + 128 * qq + 16 * (lane & 7)) =
+                wv[2 * qq + i];
         __builtin_amdgcn_wave_barrier();       // LDS accesses of one wave complete in order
-        uint2 q[8];
-        u32x4 x0[8], x1[8];
+        uint2 q[4];
+        u32x4 x0[4], x1[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int b = 8 * h + i;
+        for (int i = 0; i < 4; ++i) {
+            const int b = 4 * qq + i;
             q[i] = *reinterpret_cast<const uint2*>(tile + j * kDnStride + 32 * b + 8 * g);
             x0[i] = ua[0][b][lane];
             if (!PACK) x1[i] = ua[NPL - 1][b][lane];
         }
-        f32x4 D[8];
+        f32x4 D[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
             const bf16x8 w = i8x8_to_bf16x8(q[i].x, q[i].y);
             const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
             D[i] = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8, x0[i]), w, zf);
             if (!PACK) D[i] = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8, x1[i]), w, D[i]);
         }
-        __builtin_amdgcn_sched_barrier(0);     // eight MFMAs in flight, then their scales
+        __builtin_amdgcn_sched_barrier(0);     // four MFMAs in flight, then their scales
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int b = 8 * h + i;
+        for (int i = 0; i < 4; ++i) {
+            const int b = 4 * qq + i;
             const uint32_t sp = sw[b >> 1];
             const float dsc = b < cb ? h2f((uint16_t)((b & 1) ? (sp >> 16) : (sp & 0xffffu))) : 0.f;
 #pragma unroll
