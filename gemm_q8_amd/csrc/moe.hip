@@ -1,16 +1,17 @@
 // Routed experts with Q8_0 weights and a q8_1 input (EP page, "What changed": the q8_1 MoE input,
-// a device plan grouping the routed entries by expert, one row per entry written into a rows
-// buffer, then the single-card combine; defer page, "What it changes": rows combined weighted by
-// their routing weight).
+// the routed entries grouped by expert so each expert is computed once, then the single-card
+// combine; defer page, "What it changes": rows combined weighted by their routing weight).
 //
-// Kernels, in stream order:
-//   plan     one work-group: entries sorted by (expert, entry); distinct experts -> slots
-//   gate/up  grid (row pairs, slots): each slot's expert weights are read once for all of its
-//            tokens; per 32-block integer dots (v_dot4_i32_i8) of weight quants with the q8_1
-//            quants, scaled by both block scales; h = SiLU(gate) * up -> h[entry][F] fp32
-//   down     grid (row tiles, slots): rows of K = F bytes, lane groups per row as in the short
-//            Q8_0 read; h in registers; rows[entry][D] fp32
-//   combine  out[t] = bf16( sum_j w[t][j] * rows[t*topk + j] ), slots j in order
+// Kernels, in stream order (D <= 4096 and F in {256, 512, 1024}):
+//   gate/up  grid (row pairs, entries): the work-group of entry i works only when i is the first
+//            entry routed to its expert (a wave ballot over the ids, no plan kernel) and then
+//            serves all of that expert's entries, so each routed expert's weights are read once;
+//            per 32-block integer dots (v_dot4_i32_i8) of weight quants with the q8_1 quants,
+//            scaled by both block scales; h = SiLU(gate) * up -> h[entry][F] fp32
+//   down     grid (16-row tiles, tokens): the token's entries on MFMA, then the combine
+//            out[t] = bf16( sum_j w[t][j] * r_{t,j} ), j in order, in the same kernel
+// Other shapes: a one-work-group plan kernel (entries sorted by expert) feeds the general gate/up
+// kernel (D > 4096) and a VALU down kernel that writes rows[entry][D], then a combine kernel.
 // Experts that no token routes to are never read.
 #include "gq8_device.h"
 #include "gq8_internal.h"
@@ -194,10 +195,47 @@ struct MoeArgs {
     size_t gu_bytes, dn_bytes;
     uint16_t* out;          // [T][D]
     int T, topk, P, E, D, F;
+    const int32_t* ids;     // [T][topk] (the kernels that take no plan)
     const int32_t* plan;
     float* h;               // [P][F]
     float* rows;            // [P][D]
 };
+
+// The entries routed to entry i's expert, straight from the ids (no plan): lane l of the wave
+// holds ids[l], ids[64 + l], ... (P <= 256) and one ballot per word marks the entries whose id
+// equals ids[i]; bit k of m[w] is entry 64 w + k. Every lane gets the same (wave-uniform) masks.
+// ok is false when any id lies outside [0, E) (the call then writes zeros, as a plan error does).
+struct EntrySet {
+    uint64_t m[4];
+    int e;
+    bool ok;
+};
+
+GQ8_DEV EntrySet entry_set(const int32_t* ids, int P, int E, int i) {
+    const int lane = threadIdx.x & 63;
+    int v[4];
+    bool bad = false;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int k = 64 * w + lane;
+        v[w] = k < P ? ids[k] : -1;
+        bad = bad || (k < P && (v[w] < 0 || v[w] >= E));
+    }
+    EntrySet r;
+    r.e = ids[i];
+    r.ok = __ballot(bad) == 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) r.m[w] = __ballot(64 * w + lane < P && v[w] == r.e);
+    return r;
+}
+
+// first entry of the set (P if empty)
+GQ8_DEV int entry_first(const EntrySet& s) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+        if (s.m[w] != 0) return 64 * w + __builtin_ctzll(s.m[w]);
+    return 1 << 30;
+}
 
 constexpr int kGuRpw = 2;    // gate/up row pairs per wave
 
@@ -301,22 +339,19 @@ __global__ void __launch_bounds__(256) moe_gate_up_kernel(MoeArgs a) {
     }
 }
 
-// Gate/up with the wave's weight rows for all of D in registers (D <= 1024 NCH): the weight
-// loads of the whole row pairs are issued at once, then the slot's entries are taken one at a
-// time (x loads per entry, L2-resident), so the registers do not grow with the entry count and
-// more work-groups stay resident per CU.
+// Gate/up with the wave's weight rows for all of D in registers (D <= 1024 NCH), with no plan:
+// the work-group of grid row i works only if entry i is the first entry routed to its expert,
+// and then serves every entry of that expert (entry_set), so each routed expert's weights are
+// read once. The weight loads of the whole row pairs are issued at once, then the entries are
+// taken one at a time in ascending order (x loads per entry, L2-resident), so the registers do
+// not grow with the entry count and more work-groups stay resident per CU.
 template <int NCH>
 __global__ void __launch_bounds__(256) moe_gate_up_rows_kernel(MoeArgs a) {
-    __shared__ int32_t lplan[kPlanWords];
-    plan_to_lds(a.plan, a.P, lplan);
-    const int slot = blockIdx.y;
-    const int U = lplan[0];
-    if (slot >= U) return;
-    const int P = a.P, D = a.D, F = a.F;
-    const int e = lplan[1 + slot];
-    const int c = lplan[1 + P + slot];
-    const int st = lplan[1 + 2 * P + slot];
-    const int8_t* q = a.wgu + (size_t)e * a.gu_bytes;
+    const int i0 = blockIdx.y;
+    const EntrySet es = entry_set(a.ids, a.P, a.E, i0);
+    if (!es.ok || entry_first(es) != i0) return;
+    const int D = a.D, F = a.F;
+    const int8_t* q = a.wgu + (size_t)es.e * a.gu_bytes;
     const uint16_t* d = reinterpret_cast<const uint16_t*>(q + (size_t)2 * F * D);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int pr0 = (blockIdx.x * 4 + wave) * kGuRpw;
@@ -337,48 +372,51 @@ __global__ void __launch_bounds__(256) moe_gate_up_rows_kernel(MoeArgs a) {
             du[r][j] = d[(size_t)(F + n) * nblk + (kc >> 5)];
         }
     }
-    for (int ci = 0; ci < c; ++ci) {
-        const int ent = lplan[1 + 3 * P + st + ci];
-        const int tok = ent / a.topk;
-        v4i xv[NCH];
-        uint16_t dx[NCH];
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            const int k = j * 1024 + lane * 16;
-            const int kc = k < D ? k : D - 16;
-            xv[j] = *reinterpret_cast<const v4i*>(a.xq + (size_t)tok * D + kc);
-            dx[j] = a.xd[(size_t)tok * nblk + (kc >> 5)];
-        }
-        float ag[kGuRpw], au[kGuRpw];
+    for (int w = 0; w < 4; ++w) {
+        for (uint64_t mm = es.m[w]; mm != 0; mm &= mm - 1) {
+            const int ent = 64 * w + __builtin_ctzll(mm);
+            const int tok = ent / a.topk;
+            v4i xv[NCH];
+            uint16_t dx[NCH];
 #pragma unroll
-        for (int r = 0; r < kGuRpw; ++r) { ag[r] = 0.f; au[r] = 0.f; }
+            for (int j = 0; j < NCH; ++j) {
+                const int k = j * 1024 + lane * 16;
+                const int kc = k < D ? k : D - 16;
+                xv[j] = *reinterpret_cast<const v4i*>(a.xq + (size_t)tok * D + kc);
+                dx[j] = a.xd[(size_t)tok * nblk + (kc >> 5)];
+            }
+            float ag[kGuRpw], au[kGuRpw];
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            if (j * 1024 + lane * 16 >= D) continue;
-            const v4i x = xv[j];
-            const float dxf = h2f(dx[j]);
+            for (int r = 0; r < kGuRpw; ++r) { ag[r] = 0.f; au[r] = 0.f; }
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+                if (j * 1024 + lane * 16 >= D) continue;
+                const v4i x = xv[j];
+                const float dxf = h2f(dx[j]);
+#pragma unroll
+                for (int r = 0; r < kGuRpw; ++r) {
+                    int sg = 0, su = 0;
+                    sg = __builtin_amdgcn_sdot4(qg[r][j].x, x.x, sg, false);
+                    sg = __builtin_amdgcn_sdot4(qg[r][j].y, x.y, sg, false);
+                    sg = __builtin_amdgcn_sdot4(qg[r][j].z, x.z, sg, false);
+                    sg = __builtin_amdgcn_sdot4(qg[r][j].w, x.w, sg, false);
+                    su = __builtin_amdgcn_sdot4(qu[r][j].x, x.x, su, false);
+                    su = __builtin_amdgcn_sdot4(qu[r][j].y, x.y, su, false);
+                    su = __builtin_amdgcn_sdot4(qu[r][j].z, x.z, su, false);
+                    su = __builtin_amdgcn_sdot4(qu[r][j].w, x.w, su, false);
+                    // d_w * d_x is exact in fp32 (11-bit x 11-bit significands)
+                    ag[r] = fmaf((float)sg, h2f(dg[r][j]) * dxf, ag[r]);
+                    au[r] = fmaf((float)su, h2f(du[r][j]) * dxf, au[r]);
+                }
+            }
 #pragma unroll
             for (int r = 0; r < kGuRpw; ++r) {
-                int sg = 0, su = 0;
-                sg = __builtin_amdgcn_sdot4(qg[r][j].x, x.x, sg, false);
-                sg = __builtin_amdgcn_sdot4(qg[r][j].y, x.y, sg, false);
-                sg = __builtin_amdgcn_sdot4(qg[r][j].z, x.z, sg, false);
-                sg = __builtin_amdgcn_sdot4(qg[r][j].w, x.w, sg, false);
-                su = __builtin_amdgcn_sdot4(qu[r][j].x, x.x, su, false);
-                su = __builtin_amdgcn_sdot4(qu[r][j].y, x.y, su, false);
-                su = __builtin_amdgcn_sdot4(qu[r][j].z, x.z, su, false);
-                su = __builtin_amdgcn_sdot4(qu[r][j].w, x.w, su, false);
-                // d_w * d_x is exact in fp32 (11-bit x 11-bit significands)
-                ag[r] = fmaf((float)sg, h2f(dg[r][j]) * dxf, ag[r]);
-                au[r] = fmaf((float)su, h2f(du[r][j]) * dxf, au[r]);
+                const float g = wave_sum(ag[r]);
+                const float u = wave_sum(au[r]);
+                const int n = pr0 + r;
+                if (lane == 0 && n < F) a.h[(size_t)ent * F + n] = g / (1.0f + expf(-g)) * u;
             }
-        }
-#pragma unroll
-        for (int r = 0; r < kGuRpw; ++r) {
-            const float g = wave_sum(ag[r]);
-            const float u = wave_sum(au[r]);
-            const int n = pr0 + r;
-            if (lane == 0 && n < F) a.h[(size_t)ent * F + n] = g / (1.0f + expf(-g)) * u;
         }
     }
 }
@@ -467,132 +505,138 @@ __global__ void __launch_bounds__(256) moe_down_kernel(MoeArgs a) {
     }
 }
 
-// Down projection on MFMA (F % 64 == 0, F = 64 NL): one 16-row tile of the expert's down weight
-// per wave, 4 waves per work-group, the slot's entries as the A rows. h (fp32) is staged per
-// chunk of 8 entries as bf16 hi + lo (|h - hi - lo| <= 2^-17 |h|) in one packed A operand (rows
-// 0..7 hi, 8..15 lo of entry ci). The weight rows (F bytes each) are read straight into MFMA
-// operands: load i gives lane l the 16 bytes of row l%16 at column 64i + 16(l/16) (Q8_0 block 2i
-// in lanes 0..31, 2i+1 in lanes 32..63), and v_permlane32_swap makes both blocks' operands, so
-// lane (row j, k-group g) holds block offset {0, 16, 8, 24}[g] -- the A operand uses the same.
+// Down projection with the combine folded in (F = 64 NL): one work-group per (16 output rows,
+// token t). Wave w takes the token's entries j = w, w + 4, ... (up to two at a time in flight):
+// the entry's expert tile of 16 rows x F bytes is read straight into MFMA operands -- load i
+// gives lane l the 16 bytes of row l%16 at column 64i + 16(l/16) (Q8_0 block 2i in lanes 0..31,
+// 2i+1 in lanes 32..63), and v_permlane32_swap makes both blocks' operands, so lane (row j,
+// k-group g) holds block offset {0, 16, 8, 24}[g]. The entry's h (fp32) is staged through LDS
+// as bf16 hi and lo (|h - hi - lo| <= 2^-17 |h|); A rows 0..7 take hi and rows 8..15 lo, so
+// result rows 0 and 8 hold the two parts. The per-entry results r_j go to LDS and one wave
+// forms out[t] = bf16( sum_j w[t][j] r_j ), j in order (the combine's order). An expert that
+// two tokens route to is read by both tokens' work-groups.
 GQ8_DEV int dn_koff(int g) { return 16 * (g & 1) + 8 * (g >> 1); }
+GQ8_DEV int imin_m(int x, int y) { return x < y ? x : y; }
+
+constexpr int kMoeMaxTopk = 16;
 
 template <int NL>
-__global__ void __launch_bounds__(256) moe_down_mfma_kernel(MoeArgs a) {
+__global__ void __launch_bounds__(256) moe_down_token_kernel(MoeArgs a) {
     constexpr int NB = 2 * NL;                     // Q8_0 blocks per row
     constexpr int F = 64 * NL;
-    constexpr int NIT = NB * 32 / 256;             // staging items per thread
-    __shared__ u32x4 ua[NB][64];                   // A operands of the current entry chunk
-    __shared__ int32_t lplan[kPlanWords];
-    plan_to_lds(a.plan, a.P, lplan);
-    const int slot = blockIdx.y;
-    const int U = lplan[0];
-    if (slot >= U) return;
-    const int P = a.P, D = a.D;
-    const int e = lplan[1 + slot];
-    const int c = lplan[1 + P + slot];
-    const int st = lplan[1 + 2 * P + slot];
-    const int8_t* q = a.wdn + (size_t)e * a.dn_bytes;
-    const uint16_t* d = reinterpret_cast<const uint16_t*>(q + (size_t)D * F);
+    constexpr int EG = NL >= 16 ? 1 : 2;           // entries in flight per wave
+    constexpr int HC = (F / 8 + 63) / 64;          // 8-float pieces of h per lane
+    __shared__ __attribute__((aligned(16))) uint16_t hs[4][EG][2][F];
+    __shared__ float rr[kMoeMaxTopk][16];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j = lane & 15, g = lane >> 4;
-    const int r0 = (blockIdx.x * 4 + wave) * 16;
+    const int t = blockIdx.y, topk = a.topk, D = a.D;
+    const int r0 = blockIdx.x * 16;
     const int row = r0 + j < D ? r0 + j : D - 1;
 
-    // entries of the first chunk (uniform), then their h pieces, then the weights: the staging
-    // below waits for h only (a wave's loads complete in issue order)
-    int ent8[8];
-#pragma unroll
-    for (int ci = 0; ci < 8; ++ci) ent8[ci] = lplan[1 + 3 * P + st + (ci < c ? ci : 0)];
-    float4 hv[NIT][2];
-#pragma unroll
-    for (int k = 0; k < NIT; ++k) {
-        const int it = (int)threadIdx.x + 256 * k;
-        const int ci = it & 7, g2 = (it >> 3) & 3, b = it >> 5;
-        int ent = ent8[0];
-#pragma unroll
-        for (int cc = 1; cc < 8; ++cc) ent = ci == cc ? ent8[cc] : ent;
-        const float4* hp = reinterpret_cast<const float4*>(a.h + (size_t)ent * F + 32 * b + dn_koff(g2));
-        hv[k][0] = hp[0];
-        hv[k][1] = hp[1];
+    bool bad = false;
+    for (int k = lane; k < a.P; k += 64) {
+        const int e = a.ids[k];
+        bad = bad || e < 0 || e >= a.E;
     }
-    uint32_t sc[NL];
-    const uint32_t* dp = reinterpret_cast<const uint32_t*>(d + (size_t)row * NB);
-#pragma unroll
-    for (int i = 0; i < NL; ++i) sc[i] = dp[i];
-    v4i wv[NL];
-    const int8_t* wp = q + (size_t)row * F + 16 * g;
-#pragma unroll
-    for (int i = 0; i < NL; ++i) wv[i] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wp + 64 * i));
-    __builtin_amdgcn_sched_barrier(0);
+    const bool ok = __ballot(bad) == 0;            // wave-uniform; the same in every wave
+    const int ko = 2 * dn_koff(g);                 // byte offset of the lane's k-group in a bf16 row
+    const int hl = j < 8 ? 0 : 1;                  // A rows 0..7 hi, 8..15 lo
 
-    for (int cb = 0; cb < c; cb += 8) {
-        const int cn = c - cb < 8 ? c - cb : 8;
-        if (cb > 0) {                              // later chunks (more than 8 entries): reload
-            __syncthreads();                       // the previous chunk's operands are dead
+    for (int j0 = wave; ok && j0 < topk; j0 += 4 * EG) {
+        int ent[EG];
+        bool on[EG];
+        float4 hv[EG][HC][2];
+        uint32_t sc[EG][NL];
+        v4i wv[EG][NL];
 #pragma unroll
-            for (int ci = 0; ci < 8; ++ci) ent8[ci] = lplan[1 + 3 * P + st + cb + (ci < cn ? ci : 0)];
+        for (int u = 0; u < EG; ++u) {
+            const int jj = j0 + 4 * u;
+            on[u] = jj < topk;
+            ent[u] = t * topk + (on[u] ? jj : j0);
+            const float4* hp = reinterpret_cast<const float4*>(a.h + (size_t)ent[u] * F);
 #pragma unroll
-            for (int k = 0; k < NIT; ++k) {
-                const int it = (int)threadIdx.x + 256 * k;
-                const int ci = it & 7, g2 = (it >> 3) & 3, b = it >> 5;
-                int ent = ent8[0];
-#pragma unroll
-                for (int cc = 1; cc < 8; ++cc) ent = ci == cc ? ent8[cc] : ent;
-                const float4* hp = reinterpret_cast<const float4*>(a.h + (size_t)ent * F + 32 * b + dn_koff(g2));
-                hv[k][0] = hp[0];
-                hv[k][1] = hp[1];
+            for (int c = 0; c < HC; ++c) {
+                const int pc = imin_m(lane + 64 * c, F / 8 - 1);
+                hv[u][c][0] = hp[2 * pc];
+                hv[u][c][1] = hp[2 * pc + 1];
             }
         }
-        // stage: item (b, g2, ci): entry ci's h at columns 32 b + dn_koff(g2) .. +8 as bf16 hi
-        // (row ci) and lo (row 8 + ci); absent entries are zero rows
 #pragma unroll
-        for (int k = 0; k < NIT; ++k) {
-            const int it = (int)threadIdx.x + 256 * k;
-            const int ci = it & 7, g2 = (it >> 3) & 3, b = it >> 5;
-            const float f[8] = {hv[k][0].x, hv[k][0].y, hv[k][0].z, hv[k][0].w,
-                                hv[k][1].x, hv[k][1].y, hv[k][1].z, hv[k][1].w};
-            uint32_t h4[4], l4[4];
+        for (int u = 0; u < EG; ++u) {
+            const int8_t* q = a.wdn + (size_t)a.ids[ent[u]] * a.dn_bytes;
+            const uint32_t* dp = reinterpret_cast<const uint32_t*>(q + (size_t)D * F) + (size_t)row * (NB / 2);
 #pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                const float f0 = ci < cn ? f[2 * e2] : 0.f, f1 = ci < cn ? f[2 * e2 + 1] : 0.f;
-                const uint16_t h0 = f2bf_bits(f0), h1 = f2bf_bits(f1);
-                h4[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-                l4[e2] = (uint32_t)f2bf_bits(f0 - bf2f(h0)) | ((uint32_t)f2bf_bits(f1 - bf2f(h1)) << 16);
+            for (int i = 0; i < NL; i += 4) {
+                const u32x4 s4 = *reinterpret_cast<const u32x4*>(dp + i);
+                sc[u][i] = s4.x; sc[u][i + 1] = s4.y; sc[u][i + 2] = s4.z; sc[u][i + 3] = s4.w;
             }
-            ua[b][16 * g2 + ci] = u32x4{h4[0], h4[1], h4[2], h4[3]};
-            ua[b][16 * g2 + 8 + ci] = u32x4{l4[0], l4[1], l4[2], l4[3]};
+            const int8_t* wp = q + (size_t)row * F + 16 * g;
+#pragma unroll
+            for (int i = 0; i < NL; ++i) wv[u][i] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wp + 64 * i));
         }
-        __syncthreads();
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            const auto s02 = __builtin_amdgcn_permlane32_swap((uint32_t)wv[i].x, (uint32_t)wv[i].z, false, false);
-            const auto s13 = __builtin_amdgcn_permlane32_swap((uint32_t)wv[i].y, (uint32_t)wv[i].w, false, false);
+        for (int u = 0; u < EG; ++u) {
+            // h -> bf16 hi, lo in this wave's LDS slot
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int b = 2 * i + h;
-                const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
-                const f32x4 D4 = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8, ua[b][lane]),
-                                                    i8x8_to_bf16x8(s02[h], s13[h]), zf);
-                const float dsc = h2f((uint16_t)(h ? (sc[i] >> 16) : (sc[i] & 0xffffu)));
+            for (int c = 0; c < HC; ++c) {
+                const int pc = lane + 64 * c;
+                if (pc < F / 8) {
+                    const float f[8] = {hv[u][c][0].x, hv[u][c][0].y, hv[u][c][0].z, hv[u][c][0].w,
+                                        hv[u][c][1].x, hv[u][c][1].y, hv[u][c][1].z, hv[u][c][1].w};
+                    uint32_t h4[4], l4[4];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) acc[v] = fmaf(dsc, D4[v], acc[v]);
-            }
-        }
-        // rows 8..15 (lanes 32..63) hold the lo parts: add them to rows 0..7 (entries)
-        float tot[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) tot[v] = acc[v] + __shfl_down(acc[v], 32, 64);
-        if (lane < 32 && r0 + j < D) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int ci = 4 * g + v;
-                int ent = ent8[0];
-#pragma unroll
-                for (int cc = 1; cc < 8; ++cc) ent = ci == cc ? ent8[cc] : ent;
-                if (ci < cn) a.rows[(size_t)ent * D + r0 + j] = tot[v];
+                    for (int e2 = 0; e2 < 4; ++e2) {
+                        const uint16_t h0 = f2bf_bits(f[2 * e2]), h1 = f2bf_bits(f[2 * e2 + 1]);
+                        h4[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                        l4[e2] = (uint32_t)f2bf_bits(f[2 * e2] - bf2f(h0)) |
+                                 ((uint32_t)f2bf_bits(f[2 * e2 + 1] - bf2f(h1)) << 16);
+                    }
+                    *reinterpret_cast<u32x4*>(&hs[wave][u][0][8 * pc]) = u32x4{h4[0], h4[1], h4[2], h4[3]};
+                    *reinterpret_cast<u32x4*>(&hs[wave][u][1][8 * pc]) = u32x4{l4[0], l4[1], l4[2], l4[3]};
+                }
             }
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int u = 0; u < EG; ++u) {
+            const uint8_t* hb = reinterpret_cast<const uint8_t*>(&hs[wave][u][hl][0]);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                const auto s02 = __builtin_amdgcn_permlane32_swap((uint32_t)wv[u][i].x, (uint32_t)wv[u][i].z, false, false);
+                const auto s13 = __builtin_amdgcn_permlane32_swap((uint32_t)wv[u][i].y, (uint32_t)wv[u][i].w, false, false);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int b = 2 * i + h;
+                    const u32x4 x = *reinterpret_cast<const u32x4*>(hb + 64 * b + ko);
+                    const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
+                    const f32x4 D4 = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8, x),
+                                                        i8x8_to_bf16x8(s02[h], s13[h]), zf);
+                    const float dsc = h2f((uint16_t)(h ? (sc[u][i] >> 16) : (sc[u][i] & 0xffffu)));
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[v] = fmaf(dsc, D4[v], acc[v]);
+                }
+            }
+            // result row 8 (lanes 32..47, v = 0) holds the lo part: add it to row 0 (lanes 0..15)
+            const float tot = acc[0] + __shfl_down(acc[0], 32, 64);
+            if (on[u] && lane < 16) rr[j0 + 4 * u][j] = tot;
+        }
+        // the next round overwrites this wave's hs slot: every lane's reads come first
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    __syncthreads();
+    if (wave == 0 && lane < 16 && r0 + lane < D) {
+        float v = 0.f;
+        if (ok) {
+            for (int jj = 0; jj < topk; ++jj) v = fmaf(a.w[t * topk + jj], rr[jj][lane], v);
+        }
+        a.out[(size_t)t * D + r0 + lane] = f2bf_bits(v);
     }
 }
 
@@ -633,9 +677,16 @@ int launch_moe_routed(const int8_t* xq, const uint16_t* xd, const int32_t* ids, 
     p += round_up(P * F * sizeof(float), kCounterAlign);
     a.rows = reinterpret_cast<float*>(p);
 
-    hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(256), 0, st, ids, a.P, E, plan);
-    int rc = launch_status();
-    if (rc != GQ8_OK) return rc;
+    a.ids = ids;
+    // the plan is needed only by the fallback kernels (D > 4096 gate/up; F outside
+    // {256, 512, 1024} down)
+    const bool rows_gu = D <= 4096;
+    const bool token_dn = F == 256 || F == 512 || F == 1024;
+    int rc = GQ8_OK;
+    if (!rows_gu || !token_dn) {
+        hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(256), 0, st, ids, a.P, E, plan);
+        if ((rc = launch_status()) != GQ8_OK) return rc;
+    }
     const dim3 ggu((F + 4 * kGuRpw - 1) / (4 * kGuRpw), a.P);
     if (D <= 1024) hipLaunchKernelGGL((moe_gate_up_rows_kernel<1>), ggu, dim3(256), 0, st, a);
     else if (D <= 2048) hipLaunchKernelGGL((moe_gate_up_rows_kernel<2>), ggu, dim3(256), 0, st, a);
@@ -643,16 +694,16 @@ int launch_moe_routed(const int8_t* xq, const uint16_t* xd, const int32_t* ids, 
     else if (T <= 4) hipLaunchKernelGGL((moe_gate_up_kernel<4>), ggu, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((moe_gate_up_kernel<16>), ggu, dim3(256), 0, st, a);
     if ((rc = launch_status()) != GQ8_OK) return rc;
-    if (F == 256 || F == 512 || F == 1024) {
-        const dim3 gm((D + 63) / 64, a.P);
-        if (F == 256) hipLaunchKernelGGL((moe_down_mfma_kernel<4>), gm, dim3(256), 0, st, a);
-        else if (F == 512) hipLaunchKernelGGL((moe_down_mfma_kernel<8>), gm, dim3(256), 0, st, a);
-        else hipLaunchKernelGGL((moe_down_mfma_kernel<16>), gm, dim3(256), 0, st, a);
-    } else {
-        const int rps = 64 / (F / 16);
-        const dim3 gdn((D + 4 * kDnNrs * rps - 1) / (4 * kDnNrs * rps), a.P);
-        hipLaunchKernelGGL((moe_down_kernel<4>), gdn, dim3(256), (size_t)4 * kDnNrs * 64 * 4 * sizeof(float), st, a);
+    if (token_dn) {                        // down + combine in one kernel
+        const dim3 gt((D + 15) / 16, T);
+        if (F == 256) hipLaunchKernelGGL((moe_down_token_kernel<4>), gt, dim3(256), 0, st, a);
+        else if (F == 512) hipLaunchKernelGGL((moe_down_token_kernel<8>), gt, dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((moe_down_token_kernel<16>), gt, dim3(256), 0, st, a);
+        return launch_status();
     }
+    const int rps = 64 / (F / 16);
+    const dim3 gdn((D + 4 * kDnNrs * rps - 1) / (4 * kDnNrs * rps), a.P);
+    hipLaunchKernelGGL((moe_down_kernel<4>), gdn, dim3(256), (size_t)4 * kDnNrs * 64 * 4 * sizeof(float), st, a);
     if ((rc = launch_status()) != GQ8_OK) return rc;
     hipLaunchKernelGGL(moe_combine_kernel, dim3((T * D + 255) / 256), dim3(256), 0, st, a);
     return launch_status();

@@ -176,9 +176,9 @@ int gq8_w8a8_gemm_i32(const int8_t* xq, const int8_t* W_packed, int32_t* acc, in
                       int K, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
- * Routed experts (EP page, "What changed": q8_1 MoE input, a device plan grouping the routed
- * entries by expert, one row per entry into a rows buffer, then the single-card combine;
- * defer page, "What it changes": rows combined by routing weight).
+ * Routed experts (EP page, "What changed": q8_1 MoE input, the routed entries grouped by expert
+ * so each expert's weights are read once, then the single-card combine; defer page, "What it
+ * changes": rows combined by routing weight).
  * ------------------------------------------------------------------------------------------ */
 
 /* Softmax over E router logits per token, then the top-k experts by probability, descending
