@@ -656,15 +656,18 @@ int launch_hc_up(GemvArgs a, hipStream_t st) { GQ8_T_SWITCH(launch_up_t, a, st) 
 // The up read of the down/up pair for K == 320 and small T with the down's combine folded in:
 // waves 4..7 of the work-group add the down's slab partial sums for all T x 320 inputs (the same
 // order as hc_down_combine_kernel, so lo is bitwise the down read's output), apply rs and round
-// to bf16 into LDS, while waves 0..3 have their weight loads in flight; after one barrier waves
-// 0..3 run the up read's MFMAs as hc_up_direct_kernel does. Every work-group computes the same
+// to bf16 into LDS, while waves 0..3 have their weight loads in flight; after the combine's two
+// barriers waves 0..3 run the up read's MFMAs as hc_up_direct_kernel does. Every work-group computes the same
 // lo; work-group 0 also writes lo and rs out. Separate waves keep the partial-sum loads (L2)
 // from waiting behind the weight loads (HBM): a wave's loads complete in issue order.
 constexpr int kPairQuads = kUpCW / 4;       // float4 quads of a 320-wide row
 
 template <int T>
 __global__ void __launch_bounds__(512) hc_pair_up_kernel(GemvArgs a) {
+    constexpr int NQ = T * kPairQuads;                            // float4 quads of lo
+    constexpr int NIT = (4 * NQ + 255) / 256;                     // (quad, slab group) items per thread
     __shared__ __attribute__((aligned(16))) uint8_t xl[kMaxT][kUpLoStride];
+    __shared__ float4 red[4][NQ];                                 // slab-group sums
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int N = a.N, K = a.K;                                   // up rows, up depth (== 320)
     const int j = lane & 15, g = lane >> 4;
@@ -680,7 +683,8 @@ __global__ void __launch_bounds__(512) hc_pair_up_kernel(GemvArgs a) {
         const int8_t* wp = a.q + (size_t)row * K + 16 * g;
 #pragma unroll
         for (int i = 0; i < kUpLoads; ++i) wv[i] = ld_nt16(wp + 64 * i);
-        __syncthreads();
+        __syncthreads();                                          // slab-group sums in LDS
+        __syncthreads();                                          // lo in LDS
         const u32x4 z = {0u, 0u, 0u, 0u};
         const int tj = j < T ? j : 0;
         const int ko = 2 * up_koff(g);
@@ -710,50 +714,42 @@ __global__ void __launch_bounds__(512) hc_pair_up_kernel(GemvArgs a) {
         }
         return;
     }
-    // combine waves: rs[t] from the slab sums of squares (lane-strided, then the wave sum, as
-    // hc_down_combine_kernel does), then lo for quads (t, 4 consecutive inputs)
+    // combine waves. Item it = ct + 256 m is (quad it % NQ, slab group it / NQ): the group's
+    // ceil(S/4) consecutive slabs added in ascending order; every item's loads are issued before
+    // the first wait. Then rs[t] from the slab sums of squares (lane-strided, then the wave sum),
+    // and lo = bf16(rs * (((g0 + g1) + g2) + g3)) -- hc_down_combine_kernel's order.
     const int S = a.S;
     const int ct = (int)threadIdx.x - 256;
-    float rs[T];
-    {
-        float ss[T];
+    const int per = (S + 3) / 4;
+    const size_t plane = (size_t)T * K / 4;                       // float4s per slab plane
+    float4 gs[NIT];
+    if (S == 32) {                                                // per == 8: one batch of loads
+        float4 pv[NIT][8];
 #pragma unroll
-        for (int t = 0; t < T; ++t) ss[t] = 0.f;
-        for (int s = lane; s < S; s += 64) {
+        for (int m = 0; m < NIT; ++m) {
+            const int it = imin(ct + 256 * m, 4 * NQ - 1);
+            const int qd = it % NQ, sg = it / NQ;
+            const int t = qd / kPairQuads, n = 4 * (qd - t * kPairQuads);
+            const float4* p = reinterpret_cast<const float4*>(a.part + (size_t)t * K + n) + (size_t)8 * sg * plane;
 #pragma unroll
-            for (int t = 0; t < T; ++t) ss[t] += a.ssq[(size_t)s * T + t];
+            for (int i = 0; i < 8; ++i) pv[m][i] = p[(size_t)i * plane];
         }
 #pragma unroll
-        for (int t = 0; t < T; ++t) rs[t] = 1.0f / sqrtf(wave_sum(ss[t]) / (float)a.kd + a.eps);
-    }
-    if (blockIdx.x == 0 && ct < T && a.rs_out != nullptr) {
+        for (int m = 0; m < NIT; ++m) {
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int t = 0; t < T; ++t)
-            if (t == ct) a.rs_out[t] = rs[t];
-    }
-    const int per = (S + 3) / 4;
-    for (int qd = ct; qd < T * kPairQuads; qd += 256) {
-        const int t = qd / kPairQuads, n = 4 * (qd - t * kPairQuads);
-        const float4* p = reinterpret_cast<const float4*>(a.part + (size_t)t * K + n);
-        const size_t plane = (size_t)T * K / 4;                     // float4s per slab plane
-        float4 vg[4];
-        if (S == 32) {                      // per == 8: all 32 loads in flight at once
-            float4 pv[32];
-#pragma unroll
-            for (int i = 0; i < 32; ++i) pv[i] = p[(size_t)i * plane];
-#pragma unroll
-            for (int sg = 0; sg < 4; ++sg) {
-                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    v.x += pv[8 * sg + i].x; v.y += pv[8 * sg + i].y;
-                    v.z += pv[8 * sg + i].z; v.w += pv[8 * sg + i].w;
-                }
-                vg[sg] = v;
+            for (int i = 0; i < 8; ++i) {
+                v.x += pv[m][i].x; v.y += pv[m][i].y; v.z += pv[m][i].z; v.w += pv[m][i].w;
             }
-        } else
+            gs[m] = v;
+        }
+    } else {
 #pragma unroll
-        for (int sg = 0; sg < 4; ++sg) {
+        for (int m = 0; m < NIT; ++m) {
+            const int it = imin(ct + 256 * m, 4 * NQ - 1);
+            const int qd = it % NQ, sg = it / NQ;
+            const int t = qd / kPairQuads, n = 4 * (qd - t * kPairQuads);
+            const float4* p = reinterpret_cast<const float4*>(a.part + (size_t)t * K + n);
             const int s0 = sg * per, s1 = imin(S, s0 + per);
             float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
             for (int s = s0; s < s1; s += 8) {
@@ -767,15 +763,42 @@ __global__ void __launch_bounds__(512) hc_pair_up_kernel(GemvArgs a) {
                     v.z += in ? pv[i].z : 0.f; v.w += in ? pv[i].w : 0.f;
                 }
             }
-            vg[sg] = v;
+            gs[m] = v;
         }
+    }
+    float rs[T];
+    {
+        float ss[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) ss[t] = 0.f;
+        for (int s = lane; s < S; s += 64) {
+#pragma unroll
+            for (int t = 0; t < T; ++t) ss[t] += a.ssq[(size_t)s * T + t];
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t) rs[t] = 1.0f / sqrtf(wave_sum(ss[t]) / (float)a.kd + a.eps);
+    }
+#pragma unroll
+    for (int m = 0; m < NIT; ++m) {
+        const int it = ct + 256 * m;
+        if (it < 4 * NQ) red[it / NQ][it % NQ] = gs[m];
+    }
+    if (blockIdx.x == 0 && ct < T && a.rs_out != nullptr) {
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+            if (t == ct) a.rs_out[t] = rs[t];
+    }
+    __syncthreads();
+    for (int qd = ct; qd < NQ; qd += 256) {
+        const int t = qd / kPairQuads, n = 4 * (qd - t * kPairQuads);
         float r = rs[0];
 #pragma unroll
         for (int tt = 1; tt < T; ++tt) r = tt == t ? rs[tt] : r;
-        const float tx = ((vg[0].x + vg[1].x) + vg[2].x) + vg[3].x;
-        const float ty = ((vg[0].y + vg[1].y) + vg[2].y) + vg[3].y;
-        const float tz = ((vg[0].z + vg[1].z) + vg[2].z) + vg[3].z;
-        const float tw = ((vg[0].w + vg[1].w) + vg[2].w) + vg[3].w;
+        const float4 v0 = red[0][qd], v1 = red[1][qd], v2 = red[2][qd], v3 = red[3][qd];
+        const float tx = ((v0.x + v1.x) + v2.x) + v3.x;
+        const float ty = ((v0.y + v1.y) + v2.y) + v3.y;
+        const float tz = ((v0.z + v1.z) + v2.z) + v3.z;
+        const float tw = ((v0.w + v1.w) + v2.w) + v3.w;
         uint2 lv;
         lv.x = (uint32_t)f2bf_bits(r * tx) | ((uint32_t)f2bf_bits(r * ty) << 16);
         lv.y = (uint32_t)f2bf_bits(r * tz) | ((uint32_t)f2bf_bits(r * tw) << 16);
