@@ -656,10 +656,11 @@ int launch_hc_up(GemvArgs a, hipStream_t st) { GQ8_T_SWITCH(launch_up_t, a, st) 
 // The up read of the down/up pair for K == 320 and small T with the down's combine folded in:
 // waves 4..7 of the work-group add the down's slab partial sums for all T x 320 inputs (the same
 // order as hc_down_combine_kernel, so lo is bitwise the down read's output), apply rs and round
-// to bf16 into LDS, while waves 0..3 have their weight loads in flight; after the combine's two
-// barriers waves 0..3 run the up read's MFMAs as hc_up_direct_kernel does. Every work-group computes the same
-// lo; work-group 0 also writes lo and rs out. Separate waves keep the partial-sum loads (L2)
-// from waiting behind the weight loads (HBM): a wave's loads complete in issue order.
+// to bf16 into LDS, while waves 0..3 have their weight loads in flight; after the combine's
+// barriers waves 0..3 run the up read's MFMAs as hc_up_direct_kernel does. Every work-group
+// computes the same lo; work-group 0 also writes lo and rs out. Separate waves keep the
+// partial-sum loads from waiting behind the weight loads (a wave's loads complete in issue
+// order), and the weight loads start only after the partial-sum loads are issued.
 constexpr int kPairQuads = kUpCW / 4;       // float4 quads of a 320-wide row
 
 template <int T>
@@ -672,8 +673,11 @@ __global__ void __launch_bounds__(512) hc_pair_up_kernel(GemvArgs a) {
     const int N = a.N, K = a.K;                                   // up rows, up depth (== 320)
     const int j = lane & 15, g = lane >> 4;
     if (wave < 4) {
-        // weights and scales of this wave's 16 rows, in flight across the combine
+        // weights and scales of this wave's 16 rows, issued once the combine waves have issued
+        // their partial-sum loads (those are few and on the critical path; issued behind the
+        // weight stream they wait in the same memory queues), then in flight across the combine
         const int r0 = (blockIdx.x * 4 + wave) * 16;
+        __syncthreads();                                          // partial-sum loads issued
         const int row = imin(r0 + j, N - 1);
         uint32_t sc[kUpCB / 2];
         const uint32_t* dp = reinterpret_cast<const uint32_t*>(a.d + (size_t)row * (K >> 5));
@@ -723,6 +727,7 @@ __global__ void __launch_bounds__(512) hc_pair_up_kernel(GemvArgs a) {
     const int per = (S + 3) / 4;
     const size_t plane = (size_t)T * K / 4;                       // float4s per slab plane
     float4 gs[NIT];
+    float sv[T];                                                  // S == 32: ssq of slab lane % 32
     if (S == 32) {                                                // per == 8: one batch of loads
         float4 pv[NIT][8];
 #pragma unroll
@@ -735,6 +740,10 @@ __global__ void __launch_bounds__(512) hc_pair_up_kernel(GemvArgs a) {
             for (int i = 0; i < 8; ++i) pv[m][i] = p[(size_t)i * plane];
         }
 #pragma unroll
+        for (int t = 0; t < T; ++t) sv[t] = a.ssq[(size_t)(lane & 31) * T + t];
+        __builtin_amdgcn_sched_barrier(0);                        // every load issued, then
+        __syncthreads();                                          // the weight loads may start
+#pragma unroll
         for (int m = 0; m < NIT; ++m) {
             float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -744,6 +753,7 @@ __global__ void __launch_bounds__(512) hc_pair_up_kernel(GemvArgs a) {
             gs[m] = v;
         }
     } else {
+        __syncthreads();
 #pragma unroll
         for (int m = 0; m < NIT; ++m) {
             const int it = imin(ct + 256 * m, 4 * NQ - 1);
@@ -770,8 +780,8 @@ __global__ void __launch_bounds__(512) hc_pair_up_kernel(GemvArgs a) {
     {
         float ss[T];
 #pragma unroll
-        for (int t = 0; t < T; ++t) ss[t] = 0.f;
-        for (int s = lane; s < S; s += 64) {
+        for (int t = 0; t < T; ++t) ss[t] = (S == 32 && lane < 32) ? 0.f + sv[t] : 0.f;
+        for (int s = S == 32 ? S : lane; s < S; s += 64) {
 #pragma unroll
             for (int t = 0; t < T; ++t) ss[t] += a.ssq[(size_t)s * T + t];
         }
@@ -810,9 +820,9 @@ __global__ void __launch_bounds__(512) hc_pair_up_kernel(GemvArgs a) {
 }
 
 // The in-kernel combine reads all S x T x 320 partial sums in every up work-group (L2 traffic
-// that grows with T), the separate combine kernel costs one more launch: measured on MI355X at
-// K = 16384 (S = 32), folding wins for T <= 2 and loses from T = 3 on.
-constexpr int kPairMaxT = 2;
+// and registers that grow with T), the separate combine kernel costs one more launch: measured on
+// MI355X at K = 16384 (S = 32), folding wins up to T = 4 (T = 4: 9.9 us vs 10.8 us).
+constexpr int kPairMaxT = 4;
 
 template <int T>
 static int launch_pair_t(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st) {
