@@ -209,9 +209,11 @@ def cpu_baseline(synth, budget_s):
 
 # ------------------------------------------------------------------------------------ other configs
 
-def bench_other_configs(torch, gq8, synth, dev, stream, report):
+def bench_other_configs(torch, gq8, synth, dev, stream, report, only=None, w8a8_ms=None):
     from gemm_q8_amd.device import q8_0_from_f32, to_dev, workspace
     lines = []
+    only = set(only or ("probe", "gemv", "w8a8", "moe"))
+    ms = tuple(w8a8_ms or (1, 4, 8, 16, 32))
 
     def emit(d):
         lines.append(d)
@@ -225,7 +227,7 @@ def bench_other_configs(torch, gq8, synth, dev, stream, report):
         return t / (n_sets * reps) * 1e6
 
     # read-bandwidth probe at the same byte counts
-    for nbytes in (4_456_448, 5_570_560, 6_291_456, 8_388_608, 10_485_760):
+    for nbytes in (4_456_448, 5_570_560, 6_291_456, 8_388_608, 10_485_760) if "probe" in only else ():
         n = n_sets_for(nbytes)
         bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(n)]
         sink = torch.empty(gq8.gq8_read_probe_sink_floats(nbytes), dtype=torch.float32, device=dev)
@@ -234,6 +236,21 @@ def bench_other_configs(torch, gq8, synth, dev, stream, report):
               "GBps": round(nbytes / us / 1e3, 1)})
         del bufs
 
+    if "gemv" in only:
+        bench_gemv_sweep(torch, gq8, synth, dev, timed, emit)
+    if "w8a8" in only:
+        bench_w8a8_sweep(torch, gq8, synth, dev, timed, emit, ms)
+    if "moe" in only:
+        bench_moe(torch, gq8, synth, dev, timed, emit)
+    if report:
+        os.makedirs(os.path.dirname(report) or ".", exist_ok=True)
+        with open(report, "w") as f:
+            for d in lines:
+                f.write(json.dumps(d) + "\n")
+
+
+def bench_gemv_sweep(torch, gq8, synth, dev, timed, emit):
+    from gemm_q8_amd.device import q8_0_from_f32, to_dev, workspace
     # Q8_0 GEMV N=1024 K=4096, T sweep
     d = synth.q8_0_gemv_inputs(T=16)
     w0 = q8_0_from_f32(to_dev(d["w"]))
@@ -250,9 +267,12 @@ def bench_other_configs(torch, gq8, synth, dev, stream, report):
               "weight_GBps": round(w0.numel() / us / 1e3, 1)})
     del ws_
 
-    # W8A8
-    for (M, N, K) in [(16, 1536, 4096)] + [(m, 2560, 4096) for m in (1, 4, 8, 16, 32)] + \
-                     [(m, 4096, 2048) for m in (1, 4, 8, 16, 32)]:
+
+def bench_w8a8_sweep(torch, gq8, synth, dev, timed, emit, ms):
+    from gemm_q8_amd.device import to_dev, workspace
+    # W8A8: the M = 16 product, then the sweep over M
+    for (M, N, K) in [(16, 1536, 4096)] * (16 in ms) + [(m, 2560, 4096) for m in ms] + \
+                     [(m, 4096, 2048) for m in ms]:
         dd = synth.w8a8_inputs(M, N, K)
         wp0 = torch.empty(gq8.gq8_w8a8_packed_bytes(K, N), dtype=torch.int8, device=dev)
         gq8.gq8_w8a8_pack(to_dev(dd["W"]), K, N, wp0)
@@ -267,6 +287,9 @@ def bench_other_configs(torch, gq8, synth, dev, stream, report):
               "weight_GBps": round(N * K / us / 1e3, 1)})
         del wps
 
+
+def bench_moe(torch, gq8, synth, dev, timed, emit):
+    from gemm_q8_amd.device import to_dev
     # routed MoE: 512 experts, T=4, top-8, D=2048, F=512
     T, E, topk, D, F = 4, 512, 8, 2048, 512
     gu_b, dn_b = gq8.gq8_q8_0_bytes(2 * F, D), gq8.gq8_q8_0_bytes(D, F)
@@ -295,12 +318,6 @@ def bench_other_configs(torch, gq8, synth, dev, stream, report):
     emit({"workload": "routed MoE T=4 E=512 top-8 D=2048 F=512", "unique_experts": U,
           "us_per_call": round(us, 3), "weight_GBps": round(U * (gu_b + dn_b) / us / 1e3, 1)})
 
-    if report:
-        os.makedirs(os.path.dirname(report) or ".", exist_ok=True)
-        with open(report, "w") as f:
-            for d in lines:
-                f.write(json.dumps(d) + "\n")
-
 
 def to_host_ids(ids):
     return ids.cpu().numpy().ravel().tolist()
@@ -316,6 +333,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all-configs", action="store_true")
+    ap.add_argument("--only", default="probe,gemv,w8a8,moe",
+                    help="with --all-configs: comma-separated subset of probe,gemv,w8a8,moe")
+    ap.add_argument("--w8a8-ms", default="1,4,8,16,32", help="with --all-configs: W8A8 M values")
     ap.add_argument("--report", default="gpurun_out/bench_all.jsonl")
     ap.add_argument("--reps", type=int, default=20,
                     help="replays of each per-call timing graph (per-T pair, down, up)")
@@ -427,7 +447,8 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(synth, args.cpu_seconds)
     if args.all_configs:
-        bench_other_configs(torch, gq8, synth, dev, stream, args.report)
+        bench_other_configs(torch, gq8, synth, dev, stream, args.report, only=args.only.split(","),
+                            w8a8_ms=[int(m) for m in args.w8a8_ms.split(",")])
     print(json.dumps(result), flush=True)
 
 
