@@ -317,6 +317,20 @@ def bench_moe(torch, gq8, synth, dev, timed, emit):
         xq, xd, ids, wts, a, b, out, T, topk, E, D, F, wsp, nb, s)), n, reps=50)
     emit({"workload": "routed MoE T=4 E=512 top-8 D=2048 F=512", "unique_experts": U,
           "us_per_call": round(us, 3), "weight_GBps": round(U * (gu_b + dn_b) / us / 1e3, 1)})
+    # the same on the bf16 input: q8_1 quantization fused into the gate/up kernel, against the
+    # quantize call followed by the routed call
+    xb = to_dev(inp["x"])
+    us = timed(lambda i: (lambda s, a=agus[i % n], b=adns[i % n]: gq8.gq8_moe_q8_0_routed_bf16(
+        xb, ids, wts, a, b, out, T, topk, E, D, F, wsp, nb, s)), n, reps=50)
+    emit({"workload": "routed MoE on the bf16 input (q8_1 fused) T=4 E=512 top-8 D=2048 F=512",
+          "unique_experts": U, "us_per_call": round(us, 3), "weight_GBps": round(U * (gu_b + dn_b) / us / 1e3, 1)})
+
+    def two_calls(s, a, b):
+        gq8.gq8_q8_1_quantize(xb, T, D, xq, xd, None, s)
+        gq8.gq8_moe_q8_0_routed(xq, xd, ids, wts, a, b, out, T, topk, E, D, F, wsp, nb, s)
+    us = timed(lambda i: (lambda s, a=agus[i % n], b=adns[i % n]: two_calls(s, a, b)), n, reps=50)
+    emit({"workload": "q8_1 quantize + routed MoE T=4 E=512 top-8 D=2048 F=512",
+          "unique_experts": U, "us_per_call": round(us, 3), "weight_GBps": round(U * (gu_b + dn_b) / us / 1e3, 1)})
 
 
 def to_host_ids(ids):

@@ -32,6 +32,38 @@ GQ8_DEV uint16_t f2bf_bits(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// round to nearest integer, ties away from zero; trunc(v) and v - trunc(v) are exact in fp32
+GQ8_DEV int round_half_away(float v) {
+    const float t = truncf(v);
+    const float r = fabsf(v - t) >= 0.5f ? t + copysignf(1.0f, v) : t;
+    return (int)r;
+}
+
+// Q8_0 / q8_1 block scale: fp16 bits of amax / 127 (round to nearest even)
+GQ8_DEV uint16_t q8_scale_bits(float amax) { return f2h_bits(amax / 127.0f); }
+
+// one quant of a block with (fp16-exact) scale d: round(v / d), clamped to +-127; 0 when d = 0
+GQ8_DEV int q8_quant(float v, float d) {
+    if (d == 0.f) return 0;
+    const int qi = round_half_away(v / d);
+    return qi > 127 ? 127 : (qi < -127 ? -127 : qi);
+}
+
+// q8_quant for a bf16 value v (8-bit significand) and a block scale d = fp16 (11-bit significand)
+// without the division: v / d = (a / m) 2^e with a < 2^8 and m < 2^11 integers, so unless v / d
+// is a half-integer it lies at least 2^-12 from every half-integer, while t = |v| * rcp(d) is
+// within 2^-15 of it (|v / d| <= 128, v_rcp_f32 within 1 ulp): rounding t half up gives the same
+// integer, and an exact tie (|v| = (q + 0.5) d, a product exact in fp32) goes away from zero.
+// The result is q8_quant(v, d) bit for bit; d must be finite (callers take q8_quant otherwise).
+GQ8_DEV int q8_quant_bf16(float v, float d, float rd) {
+    if (d == 0.f) return 0;
+    const float av = fabsf(v);
+    int q = (int)(av * rd + 0.5f);
+    if (((float)q + 0.5f) * d == av) q += 1;
+    q = q > 127 ? 127 : q;
+    return v < 0.f ? -q : q;
+}
+
 // signed byte i (0..3) of a dword, as float
 template <int I>
 GQ8_DEV float sbyte_f(uint32_t w) { return (float)(int)(int8_t)(uint8_t)(w >> (8 * I)); }

@@ -189,6 +189,7 @@ int launch_moe_plan(const int32_t* ids, int T, int topk, int E, int32_t* plan, h
 struct MoeArgs {
     const int8_t* xq;       // [T][D]
     const uint16_t* xd;     // [T][D/32]
+    const uint16_t* xb;     // bf16 [T][D] (the gate/up kernel that quantizes its input itself)
     const float* w;         // routing weights [T][topk]
     const int8_t* wgu;      // gate/up arena
     const int8_t* wdn;      // down arena
@@ -345,8 +346,15 @@ __global__ void __launch_bounds__(256) moe_gate_up_kernel(MoeArgs a) {
 // read once. The weight loads of the whole row pairs are issued at once, then the entries are
 // taken one at a time in ascending order (x loads per entry, L2-resident), so the registers do
 // not grow with the entry count and more work-groups stay resident per CU.
-template <int NCH>
+//
+// XB: the input is bf16 x itself; the work-group quantizes each entry's row to q8_1 once, into
+// LDS (8 values a thread; a block's four threads share its amax through two cross-lane maxes),
+// with the q8_1 quantize kernel's rounding (q8_quant_bf16 is q8_quant bit for bit on bf16
+// values), so the quants and scales are bitwise those that kernel writes.
+template <int NCH, bool XB>
 __global__ void __launch_bounds__(256) moe_gate_up_rows_kernel(MoeArgs a) {
+    __shared__ __attribute__((aligned(16))) int8_t xq_s[XB ? 1024 * NCH : 16];   // q8_1 of the row
+    __shared__ uint16_t xd_s[XB ? 32 * NCH : 1];
     const int i0 = blockIdx.y;
     const EntrySet es = entry_set(a.ids, a.P, a.E, i0);
     if (!es.ok || entry_first(es) != i0) return;
@@ -372,6 +380,8 @@ __global__ void __launch_bounds__(256) moe_gate_up_rows_kernel(MoeArgs a) {
             du[r][j] = d[(size_t)(F + n) * nblk + (kc >> 5)];
         }
     }
+    int first_w = 0;                                    // the word holding the first entry
+    while (first_w < 3 && es.m[first_w] == 0) ++first_w;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
         for (uint64_t mm = es.m[w]; mm != 0; mm &= mm - 1) {
@@ -379,12 +389,56 @@ __global__ void __launch_bounds__(256) moe_gate_up_rows_kernel(MoeArgs a) {
             const int tok = ent / a.topk;
             v4i xv[NCH];
             uint16_t dx[NCH];
+            if constexpr (XB) {
+                // the work-group quantizes the token's row once: thread i takes 8 values (4
+                // threads a block, amax over them by two cross-lane maxes) into LDS
+                if (mm != es.m[w] || w != first_w) __syncthreads();   // the previous entry's reads
+                for (int k8 = 8 * (int)threadIdx.x; k8 < D; k8 += 8 * 256) {
+                    const u32x4 xr = *reinterpret_cast<const u32x4*>(a.xb + (size_t)tok * D + k8);
+                    const uint32_t w4[4] = {xr.x, xr.y, xr.z, xr.w};
+                    float v[8];
+                    float am = 0.f;
 #pragma unroll
-            for (int j = 0; j < NCH; ++j) {
-                const int k = j * 1024 + lane * 16;
-                const int kc = k < D ? k : D - 16;
-                xv[j] = *reinterpret_cast<const v4i*>(a.xq + (size_t)tok * D + kc);
-                dx[j] = a.xd[(size_t)tok * nblk + (kc >> 5)];
+                    for (int e = 0; e < 4; ++e) {
+                        v[2 * e] = __uint_as_float(w4[e] << 16);
+                        v[2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
+                        am = fmaxf(am, fabsf(v[2 * e]));
+                        am = fmaxf(am, fabsf(v[2 * e + 1]));
+                    }
+                    am = fmaxf(am, __shfl_xor(am, 1, 64));
+                    am = fmaxf(am, __shfl_xor(am, 2, 64));
+                    const uint16_t db = q8_scale_bits(am);
+                    const float dd = h2f(db);
+                    uint32_t q2[2] = {0u, 0u};
+                    if (dd < __builtin_inff()) {
+                        const float rd = __builtin_amdgcn_rcpf(dd);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            q2[e >> 2] |= ((uint32_t)q8_quant_bf16(v[e], dd, rd) & 0xffu) << (8 * (e & 3));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            q2[e >> 2] |= ((uint32_t)q8_quant(v[e], dd) & 0xffu) << (8 * (e & 3));
+                    }
+                    *reinterpret_cast<uint2*>(&xq_s[k8]) = make_uint2(q2[0], q2[1]);
+                    if ((k8 & 31) == 0) xd_s[k8 >> 5] = db;
+                }
+                __syncthreads();
+#pragma unroll
+                for (int j = 0; j < NCH; ++j) {
+                    const int k = j * 1024 + lane * 16;
+                    const int kc = k < D ? k : D - 16;
+                    xv[j] = *reinterpret_cast<const v4i*>(&xq_s[kc]);
+                    dx[j] = xd_s[kc >> 5];
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < NCH; ++j) {
+                    const int k = j * 1024 + lane * 16;
+                    const int kc = k < D ? k : D - 16;
+                    xv[j] = *reinterpret_cast<const v4i*>(a.xq + (size_t)tok * D + kc);
+                    dx[j] = a.xd[(size_t)tok * nblk + (kc >> 5)];
+                }
             }
             float ag[kGuRpw], au[kGuRpw];
 #pragma unroll
@@ -652,17 +706,19 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(MoeArgs a) {
     a.out[i] = f2bf_bits(v);
 }
 
+// plan | h [P][F] | rows [P][D] | q8_1 of a bf16 input: quants [T][D], scales [T][D/32]
 size_t moe_workspace_bytes(int T, int topk, int D, int F) {
     const size_t P = (size_t)T * topk;
     return round_up((1 + 4 * P) * sizeof(int32_t), kCounterAlign) +
-           round_up(P * F * sizeof(float), kCounterAlign) + round_up(P * D * sizeof(float), kCounterAlign);
+           round_up(P * F * sizeof(float), kCounterAlign) + round_up(P * D * sizeof(float), kCounterAlign) +
+           round_up((size_t)T * D, kCounterAlign) + round_up((size_t)T * (D / 32) * sizeof(uint16_t), kCounterAlign);
 }
 
-int launch_moe_routed(const int8_t* xq, const uint16_t* xd, const int32_t* ids, const float* w,
-                      const void* wgu, const void* wdn, uint16_t* out, int T, int topk, int E,
-                      int D, int F, void* ws, hipStream_t st) {
+int launch_moe_routed(const int8_t* xq, const uint16_t* xd, const uint16_t* xb, const int32_t* ids,
+                      const float* w, const void* wgu, const void* wdn, uint16_t* out, int T,
+                      int topk, int E, int D, int F, void* ws, hipStream_t st) {
     MoeArgs a{};
-    a.xq = xq; a.xd = xd; a.w = w;
+    a.xq = xq; a.xd = xd; a.xb = xb; a.w = w;
     a.wgu = static_cast<const int8_t*>(wgu);
     a.wdn = static_cast<const int8_t*>(wdn);
     a.gu_bytes = (size_t)2 * F * D + (size_t)2 * F * (D / 32) * 2;
@@ -676,21 +732,32 @@ int launch_moe_routed(const int8_t* xq, const uint16_t* xd, const int32_t* ids, 
     a.h = reinterpret_cast<float*>(p);
     p += round_up(P * F * sizeof(float), kCounterAlign);
     a.rows = reinterpret_cast<float*>(p);
-
+    p += round_up(P * D * sizeof(float), kCounterAlign);
     a.ids = ids;
+    int rc = GQ8_OK;
+    const bool rows_gu = D <= 4096;
+    if (xb != nullptr && !rows_gu) {       // bf16 input, general gate/up kernel: quantize first
+        int8_t* wq = reinterpret_cast<int8_t*>(p);
+        uint16_t* wd = reinterpret_cast<uint16_t*>(p + round_up((size_t)T * D, kCounterAlign));
+        if ((rc = launch_q8_1_quantize(xb, T, D, wq, wd, nullptr, st)) != GQ8_OK) return rc;
+        a.xq = wq; a.xd = wd; a.xb = nullptr;
+    }
     // the plan is needed only by the fallback kernels (D > 4096 gate/up; F outside
     // {256, 512, 1024} down)
-    const bool rows_gu = D <= 4096;
     const bool token_dn = F == 256 || F == 512 || F == 1024;
-    int rc = GQ8_OK;
     if (!rows_gu || !token_dn) {
         hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(256), 0, st, ids, a.P, E, plan);
         if ((rc = launch_status()) != GQ8_OK) return rc;
     }
     const dim3 ggu((F + 4 * kGuRpw - 1) / (4 * kGuRpw), a.P);
-    if (D <= 1024) hipLaunchKernelGGL((moe_gate_up_rows_kernel<1>), ggu, dim3(256), 0, st, a);
-    else if (D <= 2048) hipLaunchKernelGGL((moe_gate_up_rows_kernel<2>), ggu, dim3(256), 0, st, a);
-    else if (D <= 4096) hipLaunchKernelGGL((moe_gate_up_rows_kernel<4>), ggu, dim3(256), 0, st, a);
+    if (a.xb != nullptr) {
+        if (D <= 1024) hipLaunchKernelGGL((moe_gate_up_rows_kernel<1, true>), ggu, dim3(256), 0, st, a);
+        else if (D <= 2048) hipLaunchKernelGGL((moe_gate_up_rows_kernel<2, true>), ggu, dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((moe_gate_up_rows_kernel<4, true>), ggu, dim3(256), 0, st, a);
+    }
+    else if (D <= 1024) hipLaunchKernelGGL((moe_gate_up_rows_kernel<1, false>), ggu, dim3(256), 0, st, a);
+    else if (D <= 2048) hipLaunchKernelGGL((moe_gate_up_rows_kernel<2, false>), ggu, dim3(256), 0, st, a);
+    else if (D <= 4096) hipLaunchKernelGGL((moe_gate_up_rows_kernel<4, false>), ggu, dim3(256), 0, st, a);
     else if (T <= 4) hipLaunchKernelGGL((moe_gate_up_kernel<4>), ggu, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((moe_gate_up_kernel<16>), ggu, dim3(256), 0, st, a);
     if ((rc = launch_status()) != GQ8_OK) return rc;

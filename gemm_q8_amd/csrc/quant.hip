@@ -7,29 +7,15 @@
 
 namespace gq8 {
 
-// round to nearest integer, ties away from zero; trunc(v) and v - trunc(v) are exact in fp32
-GQ8_DEV int round_half_away(float v) {
-    const float t = truncf(v);
-    const float r = fabsf(v - t) >= 0.5f ? t + copysignf(1.0f, v) : t;
-    return (int)r;
-}
-
 // One Q8_0 block: scale bits and 32 quants from 32 fp32 values.
 GQ8_DEV uint16_t quantize_block(const float* v, int8_t* q) {
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    const uint16_t dbits = f2h_bits(amax / 127.0f);
+    const uint16_t dbits = q8_scale_bits(amax);
     const float d = h2f(dbits);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        int qi = 0;
-        if (d != 0.f) {
-            qi = round_half_away(v[i] / d);
-            qi = qi > 127 ? 127 : (qi < -127 ? -127 : qi);
-        }
-        q[i] = (int8_t)qi;
-    }
+    for (int i = 0; i < 32; ++i) q[i] = (int8_t)q8_quant(v[i], d);
     return dbits;
 }
 

@@ -53,6 +53,7 @@ _SIGS = {
     "gq8_moe_plan": (_I, [_P, _I, _I, _I, _P, _P]),
     "gq8_moe_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "gq8_moe_q8_0_routed": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P]),
+    "gq8_moe_q8_0_routed_bf16": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P]),
     "gq8_read_probe_sink_floats": (_SZ, [_SZ]),
     "gq8_read_probe": (_I, [_P, _SZ, _P, _P]),
 }
@@ -199,6 +200,13 @@ def gq8_moe_q8_0_routed(xq, xd, ids, weights, w_gate_up, w_down, out, T, topk, E
                         stream=None):
     return _check("gq8_moe_q8_0_routed", _lib.gq8_moe_q8_0_routed(
         _ptr(xq), _ptr(xd), _ptr(ids), _ptr(weights), _ptr(w_gate_up), _ptr(w_down), _ptr(out),
+        T, topk, E, D, F, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def gq8_moe_q8_0_routed_bf16(x, ids, weights, w_gate_up, w_down, out, T, topk, E, D, F, ws, ws_bytes,
+                             stream=None):
+    return _check("gq8_moe_q8_0_routed_bf16", _lib.gq8_moe_q8_0_routed_bf16(
+        _ptr(x), _ptr(ids), _ptr(weights), _ptr(w_gate_up), _ptr(w_down), _ptr(out),
         T, topk, E, D, F, _ptr(ws), ws_bytes, _stream(stream)))
 
 

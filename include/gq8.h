@@ -215,6 +215,17 @@ int gq8_moe_q8_0_routed(const int8_t* xq, const uint16_t* xd, const int32_t* ids
                         uint16_t* out, int T, int topk, int E, int D, int F,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* The routed call on the bf16 MoE input itself (EP page, "What changed": the experts take the
+ * q8_1 form of the input; here that quantization runs on the device, inside the gate/up kernel
+ * when D <= 4096, else as a quantize step into the workspace). x bf16 [T][D] is quantized per
+ * 32-block exactly as gq8_q8_1_quantize does, so out is bitwise the out of gq8_q8_1_quantize
+ * followed by gq8_moe_q8_0_routed. x must be 16-byte aligned; shapes, weights, workspace
+ * (gq8_moe_workspace_bytes) and errors as gq8_moe_q8_0_routed. */
+int gq8_moe_q8_0_routed_bf16(const uint16_t* x, const int32_t* ids, const float* weights,
+                             const void* w_gate_up, const void* w_down, uint16_t* out, int T,
+                             int topk, int E, int D, int F, void* ws, size_t ws_bytes,
+                             void* stream);
+
 /* ------------------------------------------------------------------------------------------
  * Diagnostics
  * ------------------------------------------------------------------------------------------ */

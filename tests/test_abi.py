@@ -110,3 +110,27 @@ def test_argument_checks_return_before_device_work(lib):
     # MoE limits
     assert raw.gq8_moe_q8_0_routed(dummy, dummy, dummy, dummy, dummy, dummy, dummy,
                                    4, 8, 512, 2048, 2048, None, 0, None) == lib.ESHAPE
+
+
+def test_moe_bf16_input_argument_checks(lib):
+    raw = lib.raw()
+    dummy = 1 << 20  # never dereferenced
+    # F above 1024, D not a multiple of 32, T*topk above 256
+    assert raw.gq8_moe_q8_0_routed_bf16(dummy, dummy, dummy, dummy, dummy, dummy,
+                                        4, 8, 512, 2048, 2048, None, 0, None) == lib.ESHAPE
+    assert raw.gq8_moe_q8_0_routed_bf16(dummy, dummy, dummy, dummy, dummy, dummy,
+                                        4, 8, 512, 2056, 512, None, 0, None) == lib.ESHAPE
+    assert raw.gq8_moe_q8_0_routed_bf16(dummy, dummy, dummy, dummy, dummy, dummy,
+                                        16, 17, 512, 2048, 512, None, 0, None) == lib.ESHAPE
+    # a null input, a misaligned input, a missing workspace
+    assert raw.gq8_moe_q8_0_routed_bf16(None, dummy, dummy, dummy, dummy, dummy,
+                                        4, 8, 512, 2048, 512, None, 0, None) == lib.EINVAL
+    assert raw.gq8_moe_q8_0_routed_bf16(dummy + 2, dummy, dummy, dummy, dummy, dummy,
+                                        4, 8, 512, 2048, 512, None, 0, None) == lib.EALIGN
+    assert raw.gq8_moe_q8_0_routed_bf16(dummy, dummy, dummy, dummy, dummy, dummy,
+                                        4, 8, 512, 2048, 512, None, 0, None) == lib.EWORKSPACE
+    # T = 0 is a no-op
+    assert raw.gq8_moe_q8_0_routed_bf16(None, None, None, None, None, None,
+                                        0, 8, 512, 2048, 512, None, 0, None) == lib.OK
+    # the workspace also holds the q8_1 form of a bf16 input (used when D > 4096)
+    assert lib.gq8_moe_workspace_bytes(2, 4, 8192, 256) >= 2 * 8192 + 2 * 256 * 2

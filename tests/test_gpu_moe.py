@@ -147,3 +147,62 @@ def test_moe_crowded_expert(gpu, D, F):
     blocks = lambda e: (quantize_q8_0(experts(e)["gate_up"]), quantize_q8_0(experts(e)["down"]))  # noqa: E731
     y_ref, S = moe_forward(x81, ids_ref, p_ref, blocks)
     check_bf16(to_host(out, np.uint16), y_ref, S, f"moe crowded D={D} F={F}")
+
+
+@pytest.mark.parametrize("T,E,topk,D,F", [(4, 512, 8, 2048, 512),      # the full workload
+                                          (3, 20, 4, 128, 64),         # VALU down + plan
+                                          (6, 40, 6, 1056, 96),        # ragged last chunk
+                                          (5, 12, 3, 544, 1024),
+                                          (2, 6, 2, 4160, 256)])       # D > 4096: quantize step
+def test_moe_bf16_input_is_quantize_then_routed(gpu, T, E, topk, D, F):
+    """The routed call on the bf16 input quantizes it to q8_1 on the device: bitwise the output of
+    gq8_q8_1_quantize followed by gq8_moe_q8_0_routed (itself checked against the oracle)."""
+    seed = 44
+    out, (xq, xd, ids, w, agu, adn, ws, nb) = _moe_case(gpu, T, E, topk, D, F, seed=seed)
+    x = to_dev(synth.moe_inputs(T=T, E=E, D=D, seed=seed)["x"])
+    out2 = torch.empty_like(out)
+    ws.fill_(0xFF)
+    gpu.gq8_moe_q8_0_routed_bf16(x, ids, w, agu, adn, out2, T, topk, E, D, F, ws, nb)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), f"T={T} D={D} F={F}"
+
+
+def _tie_input(T, D):
+    """bf16 input whose 32-blocks hold 127 s (so the block scale is exactly s, a power of two)
+    and half-integer multiples (j + 0.5) s, j = -127..126: every other quant is an exact tie of
+    round(x / d), which goes away from zero."""
+    x = np.empty((T, D), np.float32)
+    j = np.arange(T * D) % 254 - 127
+    x.ravel()[:] = j + 0.5
+    x = x.reshape(T, D // 32, 32)
+    x[:, :, 0] = 127.0
+    s = 2.0 ** (np.arange(D // 32) % 7 - 3)
+    x = (x * s[None, :, None]).astype(np.float32).reshape(T, D)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)    # exact: 8-bit significands
+
+
+@pytest.mark.parametrize("D,F", [(2048, 512), (1056, 96)])
+def test_moe_bf16_input_ties(gpu, D, F):
+    """Exact ties in the q8_1 quantization of the input: the fused quantization agrees bitwise
+    with gq8_q8_1_quantize (whose bytes match the oracle's quantizer) through the routed output."""
+    from oracle.q8 import quantize_q8_1_bf16 as q81
+    T, E, topk, seed = 3, 6, 2, 45
+    xb = _tie_input(T, D)
+    ids = np.array([[0, 3], [5, 0], [2, 4]], np.int32)
+    p = synth.uniform_f32(seed, "moe.ties.w", (T, topk), 0.1, 0.9)
+    experts = lambda e: synth.moe_expert_weights(e, D=D, F=F, seed=seed)  # noqa: E731
+    agu, adn = _arena(gpu, experts, E, D, F, range(E), seed)
+    xq = torch.empty((T, D), dtype=torch.int8, device="cuda")
+    xd = torch.empty((T, D // 32), dtype=torch.int16, device="cuda")
+    gpu.gq8_q8_1_quantize(to_dev(xb), T, D, xq, xd, None)
+    ref = q81(xb)
+    assert np.array_equal(to_host(xq).reshape(ref.q.shape), ref.q)   # the standalone quantizer at ties
+    nb = gpu.gq8_moe_workspace_bytes(T, topk, D, F)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    out1 = torch.empty((T, D), dtype=torch.int16, device="cuda")
+    out2 = torch.empty_like(out1)
+    dids, dp = to_dev(ids), to_dev(p)
+    gpu.gq8_moe_q8_0_routed(xq, xd, dids, dp, agu, adn, out1, T, topk, E, D, F, ws, nb)
+    gpu.gq8_moe_q8_0_routed_bf16(to_dev(xb), dids, dp, agu, adn, out2, T, topk, E, D, F, ws, nb)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
