@@ -92,3 +92,68 @@ def test_up_is_gemv_of_bf16_input():
         o, _ = hc_up(e, b)
         assert np.array_equal(o[0], fp16_to_f32(b.d[:, k // 32]).astype(np.float64) * b.q[:, k // 32, k % 32])
     assert out.shape == (3, 40) and np.all(S >= np.abs(out))
+
+
+# ---- the same reads on BF16 weights
+
+def _pow2_blocks(N, K, seed):
+    """Q8_0 blocks whose scales are powers of two: every weight d q is then a bf16 value."""
+    b = quantize_q8_0(synth.normal_f32(seed, "pin.hc.p2", (N, K), 0.0, 0.02))
+    d = fp16_to_f32(b.d)
+    d2 = (2.0 ** np.round(np.log2(np.where(d > 0, d, 1.0)))).astype(np.float32)
+    return b._replace(d=(d2.astype(np.float16)).view(np.uint16))
+
+
+def _as_bf16_weights(blocks):
+    w = (fp16_to_f32(blocks.d)[:, :, None] * blocks.q.astype(np.float32)).reshape(blocks.q.shape[0], -1)
+    bits = bf16_bits(w)
+    assert np.array_equal(bf16_to_f32(bits), w)                  # exact: d = 2^e, |q| <= 127
+    return bits
+
+
+def test_bf16_reads_equal_the_q8_reads_on_the_same_weights():
+    """Two different weight decoders (Q8_0 blocks, bf16 bit patterns) describing the same real
+    weights give the same down and up reads."""
+    from oracle.hc import hc_down_bf16, hc_up_bf16
+    b = _pow2_blocks(5, 96, seed=7)
+    W = _as_bf16_weights(b)
+    R = synth.bf16_normal(7, "pin.hc.R7", (3, 96))
+    wn = synth.bf16_normal(7, "pin.hc.wn7", (96,), 1.0, 0.1)
+    lo_q, rs_q, S_q = hc_down(R, wn, b, EPS)
+    lo_b, rs_b, S_b = hc_down_bf16(R, wn, W, EPS)
+    assert np.array_equal(rs_q, rs_b)
+    assert np.allclose(lo_b, lo_q, rtol=1e-13, atol=1e-300) and np.allclose(S_b, S_q, rtol=1e-13)
+    bu = _pow2_blocks(40, 64, seed=8)
+    lo = synth.bf16_normal(8, "pin.hc.lo8", (2, 64))
+    out_q, Sq = hc_up(lo, bu)
+    out_b, Sb = hc_up_bf16(lo, _as_bf16_weights(bu))
+    assert np.allclose(out_b, out_q, rtol=1e-13, atol=1e-300) and np.allclose(Sb, Sq, rtol=1e-13)
+
+
+def test_bf16_down_brute_force_rational():
+    from oracle.hc import hc_down_bf16
+    N, K = 3, 64
+    W = synth.bf16_normal(9, "pin.hc.Wb", (N, K), 0.0, 0.02)
+    R = synth.bf16_normal(9, "pin.hc.Rbb", (2, K))
+    wn = synth.bf16_normal(9, "pin.hc.wnbb", (K,), 1.0, 0.1)
+    lo, rs, S = hc_down_bf16(R, wn, W, EPS)
+    Rf, wf, Wf = bf16_to_f32(R), bf16_to_f32(wn), bf16_to_f32(W)
+    for t in range(2):
+        ss = sum(Fraction(float(r)) ** 2 for r in Rf[t])
+        r_t = 1.0 / math.sqrt(float(ss / K) + EPS)
+        assert abs(rs[t] - r_t) <= 1e-15 * r_t
+        for n in range(N):
+            acc = sum(Fraction(float(Wf[n, k])) * Fraction(float(Rf[t, k])) * Fraction(float(wf[k]))
+                      for k in range(K))
+            assert abs(r_t * float(acc) - lo[t, n]) <= 1e-12 * S[t, n]
+
+
+def test_bf16_up_one_hot_picks_a_weight_column():
+    from oracle.hc import hc_up_bf16
+    W = synth.bf16_normal(10, "pin.hc.Wu", (24, 64), 0.0, 0.02)
+    for k in (0, 31, 63):
+        e = np.zeros((1, 64), np.uint16)
+        e[0, k] = bf16_bits(np.float32(1.0))
+        o, S = hc_up_bf16(e, W)
+        assert np.array_equal(o[0], bf16_to_f32(W[:, k]).astype(np.float64))
+        assert np.array_equal(S[0], np.abs(o[0]))
