@@ -212,7 +212,7 @@ def cpu_baseline(synth, budget_s):
 def bench_other_configs(torch, gq8, synth, dev, stream, report, only=None, w8a8_ms=None):
     from gemm_q8_amd.device import q8_0_from_f32, to_dev, workspace
     lines = []
-    only = set(only or ("probe", "gemv", "w8a8", "moe"))
+    only = set(only or ("probe", "hcbf16", "gemv", "w8a8", "moe"))
     ms = tuple(w8a8_ms or (1, 4, 8, 16, 32))
 
     def emit(d):
@@ -236,6 +236,8 @@ def bench_other_configs(torch, gq8, synth, dev, stream, report, only=None, w8a8_
               "GBps": round(nbytes / us / 1e3, 1)})
         del bufs
 
+    if "hcbf16" in only:
+        bench_hc_bf16(torch, gq8, synth, dev, timed, emit)
     if "gemv" in only:
         bench_gemv_sweep(torch, gq8, synth, dev, timed, emit)
     if "w8a8" in only:
@@ -247,6 +249,39 @@ def bench_other_configs(torch, gq8, synth, dev, stream, report, only=None, w8a8_
         with open(report, "w") as f:
             for d in lines:
                 f.write(json.dumps(d) + "\n")
+
+
+def bench_hc_bf16(torch, gq8, synth, dev, timed, emit):
+    """The BF16 comparison read: the HC pair on BF16 weights against the Q8_0 pair, same harness
+    (per-call graphs over rotated weight copies), T in {1, 4, 6}."""
+    from gemm_q8_amd.device import q8_0_from_f32, to_dev, workspace
+    wb = synth.hc_weights_bf16()
+    bd0, bu0 = to_dev(wb["w_down"]), to_dev(wb["w_up"])
+    base = synth.hc_inputs(1)
+    qd0, qu0 = q8_0_from_f32(to_dev(base["w_down"])), q8_0_from_f32(to_dev(base["w_up"]))
+    bf_bytes = (bd0.numel() + bu0.numel()) * 2
+    q8_bytes = qd0.numel() + qu0.numel()
+    nb_, nq = n_sets_for(bf_bytes), n_sets_for(q8_bytes)
+    bds = [bd0] + [bd0.clone() for _ in range(nb_ - 1)]
+    bus = [bu0] + [bu0.clone() for _ in range(nb_ - 1)]
+    qds = [qd0] + [qd0.clone() for _ in range(nq - 1)]
+    qus = [qu0] + [qu0.clone() for _ in range(nq - 1)]
+    for T in TS:
+        d = synth.hc_inputs(T)
+        R, wn = to_dev(d["R"]), to_dev(d["w_norm"])
+        lo = torch.empty((T, N_LR), dtype=torch.int16, device=dev)
+        rs = torch.empty((T,), dtype=torch.float32, device=dev)
+        out = torch.empty((T, K_HC), dtype=torch.int16, device=dev)
+        nbw = gq8.gq8_workspace_bytes(gq8.OP_HC_PAIR, T, N_LR, K_HC)
+        wsp = workspace(nbw)
+        us_b = timed(lambda i: (lambda s, a=bds[i % nb_], b=bus[i % nb_]: gq8.gq8_hc_bf16_pair(
+            a, R, wn, 1e-6, b, lo, rs, out, T, N_LR, K_HC, wsp, nbw, s)), nb_)
+        us_q = timed(lambda i: (lambda s, a=qds[i % nq], b=qus[i % nq]: gq8.gq8_hc_q8_pair(
+            a, R, wn, 1e-6, b, lo, rs, out, T, N_LR, K_HC, wsp, nbw, s)), nq)
+        emit({"workload": "HC pair on BF16 weights (comparison read) 320x16384 + 16384x320", "T": T,
+              "us_per_call": round(us_b, 3), "weight_GBps": round(bf_bytes / us_b / 1e3, 1),
+              "q8_0_pair_us": round(us_q, 3), "bf16_over_q8_0": round(us_b / us_q, 3)})
+    del bds, bus, qds, qus
 
 
 def bench_gemv_sweep(torch, gq8, synth, dev, timed, emit):
@@ -347,8 +382,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all-configs", action="store_true")
-    ap.add_argument("--only", default="probe,gemv,w8a8,moe",
-                    help="with --all-configs: comma-separated subset of probe,gemv,w8a8,moe")
+    ap.add_argument("--only", default="probe,hcbf16,gemv,w8a8,moe",
+                    help="with --all-configs: comma-separated subset of probe,hcbf16,gemv,w8a8,moe")
     ap.add_argument("--w8a8-ms", default="1,4,8,16,32", help="with --all-configs: W8A8 M values")
     ap.add_argument("--report", default="gpurun_out/bench_all.jsonl")
     ap.add_argument("--reps", type=int, default=20,

@@ -223,6 +223,34 @@ GQ8_EXPORT int gq8_hc_q8_pair(const void* w_down, const uint16_t* R, const uint1
     return launch_hc_pair(dn, up, ws, S(stream));
 }
 
+GQ8_EXPORT int gq8_hc_bf16_pair(const uint16_t* w_down, const uint16_t* R, const uint16_t* w_norm,
+                                float eps, const uint16_t* w_up, uint16_t* lo, float* rs_out,
+                                uint16_t* out, int T, int Nlr, int Khc, void* ws, size_t ws_bytes,
+                                void* stream) {
+    if (T < 0 || Nlr < 0 || Khc < 0) return GQ8_EINVAL;
+    if (!q8_shape_ok(T, Nlr, Khc) || Nlr % 32 != 0 || Nlr > 1024 || Khc == 0 || Nlr == 0)
+        return GQ8_ESHAPE;
+    if (T == 0) return GQ8_OK;
+    if (w_down == nullptr || R == nullptr || w_norm == nullptr || w_up == nullptr ||
+        lo == nullptr || out == nullptr)
+        return GQ8_EINVAL;
+    if (!aligned16(w_down) || !aligned16(R) || !aligned16(w_norm) || !aligned16(w_up) ||
+        !aligned16(lo))
+        return GQ8_EALIGN;
+    if (!(eps >= 0.f)) return GQ8_EINVAL;
+    int rc = check_ws(ws, ws_bytes, hc_down_workspace_bytes(T, Nlr, Khc));
+    if (rc != GQ8_OK) return rc;
+    if (device_cus() == 0) return GQ8_ENODEV;
+    GemvArgs dn{};
+    dn.q = reinterpret_cast<const int8_t*>(w_down);
+    dn.x = R; dn.wnorm = w_norm; dn.T = T; dn.N = Nlr; dn.K = Khc; dn.out = lo;
+    dn.rs_out = rs_out; dn.eps = eps;
+    GemvArgs up{};
+    up.q = reinterpret_cast<const int8_t*>(w_up);
+    up.x = lo; up.T = T; up.N = Khc; up.K = Nlr; up.out = out;
+    return launch_hc_bf16_pair(dn, up, ws, S(stream));
+}
+
 // ---------------------------------------------------------------------------------- W8A8
 
 GQ8_EXPORT size_t gq8_w8a8_packed_bytes(int K, int N) {

@@ -179,15 +179,22 @@ constexpr int kDnRows = 64;                // rows per work-group: four waves of
 // XF (the Q8_0 GEMV at larger T): the A operand is x itself (fp32 [T][K]) instead of R * w_norm;
 // hi = bf16(x) and lo = bf16(x - hi), both rounded to nearest, leave |x - hi - lo| <= 2^-17 |x|,
 // far inside the read's tolerance; no sums of squares.
-template <int T, bool XF = false>
+//
+// WB (the BF16 comparison read): the weights are bf16 [N][K], no block scales. A wave's tile is
+// 16 x 1024 bytes, read in four quarters of four 1 KiB loads (four rows x 256 bytes each); the
+// MFMA B operand is 8 bf16 straight from the LDS tile and the block results chain in the MFMA
+// accumulator (A is zero past the slab end).
+template <int T, bool XF = false, bool WB = false>
 __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
     constexpr bool PACK = T <= 8;
     constexpr int NPL = PACK ? 1 : 2;                              // A planes (hi, lo)
     constexpr int TR = PACK ? 8 : 16;                              // token rows per plane
     constexpr int NI = kDnNB * 4 * TR / 256;                       // staging items per thread
+    constexpr int WS = WB ? 2 * kDownSlab + 16 : kDnStride;        // LDS tile row stride (bytes)
+    constexpr int NW = WB ? 16 : 8;                                // weight loads per lane
     __shared__ u32x4 ua[NPL][kDnNB][64];                           // A operands, lane order
     __shared__ float sqw[4][TR];                                   // per-wave sums of R^2
-    __shared__ __attribute__((aligned(16))) uint8_t wt[4][16 * kDnStride];
+    __shared__ __attribute__((aligned(16))) uint8_t wt[4][16 * WS];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int N = a.N, K = a.K, nblk = K >> 5;
     const int S = a.S;
@@ -231,7 +238,7 @@ __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
     //    contiguous bytes when the slab is whole and scale rows are 16-byte aligned)
     const int j = lane & 15, g = lane >> 4;
     uint32_t sw[8];
-    {
+    if (!WB) {
         const int row = imin(r0 + j, N - 1);
         const uint16_t* dr = a.d + (size_t)row * nblk + (k0 >> 5);
         if (cb == kDnNB && (nblk & 7) == 0) {
@@ -250,12 +257,23 @@ __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
     }
     // 1. weights: quarter q = i / 2 covers columns 128q .. +128; load i covers rows 8(i%2) ..
     //    +8 of it (8 lanes a row)
-    u32x4 wv[8];
+    u32x4 wv[NW];
+    if constexpr (WB) {
+        // quarter q = i / 4 covers bytes 256q .. +256 of the slab's 1024-byte rows; load i covers
+        // rows 4(i%4) .. +4 of it (16 lanes a row)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = imin(r0 + 8 * (i & 1) + (lane >> 3), N - 1);
-        const int col = k0 + imin(128 * (i >> 1) + 16 * (lane & 7), cw - 16);
-        wv[i] = ld_nt16(a.q + (size_t)row * K + col);
+        for (int i = 0; i < NW; ++i) {
+            const int row = imin(r0 + 4 * (i & 3) + (lane >> 4), N - 1);
+            const int col = 2 * k0 + imin(256 * (i >> 2) + 16 * (lane & 15), 2 * cw - 16);
+            wv[i] = ld_nt16(a.q + (size_t)row * 2 * K + col);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            const int row = imin(r0 + 8 * (i & 1) + (lane >> 3), N - 1);
+            const int col = k0 + imin(128 * (i >> 1) + 16 * (lane & 7), cw - 16);
+            wv[i] = ld_nt16(a.q + (size_t)row * K + col);
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -315,11 +333,29 @@ __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
     //    T > 8) on the exact operands and the block scale (0 past the slab end)
     uint8_t* tile = wt[wave];
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (WB) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<u32x4*>(tile + (4 * i + (lane >> 4)) * WS + 256 * qq + 16 * (lane & 15)) =
+                    wv[4 * qq + i];
+            __builtin_amdgcn_wave_barrier();   // LDS accesses of one wave complete in order
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int b = 4 * qq + i;
+                const u32x4 w = *reinterpret_cast<const u32x4*>(tile + j * WS + 64 * b + 16 * g);
+                acc = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8, ua[0][b][lane]), __builtin_bit_cast(bf16x8, w), acc);
+                if (!PACK) acc = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8, ua[NPL - 1][b][lane]), __builtin_bit_cast(bf16x8, w), acc);
+            }
+        }
+    }
+    if constexpr (!WB)
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-            *reinterpret_cast<u32x4*>(tile + (8 * i + (lane >> 3)) * kDnStride + 128 * qq + 16 * (lane & 7)) =
+            *reinterpret_cast<u32x4*>(tile + (8 * i + (lane >> 3)) * WS + 128 * qq + 16 * (lane & 7)) =
                 wv[2 * qq + i];
         __builtin_amdgcn_wave_barrier();       // LDS accesses of one wave complete in order
         uint2 q[4];
@@ -327,7 +363,7 @@ __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int b = 4 * qq + i;
-            q[i] = *reinterpret_cast<const uint2*>(tile + j * kDnStride + 32 * b + 8 * g);
+            q[i] = *reinterpret_cast<const uint2*>(tile + j * WS + 32 * b + 8 * g);
             x0[i] = ua[0][b][lane];
             if (!PACK) x1[i] = ua[NPL - 1][b][lane];
         }
@@ -639,6 +675,63 @@ __global__ void __launch_bounds__(256) hc_up_direct_kernel(GemvArgs a) {
     }
 }
 
+// The BF16 comparison up read (any K % 32 == 0): one wave per 16 output rows, the input staged
+// per 320-column chunk in LDS; lane l loads the 16 bytes of row l%16 at column 32b + 8(l/16) of
+// block b, the MFMA B operand as it stands, and the blocks chain in the accumulator.
+template <int T>
+__global__ void __launch_bounds__(256) hc_up_bf16_kernel(GemvArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t xl[kMaxT][kUpLoStride];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int N = a.N, K = a.K;
+    const int r0 = (blockIdx.x * 4 + wave) * 16;
+    const int j = lane & 15, g = lane >> 4;
+    const int row = imin(r0 + j, N - 1);
+    const uint16_t* lo = reinterpret_cast<const uint16_t*>(a.x);
+    const uint8_t* wr = reinterpret_cast<const uint8_t*>(a.q) + (size_t)row * 2 * K;
+    constexpr int npx = kUpCW / 8;                                  // 16-byte pieces per chunk row
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const int tj = j < T ? j : 0;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < K; c0 += kUpCW) {
+        const int cbn = imin(kUpCB, (K - c0) >> 5);                  // blocks in this chunk
+        const int npc = 4 * cbn;                                    // pieces in this chunk row
+        u32x4 xv[3];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int e = imin(i * 256 + (int)threadIdx.x, T * npx - 1);
+            const int t = e / npx, pc = imin(e - t * npx, npc - 1);
+            xv[i] = *reinterpret_cast<const u32x4*>(lo + (size_t)t * K + c0 + 8 * pc);
+        }
+        u32x4 wb[kUpCB];
+#pragma unroll
+        for (int b = 0; b < kUpCB; ++b) wb[b] = ld_nt16(wr + 2 * (c0 + 32 * imin(b, cbn - 1)) + 16 * g);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int e = i * 256 + (int)threadIdx.x;
+            if (e < T * npx) {
+                const int t = e / npx, pc = e - t * npx;
+                if (pc < npc) *reinterpret_cast<u32x4*>(&xl[t][16 * pc]) = xv[i];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < kUpCB; ++b) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(&xl[tj][64 * b + 16 * g]);
+            acc = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8, (j < T && b < cbn) ? x : z),
+                                     __builtin_bit_cast(bf16x8, wb[b]), acc);
+        }
+        if (c0 + kUpCW < K) __syncthreads();                // the next chunk overwrites LDS
+    }
+    uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+    const int n = r0 + j;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int t = 4 * g + v;
+        if (t < T && n < N) out[(size_t)t * N + n] = f2bf_bits(acc[v]);
+    }
+}
+
 template <int T>
 static int launch_up_t(GemvArgs a, hipStream_t st) {
     const int ntile = (a.N + 15) / 16;
@@ -663,7 +756,9 @@ int launch_hc_up(GemvArgs a, hipStream_t st) { GQ8_T_SWITCH(launch_up_t, a, st) 
 // order), and the weight loads start only after the partial-sum loads are issued.
 constexpr int kPairQuads = kUpCW / 4;       // float4 quads of a 320-wide row
 
-template <int T>
+// WB (the BF16 comparison read): bf16 weights [N][320]; lane l loads the 16 bytes of row l%16 at
+// column 32b + 8(l/16) for block b, which is the MFMA B operand as it stands (no scales).
+template <int T, bool WB = false>
 __global__ void __launch_bounds__(512) hc_pair_up_kernel(GemvArgs a) {
     constexpr int NQ = T * kPairQuads;                            // float4 quads of lo
     constexpr int NIT = (4 * NQ + 255) / 256;                     // (quad, slab group) items per thread
@@ -679,22 +774,37 @@ __global__ void __launch_bounds__(512) hc_pair_up_kernel(GemvArgs a) {
         const int r0 = (blockIdx.x * 4 + wave) * 16;
         __syncthreads();                                          // partial-sum loads issued
         const int row = imin(r0 + j, N - 1);
-        uint32_t sc[kUpCB / 2];
-        const uint32_t* dp = reinterpret_cast<const uint32_t*>(a.d + (size_t)row * (K >> 5));
-#pragma unroll
-        for (int i = 0; i < kUpCB / 2; ++i) sc[i] = dp[i];
-        u32x4 wv[kUpLoads];
-        const int8_t* wp = a.q + (size_t)row * K + 16 * g;
-#pragma unroll
-        for (int i = 0; i < kUpLoads; ++i) wv[i] = ld_nt16(wp + 64 * i);
-        __syncthreads();                                          // slab-group sums in LDS
-        __syncthreads();                                          // lo in LDS
         const u32x4 z = {0u, 0u, 0u, 0u};
         const int tj = j < T ? j : 0;
-        const int ko = 2 * up_koff(g);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (WB) {
+            u32x4 wb[kUpCB];
+            const uint8_t* wp = reinterpret_cast<const uint8_t*>(a.q) + (size_t)row * 2 * K + 16 * g;
 #pragma unroll
-        for (int i = 0; i < kUpLoads; ++i) {
+            for (int b = 0; b < kUpCB; ++b) wb[b] = ld_nt16(wp + 64 * b);
+            __syncthreads();                                      // slab-group sums in LDS
+            __syncthreads();                                      // lo in LDS
+#pragma unroll
+            for (int b = 0; b < kUpCB; ++b) {
+                const u32x4 x = *reinterpret_cast<const u32x4*>(&xl[tj][64 * b + 16 * g]);
+                acc = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8, j < T ? x : z), __builtin_bit_cast(bf16x8, wb[b]), acc);
+            }
+        }
+        uint32_t sc[kUpCB / 2];
+        u32x4 wv[kUpLoads];
+        if constexpr (!WB) {
+            const uint32_t* dp = reinterpret_cast<const uint32_t*>(a.d + (size_t)row * (K >> 5));
+#pragma unroll
+            for (int i = 0; i < kUpCB / 2; ++i) sc[i] = dp[i];
+            const int8_t* wp = a.q + (size_t)row * K + 16 * g;
+#pragma unroll
+            for (int i = 0; i < kUpLoads; ++i) wv[i] = ld_nt16(wp + 64 * i);
+            __syncthreads();                                      // slab-group sums in LDS
+            __syncthreads();                                      // lo in LDS
+        }
+        const int ko = 2 * up_koff(g);
+#pragma unroll
+        for (int i = 0; i < (WB ? 0 : kUpLoads); ++i) {
             const auto s02 = __builtin_amdgcn_permlane32_swap(wv[i].x, wv[i].z, false, false);
             const auto s13 = __builtin_amdgcn_permlane32_swap(wv[i].y, wv[i].w, false, false);
 #pragma unroll
@@ -853,6 +963,38 @@ int launch_hc_pair(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st) {
     }
     GemvArgs& a = dn;
     GQ8_T_SWITCH(launch_pair_t, dn, up, ws, st)
+}
+
+// ------------------------------------------------------------------------------ BF16 pair
+
+template <int T>
+static int launch_bf16_pair_t(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st) {
+    const int S = hc_down_slabs(dn.K);
+    char* w = static_cast<char*>(ws);
+    dn.S = S;
+    dn.part = reinterpret_cast<float*>(w);
+    dn.ssq = reinterpret_cast<float*>(w + round_up((size_t)S * T * dn.N * sizeof(float), kCounterAlign));
+    hipLaunchKernelGGL((hc_down_partial_kernel<T, false, true>), dim3(S * ((dn.N + kDnRows - 1) / kDnRows)), dim3(256), 0, st, dn);
+    int rc = launch_status();
+    if (rc != GQ8_OK) return rc;
+    const int ntile = (up.N + 15) / 16;
+    if constexpr (T <= kPairMaxT) {
+        if (up.K == kUpCW) {               // the combine inside the up kernel
+            up.S = S; up.part = dn.part; up.ssq = dn.ssq; up.eps = dn.eps; up.kd = dn.K;
+            up.rs_out = dn.rs_out; up.lo_out = dn.out;
+            hipLaunchKernelGGL((hc_pair_up_kernel<T, true>), dim3((ntile + 3) / 4), dim3(512), 0, st, up);
+            return launch_status();
+        }
+    }
+    hipLaunchKernelGGL(hc_down_combine_kernel<false>, dim3((dn.N + 63) / 64, T), dim3(256), 0, st, dn);
+    if ((rc = launch_status()) != GQ8_OK) return rc;
+    hipLaunchKernelGGL((hc_up_bf16_kernel<T>), dim3((ntile + 3) / 4), dim3(256), 0, st, up);
+    return launch_status();
+}
+
+int launch_hc_bf16_pair(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st) {
+    GemvArgs& a = dn;
+    GQ8_T_SWITCH(launch_bf16_pair_t, dn, up, ws, st)
 }
 
 }  // namespace gq8

@@ -62,6 +62,9 @@ int launch_hc_up(GemvArgs a, hipStream_t st);
 // combine runs inside the up kernel (two launches instead of three). dn.out = lo (bf16 [T][dn.N]).
 int launch_hc_pair(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st);
 
+// the same pair on BF16 weights (q = the bf16 weight bytes, d unused): the comparison read
+int launch_hc_bf16_pair(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st);
+
 // ---------------------------------------------------------------- W8A8
 
 struct W8Plan {

@@ -44,6 +44,7 @@ _SIGS = {
     "gq8_hc_q8_down": (_I, [_P, _P, _P, _F, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_hc_q8_up": (_I, [_P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_hc_q8_pair": (_I, [_P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "gq8_hc_bf16_pair": (_I, [_P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_w8a8_packed_bytes": (_SZ, [_I, _I]),
     "gq8_w8a8_pack": (_I, [_P, _I, _I, _P, _P]),
     "gq8_w8a8_gemm": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
@@ -156,6 +157,13 @@ def gq8_hc_q8_up(w_split, lo, out, T, N, K, ws, ws_bytes, stream=None):
 def gq8_hc_q8_pair(w_down, R, w_norm, eps, w_up, lo, rs_out, out, T, Nlr, Khc, ws, ws_bytes,
                    stream=None):
     return _check("gq8_hc_q8_pair", _lib.gq8_hc_q8_pair(
+        _ptr(w_down), _ptr(R), _ptr(w_norm), eps, _ptr(w_up), _ptr(lo), _ptr(rs_out), _ptr(out),
+        T, Nlr, Khc, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def gq8_hc_bf16_pair(w_down, R, w_norm, eps, w_up, lo, rs_out, out, T, Nlr, Khc, ws, ws_bytes,
+                     stream=None):
+    return _check("gq8_hc_bf16_pair", _lib.gq8_hc_bf16_pair(
         _ptr(w_down), _ptr(R), _ptr(w_norm), eps, _ptr(w_up), _ptr(lo), _ptr(rs_out), _ptr(out),
         T, Nlr, Khc, _ptr(ws), ws_bytes, _stream(stream)))
 

@@ -93,6 +93,15 @@ def hc_inputs(T, K=16384, N=320, seed=0):
     }
 
 
+def hc_weights_bf16(K=16384, N=320, seed=0):
+    """The hyper-connection weights of hc_inputs (same draws) as bf16 bit patterns, by
+    truncation: W_down [N,K], W_up [K,N] (the BF16 comparison read)."""
+    return {
+        "w_down": bf16_normal(seed, "hc.w_down", (N, K), 0.0, 0.02),
+        "w_up": bf16_normal(seed, "hc.w_up", (K, N), 0.0, 0.02),
+    }
+
+
 def w8a8_inputs(M, N, K, seed=0):
     """W8A8: x_q int8 [M,K], W int8 [K,N] (logical, k-major), scales U(1e-3,1e-2)."""
     return {

@@ -153,6 +153,16 @@ int gq8_hc_q8_pair(const void* w_down, const uint16_t* R, const uint16_t* w_norm
                    const void* w_up, uint16_t* lo, float* rs_out, uint16_t* out,
                    int T, int Nlr, int Khc, void* ws, size_t ws_bytes, void* stream);
 
+/* The same pair on BF16 weights: the read the Q8_0 pair replaces (HC-Q8 page, "Summary": the
+ * kernel-level BF16 -> Q8_0 read times), kept as an in-library comparison read measured with the
+ * same harness. w_down bf16 [Nlr][Khc] and w_up bf16 [Khc][Nlr], row-major, 16-byte aligned; every
+ * other argument, the shapes, the workspace (gq8_workspace_bytes(GQ8_OP_HC_PAIR, T, Nlr, Khc)),
+ * lo, rs_out and the errors are as in gq8_hc_q8_pair; lo and out are within the same pass rule
+ * of the BF16 oracle reads. */
+int gq8_hc_bf16_pair(const uint16_t* w_down, const uint16_t* R, const uint16_t* w_norm, float eps,
+                     const uint16_t* w_up, uint16_t* lo, float* rs_out, uint16_t* out, int T,
+                     int Nlr, int Khc, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------------------------
  * W8A8 (W8A8 page, operator statement): int8 x_q[M][K] @ int8 W[K][N] -> int32, then
  * * x_scale[M] * w_scale[N] -> bf16[M][N], M = 1..32.
