@@ -206,3 +206,15 @@ def test_moe_bf16_input_ties(gpu, D, F):
     gpu.gq8_moe_q8_0_routed_bf16(to_dev(xb), dids, dp, agu, adn, out2, T, topk, E, D, F, ws, nb)
     torch.cuda.synchronize()
     assert torch.equal(out1, out2)
+
+
+@pytest.mark.parametrize("T,E,topk,D,F", [(16, 300, 16, 1024, 256), (16, 40, 16, 160, 512)])
+def test_moe_most_entries(gpu, T, E, topk, D, F):
+    """T * topk = 256 entries, the most the routed call takes: the entries of an expert span all
+    four 64-entry words of the id ballot (E = 40: every expert has several entries)."""
+    out, (xq, xd, ids, w, agu, adn, ws, nb) = _moe_case(gpu, T, E, topk, D, F, seed=46)
+    x = to_dev(synth.moe_inputs(T=T, E=E, D=D, seed=46)["x"])
+    out2 = torch.empty_like(out)
+    gpu.gq8_moe_q8_0_routed_bf16(x, ids, w, agu, adn, out2, T, topk, E, D, F, ws, nb)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)

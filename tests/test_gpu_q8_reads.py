@@ -279,3 +279,29 @@ def test_pair_graph_replay_and_poison(gpu):
             g.replay()
         torch.cuda.synchronize()
         assert torch.equal(lo, lo0) and torch.equal(rs, rs0) and torch.equal(out, out0)
+
+
+@pytest.mark.parametrize("T", [1, 3, 8])
+def test_gemv_long_rows(gpu, T):
+    """K = 20480: more 1 KiB chunks than the 16 waves of a work-group (VALU path), 40 slabs (MFMA)."""
+    N, K = 48, 20480
+    w = synth.normal_f32(12, "gpu.gemv.long.w", (N, K), 0.0, 0.02)
+    x = synth.normal_f32(12, "gpu.gemv.long.x", (T, K))
+    y, _, _ = _gemv(gpu, q8_0_from_f32(to_dev(w)), to_dev(x), T, N, K)
+    torch.cuda.synchronize()
+    y_ref, S = q8_0_gemv(quantize_q8_0(w), x)
+    check_f32(to_host(y), y_ref, S, f"gemv long T={T}")
+
+
+@pytest.mark.parametrize("T,Nlr,Khc", [(2, 1024, 4096), (5, 1024, 2080)])
+def test_pair_widest_low_rank(gpu, T, Nlr, Khc):
+    """Nlr = 1024, the widest up depth (four 320-column chunks, the last ragged)."""
+    d = synth.hc_inputs(T, K=Khc, N=Nlr, seed=42)
+    wd, wu = q8_0_from_f32(to_dev(d["w_down"])), q8_0_from_f32(to_dev(d["w_up"]))
+    lo, rs, out = _pair(gpu, wd, to_dev(d["R"]), to_dev(d["w_norm"]), wu, T, Nlr, Khc)
+    torch.cuda.synchronize()
+    lo_ref, rs_ref, S = hc_down(d["R"], d["w_norm"], quantize_q8_0(d["w_down"]))
+    check_bf16(to_host(lo, np.uint16), lo_ref, S, f"pair down T={T} Nlr={Nlr}")
+    assert np.allclose(to_host(rs), rs_ref, rtol=1e-5, atol=0)
+    out_ref, S_up = hc_up(to_host(lo, np.uint16), quantize_q8_0(d["w_up"]))
+    check_bf16(to_host(out, np.uint16), out_ref, S_up, f"pair up T={T} Nlr={Nlr}")

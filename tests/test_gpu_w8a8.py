@@ -101,3 +101,13 @@ def test_w8a8_graph_replay_and_poison(gpu):
         assert torch.equal(out, ref)
         if cb:
             assert int(ws[:cb].count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("M", [1, 16, 32])
+def test_w8a8_max_depth(gpu, M):
+    """K = 8192, the largest depth (16 waves x 8 k-steps of 64), exact against the oracle."""
+    N, K = 80, 8192
+    d = synth.w8a8_inputs(M, N, K, seed=3)
+    acc_ref, out_ref = w8a8_gemm(d["xq"], d["x_scale"], d["W"], d["w_scale"])
+    assert np.array_equal(_run(gpu, d, M, N, K, i32=True), acc_ref)
+    assert np.array_equal(_run(gpu, d, M, N, K), out_ref)
