@@ -23,6 +23,10 @@ Readings taken where the pages are not explicit:
     h = SiLU(g) * u unquantized (h is not re-quantized);
   * combine: y[t] = sum over slots j = 0..k-1 of p[t, j] * row[t, j], in slot order,
     stored as bf16.
+  * the variant with h re-quantized (h_q8_1=True): h is rounded to fp32 (the precision the
+    kernels keep it in), then quantized to q8_1 per 32-block with the input's rule (fp16
+    amax / 127, fp32 quotient rounded half away from zero), and the down projection reads the
+    dequantized d * q.
 All real arithmetic is float64, integer dots int64.
 """
 from __future__ import annotations
@@ -30,7 +34,7 @@ from __future__ import annotations
 import numpy as np
 
 from .numerics import fp16_to_f32
-from .q8 import dequantize
+from .q8 import dequantize, quantize_q8_0
 
 
 def route(logits, topk):
@@ -65,17 +69,26 @@ def _gate_up(x81, t, gu):
     return np.sum(dw * dx[None, :] * qi, axis=1)
 
 
-def expert_rows(x81, t, gu, dn):
-    """One entry: returns (row float64 [D], S_row float64 [D]) where S_row = sum_k |d q h_k|."""
+def requantize_h(h):
+    """h (float64 [F]) -> the real values d * q of its q8_1 form (float64 [F]), h first rounded to
+    fp32."""
+    return dequantize(quantize_q8_0(np.asarray(h, dtype=np.float32)[None, :]))[0]
+
+
+def expert_rows(x81, t, gu, dn, h_q8_1=False):
+    """One entry: returns (row float64 [D], S_row float64 [D]) where S_row = sum_k |d q h_k|
+    (h_k the down read's input: h itself, or its q8_1 values for h_q8_1)."""
     F = gu.q.shape[0] // 2
     gu_v = _gate_up(x81, t, gu)
     g, u = gu_v[:F], gu_v[F:]
     h = g / (1.0 + np.exp(-g)) * u
+    if h_q8_1:
+        h = requantize_h(h)
     W = dequantize(dn)
     return W @ h, np.abs(W) @ np.abs(h)
 
 
-def moe_forward(x81, ids, p, expert_blocks):
+def moe_forward(x81, ids, p, expert_blocks, h_q8_1=False):
     """y[t] = sum_j p[t, j] * expert_rows(ids[t, j]).
 
     x81: q8_1 blocks of the input [T, D]; expert_blocks(e) -> (gate_up Q8Blocks [2F, D],
@@ -92,7 +105,7 @@ def moe_forward(x81, ids, p, expert_blocks):
             e = int(ids[t, j])
             if e not in cache:
                 cache[e] = expert_blocks(e)
-            r, s = expert_rows(x81, t, *cache[e])
+            r, s = expert_rows(x81, t, *cache[e], h_q8_1=h_q8_1)
             y[t] += p[t, j] * r
             S[t] += abs(p[t, j]) * s
     return y, S

@@ -74,3 +74,44 @@ def test_forward_is_weighted_sum_and_linear_in_weights():
     # one expert with weight one is that expert's rows
     y1, _ = moe_forward(x81, np.array([[4], [4]]), np.ones((2, 1)), blocks)
     assert np.allclose(y1[0], expert_rows(x81, 0, *blocks(4))[0], rtol=0, atol=0)
+
+
+def test_requantized_h_within_the_dequantization_bound():
+    """The q8_1(h) variant: every value of the down read's input moves by at most half its block's
+    scale (plus the fp32 rounding of h), so each output row moves by at most
+    sum_k |w_k| (d_blk(k) / 2 + |h_k| 2^-24); the variant reads each block's own scale."""
+    from oracle.moe import requantize_h
+    from oracle.numerics import fp16_to_f32
+    D, F = 64, 96
+    x81 = quantize_q8_1_bf16(synth.bf16_normal(9, "pin.moe.x3", (1, D)))
+    gu, dn = _tiny_expert(5, D, F)
+    r0, _ = expert_rows(x81, 0, gu, dn)
+    rq, Sq = expert_rows(x81, 0, gu, dn, h_q8_1=True)
+    gu_v = dequantize(gu) @ dequantize(x81)[0]
+    g, u = gu_v[:F], gu_v[F:]
+    h = g * u / (1.0 + np.exp(-g))
+    hq = requantize_h(h)
+    d = fp16_to_f32(quantize_q8_0(h.astype(np.float32)[None, :]).d[0]).astype(np.float64)
+    dk = np.repeat(d, 32)
+    assert np.all(np.abs(hq - h) <= dk / 2 * (1 + 2.0 ** -10) + np.abs(h) * 2.0 ** -24)
+    W = dequantize(dn)
+    bound = np.abs(W) @ (dk / 2 * (1 + 2.0 ** -10) + np.abs(h) * 2.0 ** -24)
+    assert np.all(np.abs(rq - r0) <= bound * (1 + 1e-12))
+    assert np.any(rq != r0)                                     # it is a different read
+    assert np.allclose(rq, W @ hq, rtol=1e-13, atol=0) and np.all(Sq >= np.abs(rq))
+    # each block's values are its own scale times integers in [-127, 127]
+    k = np.rint(hq / dk)
+    assert np.array_equal(hq, k * dk) and np.max(np.abs(k)) <= 127
+    assert np.all(np.max(np.abs(k.reshape(-1, 32)), axis=1)[d > 0] == 127)
+
+
+def test_requantized_forward_passes_the_flag_through():
+    D, F = 64, 32
+    x81 = quantize_q8_1_bf16(synth.bf16_normal(10, "pin.moe.x4", (2, D)))
+    ids = np.array([[3, 1], [1, 4]])
+    p = np.array([[0.6, 0.4], [0.25, 0.75]])
+    blocks = lambda e: _tiny_expert(e, D, F)  # noqa: E731
+    yq, _ = moe_forward(x81, ids, p, blocks, h_q8_1=True)
+    for t in range(2):
+        want = sum(p[t, j] * expert_rows(x81, t, *blocks(ids[t, j]), h_q8_1=True)[0] for j in range(2))
+        assert np.allclose(yq[t], want, rtol=1e-13, atol=1e-16)
