@@ -360,6 +360,14 @@ def bench_moe(torch, gq8, synth, dev, timed, emit):
     emit({"workload": "routed MoE on the bf16 input (q8_1 fused) T=4 E=512 top-8 D=2048 F=512",
           "unique_experts": U, "us_per_call": round(us, 3), "weight_GBps": round(U * (gu_b + dn_b) / us / 1e3, 1)})
 
+    for flags, name in ((gq8.MOE_H_Q8_1, "routed MoE, down read on q8_1(h)"),
+                        (gq8.MOE_X_BF16 | gq8.MOE_H_Q8_1, "routed MoE on the bf16 input, down read on q8_1(h)")):
+        xx, xs = (xb, None) if flags & gq8.MOE_X_BF16 else (xq, xd)
+        us = timed(lambda i: (lambda s, a=agus[i % n], b=adns[i % n]: gq8.gq8_moe_q8_0_routed_flags(
+            xx, xs, ids, wts, a, b, out, T, topk, E, D, F, flags, wsp, nb, s)), n, reps=50)
+        emit({"workload": name + " T=4 E=512 top-8 D=2048 F=512", "unique_experts": U,
+              "us_per_call": round(us, 3), "weight_GBps": round(U * (gu_b + dn_b) / us / 1e3, 1)})
+
     def two_calls(s, a, b):
         gq8.gq8_q8_1_quantize(xb, T, D, xq, xd, None, s)
         gq8.gq8_moe_q8_0_routed(xq, xd, ids, wts, a, b, out, T, topk, E, D, F, wsp, nb, s)

@@ -346,7 +346,7 @@ GQ8_EXPORT int gq8_moe_q8_0_routed(const int8_t* xq, const uint16_t* xd, const i
     if (rc != GQ8_OK) return rc;
     if (device_cus() == 0) return GQ8_ENODEV;
     return launch_moe_routed(xq, xd, nullptr, ids, weights, w_gate_up, w_down, out, T, topk, E, D,
-                             F, ws, S(stream));
+                             F, false, ws, S(stream));
 }
 
 GQ8_EXPORT int gq8_moe_q8_0_routed_bf16(const uint16_t* x, const int32_t* ids, const float* weights,
@@ -366,7 +366,31 @@ GQ8_EXPORT int gq8_moe_q8_0_routed_bf16(const uint16_t* x, const int32_t* ids, c
     if (rc != GQ8_OK) return rc;
     if (device_cus() == 0) return GQ8_ENODEV;
     return launch_moe_routed(nullptr, nullptr, x, ids, weights, w_gate_up, w_down, out, T, topk, E,
-                             D, F, ws, S(stream));
+                             D, F, false, ws, S(stream));
+}
+
+GQ8_EXPORT int gq8_moe_q8_0_routed_flags(const void* x, const uint16_t* xd, const int32_t* ids,
+                                         const float* weights, const void* w_gate_up,
+                                         const void* w_down, uint16_t* out, int T, int topk, int E,
+                                         int D, int F, int flags, void* ws, size_t ws_bytes,
+                                         void* stream) {
+    if (T < 0 || topk < 0 || E < 0 || D < 0 || F < 0) return GQ8_EINVAL;
+    if (flags & ~(GQ8_MOE_X_BF16 | GQ8_MOE_H_Q8_1)) return GQ8_EINVAL;
+    if (T == 0) return GQ8_OK;
+    const bool xb = (flags & GQ8_MOE_X_BF16) != 0, hq = (flags & GQ8_MOE_H_Q8_1) != 0;
+    if (T > kMaxT || topk < 1 || T * topk > 256 || E < 1 || D < 32 || D % 32 != 0 || F < 32 ||
+        F % 32 != 0 || F > 1024 || (hq && F != 256 && F != 512 && F != 1024))
+        return GQ8_ESHAPE;
+    if (x == nullptr || (!xb && xd == nullptr) || ids == nullptr || weights == nullptr ||
+        w_gate_up == nullptr || w_down == nullptr || out == nullptr)
+        return GQ8_EINVAL;
+    if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(w_down)) return GQ8_EALIGN;
+    int rc = check_ws(ws, ws_bytes, moe_workspace_bytes(T, topk, D, F));
+    if (rc != GQ8_OK) return rc;
+    if (device_cus() == 0) return GQ8_ENODEV;
+    return launch_moe_routed(xb ? nullptr : static_cast<const int8_t*>(x), xb ? nullptr : xd,
+                             xb ? static_cast<const uint16_t*>(x) : nullptr, ids, weights,
+                             w_gate_up, w_down, out, T, topk, E, D, F, hq, ws, S(stream));
 }
 
 // ---------------------------------------------------------------------------------- probe

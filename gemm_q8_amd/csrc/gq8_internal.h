@@ -95,9 +95,10 @@ int launch_moe_route(const float* logits, int T, int E, int topk, int32_t* ids, 
                      hipStream_t st);
 int launch_moe_plan(const int32_t* ids, int T, int topk, int E, int32_t* plan, hipStream_t st);
 size_t moe_workspace_bytes(int T, int topk, int D, int F);
-// xb != nullptr: bf16 input quantized to q8_1 on the device (xq, xd unused)
+// xb != nullptr: bf16 input quantized to q8_1 on the device (xq, xd unused); hq: the down read
+// takes q8_1(h) (F in {256, 512, 1024}, else GQ8_ESHAPE)
 int launch_moe_routed(const int8_t* xq, const uint16_t* xd, const uint16_t* xb, const int32_t* ids,
                       const float* w, const void* wgu, const void* wdn, uint16_t* out, int T,
-                      int topk, int E, int D, int F, void* ws, hipStream_t st);
+                      int topk, int E, int D, int F, bool hq, void* ws, hipStream_t st);
 
 }  // namespace gq8

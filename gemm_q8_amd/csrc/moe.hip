@@ -574,13 +574,21 @@ GQ8_DEV int imin_m(int x, int y) { return x < y ? x : y; }
 
 constexpr int kMoeMaxTopk = 16;
 
-template <int NL>
+//
+// HQ (the variant whose down read takes q8_1(h)): the staging quantizes the entry's h per
+// 32-block (four lanes a block, the input's q8_1 rule) into int8 codes and fp16 scales in LDS,
+// and each block is one v_mfma_i32_16x16x32_i8 of those codes with the weight quants as the
+// loads give them (no conversion); its int32 result times d_w * d_h (exact in fp32) accumulates
+// in fp32.
+template <int NL, bool HQ>
 __global__ void __launch_bounds__(256) moe_down_token_kernel(MoeArgs a) {
     constexpr int NB = 2 * NL;                     // Q8_0 blocks per row
     constexpr int F = 64 * NL;
     constexpr int EG = NL >= 16 ? 1 : 2;           // entries in flight per wave
     constexpr int HC = (F / 8 + 63) / 64;          // 8-float pieces of h per lane
-    __shared__ __attribute__((aligned(16))) uint16_t hs[4][EG][2][F];
+    __shared__ __attribute__((aligned(16))) uint16_t hs[HQ ? 1 : 4][EG][2][HQ ? 8 : F];
+    __shared__ __attribute__((aligned(16))) int8_t hq[HQ ? 4 : 1][EG][HQ ? F : 16];
+    __shared__ uint16_t hdq[HQ ? 4 : 1][EG][HQ ? NB : 1];
     __shared__ float rr[kMoeMaxTopk][16];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j = lane & 15, g = lane >> 4;
@@ -631,7 +639,32 @@ __global__ void __launch_bounds__(256) moe_down_token_kernel(MoeArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < EG; ++u) {
+        for (int u = 0; u < EG && HQ; ++u) {
+            // h -> q8_1 codes and block scales in this wave's LDS slot
+#pragma unroll
+            for (int c = 0; c < HC; ++c) {
+                const int pc = lane + 64 * c;
+                if (pc < F / 8) {
+                    const float f[8] = {hv[u][c][0].x, hv[u][c][0].y, hv[u][c][0].z, hv[u][c][0].w,
+                                        hv[u][c][1].x, hv[u][c][1].y, hv[u][c][1].z, hv[u][c][1].w};
+                    float am = 0.f;
+#pragma unroll
+                    for (int e2 = 0; e2 < 8; ++e2) am = fmaxf(am, fabsf(f[e2]));
+                    am = fmaxf(am, __shfl_xor(am, 1, 64));
+                    am = fmaxf(am, __shfl_xor(am, 2, 64));
+                    const uint16_t db = q8_scale_bits(am);
+                    const float dd = h2f(db);
+                    uint32_t q2[2] = {0u, 0u};
+#pragma unroll
+                    for (int e2 = 0; e2 < 8; ++e2)
+                        q2[e2 >> 2] |= ((uint32_t)q8_quant(f[e2], dd) & 0xffu) << (8 * (e2 & 3));
+                    *reinterpret_cast<uint2*>(&hq[HQ ? wave : 0][u][HQ ? 8 * pc : 0]) = make_uint2(q2[0], q2[1]);
+                    if ((pc & 3) == 0) hdq[HQ ? wave : 0][u][HQ ? pc >> 2 : 0] = db;
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < EG && !HQ; ++u) {
             // h -> bf16 hi, lo in this wave's LDS slot
 #pragma unroll
             for (int c = 0; c < HC; ++c) {
@@ -647,8 +680,8 @@ __global__ void __launch_bounds__(256) moe_down_token_kernel(MoeArgs a) {
                         l4[e2] = (uint32_t)f2bf_bits(f[2 * e2] - bf2f(h0)) |
                                  ((uint32_t)f2bf_bits(f[2 * e2 + 1] - bf2f(h1)) << 16);
                     }
-                    *reinterpret_cast<u32x4*>(&hs[wave][u][0][8 * pc]) = u32x4{h4[0], h4[1], h4[2], h4[3]};
-                    *reinterpret_cast<u32x4*>(&hs[wave][u][1][8 * pc]) = u32x4{l4[0], l4[1], l4[2], l4[3]};
+                    *reinterpret_cast<u32x4*>(&hs[HQ ? 0 : wave][u][0][HQ ? 0 : 8 * pc]) = u32x4{h4[0], h4[1], h4[2], h4[3]};
+                    *reinterpret_cast<u32x4*>(&hs[HQ ? 0 : wave][u][1][HQ ? 0 : 8 * pc]) = u32x4{l4[0], l4[1], l4[2], l4[3]};
                 }
             }
         }
@@ -656,8 +689,32 @@ __global__ void __launch_bounds__(256) moe_down_token_kernel(MoeArgs a) {
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-        for (int u = 0; u < EG; ++u) {
-            const uint8_t* hb = reinterpret_cast<const uint8_t*>(&hs[wave][u][hl][0]);
+        for (int u = 0; u < EG && HQ; ++u) {
+            const int8_t* qb = &hq[HQ ? wave : 0][u][0];
+            float acc0 = 0.f;
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                const auto s02 = __builtin_amdgcn_permlane32_swap((uint32_t)wv[u][i].x, (uint32_t)wv[u][i].z, false, false);
+                const auto s13 = __builtin_amdgcn_permlane32_swap((uint32_t)wv[u][i].y, (uint32_t)wv[u][i].w, false, false);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int b = 2 * i + h;
+                    const uint2 xa = *reinterpret_cast<const uint2*>(qb + (HQ ? 32 * b + dn_koff(g) : 0));
+                    const long av = (long)(((unsigned long)xa.y << 32) | xa.x);
+                    const long bv = (long)(((unsigned long)s13[h] << 32) | s02[h]);
+                    const v4i zi = {0, 0, 0, 0};
+                    const v4i Di = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, bv, zi, 0, 0, 0);
+                    const float dwh = h2f((uint16_t)(h ? (sc[u][i] >> 16) : (sc[u][i] & 0xffffu))) *
+                                      h2f(hdq[HQ ? wave : 0][u][HQ ? b : 0]);     // exact in fp32
+                    acc0 = fmaf((float)Di[0], dwh, acc0);
+                }
+            }
+            // result row 0 (lanes 0..15, v = 0): every A row holds the same codes
+            if (on[u] && lane < 16) rr[j0 + 4 * u][j] = acc0;
+        }
+#pragma unroll
+        for (int u = 0; u < EG && !HQ; ++u) {
+            const uint8_t* hb = reinterpret_cast<const uint8_t*>(&hs[HQ ? 0 : wave][u][hl][0]);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
@@ -716,7 +773,8 @@ size_t moe_workspace_bytes(int T, int topk, int D, int F) {
 
 int launch_moe_routed(const int8_t* xq, const uint16_t* xd, const uint16_t* xb, const int32_t* ids,
                       const float* w, const void* wgu, const void* wdn, uint16_t* out, int T,
-                      int topk, int E, int D, int F, void* ws, hipStream_t st) {
+                      int topk, int E, int D, int F, bool hq, void* ws, hipStream_t st) {
+    if (hq && F != 256 && F != 512 && F != 1024) return GQ8_ESHAPE;
     MoeArgs a{};
     a.xq = xq; a.xd = xd; a.xb = xb; a.w = w;
     a.wgu = static_cast<const int8_t*>(wgu);
@@ -763,9 +821,15 @@ int launch_moe_routed(const int8_t* xq, const uint16_t* xd, const uint16_t* xb, 
     if ((rc = launch_status()) != GQ8_OK) return rc;
     if (token_dn) {                        // down + combine in one kernel
         const dim3 gt((D + 15) / 16, T);
-        if (F == 256) hipLaunchKernelGGL((moe_down_token_kernel<4>), gt, dim3(256), 0, st, a);
-        else if (F == 512) hipLaunchKernelGGL((moe_down_token_kernel<8>), gt, dim3(256), 0, st, a);
-        else hipLaunchKernelGGL((moe_down_token_kernel<16>), gt, dim3(256), 0, st, a);
+        if (hq) {
+            if (F == 256) hipLaunchKernelGGL((moe_down_token_kernel<4, true>), gt, dim3(256), 0, st, a);
+            else if (F == 512) hipLaunchKernelGGL((moe_down_token_kernel<8, true>), gt, dim3(256), 0, st, a);
+            else hipLaunchKernelGGL((moe_down_token_kernel<16, true>), gt, dim3(256), 0, st, a);
+        } else {
+            if (F == 256) hipLaunchKernelGGL((moe_down_token_kernel<4, false>), gt, dim3(256), 0, st, a);
+            else if (F == 512) hipLaunchKernelGGL((moe_down_token_kernel<8, false>), gt, dim3(256), 0, st, a);
+            else hipLaunchKernelGGL((moe_down_token_kernel<16, false>), gt, dim3(256), 0, st, a);
+        }
         return launch_status();
     }
     const int rps = 64 / (F / 16);

@@ -20,6 +20,7 @@ _lib = ctypes.CDLL(_LIB_PATH)
 LIB_PATH = _LIB_PATH
 
 OK, EINVAL, ESHAPE, EALIGN, EWORKSPACE, ECAPTURE, EHIP, ENODEV = 0, -1, -2, -3, -4, -5, -6, -7
+MOE_X_BF16, MOE_H_Q8_1 = 1, 2
 OP_Q8_0_GEMV, OP_HC_DOWN, OP_HC_UP, OP_W8A8, OP_HC_PAIR = 1, 2, 3, 4, 5
 
 _P = ctypes.c_void_p
@@ -55,6 +56,7 @@ _SIGS = {
     "gq8_moe_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "gq8_moe_q8_0_routed": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P]),
     "gq8_moe_q8_0_routed_bf16": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P]),
+    "gq8_moe_q8_0_routed_flags": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _SZ, _P]),
     "gq8_read_probe_sink_floats": (_SZ, [_SZ]),
     "gq8_read_probe": (_I, [_P, _SZ, _P, _P]),
 }
@@ -216,6 +218,13 @@ def gq8_moe_q8_0_routed_bf16(x, ids, weights, w_gate_up, w_down, out, T, topk, E
     return _check("gq8_moe_q8_0_routed_bf16", _lib.gq8_moe_q8_0_routed_bf16(
         _ptr(x), _ptr(ids), _ptr(weights), _ptr(w_gate_up), _ptr(w_down), _ptr(out),
         T, topk, E, D, F, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def gq8_moe_q8_0_routed_flags(x, xd, ids, weights, w_gate_up, w_down, out, T, topk, E, D, F, flags,
+                              ws, ws_bytes, stream=None):
+    return _check("gq8_moe_q8_0_routed_flags", _lib.gq8_moe_q8_0_routed_flags(
+        _ptr(x), _ptr(xd), _ptr(ids), _ptr(weights), _ptr(w_gate_up), _ptr(w_down), _ptr(out),
+        T, topk, E, D, F, flags, _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def gq8_read_probe_sink_floats(nbytes):

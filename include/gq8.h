@@ -236,6 +236,25 @@ int gq8_moe_q8_0_routed_bf16(const uint16_t* x, const int32_t* ids, const float*
                              int topk, int E, int D, int F, void* ws, size_t ws_bytes,
                              void* stream);
 
+/* The routed call with options (flags, a bitwise or):
+ *   GQ8_MOE_X_BF16  x is the bf16 input [T][D] (xd unused), quantized to q8_1 as in
+ *                   gq8_moe_q8_0_routed_bf16; else x is the int8 q8_1 quants with scales xd.
+ *   GQ8_MOE_H_Q8_1  the variant whose down read takes h in q8_1 form (the form the EP page
+ *                   gives the MoE input, "What changed", applied to h): h rounded to fp32, then
+ *                   quantized per 32-block with the input's rule, and the down read's blocks are
+ *                   integer dots of those codes with the weight quants, scaled by both scales.
+ *                   A different, slightly less exact read than the default (h in fp32), within
+ *                   the same pass rule of the oracle's variant. Needs F in {256, 512, 1024}, else
+ *                   GQ8_ESHAPE.
+ * Other flag bits: GQ8_EINVAL. Shapes, weights, workspace and errors otherwise as
+ * gq8_moe_q8_0_routed; flags = 0 is gq8_moe_q8_0_routed and GQ8_MOE_X_BF16 alone is
+ * gq8_moe_q8_0_routed_bf16, bit for bit. */
+enum { GQ8_MOE_X_BF16 = 1, GQ8_MOE_H_Q8_1 = 2 };
+int gq8_moe_q8_0_routed_flags(const void* x, const uint16_t* xd, const int32_t* ids,
+                              const float* weights, const void* w_gate_up, const void* w_down,
+                              uint16_t* out, int T, int topk, int E, int D, int F, int flags,
+                              void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------------------------
  * Diagnostics
  * ------------------------------------------------------------------------------------------ */

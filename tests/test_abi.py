@@ -134,3 +134,20 @@ def test_moe_bf16_input_argument_checks(lib):
                                         0, 8, 512, 2048, 512, None, 0, None) == lib.OK
     # the workspace also holds the q8_1 form of a bf16 input (used when D > 4096)
     assert lib.gq8_moe_workspace_bytes(2, 4, 8192, 256) >= 2 * 8192 + 2 * 256 * 2
+
+
+def test_moe_flags_argument_checks(lib):
+    raw = lib.raw()
+    dummy = 1 << 20  # never dereferenced
+    assert lib.MOE_X_BF16 == 1 and lib.MOE_H_Q8_1 == 2
+    # unknown flag bits
+    assert raw.gq8_moe_q8_0_routed_flags(dummy, dummy, dummy, dummy, dummy, dummy, dummy,
+                                         4, 8, 512, 2048, 512, 4, None, 0, None) == lib.EINVAL
+    # q8_1(h) needs F in {256, 512, 1024}
+    assert raw.gq8_moe_q8_0_routed_flags(dummy, dummy, dummy, dummy, dummy, dummy, dummy,
+                                         4, 8, 512, 2048, 96, lib.MOE_H_Q8_1, None, 0, None) == lib.ESHAPE
+    # the int8 input needs its scales; the bf16 input does not
+    assert raw.gq8_moe_q8_0_routed_flags(dummy, None, dummy, dummy, dummy, dummy, dummy,
+                                         4, 8, 512, 2048, 512, 0, None, 0, None) == lib.EINVAL
+    assert raw.gq8_moe_q8_0_routed_flags(dummy, None, dummy, dummy, dummy, dummy, dummy,
+                                         4, 8, 512, 2048, 512, lib.MOE_X_BF16, None, 0, None) == lib.EWORKSPACE

@@ -218,3 +218,32 @@ def test_moe_most_entries(gpu, T, E, topk, D, F):
     gpu.gq8_moe_q8_0_routed_bf16(x, ids, w, agu, adn, out2, T, topk, E, D, F, ws, nb)
     torch.cuda.synchronize()
     assert torch.equal(out, out2)
+
+
+@pytest.mark.parametrize("T,E,topk,D,F", [(4, 512, 8, 2048, 512), (3, 20, 4, 544, 256),
+                                          (5, 12, 3, 1056, 1024), (16, 40, 16, 160, 512)])
+def test_moe_flags(gpu, T, E, topk, D, F):
+    """gq8_moe_q8_0_routed_flags: flags 0 and X_BF16 are bitwise the two named calls; H_Q8_1 (the
+    down read on q8_1(h), integer dots) passes the rule against the oracle's variant, on the int8
+    and on the bf16 input (bitwise the same)."""
+    seed = 47
+    out, (xq, xd, ids, w, agu, adn, ws, nb) = _moe_case(gpu, T, E, topk, D, F, seed=seed)
+    inp = synth.moe_inputs(T=T, E=E, D=D, seed=seed)
+    xb = to_dev(inp["x"])
+    o = {f: torch.empty_like(out) for f in (0, 1, 2, 3)}
+    gpu.gq8_moe_q8_0_routed_flags(xq, xd, ids, w, agu, adn, o[0], T, topk, E, D, F, 0, ws, nb)
+    gpu.gq8_moe_q8_0_routed_flags(xb, None, ids, w, agu, adn, o[1], T, topk, E, D, F,
+                                  gpu.MOE_X_BF16, ws, nb)
+    gpu.gq8_moe_q8_0_routed_flags(xq, xd, ids, w, agu, adn, o[2], T, topk, E, D, F,
+                                  gpu.MOE_H_Q8_1, ws, nb)
+    gpu.gq8_moe_q8_0_routed_flags(xb, None, ids, w, agu, adn, o[3], T, topk, E, D, F,
+                                  gpu.MOE_X_BF16 | gpu.MOE_H_Q8_1, ws, nb)
+    torch.cuda.synchronize()
+    assert torch.equal(o[0], out) and torch.equal(o[1], out)
+    assert torch.equal(o[3], o[2])
+    ids_ref, p_ref = route(inp["logits"], topk)
+    experts = lambda e: synth.moe_expert_weights(e, D=D, F=F, seed=seed)  # noqa: E731
+    blocks = lambda e: (quantize_q8_0(experts(e)["gate_up"]), quantize_q8_0(experts(e)["down"]))  # noqa: E731
+    y_ref, S = moe_forward(quantize_q8_1_bf16(inp["x"]), ids_ref, p_ref, blocks, h_q8_1=True)
+    check_bf16(to_host(o[2], np.uint16), y_ref, S, f"moe q8_1(h) T={T} D={D} F={F}")
+    assert not torch.equal(o[2], out)                           # a different read
