@@ -14,9 +14,14 @@ Output: one JSON line on stdout (metric = weight bytes / time in GB/s), with
                 launch stream, graphs of back-to-back calls), against 8 TB/s; the call is two
                 kernels (the down read's partial sums, then the up read with the down's
                 combine inside), whose separate durations the rocprofv3 summary gives;
-  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload.
---all-configs also times the other workloads (Q8_0 GEMV T sweep, W8A8 sweep, routed MoE)
-and writes their lines to --report (default gpurun_out/bench_all.jsonl) and stderr.
+  config        per-T pair call times: the mean, the median and p90 over --reps samples of one
+                rotation each, and a hot-cache run (one weight set: cache, not HBM, context only);
+                the sha256 of the library that ran;
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload (host CPU model
+                and thread counts stated).
+--all-configs also times the other workloads (BF16 comparison pair, Q8_0 GEMV T sweep, W8A8
+sweep, routed MoE variants) and writes their lines to --report (default
+gpurun_out/bench_all.jsonl) and stderr; --only and --w8a8-ms select among them.
 """
 from __future__ import annotations
 
@@ -178,6 +183,21 @@ def hc_kernel_bytes(kind, T):
 
 # ------------------------------------------------------------------------------------ CPU baseline
 
+def lib_sha256(path):
+    import hashlib
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(synth, budget_s):
     """The oracle (test infrastructure) on the same workload: down + up for T = 1, 4, 6 per
     step, repeated until about `budget_s` seconds have been spent."""
@@ -203,6 +223,7 @@ def cpu_baseline(synth, budget_s):
             break
     wbytes = steps * len(TS) * 2 * (K_HC * N_LR + K_HC * N_LR // 32 * 2)
     return {"value": round(wbytes / el / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model(), "host_threads": os.cpu_count(),
             "sample": f"{steps} oracle steps (down+up read at T=1,4,6 each, full size) in {el:.1f} s; "
                       f"numpy float64 on the host, BLAS threads={cores}"}
 
@@ -435,21 +456,34 @@ def main():
     per_call = {}
     kern = {}
     reps = max(1, args.reps)
+    dist = {}
+    hot = {}
     for T in TS:
         for kind, mk in (("pair", hc_pair_fn), ("down", hc_down_fn), ("up", hc_up_fn)):
             g = GraphSteps(torch, stream, lambda i, T=T, mk=mk: [mk(gq8, h, T, i)], n)
             g.run(n)
-            tk = time_region(torch, stream, lambda: g.run(n * reps))
+            # reps samples of one rotation each (n calls): the mean over all, and the median and
+            # p90 of the per-sample per-call times
+            ts = [time_region(torch, stream, lambda: g.run(n)) for _ in range(reps)]
+            tk = sum(ts)
             k = kern.setdefault(kind, {"t": 0.0, "bytes": 0, "launches": 0})
             k["t"] += tk
             k["bytes"] += hc_kernel_bytes(kind, T) * n * reps
             k["launches"] += n * reps
             if kind == "pair":
                 per_call[f"T{T}"] = round(tk / (n * reps) * 1e6, 3)
+                us = np.array(ts) / n * 1e6
+                dist[f"T{T}"] = {"median": round(float(np.median(us)), 3),
+                                 "p90": round(float(np.percentile(us, 90)), 3)}
+        # hot cache: the same call on one weight set (5.6 MB per read stays in the 256 MB MALL)
+        g = GraphSteps(torch, stream, lambda i, T=T: [hc_pair_fn(gq8, h, T, 0)], n)
+        g.run(n)
+        hot[f"T{T}"] = round(time_region(torch, stream, lambda: g.run(n * reps)) / (n * reps) * 1e6, 3)
     dom = "pair"
     kd = kern[dom]
     avg_us = kd["t"] / kd["launches"] * 1e6
     achieved = kd["bytes"] / kd["t"] / 1e9
+    log(f"[bench] per-call pair us {per_call}; median/p90 {dist}; hot cache {hot}")
     log(f"[bench] per-call pair us {per_call}; calls: " + ", ".join(
         f"{k} {v['t'] / v['launches'] * 1e6:.3f} us" for k, v in kern.items()))
 
@@ -485,6 +519,10 @@ def main():
             "weight_sets_rotated": h["n_sets"],
             "hipgraph": True,
             "us_per_pair": per_call,
+            "us_per_pair_median_p90": dist,
+            "us_per_pair_hot_cache": hot,
+            "hot_cache_note": "one weight set replayed: cache, not HBM (context only)",
+            "lib_sha256": lib_sha256(gq8.LIB_PATH),
             "baseline_note": "vs_baseline divides by the HC-Q8 page's Arc Pro B70 Q8_0 read times "
                              "(24.7/29.3/34.4 us at T=1/4/6): another machine, context only",
         },
