@@ -50,3 +50,27 @@ def test_bf16_pair_replay_with_poisoned_workspace(gpu):
         lo, rs, out, _ = _bf16_pair(gpu, *args, ws=ws)
         torch.cuda.synchronize()
         assert torch.equal(lo, lo0) and torch.equal(rs, rs0) and torch.equal(out, out0)
+
+
+def test_bf16_pair_graph_replay(gpu):
+    T, Nlr, Khc = 6, 320, 16384
+    d = synth.hc_inputs(T, K=Khc, N=Nlr, seed=52)
+    w = synth.hc_weights_bf16(K=Khc, N=Nlr, seed=52)
+    wd, R, wn, wu = to_dev(w["w_down"]), to_dev(d["R"]), to_dev(d["w_norm"]), to_dev(w["w_up"])
+    lo0, rs0, out0, ws = _bf16_pair(gpu, wd, R, wn, wu, T, Nlr, Khc)
+    torch.cuda.synchronize()
+    nb = ws.numel()
+    lo, rs, out = torch.empty_like(lo0), torch.empty_like(rs0), torch.empty_like(out0)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            gpu.gq8_hc_bf16_pair(wd, R, wn, 1e-6, wu, lo, rs, out, T, Nlr, Khc, ws, nb, s)
+    for _ in range(3):
+        lo.zero_(); rs.zero_(); out.zero_()
+        ws.fill_(0xFF)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(lo, lo0) and torch.equal(rs, rs0) and torch.equal(out, out0)

@@ -247,3 +247,38 @@ def test_moe_flags(gpu, T, E, topk, D, F):
     y_ref, S = moe_forward(quantize_q8_1_bf16(inp["x"]), ids_ref, p_ref, blocks, h_q8_1=True)
     check_bf16(to_host(o[2], np.uint16), y_ref, S, f"moe q8_1(h) T={T} D={D} F={F}")
     assert not torch.equal(o[2], out)                           # a different read
+
+
+def test_moe_graph_replay(gpu):
+    """The routed calls (each flag combination) captured into one hipGraph and replayed, with
+    eager work and a poisoned workspace between replays: every replay equals the eager output."""
+    T, E, topk, D, F = 4, 64, 8, 2048, 512
+    out, (xq, xd, ids, w, agu, adn, ws, nb) = _moe_case(gpu, T, E, topk, D, F, seed=48)
+    xb = to_dev(synth.moe_inputs(T=T, E=E, D=D, seed=48)["x"])
+    flags = (0, gpu.MOE_X_BF16, gpu.MOE_H_Q8_1, gpu.MOE_X_BF16 | gpu.MOE_H_Q8_1)
+    outs = [torch.empty_like(out) for _ in flags]
+
+    def calls(stream=None):
+        for f, o in zip(flags, outs):
+            xx, xs = (xb, None) if f & gpu.MOE_X_BF16 else (xq, xd)
+            gpu.gq8_moe_q8_0_routed_flags(xx, xs, ids, w, agu, adn, o, T, topk, E, D, F, f, ws, nb, stream)
+
+    calls()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    assert torch.equal(ref[0], out)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            calls(s)
+    for _ in range(3):
+        for o in outs:
+            o.zero_()
+        ws.fill_(0xA5)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+        torch.cuda.synchronize()
+        for o, r in zip(outs, ref):
+            assert torch.equal(o, r)

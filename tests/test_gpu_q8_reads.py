@@ -305,3 +305,28 @@ def test_pair_widest_low_rank(gpu, T, Nlr, Khc):
     assert np.allclose(to_host(rs), rs_ref, rtol=1e-5, atol=0)
     out_ref, S_up = hc_up(to_host(lo, np.uint16), quantize_q8_0(d["w_up"]))
     check_bf16(to_host(out, np.uint16), out_ref, S_up, f"pair up T={T} Nlr={Nlr}")
+
+
+def test_gemv_mfma_graph_replay(gpu):
+    """The T >= 5 GEMV (slab partials in the workspace, then the combine) in a hipGraph: replays
+    with the workspace poisoned in between equal the eager result."""
+    T, N, K = 8, 1024, 4096
+    w = synth.normal_f32(13, "gpu.gemv.g.w", (N, K), 0.0, 0.02)
+    x = to_dev(synth.normal_f32(13, "gpu.gemv.g.x", (T, K)))
+    wb = q8_0_from_f32(to_dev(w))
+    y0, ws, nb = _gemv(gpu, wb, x, T, N, K)
+    torch.cuda.synchronize()
+    y = torch.empty_like(y0)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            gpu.gq8_q8_0_gemv(wb, x, y, T, N, K, ws, nb, s)
+    for _ in range(3):
+        y.zero_()
+        ws.fill_(0xFF)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y0)
