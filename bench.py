@@ -101,19 +101,30 @@ def time_region(torch, stream, fn):
     return e0.elapsed_time(e1) * 1e-3       # seconds
 
 
+def code_digest(root, files):
+    """sha256 of the sources' code: comments and whitespace removed, so that a change to the
+    comments alone keeps the digest and any change to the code changes it."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in files:
+        text = open(os.path.join(root, f)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
+
+
 def recorded_traffic():
     """HBM bytes per pair call from the committed FETCH_SIZE / WRITE_SIZE summary, or None when
-    the kernel sources have changed since those counters were taken."""
-    import hashlib
+    the kernel code has changed since those counters were taken."""
     root = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(root, "profiles", "hc_pair_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    h = hashlib.sha256()
-    for f in rec["sources"]:
-        h.update(open(os.path.join(root, f), "rb").read())
-    return rec["traffic_bytes_per_pair_call"] if h.hexdigest() == rec["kernel_sources_sha256"] else None
+    ok = code_digest(root, rec["sources"]) == rec["kernel_code_sha256"]
+    return rec["traffic_bytes_per_pair_call"] if ok else None
 
 
 def n_sets_for(nbytes, multiple=1):

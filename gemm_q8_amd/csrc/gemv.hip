@@ -1,21 +1,27 @@
 // Q8_0 reads (HC-Q8 page, "What changed"): the Q8_0 matrix-vector product with fp32 x, the fused
-// RMSNorm + Q8_0 hyper-connection down read and the Q8_0 up read.
+// RMSNorm + Q8_0 hyper-connection down read, the Q8_0 up read, the two as one call, and the same
+// pair on BF16 weights (the comparison read the Q8_0 read replaces).
 //
-// Every weight byte is read once from HBM with 16-byte non-temporal loads. Each wave issues all
-// of its loads (clamped to valid addresses, never behind a branch) before its first arithmetic,
-// so a wave costs one memory latency, not one per load; a kernel launch costs more than most of
-// these reads, so each operation is one kernel where the shape allows it.
+// Every weight byte is read once from HBM with 16-byte non-temporal loads. Each wave issues its
+// loads (clamped to valid addresses, never behind a branch) before its first arithmetic, in the
+// order the work consumes them (a wave's loads complete in issue order), so a wave costs about
+// one memory latency; a kernel launch costs more than most of these reads, so each operation is
+// one or two kernels.
 //
-//  * GEMV (fp32 x): a work-group owns RW rows and all of K; wave w reads 1024-column chunks
-//    w, w+NW, ... (one 1 KiB contiguous load per row per chunk); lane partials are reduced over
-//    the wave (DPP) and the waves' sums are added through LDS in wave order. No split-K.
-//  * down read: 32 rows x 32 columns (one Q8_0 block) per bf16 MFMA pair. u = R * w_norm is
-//    exact in fp32 (8-bit x 8-bit significands) and is split exactly into bf16 hi + lo, so the
-//    MFMA products are exact. A work-group holds up to 16 row tiles and one 128-column slab and
-//    stages u (and the slab's sums of R^2) in LDS once for all of them. The partial sums of the
-//    K slabs go to the workspace; a second kernel adds them in ascending slab order, applies
-//    rs = 1/sqrt(mean R^2 + eps) and rounds to bf16.
-//  * up read: lo is bf16, exact as an MFMA operand; one wave owns 32 rows and all of K.
+//  * GEMV, T <= 4 (gemv_rows_kernel): a work-group owns RW rows and all of K; wave w reads
+//    1024-column chunks w, w+NW, ...; lane partials are reduced over the wave (DPP) and the
+//    waves' sums are added through LDS in wave order. T >= 5: the down read's slab kernel with
+//    x split into bf16 hi + lo as the MFMA A operand, then the combine kernel without rs.
+//  * down read (hc_down_partial_kernel): a work-group takes a 512-column slab x 64 rows, one
+//    16-row 16x16x32 bf16 MFMA tile per wave. u = R * w_norm is exact in fp32 (8-bit x 8-bit
+//    significands) and splits exactly into bf16 hi + lo, so the MFMA products are exact; it is
+//    staged once per work-group in LDS. The wave's weight tile goes through an LDS transpose in
+//    four column quarters. The slab partial sums and sums of R^2 go to the workspace, and a
+//    combine (hc_down_combine_kernel, or inside the up kernel for small T) adds them in a fixed
+//    order, applies rs = 1/sqrt(mean R^2 + eps) and rounds to bf16.
+//  * up read (hc_up_direct_kernel): one wave per 16 output rows over K = 320 columns; the weight
+//    loads become MFMA operands directly through v_permlane32_swap (no LDS). hc_pair_up_kernel
+//    adds the down read's combine in four extra waves of the same work-group.
 #include "gq8_device.h"
 #include "gq8_internal.h"
 
