@@ -145,7 +145,7 @@ int gq8_hc_q8_up(const void* w_split, const uint16_t* lo, uint16_t* out, int T, 
  *   lo  = gq8_hc_q8_down(w_down [Nlr][Khc], R [T][Khc], w_norm [Khc])     bf16 [T][Nlr]
  *   out = gq8_hc_q8_up(w_up [Khc][Nlr], lo)                                bf16 [T][Khc]
  * lo, rs_out and out are bitwise what the two separate calls produce. For Nlr == 320 and
- * T <= 2 the down read's combine of its split partial sums runs inside the up kernel (two kernel
+ * T <= 4 the down read's combine of its split partial sums runs inside the up kernel (two kernel
  * launches instead of three); otherwise the two calls' kernels run in sequence. lo is written (bf16
  * [T][Nlr], 16-byte aligned, required); rs_out fp32 [T] is nullable. T = 1..16, Khc % 32 == 0,
  * Nlr % 32 == 0, 0 < Nlr <= 1024. Workspace: gq8_workspace_bytes(GQ8_OP_HC_PAIR, T, Nlr, Khc). */
