@@ -58,7 +58,7 @@ int launch_hc_down(GemvArgs a, void* ws, hipStream_t st);
 // Q8_0 up read (bf16 x, K <= 1024): MFMA, one wave per 16 output rows, no workspace.
 int launch_hc_up(GemvArgs a, hipStream_t st);
 
-// the down read then the up read on its output; for an up depth of 320 and T <= 2 the down's
+// the down read then the up read on its output; for an up depth of 320 and T <= 4 the down's
 // combine runs inside the up kernel (two launches instead of three). dn.out = lo (bf16 [T][dn.N]).
 int launch_hc_pair(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st);
 
