@@ -18,7 +18,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .numerics import bf16_bits, f32
+from .numerics import bf16_bits, bf16_to_f32, f32, round_half_away
 
 
 def w8a8_acc(xq, W):
@@ -40,3 +40,21 @@ def w8a8_gemm(xq, x_scale, W, w_scale):
     """Returns (acc int64 [M, N], out bf16 bits [M, N])."""
     acc = w8a8_acc(xq, W)
     return acc, w8a8_epilogue(acc, x_scale, w_scale)
+
+
+def quantize_per_token(x_bits):
+    """Per-token int8 of a bf16 activation [M, K] (bit patterns): the x_q and x_scale the W8A8
+    operator takes, made on the device ahead of the product (the W8A8 page times the product
+    without it). The page fixes only the form (int8 per element, one fp32 scale per row);
+    reading: symmetric in the row's largest magnitude, all in fp32 --
+      amax = max_k |x[m, k]|,  x_scale = amax / 127,  inv = 127 / amax  (0 when amax = 0),
+      x_q = clamp(round_half_away(x * inv), -127, 127)
+    (one rounded division per row, then one rounded product per element). Returns (x_q int8
+    [M, K], x_scale float32 [M])."""
+    x = bf16_to_f32(x_bits).astype(np.float32)
+    amax = np.max(np.abs(x), axis=1).astype(np.float32) if x.shape[1] else np.zeros(x.shape[0], np.float32)
+    xs = f32(amax / np.float32(127))
+    pos = amax > 0
+    inv = np.where(pos, f32(np.float32(127) / np.where(pos, amax, np.float32(1))), np.float32(0))
+    q = round_half_away(f32(x * f32(inv)[:, None]))
+    return np.clip(q, -127, 127).astype(np.int8), xs

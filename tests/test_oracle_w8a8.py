@@ -49,3 +49,38 @@ def test_gemm_shapes_and_int32_range():
     d = synth.w8a8_inputs(16, 48, 256)
     acc, out = w8a8_gemm(d["xq"], d["x_scale"], d["W"], d["w_scale"])
     assert acc.shape == (16, 48) and out.shape == (16, 48) and out.dtype == np.uint16
+
+
+# ---- per-token quantization of a bf16 activation
+
+def test_per_token_quantization_bounds_and_extremes():
+    from oracle.numerics import bf16_bits, bf16_to_f32
+    from oracle.w8a8 import quantize_per_token
+    x = synth.bf16_normal(20, "pin.w8.xq", (5, 256))
+    q, xs = quantize_per_token(x)
+    xf = bf16_to_f32(x).astype(np.float64)
+    amax = np.max(np.abs(xf), axis=1)
+    assert np.array_equal(xs, (amax / 127).astype(np.float32))
+    # the largest magnitude of each row maps to +-127, every code is within the row's range
+    for m in range(5):
+        k = int(np.argmax(np.abs(xf[m])))
+        assert abs(int(q[m, k])) == 127 and np.sign(q[m, k]) == np.sign(xf[m, k])
+    # dequantization error: at most half a scale (plus the rounded products' slack)
+    err = np.abs(q.astype(np.float64) * xs[:, None].astype(np.float64) - xf)
+    assert np.all(err <= xs[:, None] * (0.5 + 1e-5))
+    # a zero row: scale 0, quants 0; a row scaled by a power of two keeps its quants
+    z, zs = quantize_per_token(np.zeros((1, 64), np.uint16))
+    assert zs[0] == 0 and not z.any()
+    x4 = bf16_bits(bf16_to_f32(x) * np.float32(4.0))
+    q4, xs4 = quantize_per_token(x4)
+    assert np.array_equal(q4, q) and np.array_equal(xs4, 4 * xs)
+
+
+def test_per_token_quantization_ties_go_away_from_zero():
+    from oracle.numerics import bf16_bits
+    from oracle.w8a8 import quantize_per_token
+    # amax = 127 makes inv = 1 exactly: x = j + 0.5 are exact ties
+    row = np.array([127.0, 0.5, -0.5, 2.5, -2.5, 126.5, -126.5, 3.0], np.float32)
+    q, xs = quantize_per_token(bf16_bits(row)[None, :])
+    assert xs[0] == np.float32(1.0)
+    assert q[0].tolist() == [127, 1, -1, 3, -3, 127, -127, 3]
