@@ -352,6 +352,26 @@ def bench_w8a8_sweep(torch, gq8, synth, dev, timed, emit, ms):
         us = timed(lambda i: (lambda s, w=wps[i % n]: gq8.gq8_w8a8_gemm(xq, xs, w, wsc, out, M, N, K, wsp, nb, s)), n)
         emit({"workload": "W8A8", "M": M, "N": N, "K": K, "us_per_call": round(us, 3),
               "weight_GBps": round(N * K / us / 1e3, 1)})
+        # the same product on a bf16 x: per-token quantization inside the product kernel, against
+        # the quantize kernel followed by the int8 product
+        db = synth.w8a8_bf16_inputs(M, N, K)
+        xb = to_dev(db["x"])
+        xq2 = torch.empty((M, K), dtype=torch.int8, device=dev)
+        xs2 = torch.empty((M,), dtype=torch.float32, device=dev)
+        nbx = gq8.gq8_workspace_bytes(gq8.OP_W8A8_BF16X, M, N, K)
+        wsx = workspace(nbx)
+        us = timed(lambda i: (lambda s, w=wps[i % n]: gq8.gq8_w8a8_gemm_bf16x(
+            xb, w, wsc, out, None, None, M, N, K, wsx, nbx, s)), n)
+        emit({"workload": "W8A8 on a bf16 x" + (" (per-token quantization fused)" if nbx == 0 else
+                                                " (two kernels, staged in the workspace)"),
+              "M": M, "N": N, "K": K, "us_per_call": round(us, 3), "weight_GBps": round(N * K / us / 1e3, 1)})
+
+        def two(s, w):
+            gq8.gq8_quantize_per_token(xb, M, K, xq2, xs2, s)
+            gq8.gq8_w8a8_gemm(xq2, xs2, w, wsc, out, M, N, K, wsp, nb, s)
+        us = timed(lambda i: (lambda s, w=wps[i % n]: two(s, w)), n)
+        emit({"workload": "W8A8 on a bf16 x (quantize kernel, then the product)", "M": M, "N": N,
+              "K": K, "us_per_call": round(us, 3), "weight_GBps": round(N * K / us / 1e3, 1)})
         del wps
 
 

@@ -98,6 +98,12 @@ static bool q8_shape_ok(int T, int N, int K) {
     return T >= 0 && T <= kMaxT && N >= 0 && K >= 0 && K % 32 == 0;
 }
 
+// x_q staging of the bf16-activation product when it runs as two kernels: x_q [M][K] at 0, then
+// x_scale [M] at the next 256-byte boundary
+static size_t bf16x_stage_bytes(int M, int K) {
+    return (((size_t)M * K + 255) & ~(size_t)255) + (size_t)M * sizeof(float);
+}
+
 GQ8_EXPORT size_t gq8_workspace_counter_bytes(int op, int rows, int N, int K) {
     (void)op; (void)rows; (void)N; (void)K;
     return 0;   // no operation keeps arrival counters: split sums are combined by a second kernel
@@ -112,6 +118,10 @@ GQ8_EXPORT size_t gq8_workspace_bytes(int op, int rows, int N, int K) {
         case GQ8_OP_Q8_0_GEMV:
             if (!q8_shape_ok(rows, N, K)) return 0;
             return gemv_workspace_bytes(rows, N, K);
+        case GQ8_OP_W8A8_BF16X:
+            if (rows <= 0 || N <= 0 || K <= 0 || rows > kMaxM || K % 16 != 0 || bf16x_fused(rows, K))
+                return 0;
+            return bf16x_stage_bytes(rows, K);
         case GQ8_OP_HC_UP:
         case GQ8_OP_W8A8:
         default:
@@ -282,6 +292,57 @@ static int w8a8_common(const int8_t* xq, const float* xs, const int8_t* wp, cons
     if (!aligned16(xq) || !aligned16(wp)) return GQ8_EALIGN;
     if (device_cus() == 0) return GQ8_ENODEV;
     return launch_w8a8(plan_w8a8(M, N, K), xq, xs, wp, wsc, out, i32, M, N, K, S(stream));
+}
+
+GQ8_EXPORT int gq8_quantize_per_token(const uint16_t* x, int M, int K, int8_t* xq, float* xs,
+                                      void* stream) {
+    if (M < 0 || K < 0) return GQ8_EINVAL;
+    if (K % 16 != 0) return GQ8_ESHAPE;
+    if (M == 0) return GQ8_OK;
+    if (xs == nullptr || (K > 0 && (x == nullptr || xq == nullptr))) return GQ8_EINVAL;
+    if (K > 0 && (!aligned16(x) || !aligned16(xq))) return GQ8_EALIGN;
+    if (device_cus() == 0) return GQ8_ENODEV;
+    if (K == 0) return launch_fill_zero(xs, (size_t)M * sizeof(float), S(stream));
+    return launch_per_token_quantize(x, M, K, xq, xs, S(stream));
+}
+
+GQ8_EXPORT int gq8_w8a8_gemm_bf16x(const uint16_t* x, const int8_t* W_packed, const float* w_scale,
+                                   uint16_t* out, int8_t* xq_out, float* xs_out, int M, int N,
+                                   int K, void* ws, size_t ws_bytes, void* stream) {
+    if (M < 0 || N < 0 || K < 0) return GQ8_EINVAL;
+    if (M > kMaxM || K % 16 != 0 || K > kW8MaxK) return GQ8_ESHAPE;
+    if (M == 0 || N == 0) return GQ8_OK;
+    if (out == nullptr) return GQ8_EINVAL;
+    if (K == 0) {
+        if (device_cus() == 0) return GQ8_ENODEV;
+        if (xs_out != nullptr) {
+            const int rc = launch_fill_zero(xs_out, (size_t)M * sizeof(float), S(stream));
+            if (rc != GQ8_OK) return rc;
+        }
+        return launch_fill_zero(out, (size_t)M * N * 2, S(stream));
+    }
+    if (x == nullptr || W_packed == nullptr || w_scale == nullptr) return GQ8_EINVAL;
+    if (!aligned16(x) || !aligned16(W_packed) || (xq_out != nullptr && !aligned16(xq_out)))
+        return GQ8_EALIGN;
+    const bool fused = bf16x_fused(M, K);
+    if (!fused && (xq_out == nullptr || xs_out == nullptr)) {
+        const int rc = check_ws(ws, ws_bytes, bf16x_stage_bytes(M, K));
+        if (rc != GQ8_OK) return rc;
+    }
+    if (device_cus() == 0) return GQ8_ENODEV;
+    const W8Plan plan = plan_w8a8(M, N, K);
+    if (fused)
+        return launch_w8a8(plan, nullptr, nullptr, W_packed, w_scale, out, false, M, N, K,
+                           S(stream), x, xq_out, xs_out);
+    // larger x: the per-token quantize kernel, then the int8 product on its output
+    int8_t* xq = xq_out != nullptr ? xq_out : static_cast<int8_t*>(ws);
+    float* xs = xs_out != nullptr
+                    ? xs_out
+                    : reinterpret_cast<float*>(static_cast<char*>(ws) + bf16x_stage_bytes(M, K) -
+                                               (size_t)M * sizeof(float));
+    const int rc = launch_per_token_quantize(x, M, K, xq, xs, S(stream));
+    if (rc != GQ8_OK) return rc;
+    return launch_w8a8(plan, xq, xs, W_packed, w_scale, out, false, M, N, K, S(stream));
 }
 
 GQ8_EXPORT int gq8_w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* W_packed,

@@ -75,8 +75,16 @@ struct W8Plan {
     int kpw;           // k-steps per wave
 };
 W8Plan plan_w8a8(int M, int N, int K);
+// xb != nullptr: bf16 x quantized per token inside the kernel (xq, xs unused; bf16x_fused(M, K));
+// xq_out / xs_out (nullable) receive the quantized x from work-group 0. Each work-group
+// re-quantizes all of x, which pays while x is small (measured: up to 16384 values).
+constexpr int kFusedBf16xM = 8;
+constexpr int kFusedBf16xElems = 16384;
+inline bool bf16x_fused(int M, int K) { return M <= kFusedBf16xM && M * K <= kFusedBf16xElems; }
 int launch_w8a8(const W8Plan& p, const int8_t* xq, const float* xs, const int8_t* wp,
-                const float* ws_scale, void* out, bool i32_out, int M, int N, int K, hipStream_t st);
+                const float* ws_scale, void* out, bool i32_out, int M, int N, int K, hipStream_t st,
+                const uint16_t* xb = nullptr, int8_t* xq_out = nullptr, float* xs_out = nullptr);
+int launch_per_token_quantize(const uint16_t* x, int M, int K, int8_t* xq, float* xs, hipStream_t st);
 
 // ---------------------------------------------------------------- small kernels
 

@@ -21,7 +21,7 @@ LIB_PATH = _LIB_PATH
 
 OK, EINVAL, ESHAPE, EALIGN, EWORKSPACE, ECAPTURE, EHIP, ENODEV = 0, -1, -2, -3, -4, -5, -6, -7
 MOE_X_BF16, MOE_H_Q8_1 = 1, 2
-OP_Q8_0_GEMV, OP_HC_DOWN, OP_HC_UP, OP_W8A8, OP_HC_PAIR = 1, 2, 3, 4, 5
+OP_Q8_0_GEMV, OP_HC_DOWN, OP_HC_UP, OP_W8A8, OP_HC_PAIR, OP_W8A8_BF16X = 1, 2, 3, 4, 5, 6
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -50,6 +50,8 @@ _SIGS = {
     "gq8_w8a8_pack": (_I, [_P, _I, _I, _P, _P]),
     "gq8_w8a8_gemm": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_w8a8_gemm_i32": (_I, [_P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "gq8_quantize_per_token": (_I, [_P, _I, _I, _P, _P, _P]),
+    "gq8_w8a8_gemm_bf16x": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_moe_route": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "gq8_moe_plan_words": (_SZ, [_I, _I]),
     "gq8_moe_plan": (_I, [_P, _I, _I, _I, _P, _P]),
@@ -187,6 +189,17 @@ def gq8_w8a8_gemm(xq, x_scale, W_packed, w_scale, out, M, N, K, ws, ws_bytes, st
 def gq8_w8a8_gemm_i32(xq, W_packed, acc, M, N, K, ws, ws_bytes, stream=None):
     return _check("gq8_w8a8_gemm_i32", _lib.gq8_w8a8_gemm_i32(
         _ptr(xq), _ptr(W_packed), _ptr(acc), M, N, K, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def gq8_quantize_per_token(x, M, K, xq, xs, stream=None):
+    return _check("gq8_quantize_per_token", _lib.gq8_quantize_per_token(
+        _ptr(x), M, K, _ptr(xq), _ptr(xs), _stream(stream)))
+
+
+def gq8_w8a8_gemm_bf16x(x, W_packed, w_scale, out, xq_out, xs_out, M, N, K, ws, ws_bytes, stream=None):
+    return _check("gq8_w8a8_gemm_bf16x", _lib.gq8_w8a8_gemm_bf16x(
+        _ptr(x), _ptr(W_packed), _ptr(w_scale), _ptr(out), _ptr(xq_out), _ptr(xs_out), M, N, K,
+        _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def gq8_moe_route(logits, T, E, topk, ids, weights, stream=None):

@@ -112,6 +112,18 @@ def w8a8_inputs(M, N, K, seed=0):
     }
 
 
+def w8a8_bf16_inputs(M, N, K, seed=0):
+    """W8A8 on a bf16 activation: x bf16 [M,K] ~ N(0,1) times a per-row factor U(0.05, 20) (rows
+    of different magnitude), W int8 [K,N], w_scale U(1e-3,1e-2)."""
+    rowf = uniform_f32(seed, "w8a8b.rowf", (M, 1), 0.05, 20.0)
+    x = (normal_f32(seed, "w8a8b.x", (M, K)) * rowf).astype(np.float32)
+    return {
+        "x": (x.view(np.uint32) >> np.uint32(16)).astype(np.uint16),
+        "W": int8_uniform(seed, "w8a8.W", (K, N)),
+        "w_scale": uniform_f32(seed, "w8a8.w_scale", (N,), 1e-3, 1e-2),
+    }
+
+
 def moe_expert_weights(e, D=2048, F=512, seed=0):
     """Expert e's fp32 weights: gate/up [2F, D] (gate rows first) and down [D, F]."""
     return {

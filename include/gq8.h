@@ -47,7 +47,8 @@ enum gq8_op {
     GQ8_OP_HC_DOWN = 2,
     GQ8_OP_HC_UP = 3,
     GQ8_OP_W8A8 = 4,
-    GQ8_OP_HC_PAIR = 5     /* rows = T, N = Nlr, K = Khc of gq8_hc_q8_pair */
+    GQ8_OP_HC_PAIR = 5,    /* rows = T, N = Nlr, K = Khc of gq8_hc_q8_pair */
+    GQ8_OP_W8A8_BF16X = 6  /* rows = M of gq8_w8a8_gemm_bf16x */
 };
 
 /* Static string for a status code. Host only. */
@@ -184,6 +185,30 @@ int gq8_w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* W_packed
  * Both W8A8 calls: M = 0..32, K % 16 == 0, K <= 8192 (GQ8_ESHAPE above), no workspace. */
 int gq8_w8a8_gemm_i32(const int8_t* xq, const int8_t* W_packed, int32_t* acc, int M, int N,
                       int K, void* ws, size_t ws_bytes, void* stream);
+
+/* Per-token int8 of a bf16 activation: the x_q and x_scale the W8A8 product takes (W8A8 page,
+ * operator statement: int8 activation rows with one fp32 scale per row; the page does not say
+ * how they are made, and the reading here is symmetric in each row's largest magnitude):
+ *   amax = max_k |x[m][k]|, xs[m] = amax / 127, inv = 127 / amax (both 0 when amax == 0),
+ *   xq[m][k] = clamp(round_half_away(x[m][k] * inv), -127, 127),
+ * each quotient and product rounded to nearest-even fp32 (no fused multiply-add).
+ * x bf16 [M][K], xq int8 [M][K] (both 16-byte aligned), xs fp32 [M]. M >= 0, K % 16 == 0;
+ * K == 0 writes xs = 0. Errors: GQ8_EINVAL (negative size, null pointer), GQ8_ESHAPE,
+ * GQ8_EALIGN, GQ8_ENODEV. */
+int gq8_quantize_per_token(const uint16_t* x, int M, int K, int8_t* xq, float* xs, void* stream);
+
+/* W8A8 on a bf16 activation: gq8_quantize_per_token(x), then gq8_w8a8_gemm on its x_q / x_scale.
+ * out is bit-identical to that pair of calls. M <= 8 and M * K <= 16384: ONE kernel, in which
+ * every work-group quantizes x into LDS while its weight tile streams in (no x_q round trip
+ * through memory). Otherwise the two kernels, x_q / x_scale staged in xq_out / xs_out when both
+ * are given, else in the workspace (gq8_workspace_bytes(GQ8_OP_W8A8_BF16X, M, N, K) bytes,
+ * 16-byte aligned; 0 for the one-kernel shapes). x bf16 [M][K] (16-byte aligned, finite); W_packed, w_scale, out, shapes and errors as
+ * gq8_w8a8_gemm (M = 0..32, K % 16 == 0, K <= 8192; K == 0 writes zeros and xs_out = 0), plus
+ * GQ8_EWORKSPACE. xq_out int8 [M][K] (16-byte aligned) and xs_out fp32 [M] are nullable: when
+ * given they receive that x_q and x_scale. */
+int gq8_w8a8_gemm_bf16x(const uint16_t* x, const int8_t* W_packed, const float* w_scale,
+                        uint16_t* out, int8_t* xq_out, float* xs_out, int M, int N, int K,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Routed experts (EP page, "What changed": q8_1 MoE input, the routed entries grouped by expert

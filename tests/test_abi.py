@@ -151,3 +151,37 @@ def test_moe_flags_argument_checks(lib):
                                          4, 8, 512, 2048, 512, 0, None, 0, None) == lib.EINVAL
     assert raw.gq8_moe_q8_0_routed_flags(dummy, None, dummy, dummy, dummy, dummy, dummy,
                                          4, 8, 512, 2048, 512, lib.MOE_X_BF16, None, 0, None) == lib.EWORKSPACE
+
+
+def test_per_token_argument_checks(lib):
+    raw = lib.raw()
+    dummy = 1 << 20  # never dereferenced
+    # K not a multiple of 16, a negative size, a null scale output, misaligned input / quants
+    assert raw.gq8_quantize_per_token(dummy, 4, 40, dummy, dummy, None) == lib.ESHAPE
+    assert raw.gq8_quantize_per_token(dummy, -1, 64, dummy, dummy, None) == lib.EINVAL
+    assert raw.gq8_quantize_per_token(dummy, 4, 64, dummy, None, None) == lib.EINVAL
+    assert raw.gq8_quantize_per_token(dummy + 2, 4, 64, dummy, dummy, None) == lib.EALIGN
+    assert raw.gq8_quantize_per_token(dummy, 4, 64, dummy + 8, dummy, None) == lib.EALIGN
+    assert raw.gq8_quantize_per_token(None, 0, 64, None, None, None) == lib.OK
+    # fused product: M above 32, K off 16 or above 8192, a null weight, misaligned x / x_q out
+    args = lambda x, xq, M, K: (x, dummy, dummy, dummy, xq, dummy, M, 16, K, None, 0, None)  # noqa: E731
+    assert raw.gq8_w8a8_gemm_bf16x(*args(dummy, None, 33, 64)) == lib.ESHAPE
+    assert raw.gq8_w8a8_gemm_bf16x(*args(dummy, None, 4, 40)) == lib.ESHAPE
+    assert raw.gq8_w8a8_gemm_bf16x(*args(dummy, None, 4, 8192 + 16)) == lib.ESHAPE
+    assert raw.gq8_w8a8_gemm_bf16x(None, dummy, dummy, dummy, None, None, 4, 16, 64,
+                                   None, 0, None) == lib.EINVAL
+    assert raw.gq8_w8a8_gemm_bf16x(dummy, None, dummy, dummy, None, None, 4, 16, 64,
+                                   None, 0, None) == lib.EINVAL
+    assert raw.gq8_w8a8_gemm_bf16x(*args(dummy + 2, None, 4, 64)) == lib.EALIGN
+    assert raw.gq8_w8a8_gemm_bf16x(*args(dummy, dummy + 4, 4, 64)) == lib.EALIGN
+    assert raw.gq8_w8a8_gemm_bf16x(*args(None, None, 0, 64)) == lib.OK
+    # past 8 rows or 16384 values x_q / x_scale are staged: in both outputs, else in a workspace
+    assert lib.gq8_workspace_bytes(lib.OP_W8A8_BF16X, 4, 1536, 4096) == 0
+    assert lib.gq8_workspace_bytes(lib.OP_W8A8_BF16X, 8, 1536, 2048) == 0
+    assert lib.gq8_workspace_bytes(lib.OP_W8A8_BF16X, 8, 1536, 4096) == 8 * 4096 + 8 * 4
+    assert lib.gq8_workspace_bytes(lib.OP_W8A8_BF16X, 16, 1536, 4096) == 16 * 4096 + 16 * 4
+    assert lib.gq8_workspace_bytes(lib.OP_W8A8_BF16X, 9, 8, 48) == 512 + 9 * 4
+    assert raw.gq8_w8a8_gemm_bf16x(dummy, dummy, dummy, dummy, None, None, 16, 16, 64,
+                                   None, 0, None) == lib.EWORKSPACE
+    assert raw.gq8_w8a8_gemm_bf16x(dummy, dummy, dummy, dummy, dummy, None, 16, 16, 64,
+                                   dummy, 16 * 64, None) == lib.EWORKSPACE
