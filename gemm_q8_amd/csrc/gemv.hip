@@ -8,7 +8,9 @@
 // one memory latency; a kernel launch costs more than most of these reads, so each operation is
 // one or two kernels.
 //
-//  * GEMV, T <= 4 (gemv_rows_kernel): a work-group owns RW rows and all of K; wave w reads
+//  * GEMV, T <= 3 and K <= 4096 (gemv_wave_kernel): one wave owns one or two whole rows, lane
+//    partials over its chunks, one wave sum (DPP, then the 16- and 32-lane swaps), no LDS.
+//    Other T <= 4 (gemv_rows_kernel): a work-group owns RW rows and all of K; wave w reads
 //    1024-column chunks w, w+NW, ...; lane partials are reduced over the wave (DPP) and the
 //    waves' sums are added through LDS in wave order. T >= 5: the down read's slab kernel with
 //    x split into bf16 hi + lo as the MFMA A operand, then the combine kernel without rs.
@@ -120,6 +122,71 @@ __global__ void __launch_bounds__(64 * MAXW) gemv_rows_kernel(GemvArgs a) {
     }
 }
 
+// T <= 3, K <= 4096: one wave per work-group owns RW whole rows. Lane l takes columns
+// 1024c + 16l of every chunk c: x for all of K and the RW rows' weights are loaded up front (x
+// first), each lane sums its chunks in order, and one wave sum per (row, token) ends the work:
+// no LDS, no barrier (a cross-wave sum through LDS and a barrier cost more than the extra x
+// reads of wave-owned rows here).
+template <int T, int RW, int NCH>
+__global__ void __launch_bounds__(64) gemv_wave_kernel(GemvArgs a) {
+    const int lane = threadIdx.x;
+    const int N = a.N, K = a.K, nblk = K >> 5;
+    const int row0 = blockIdx.x * RW;
+    const float* x = reinterpret_cast<const float*>(a.x);
+    float xv[T][NCH][16];
+    int kc[NCH];
+    bool kok[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int k = c * 1024 + lane * 16;
+        kok[c] = k < K;                                   // K % 32 == 0: k + 16 <= K
+        kc[c] = kok[c] ? k : K - 16;
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) load16_f32(x + (size_t)t * K + kc[c], xv[t][c]);
+    u32x4 wq[RW][NCH];
+    uint16_t wd[RW][NCH];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+        const int row = imin(row0 + r, N - 1);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            wd[r][c] = a.d[(size_t)row * nblk + (kc[c] >> 5)];
+            wq[r][c] = ld_nt16(a.q + (size_t)row * K + kc[c]);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            float acc = 0.f;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)       // a clamped chunk (k >= K) gets scale 0
+                acc = fmaf(dot16_i8_f32(wq[r][c], xv[t][c]), kok[c] ? h2f(wd[r][c]) : 0.f, acc);
+            const float v = wave_sum_swap(acc);
+            if (lane == r * T + t && row0 + r < N) reinterpret_cast<float*>(a.out)[(size_t)t * N + row0 + r] = v;
+        }
+}
+
+template <int T, int RW>
+static void launch_gemv_wave_rw(GemvArgs a, hipStream_t st) {
+    const dim3 g((a.N + RW - 1) / RW), b(64);
+    switch ((a.K + 1023) / 1024) {
+        case 1: hipLaunchKernelGGL((gemv_wave_kernel<T, RW, 1>), g, b, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((gemv_wave_kernel<T, RW, 2>), g, b, 0, st, a); break;
+        case 3: hipLaunchKernelGGL((gemv_wave_kernel<T, RW, 3>), g, b, 0, st, a); break;
+        default: hipLaunchKernelGGL((gemv_wave_kernel<T, RW, 4>), g, b, 0, st, a); break;
+    }
+}
+
+// wave-owned rows up to this many tokens and this depth (measured at 1024 x 4096: T = 1 / 2 / 3
+// 3.16 / 3.73 / 4.58 us against 3.50 / 4.04 / 4.89 with the work-group kernel; T = 4 spills)
+constexpr int kGemvWaveMaxT = 3;
+constexpr int kGemvWaveMaxK = 4096;
+
 template <int T> constexpr int gemv_rw() { return T == 2 ? 4 : (T <= 4 ? 2 : 1); }
 
 // From this many token rows on, the GEMV runs on MFMA (the down read's slab kernel with x as the
@@ -134,6 +201,12 @@ template <int T>
 static int launch_gemv_t(GemvArgs a, void* ws, hipStream_t st) {
     if constexpr (T >= kGemvMfmaT) {
         if (a.K > 0) return launch_gemv_mfma_t<T>(a, ws, st);
+    }
+    if constexpr (T <= kGemvWaveMaxT) {
+        if (a.K <= kGemvWaveMaxK) {
+            launch_gemv_wave_rw<T, (T == 1 ? 1 : 2)>(a, st);
+            return launch_status();
+        }
     }
     constexpr int RW = gemv_rw<T>();
     int nw = (a.K + 1023) / 1024;

@@ -134,4 +134,19 @@ GQ8_DEV float wave_sum(float v) {
     return v;
 }
 
+// The same sum without LDS: the DPP steps within each 16-lane row, then v_permlane16_swap and
+// v_permlane32_swap (gfx950) bring in the other rows; every lane gets the same bits.
+GQ8_DEV float wave_sum_swap(float v) {
+    v += dpp_mov<0xB1>(v);
+    v += dpp_mov<0x4E>(v);
+    v += dpp_mov<0x141>(v);
+    v += dpp_mov<0x140>(v);
+    const int lane = threadIdx.x & 63;
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v += __uint_as_float((lane & 16) ? r[0] : r[1]);          // the neighbouring 16-lane row
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v += __uint_as_float((lane & 32) ? h[0] : h[1]);          // the other 32-lane half
+    return v;
+}
+
 }  // namespace gq8

@@ -24,7 +24,9 @@ def _gemv(gpu, wbuf, x, T, N, K):
 
 
 @pytest.mark.parametrize("T,N,K", [(1, 96, 4096), (3, 37, 1056), (5, 130, 2080), (8, 64, 96),
-                                   (11, 33, 320), (16, 70, 4096), (2, 5, 32), (4, 300, 1024)])
+                                   (11, 33, 320), (16, 70, 4096), (2, 5, 32), (4, 300, 1024),
+                                   (2, 77, 3104), (3, 9, 2080), (1, 1, 64), (2, 1, 4096),
+                                   (1, 333, 4064), (3, 130, 4096)])
 def test_gemv_matches_oracle(gpu, T, N, K):
     w = synth.normal_f32(10, "gpu.gemv.w", (N, K), 0.0, 0.02)
     x = synth.normal_f32(10, "gpu.gemv.x", (T, K))
@@ -54,6 +56,24 @@ def test_gemv_one_hot_is_exact(gpu):
     for t, k in enumerate(ks):
         want = fp16_to_f32(b.d[:, k // 32]) * b.q[:, k // 32, k % 32].astype(np.float32)
         assert np.array_equal(y[t], want)
+
+
+@pytest.mark.parametrize("N,K", [(31, 4096), (7, 2080)])
+def test_gemv_one_hot_few_rows_is_exact(gpu, N, K):
+    """The wave-owned kernel (T <= 3): one-hot x gives d * q exactly (all other terms are zeros)."""
+    w = synth.normal_f32(12, "gpu.gemv.oh3", (N, K), 0.0, 0.02)
+    ks = [0, 1023, K - 1]
+    b = quantize_q8_0(w)
+    for T in (1, 2, 3):
+        x = np.zeros((T, K), np.float32)
+        for t in range(T):
+            x[t, ks[t]] = 1.0
+        y, _, _ = _gemv(gpu, q8_0_from_f32(to_dev(w)), to_dev(x), T, N, K)
+        y = to_host(y)
+        for t in range(T):
+            k = ks[t]
+            want = fp16_to_f32(b.d[:, k // 32]) * b.q[:, k // 32, k % 32].astype(np.float32)
+            assert np.array_equal(y[t], want), f"T={T} k={k}"
 
 
 def test_gemv_reads_the_scales(gpu):
