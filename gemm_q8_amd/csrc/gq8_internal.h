@@ -68,7 +68,7 @@ int launch_hc_bf16_pair(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st);
 // ---------------------------------------------------------------- W8A8
 
 struct W8Plan {
-    bool mfma;         // int8 MFMA path (M >= 16) or VALU dot4 path
+    bool mfma;         // int8 MFMA path (M >= 2) or VALU dot4 path (M == 1)
     int ntiles;        // N rounded up to 16, / 16: one work-group each
     int ksteps;        // K rounded up to 64, / 64
     int nw;            // waves per work-group (<= 16)
