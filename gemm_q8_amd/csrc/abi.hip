@@ -139,6 +139,13 @@ GQ8_EXPORT int gq8_workspace_init(void* ws, size_t bytes, void* stream) {
     return launch_fill_zero(ws, bytes, S(stream));
 }
 
+GQ8_EXPORT int gq8_workspace_check(const void* ws, size_t bytes, void* stream, int* nonzero_counters) {
+    (void)stream;
+    if (nonzero_counters == nullptr || (ws == nullptr && bytes > 0)) return GQ8_EINVAL;
+    *nonzero_counters = 0;      // gq8_workspace_counter_bytes() is 0 for every operation
+    return GQ8_OK;
+}
+
 // ---------------------------------------------------------------------------------- Q8_0 reads
 
 GQ8_EXPORT int gq8_q8_0_gemv(const void* w_split, const float* x, float* y, int T, int N, int K,

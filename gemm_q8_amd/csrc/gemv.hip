@@ -814,10 +814,12 @@ __global__ void __launch_bounds__(256) hc_up_bf16_kernel(GemvArgs a) {
 template <int T>
 static int launch_up_t(GemvArgs a, hipStream_t st) {
     const int ntile = (a.N + 15) / 16;
-    if (a.K % kUpCW == 0)
+    if (a.K % kUpCW == 0) {
         hipLaunchKernelGGL((hc_up_direct_kernel<T>), dim3((ntile + 3) / 4), dim3(256), 0, st, a);
-    else
+    } else {
+        GQ8_NOTE_GENERAL("up read: depth not a multiple of 320, general up kernel (LDS staged)");
         hipLaunchKernelGGL((hc_up_kernel<T>), dim3((ntile + 3) / 4), dim3(256), 0, st, a);
+    }
     return launch_status();
 }
 

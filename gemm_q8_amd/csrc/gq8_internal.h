@@ -2,12 +2,23 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stdio.h>
+
+#include <atomic>
 #include <stddef.h>
 #include <stdint.h>
 
 #include "../../include/gq8.h"
 
 #define GQ8_EXPORT extern "C" __attribute__((visibility("default")))
+
+// A shape outside the tuned set runs the general kernels of the same family (correct, slower):
+// said once per process and call site on stderr.
+#define GQ8_NOTE_GENERAL(msg)                                                                   \
+    do {                                                                                        \
+        static std::atomic<bool> said_{false};                                                  \
+        if (!said_.exchange(true)) fprintf(stderr, "gq8: %s\n", msg);                            \
+    } while (0)
 
 namespace gq8 {
 

@@ -804,6 +804,7 @@ int launch_moe_routed(const int8_t* xq, const uint16_t* xd, const uint16_t* xb, 
     // {256, 512, 1024} down)
     const bool token_dn = F == 256 || F == 512 || F == 1024;
     if (!rows_gu || !token_dn) {
+        GQ8_NOTE_GENERAL("routed experts: D > 4096 or F not in {256, 512, 1024}, plan-based general kernels");
         hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(256), 0, st, ids, a.P, E, plan);
         if ((rc = launch_status()) != GQ8_OK) return rc;
     }

@@ -51,6 +51,10 @@ _SIGS = {
     "gq8_w8a8_gemm": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_w8a8_gemm_i32": (_I, [_P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_quantize_per_token": (_I, [_P, _I, _I, _P, _P, _P]),
+    "gq8_q8_0_quantize_host": (_I, [_P, _I, _I, _P]),
+    "gq8_q8_0_split_from_blocks_host": (_I, [_P, _I, _I, _P]),
+    "gq8_q8_1_quantize_host": (_I, [_P, _I, _I, _P, _P, _P]),
+    "gq8_workspace_check": (_I, [_P, _SZ, _P, _P]),
     "gq8_w8a8_gemm_bf16x": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_moe_route": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "gq8_moe_plan_words": (_SZ, [_I, _I]),
@@ -80,6 +84,9 @@ def _ptr(x):
         return None
     if isinstance(x, int):
         return x
+    if hasattr(x, "__array_interface__"):        # numpy array on the host (the _host calls)
+        assert x.flags["C_CONTIGUOUS"], "host arrays must be contiguous"
+        return x.__array_interface__["data"][0]
     return x.data_ptr()
 
 
@@ -189,6 +196,28 @@ def gq8_w8a8_gemm(xq, x_scale, W_packed, w_scale, out, M, N, K, ws, ws_bytes, st
 def gq8_w8a8_gemm_i32(xq, W_packed, acc, M, N, K, ws, ws_bytes, stream=None):
     return _check("gq8_w8a8_gemm_i32", _lib.gq8_w8a8_gemm_i32(
         _ptr(xq), _ptr(W_packed), _ptr(acc), M, N, K, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def gq8_q8_0_quantize_host(w, rows, K, split_out):
+    return _check("gq8_q8_0_quantize_host", _lib.gq8_q8_0_quantize_host(_ptr(w), rows, K, _ptr(split_out)))
+
+
+def gq8_q8_0_split_from_blocks_host(blocks34, rows, K, split_out):
+    return _check("gq8_q8_0_split_from_blocks_host",
+                  _lib.gq8_q8_0_split_from_blocks_host(_ptr(blocks34), rows, K, _ptr(split_out)))
+
+
+def gq8_q8_1_quantize_host(x_bf16, rows, K, q, d, s=None):
+    return _check("gq8_q8_1_quantize_host",
+                  _lib.gq8_q8_1_quantize_host(_ptr(x_bf16), rows, K, _ptr(q), _ptr(d), _ptr(s)))
+
+
+def gq8_workspace_check(ws, nbytes, stream=None):
+    """Number of non-zero arrival counters of a workspace (no entry point keeps any: 0)."""
+    out = ctypes.c_int(-1)
+    _check("gq8_workspace_check", _lib.gq8_workspace_check(
+        _ptr(ws), nbytes, None if stream is None else _stream(stream), ctypes.addressof(out)))
+    return out.value
 
 
 def gq8_quantize_per_token(x, M, K, xq, xs, stream=None):

@@ -88,6 +88,16 @@ int gq8_q8_0_split_from_blocks(const void* blocks34, int rows, int K, void* w_sp
 int gq8_q8_1_quantize(const uint16_t* x_bf16, int rows, int K, int8_t* q, uint16_t* d,
                       uint16_t* s, void* stream);
 
+/* Host-side preparation: the same three operations on host memory in plain C++ (no device,
+ * stream or HIP call), for loaders that prepare weights before upload (HC-Q8 page, "What
+ * changed": the loader quantizes a BF16 tensor to Q8_0 at load and uploads the split layout).
+ * Byte-identical to gq8_q8_0_quantize, gq8_q8_0_split_from_blocks and gq8_q8_1_quantize.
+ * Errors: GQ8_EINVAL (negative size, null pointer), GQ8_ESHAPE (K % 32 != 0). */
+int gq8_q8_0_quantize_host(const float* w, int rows, int K, void* split_out);
+int gq8_q8_0_split_from_blocks_host(const void* blocks34, int rows, int K, void* split_out);
+int gq8_q8_1_quantize_host(const uint16_t* x_bf16, int rows, int K, int8_t* q, uint16_t* d,
+                           uint16_t* s);
+
 /* ------------------------------------------------------------------------------------------
  * Workspace: device scratch that a compute call needs beyond its inputs and outputs.
  *   - size it with gq8_workspace_bytes() for the exact (op, rows, N, K) of the call; 0 means the
@@ -107,6 +117,12 @@ int gq8_q8_1_quantize(const uint16_t* x_bf16, int rows, int K, int8_t* q, uint16
 size_t gq8_workspace_bytes(int op, int rows, int N, int K);
 size_t gq8_workspace_counter_bytes(int op, int rows, int N, int K);
 int gq8_workspace_init(void* ws, size_t bytes, void* stream);
+/* Debug check of a workspace's arrival counters: *nonzero_counters = how many are not zero. No
+ * entry point keeps arrival counters (split sums are combined by a second kernel or inside the
+ * consuming kernel, in a fixed order), so the count is 0 and nothing is read; it is kept for
+ * callers written against a counter-based workspace contract. Errors: GQ8_EINVAL (null
+ * nonzero_counters, or null ws with bytes > 0). */
+int gq8_workspace_check(const void* ws, size_t bytes, void* stream, int* nonzero_counters);
 
 /* Q8_0 matrix-vector product for T = 1..16 token rows (HC-Q8 page, "What changed": w = d*q,
  * exact in fp32):
