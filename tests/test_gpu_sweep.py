@@ -1,6 +1,7 @@
 """GPU parity over seeded random shapes within each entry point's limits (Q8_0 GEMV, the HC down
-and up reads and the pair, W8A8, the routed experts), each against the oracle at the same pass
-rules as the fixed-shape tests, plus the zero-depth calls (outputs filled with zeros)."""
+and up reads and the pair, W8A8 on int8 and on bf16 activations, the per-token quantizer, the
+routed experts), each against the oracle at the same pass rules as the fixed-shape tests, plus
+the zero-depth calls (outputs filled with zeros)."""
 import numpy as np
 import pytest
 import torch
@@ -10,7 +11,7 @@ from gemm_q8_amd.device import q8_0_from_f32, to_dev, to_host, workspace
 from oracle.hc import hc_down, hc_up
 from oracle.moe import moe_forward, route
 from oracle.q8 import q8_0_gemv, quantize_q8_0, quantize_q8_1_bf16
-from oracle.w8a8 import w8a8_gemm
+from oracle.w8a8 import quantize_per_token, w8a8_gemm
 from tests.helpers import check_bf16, check_f32
 
 pytestmark = pytest.mark.gpu
@@ -29,6 +30,12 @@ W8 = _shapes("w8a8", 10, lambda g: (int(g.integers(1, 33)), int(g.integers(1, 50
                                     16 * int(g.integers(1, 513))))
 
 
+GEMV_FEW = _shapes("gemv-few", 8, lambda g: (int(g.integers(1, 4)), int(g.integers(1, 900)),
+                                              32 * int(g.integers(1, 129))))
+W8B = _shapes("w8a8-bf16x", 10, lambda g: (int(g.integers(1, 33)), int(g.integers(1, 500)),
+                                           16 * int(g.integers(1, 513))))
+
+
 def _moe_draw(g):
     T = int(g.integers(1, 17))
     topk = int(g.integers(1, min(16, 256 // T) + 1))
@@ -41,7 +48,7 @@ def _moe_draw(g):
 MOE = _shapes("moe", 8, _moe_draw)
 
 
-@pytest.mark.parametrize("T,N,K", GEMV)
+@pytest.mark.parametrize("T,N,K", GEMV + GEMV_FEW)
 def test_sweep_gemv(gpu, T, N, K):
     w = synth.normal_f32(60, "sweep.gemv.w", (N, K), 0.0, 0.02)
     x = synth.normal_f32(60, "sweep.gemv.x", (T, K))
@@ -86,6 +93,26 @@ def test_sweep_w8a8(gpu, M, N, K):
     torch.cuda.synchronize()
     acc_ref, out_ref = w8a8_gemm(d["xq"], d["x_scale"], d["W"], d["w_scale"])
     assert np.array_equal(to_host(acc), acc_ref), f"M={M} N={N} K={K}"
+    assert np.array_equal(to_host(out, np.uint16), out_ref), f"M={M} N={N} K={K}"
+
+
+@pytest.mark.parametrize("M,N,K", W8B)
+def test_sweep_w8a8_bf16x(gpu, M, N, K):
+    d = synth.w8a8_bf16_inputs(M, N, K, seed=64)
+    wp = torch.empty(gpu.gq8_w8a8_packed_bytes(K, N), dtype=torch.int8, device="cuda")
+    gpu.gq8_w8a8_pack(to_dev(d["W"]), K, N, wp)
+    nb = gpu.gq8_workspace_bytes(gpu.OP_W8A8_BF16X, M, N, K)
+    out = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    xs = torch.empty((M,), dtype=torch.float32, device="cuda")
+    x = to_dev(d["x"])
+    gpu.gq8_w8a8_gemm_bf16x(x, wp, to_dev(d["w_scale"]), out, None, None, M, N, K, workspace(nb), nb)
+    gpu.gq8_quantize_per_token(x, M, K, xq, xs)
+    torch.cuda.synchronize()
+    xq_ref, xs_ref = quantize_per_token(d["x"])
+    _, out_ref = w8a8_gemm(xq_ref, xs_ref, d["W"], d["w_scale"])
+    assert np.array_equal(to_host(xq), xq_ref), f"M={M} K={K}"
+    assert np.array_equal(to_host(xs).view(np.uint32), xs_ref.view(np.uint32)), f"M={M} K={K}"
     assert np.array_equal(to_host(out, np.uint16), out_ref), f"M={M} N={N} K={K}"
 
 
