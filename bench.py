@@ -259,8 +259,10 @@ def bench_other_configs(torch, gq8, synth, dev, stream, report, only=None, w8a8_
         return t / (n_sets * reps) * 1e6
 
     # read-bandwidth probe at the same byte counts
-    for nbytes in (4_456_448, 5_570_560, 6_291_456, 8_388_608, 10_485_760) if "probe" in only else ():
-        n = n_sets_for(nbytes)
+    # (4 KiB: one work-group, the launch floor; the large sizes: how close a plain stream gets)
+    for nbytes in (4096, 4_456_448, 5_570_560, 6_291_456, 8_388_608, 10_485_760, 33_554_432,
+                   134_217_728, 536_870_912) if "probe" in only else ():
+        n = min(n_sets_for(nbytes), 256)         # the 4 KiB floor needs no rotation
         bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(n)]
         sink = torch.empty(gq8.gq8_read_probe_sink_floats(nbytes), dtype=torch.float32, device=dev)
         us = timed(lambda i: (lambda s, b=bufs[i % n]: gq8.gq8_read_probe(b, nbytes, sink, s)), n)
