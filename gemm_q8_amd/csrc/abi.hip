@@ -1,5 +1,6 @@
 // C ABI of libgq8.so: argument checks, dispatch to the kernel launchers, workspace sizing.
 // Every entry point validates before enqueueing anything and never allocates or synchronizes.
+#include <stdlib.h>
 #include <string.h>
 
 #include "gq8_internal.h"
@@ -18,6 +19,15 @@ int device_cus() {
     if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return 0;
     if (dev < 64) cached[dev] = prop.multiProcessorCount;
     return prop.multiProcessorCount;
+}
+
+bool force_general() {
+    const char* v = getenv("GQ8_FORCE_GENERIC");
+    if (v == nullptr || strcmp(v, "0") == 0 || v[0] == '\0') return false;
+    if (strcmp(v, "1") == 0) return true;
+    static std::atomic<bool> said{false};
+    if (!said.exchange(true)) fprintf(stderr, "gq8: GQ8_FORCE_GENERIC=%s not understood (0 or 1); ignored\n", v);
+    return false;
 }
 
 }  // namespace gq8

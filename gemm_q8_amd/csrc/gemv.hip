@@ -203,7 +203,7 @@ static int launch_gemv_t(GemvArgs a, void* ws, hipStream_t st) {
         if (a.K > 0) return launch_gemv_mfma_t<T>(a, ws, st);
     }
     if constexpr (T <= kGemvWaveMaxT) {
-        if (a.K <= kGemvWaveMaxK) {
+        if (a.K <= kGemvWaveMaxK && !force_general()) {
             launch_gemv_wave_rw<T, (T == 1 ? 1 : 2)>(a, st);
             return launch_status();
         }
@@ -814,10 +814,10 @@ __global__ void __launch_bounds__(256) hc_up_bf16_kernel(GemvArgs a) {
 template <int T>
 static int launch_up_t(GemvArgs a, hipStream_t st) {
     const int ntile = (a.N + 15) / 16;
-    if (a.K % kUpCW == 0) {
+    if (a.K % kUpCW == 0 && !force_general()) {
         hipLaunchKernelGGL((hc_up_direct_kernel<T>), dim3((ntile + 3) / 4), dim3(256), 0, st, a);
     } else {
-        GQ8_NOTE_GENERAL("up read: depth not a multiple of 320, general up kernel (LDS staged)");
+        GQ8_NOTE_GENERAL("up read: general up kernel (LDS staged): depth not a multiple of 320, or forced");
         hipLaunchKernelGGL((hc_up_kernel<T>), dim3((ntile + 3) / 4), dim3(256), 0, st, a);
     }
     return launch_status();
@@ -1038,7 +1038,7 @@ static int launch_pair_t(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st) {
 }
 
 int launch_hc_pair(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st) {
-    if (up.K != kUpCW) {                   // no fused variant: the down read, then the up read
+    if (up.K != kUpCW || force_general()) {   // no fused variant: the down read, then the up read
         const int rc = launch_hc_down(dn, ws, st);
         return rc != GQ8_OK ? rc : launch_hc_up(up, st);
     }

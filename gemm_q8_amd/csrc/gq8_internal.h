@@ -22,6 +22,11 @@
 
 namespace gq8 {
 
+// Debug switch GQ8_FORCE_GENERIC: "1" sends every call to the general kernels of its family (the
+// paths a shape outside the tuned set takes), so that tests can check them at the tuned shapes;
+// unset or "0": off; any other value: off, said once on stderr. Read on every call.
+bool force_general();
+
 constexpr int kMaxT = 16;        // token rows of the Q8_0 reads
 constexpr int kMaxM = 32;        // rows of the W8A8 product
 constexpr int kW8MaxK = 8192;    // W8A8 depth: 16 waves x 8 k-steps of 64

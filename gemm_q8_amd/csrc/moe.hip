@@ -793,7 +793,8 @@ int launch_moe_routed(const int8_t* xq, const uint16_t* xd, const uint16_t* xb, 
     p += round_up(P * D * sizeof(float), kCounterAlign);
     a.ids = ids;
     int rc = GQ8_OK;
-    const bool rows_gu = D <= 4096;
+    const bool general = force_general();
+    const bool rows_gu = D <= 4096 && !general;
     if (xb != nullptr && !rows_gu) {       // bf16 input, general gate/up kernel: quantize first
         int8_t* wq = reinterpret_cast<int8_t*>(p);
         uint16_t* wd = reinterpret_cast<uint16_t*>(p + round_up((size_t)T * D, kCounterAlign));
@@ -802,23 +803,25 @@ int launch_moe_routed(const int8_t* xq, const uint16_t* xd, const uint16_t* xb, 
     }
     // the plan is needed only by the fallback kernels (D > 4096 gate/up; F outside
     // {256, 512, 1024} down)
-    const bool token_dn = F == 256 || F == 512 || F == 1024;
+    // (the q8_1(h) down read exists only as the token kernel: the switch leaves it there)
+    const bool token_dn = (F == 256 || F == 512 || F == 1024) && (!general || hq);
     if (!rows_gu || !token_dn) {
-        GQ8_NOTE_GENERAL("routed experts: D > 4096 or F not in {256, 512, 1024}, plan-based general kernels");
+        GQ8_NOTE_GENERAL("routed experts: plan-based general kernels: D > 4096, F not in {256, 512, 1024}, or forced");
         hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(256), 0, st, ids, a.P, E, plan);
         if ((rc = launch_status()) != GQ8_OK) return rc;
     }
     const dim3 ggu((F + 4 * kGuRpw - 1) / (4 * kGuRpw), a.P);
-    if (a.xb != nullptr) {
+    if (!rows_gu) {                        // the general gate/up kernel (a.xb is q8_1 by now)
+        if (T <= 4) hipLaunchKernelGGL((moe_gate_up_kernel<4>), ggu, dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((moe_gate_up_kernel<16>), ggu, dim3(256), 0, st, a);
+    } else if (a.xb != nullptr) {
         if (D <= 1024) hipLaunchKernelGGL((moe_gate_up_rows_kernel<1, true>), ggu, dim3(256), 0, st, a);
         else if (D <= 2048) hipLaunchKernelGGL((moe_gate_up_rows_kernel<2, true>), ggu, dim3(256), 0, st, a);
         else hipLaunchKernelGGL((moe_gate_up_rows_kernel<4, true>), ggu, dim3(256), 0, st, a);
     }
     else if (D <= 1024) hipLaunchKernelGGL((moe_gate_up_rows_kernel<1, false>), ggu, dim3(256), 0, st, a);
     else if (D <= 2048) hipLaunchKernelGGL((moe_gate_up_rows_kernel<2, false>), ggu, dim3(256), 0, st, a);
-    else if (D <= 4096) hipLaunchKernelGGL((moe_gate_up_rows_kernel<4, false>), ggu, dim3(256), 0, st, a);
-    else if (T <= 4) hipLaunchKernelGGL((moe_gate_up_kernel<4>), ggu, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((moe_gate_up_kernel<16>), ggu, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((moe_gate_up_rows_kernel<4, false>), ggu, dim3(256), 0, st, a);
     if ((rc = launch_status()) != GQ8_OK) return rc;
     if (token_dn) {                        // down + combine in one kernel
         const dim3 gt((D + 15) / 16, T);
