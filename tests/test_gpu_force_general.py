@@ -104,3 +104,32 @@ def test_workspace_init_zero_fills_and_refuses_capture(gpu):
             rc = raw.gq8_workspace_init(ws.data_ptr(), nb, s.cuda_stream)
             ws.zero_()                                 # the graph holds one ordinary node
     assert rc == gpu.ECAPTURE
+
+
+_NOTE_SCRIPT = r"""
+import torch
+from gemm_q8_amd import gq8
+x = torch.zeros((1, 320), dtype=torch.int16, device="cuda")
+w = torch.zeros(gq8.gq8_q8_0_bytes(64, 320), dtype=torch.uint8, device="cuda")
+out = torch.empty((1, 64), dtype=torch.int16, device="cuda")
+for _ in range(3):
+    gq8.gq8_hc_q8_up(w, x, out, 1, 64, 320, None, 0)
+torch.cuda.synchronize()
+print("calls done")
+"""
+
+
+@pytest.mark.parametrize("value,expect", [("1", "gq8: up read: general up kernel"),
+                                          ("yes", "gq8: GQ8_FORCE_GENERIC=yes not understood")])
+def test_general_path_note_is_said_once(value, expect):
+    """A fresh process: three calls, the note on stderr exactly once."""
+    import os
+    import subprocess
+    import sys
+    env = dict(os.environ, GQ8_FORCE_GENERIC=value)
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _NOTE_SCRIPT], cwd=root, env=env, capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "calls done" in r.stdout
+    assert sum(line.startswith(expect) for line in r.stderr.splitlines()) == 1, r.stderr[-2000:]
