@@ -1,10 +1,11 @@
 // Host-side weight and activation preparation (plain C++ on host memory; no HIP call): the Q8_0
 // quantizer (HC-Q8 page, "What changed": ggml's rounding, d = amax / 127 stored as fp16 and
-// q = round(w / d)), the 34-byte-block to split-layout reorder, and the q8_1 quantizer of a bf16
-// activation (EP page, "What changed": the q8_1 MoE input). The rounding is that of the device
-// quantizers: fp32 quotients, fp16 round to nearest even, round half away from zero, quants
-// clamped to [-127, 127], all-zero quants for a zero scale. Compiled without floating-point
-// contraction or fast-math.
+// q = round(w / d)), the 34-byte-block to split-layout reorder, the q8_1 quantizer of a bf16
+// activation (EP page, "What changed": the q8_1 MoE input), and the W8A8 weight packer (W8A8
+// page, "Cross-shape rules": the cold weight packed once into the product's fragment layout).
+// The rounding is that of the device quantizers: fp32 quotients, fp16 round to nearest even,
+// round half away from zero, quants clamped to [-127, 127], all-zero quants for a zero scale.
+// Compiled without floating-point contraction or fast-math.
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -136,5 +137,27 @@ GQ8_HOST_EXPORT int gq8_q8_1_quantize_host(const uint16_t* x_bf16, int rows, int
                 s[(size_t)r * nblk + b] = f32_to_f16(f16_to_f32(db) * (float)sum);
             }
         }
+    return GQ8_OK;
+}
+
+// W[K][N] int8 (logical, row-major) -> 16-column x 64-k fragments: slot (tile nt, k-step ks, lane
+// l) holds the 16 bytes W[64 ks + 16 (l / 16) + e][16 nt + l % 16], e = 0..15, zero past K or N;
+// slots in (nt, ks, l) order. The layout of gq8_w8a8_pack.
+GQ8_HOST_EXPORT int gq8_w8a8_pack_host(const int8_t* W, int K, int N, int8_t* W_packed) {
+    if (K < 0 || N < 0) return GQ8_EINVAL;
+    if (K % 16 != 0) return GQ8_ESHAPE;
+    if (K == 0 || N == 0) return GQ8_OK;
+    if (W == nullptr || W_packed == nullptr) return GQ8_EINVAL;
+    const int ntiles = (N + 15) / 16, ksteps = (K + 63) / 64;
+    int8_t* out = W_packed;
+    for (int nt = 0; nt < ntiles; ++nt)
+        for (int ks = 0; ks < ksteps; ++ks)
+            for (int l = 0; l < 64; ++l) {
+                const int n = 16 * nt + l % 16, k0 = 64 * ks + 16 * (l / 16);
+                for (int e = 0; e < 16; ++e) {
+                    const int k = k0 + e;
+                    *out++ = (n < N && k < K) ? W[(size_t)k * N + n] : (int8_t)0;
+                }
+            }
     return GQ8_OK;
 }

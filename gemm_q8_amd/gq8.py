@@ -54,6 +54,7 @@ _SIGS = {
     "gq8_q8_0_quantize_host": (_I, [_P, _I, _I, _P]),
     "gq8_q8_0_split_from_blocks_host": (_I, [_P, _I, _I, _P]),
     "gq8_q8_1_quantize_host": (_I, [_P, _I, _I, _P, _P, _P]),
+    "gq8_w8a8_pack_host": (_I, [_P, _I, _I, _P]),
     "gq8_workspace_check": (_I, [_P, _SZ, _P, _P]),
     "gq8_w8a8_gemm_bf16x": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_moe_route": (_I, [_P, _I, _I, _I, _P, _P, _P]),
@@ -210,6 +211,10 @@ def gq8_q8_0_split_from_blocks_host(blocks34, rows, K, split_out):
 def gq8_q8_1_quantize_host(x_bf16, rows, K, q, d, s=None):
     return _check("gq8_q8_1_quantize_host",
                   _lib.gq8_q8_1_quantize_host(_ptr(x_bf16), rows, K, _ptr(q), _ptr(d), _ptr(s)))
+
+
+def gq8_w8a8_pack_host(W, K, N, W_packed):
+    return _check("gq8_w8a8_pack_host", _lib.gq8_w8a8_pack_host(_ptr(W), K, N, _ptr(W_packed)))
 
 
 def gq8_workspace_check(ws, nbytes, stream=None):

@@ -97,6 +97,9 @@ int gq8_q8_0_quantize_host(const float* w, int rows, int K, void* split_out);
 int gq8_q8_0_split_from_blocks_host(const void* blocks34, int rows, int K, void* split_out);
 int gq8_q8_1_quantize_host(const uint16_t* x_bf16, int rows, int K, int8_t* q, uint16_t* d,
                            uint16_t* s);
+/* The W8A8 weight packer on the host: byte-identical to gq8_w8a8_pack (W int8 [K][N] row-major,
+ * W_packed gq8_w8a8_packed_bytes(K, N) bytes). K % 16 == 0. */
+int gq8_w8a8_pack_host(const int8_t* W, int K, int N, int8_t* W_packed);
 
 /* ------------------------------------------------------------------------------------------
  * Workspace: device scratch that a compute call needs beyond its inputs and outputs.

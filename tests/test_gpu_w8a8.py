@@ -111,3 +111,21 @@ def test_w8a8_max_depth(gpu, M):
     acc_ref, out_ref = w8a8_gemm(d["xq"], d["x_scale"], d["W"], d["w_scale"])
     assert np.array_equal(_run(gpu, d, M, N, K, i32=True), acc_ref)
     assert np.array_equal(_run(gpu, d, M, N, K), out_ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 1536, 4096), (5, 37, 80)])
+def test_w8a8_host_pack_equals_device_pack(gpu, M, N, K):
+    """gq8_w8a8_pack_host writes the bytes gq8_w8a8_pack writes; the product on them is exact."""
+    d = synth.w8a8_inputs(M, N, K, seed=12)
+    host = np.zeros(gpu.gq8_w8a8_packed_bytes(K, N), np.int8)
+    gpu.gq8_w8a8_pack_host(np.ascontiguousarray(d["W"]), K, N, host)
+    dev = _pack(gpu, d["W"])
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(dev), host)
+    wp = to_dev(host)
+    nb = gpu.gq8_workspace_bytes(gpu.OP_W8A8, M, N, K)
+    out = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    gpu.gq8_w8a8_gemm(to_dev(d["xq"]), to_dev(d["x_scale"]), wp, to_dev(d["w_scale"]), out, M, N, K,
+                      workspace(nb), nb)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(out, np.uint16), w8a8_gemm(d["xq"], d["x_scale"], d["W"], d["w_scale"])[1])

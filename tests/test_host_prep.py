@@ -100,3 +100,25 @@ def test_workspace_check_reports_no_counters(lib):
     assert lib.gq8_workspace_check(buf, buf.nbytes) == 0
     raw = lib.raw()
     assert raw.gq8_workspace_check(None, 64, None, None) == lib.EINVAL
+
+
+@pytest.mark.parametrize("K,N", [(4096, 48), (80, 17), (16, 1)])
+def test_w8a8_pack_host_places_every_byte(lib, K, N):
+    """Every W[k][n] lands in slot (n // 16, k // 64, 16 (k % 64 // 16) + n % 16) at byte k % 16, and
+    the padding past K or N is zero."""
+    W = synth.int8_uniform(9, "host.w8.pack", (K, N))
+    nb = lib.gq8_w8a8_packed_bytes(K, N)
+    buf = np.full(nb, 0x55, np.int8)
+    lib.gq8_w8a8_pack_host(np.ascontiguousarray(W), K, N, buf)
+    ksteps = (K + 63) // 64
+    slots = buf.reshape((N + 15) // 16, ksteps, 64, 16)
+    k = np.arange(K)[:, None]
+    n = np.arange(N)[None, :]
+    got = slots[n // 16, k // 64, 16 * ((k % 64) // 16) + n % 16, k % 16]
+    assert np.array_equal(got, W)
+    mask = np.zeros(slots.shape, bool)
+    mask[n // 16, k // 64, 16 * ((k % 64) // 16) + n % 16, k % 16] = True
+    assert not slots[~mask].any()
+    raw = lib.raw()
+    assert raw.gq8_w8a8_pack_host(1 << 20, 40, 8, 1 << 20) == lib.ESHAPE
+    assert raw.gq8_w8a8_pack_host(None, 64, 8, 1 << 20) == lib.EINVAL
