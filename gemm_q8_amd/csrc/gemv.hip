@@ -9,7 +9,7 @@
 // one or two kernels.
 //
 //  * GEMV, T <= 3 and K <= 4096 (gemv_wave_kernel): one wave owns one or two whole rows, lane
-//    partials over its chunks, one wave sum (DPP, then the 16- and 32-lane swaps), no LDS.
+//    partials over its chunks, one wave sum, no LDS.
 //    Other T <= 4 (gemv_rows_kernel): a work-group owns RW rows and all of K; wave w reads
 //    1024-column chunks w, w+NW, ...; lane partials are reduced over the wave (DPP) and the
 //    waves' sums are added through LDS in wave order. T >= 5: the down read's slab kernel with
@@ -166,7 +166,7 @@ __global__ void __launch_bounds__(64) gemv_wave_kernel(GemvArgs a) {
 #pragma unroll
             for (int c = 0; c < NCH; ++c)       // a clamped chunk (k >= K) gets scale 0
                 acc = fmaf(dot16_i8_f32(wq[r][c], xv[t][c]), kok[c] ? h2f(wd[r][c]) : 0.f, acc);
-            const float v = wave_sum_swap(acc);
+            const float v = wave_sum(acc);
             if (lane == r * T + t && row0 + r < N) reinterpret_cast<float*>(a.out)[(size_t)t * N + row0 + r] = v;
         }
 }

@@ -123,29 +123,19 @@ GQ8_DEV float dpp_mov(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
-// Sum over the 64 lanes; every lane gets the same bits (each step adds a symmetric pair).
+// Sum over the 64 lanes; every lane gets the same bits (each step adds a symmetric pair): the DPP
+// steps within each 16-lane row, then v_permlane16_swap and v_permlane32_swap (gfx950) bring in
+// the neighbouring row and the other half, with no LDS round trip.
 GQ8_DEV float wave_sum(float v) {
     v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
     v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
     v += dpp_mov<0x141>(v);  // row_half_mirror
     v += dpp_mov<0x140>(v);  // row_mirror
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
-}
-
-// The same sum without LDS: the DPP steps within each 16-lane row, then v_permlane16_swap and
-// v_permlane32_swap (gfx950) bring in the other rows; every lane gets the same bits.
-GQ8_DEV float wave_sum_swap(float v) {
-    v += dpp_mov<0xB1>(v);
-    v += dpp_mov<0x4E>(v);
-    v += dpp_mov<0x141>(v);
-    v += dpp_mov<0x140>(v);
     const int lane = threadIdx.x & 63;
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v += __uint_as_float((lane & 16) ? r[0] : r[1]);          // the neighbouring 16-lane row
+    v += __uint_as_float((lane & 16) ? r[0] : r[1]);          // lane l ^ 16
     const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v += __uint_as_float((lane & 32) ? h[0] : h[1]);          // the other 32-lane half
+    v += __uint_as_float((lane & 32) ? h[0] : h[1]);          // lane l ^ 32
     return v;
 }
 
