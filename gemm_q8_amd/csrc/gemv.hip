@@ -404,7 +404,8 @@ __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
     // sums of R^2 of token t: over the lanes of the wave holding t (lane bits above TR), then
     // over the waves (in the epilogue), in a fixed order
 #pragma unroll
-    for (int m = TR; m < 64; m <<= 1) r2acc += __shfl_xor(r2acc, m, 64);
+    for (int m = TR; m < 64; m <<= 1)
+        r2acc += m == 8 ? lane_xor8f(r2acc) : (m == 16 ? lane_xor16f(r2acc) : lane_xor32f(r2acc));
     if (lane < TR) sqw[wave][lane] = r2acc;
     __syncthreads();
 
@@ -471,7 +472,7 @@ __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
         // rows 8..15 (lanes 32..63) hold the lo parts of tokens 0..7: add them to rows 0..7
         float tot[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) tot[v] = acc[v] + __shfl_down(acc[v], 32, 64);
+        for (int v = 0; v < 4; ++v) tot[v] = acc[v] + lane_xor32f(acc[v]);   // lanes < 32: l + 32
         if (lane < 32) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {

@@ -123,6 +123,38 @@ GQ8_DEV float dpp_mov(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
+// Lane l's value from lane l ^ 16 / l ^ 32 (v_permlane16_swap / v_permlane32_swap, no LDS), from
+// l ^ 8 (DPP row rotate by 8 within a 16-lane row), and from l ^ 1 / l ^ 2 (DPP quad_perm).
+GQ8_DEV uint32_t lane_xor16(uint32_t v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (threadIdx.x & 16) ? r[0] : r[1];
+}
+GQ8_DEV uint32_t lane_xor32(uint32_t v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (threadIdx.x & 32) ? r[0] : r[1];
+}
+template <int CTRL>
+GQ8_DEV uint32_t dpp_u32(uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true); }
+GQ8_DEV uint32_t lane_xor8(uint32_t v) { return dpp_u32<0x128>(v); }      // row_ror:8
+GQ8_DEV uint32_t lane_xor1(uint32_t v) { return dpp_u32<0xB1>(v); }       // quad_perm [1,0,3,2]
+GQ8_DEV uint32_t lane_xor2(uint32_t v) { return dpp_u32<0x4E>(v); }       // quad_perm [2,3,0,1]
+GQ8_DEV float lane_xor16f(float v) { return __uint_as_float(lane_xor16(__float_as_uint(v))); }
+GQ8_DEV float lane_xor32f(float v) { return __uint_as_float(lane_xor32(__float_as_uint(v))); }
+GQ8_DEV float lane_xor8f(float v) { return __uint_as_float(lane_xor8(__float_as_uint(v))); }
+GQ8_DEV float lane_xor1f(float v) { return __uint_as_float(lane_xor1(__float_as_uint(v))); }
+GQ8_DEV float lane_xor2f(float v) { return __uint_as_float(lane_xor2(__float_as_uint(v))); }
+
+// Max over the 64 lanes of unsigned values (every lane gets it)
+GQ8_DEV uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, lane_xor1(v));
+    v = max(v, lane_xor2(v));
+    v = max(v, dpp_u32<0x141>(v));   // row_half_mirror: the other quad of the half-row
+    v = max(v, lane_xor8(v));
+    v = max(v, lane_xor16(v));
+    v = max(v, lane_xor32(v));
+    return v;
+}
+
 // Sum over the 64 lanes; every lane gets the same bits (each step adds a symmetric pair): the DPP
 // steps within each 16-lane row, then v_permlane16_swap and v_permlane32_swap (gfx950) bring in
 // the neighbouring row and the other half, with no LDS round trip.

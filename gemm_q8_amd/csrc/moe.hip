@@ -405,8 +405,8 @@ __global__ void __launch_bounds__(256) moe_gate_up_rows_kernel(MoeArgs a) {
                         am = fmaxf(am, fabsf(v[2 * e]));
                         am = fmaxf(am, fabsf(v[2 * e + 1]));
                     }
-                    am = fmaxf(am, __shfl_xor(am, 1, 64));
-                    am = fmaxf(am, __shfl_xor(am, 2, 64));
+                    am = fmaxf(am, lane_xor1f(am));
+                    am = fmaxf(am, lane_xor2f(am));
                     const uint16_t db = q8_scale_bits(am);
                     const float dd = h2f(db);
                     uint32_t q2[2] = {0u, 0u};
@@ -650,8 +650,8 @@ __global__ void __launch_bounds__(256) moe_down_token_kernel(MoeArgs a) {
                     float am = 0.f;
 #pragma unroll
                     for (int e2 = 0; e2 < 8; ++e2) am = fmaxf(am, fabsf(f[e2]));
-                    am = fmaxf(am, __shfl_xor(am, 1, 64));
-                    am = fmaxf(am, __shfl_xor(am, 2, 64));
+                    am = fmaxf(am, lane_xor1f(am));
+                    am = fmaxf(am, lane_xor2f(am));
                     const uint16_t db = q8_scale_bits(am);
                     const float dd = h2f(db);
                     uint32_t q2[2] = {0u, 0u};
@@ -733,7 +733,7 @@ __global__ void __launch_bounds__(256) moe_down_token_kernel(MoeArgs a) {
                 }
             }
             // result row 8 (lanes 32..47, v = 0) holds the lo part: add it to row 0 (lanes 0..15)
-            const float tot = acc[0] + __shfl_down(acc[0], 32, 64);
+            const float tot = acc[0] + lane_xor32f(acc[0]);     // lanes < 32: l + 32
             if (on[u] && lane < 16) rr[j0 + 4 * u][j] = tot;
         }
         // the next round overwrites this wave's hs slot: every lane's reads come first

@@ -222,8 +222,7 @@ __global__ void __launch_bounds__(1024) w8a8_bf16x_kernel(W8Args a) {
         uint32_t m = absmax8_bf16_bits(r[j]);
         const int rlo = __builtin_amdgcn_readfirstlane(row[j]);
         if (rlo == __shfl(row[j], 63, 64)) {             // chunks ascend with the lane
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) m = umax32(m, (uint32_t)__shfl_xor((int)m, o, 64));
+            m = wave_max_u32(m);
             if (lane == 0) atomicMax(&am_s[rlo], m);
         } else {
             atomicMax(&am_s[row[j]], m);
@@ -298,8 +297,8 @@ __global__ void __launch_bounds__(1024) w8a8_dot_kernel(W8Args a) {
 #pragma unroll
     for (int m = 0; m < MC; ++m) {
         int t = acc[m];
-        t += __shfl_xor(t, 16, 64);
-        t += __shfl_xor(t, 32, 64);
+        t += (int)lane_xor16((uint32_t)t);
+        t += (int)lane_xor32((uint32_t)t);
         if (lane < 16 && m < a.M) tile[wave][m][lane] = t;
     }
     w8a8_finish(a, nt, nw, tile, sc);
@@ -378,8 +377,7 @@ __global__ void __launch_bounds__(256) per_token_quantize_kernel(const uint16_t*
     uint32_t ab = 0u;
     for (int k = 8 * (int)threadIdx.x; k < K; k += 8 * 256)
         ab = umax32(ab, absmax8_bf16_bits(*reinterpret_cast<const u32x4*>(row + k)));
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) ab = umax32(ab, (uint32_t)__shfl_xor((int)ab, o, 64));
+    ab = wave_max_u32(ab);
     if (lane == 0) wmax[wave] = ab;
     __syncthreads();
     const float am = bf16_bits_to_f32(umax32(umax32(wmax[0], wmax[1]), umax32(wmax[2], wmax[3])));
