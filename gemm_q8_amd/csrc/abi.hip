@@ -10,14 +10,17 @@ using namespace gq8;
 namespace gq8 {
 
 int device_cus() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];     // zero-initialised (static storage); 0 = not yet known
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    if (dev < 64) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
     if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return 0;
-    if (dev < 64) cached[dev] = prop.multiProcessorCount;
+    if (dev < 64) cached[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
     return prop.multiProcessorCount;
 }
 
@@ -33,6 +36,16 @@ bool force_general() {
 }  // namespace gq8
 
 static inline hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
+
+// Size limits, far above any decode-time shape, that keep every launch below 2^32 work-items and
+// the kernels' int index arithmetic in range; a call beyond them returns GQ8_ESHAPE.
+constexpr int64_t kMaxQ8Rows = int64_t(1) << 21;     // output rows of a Q8_0 read
+constexpr int64_t kMaxQ8Depth = int64_t(1) << 24;    // depth of a Q8_0 read
+constexpr int64_t kMaxQ8Elems = int64_t(1) << 38;    // rows x depth of a Q8_0 read
+constexpr int64_t kMaxW8N = int64_t(1) << 24;        // W8A8 output columns
+constexpr int64_t kMaxMoeD = int64_t(1) << 20;       // routed-expert model width
+constexpr int64_t kMaxRouteT = int64_t(1) << 23;     // token rows of the top-k and the per-token quantizer
+constexpr uint64_t kMaxItems = (uint64_t(1) << 32) - 256;   // one-work-item-per-element launches
 
 static int check_ws(void* ws, size_t ws_bytes, size_t need) {
     if (need == 0) return GQ8_OK;
@@ -73,7 +86,7 @@ GQ8_EXPORT size_t gq8_q8_0_bytes(int64_t rows, int64_t K) {
 
 GQ8_EXPORT int gq8_q8_0_quantize(const float* w, int rows, int K, void* w_split, void* stream) {
     if (rows < 0 || K < 0) return GQ8_EINVAL;
-    if (K % 32 != 0) return GQ8_ESHAPE;
+    if (K % 32 != 0 || (uint64_t)rows * (uint64_t)(K / 32) > kMaxItems) return GQ8_ESHAPE;
     if (rows == 0 || K == 0) return GQ8_OK;
     if (w == nullptr || w_split == nullptr) return GQ8_EINVAL;
     if (!aligned16(w) || !aligned16(w_split)) return GQ8_EALIGN;
@@ -84,7 +97,7 @@ GQ8_EXPORT int gq8_q8_0_quantize(const float* w, int rows, int K, void* w_split,
 GQ8_EXPORT int gq8_q8_0_split_from_blocks(const void* blocks34, int rows, int K, void* w_split,
                                           void* stream) {
     if (rows < 0 || K < 0) return GQ8_EINVAL;
-    if (K % 32 != 0) return GQ8_ESHAPE;
+    if (K % 32 != 0 || (uint64_t)rows * (uint64_t)(K / 32) > kMaxItems) return GQ8_ESHAPE;
     if (rows == 0 || K == 0) return GQ8_OK;
     if (blocks34 == nullptr || w_split == nullptr) return GQ8_EINVAL;
     if (!aligned16(w_split)) return GQ8_EALIGN;
@@ -95,7 +108,7 @@ GQ8_EXPORT int gq8_q8_0_split_from_blocks(const void* blocks34, int rows, int K,
 GQ8_EXPORT int gq8_q8_1_quantize(const uint16_t* x_bf16, int rows, int K, int8_t* q, uint16_t* d,
                                  uint16_t* s, void* stream) {
     if (rows < 0 || K < 0) return GQ8_EINVAL;
-    if (K % 32 != 0) return GQ8_ESHAPE;
+    if (K % 32 != 0 || (uint64_t)rows * (uint64_t)(K / 32) > kMaxItems) return GQ8_ESHAPE;
     if (rows == 0 || K == 0) return GQ8_OK;
     if (x_bf16 == nullptr || q == nullptr || d == nullptr) return GQ8_EINVAL;
     if (device_cus() == 0) return GQ8_ENODEV;
@@ -105,7 +118,8 @@ GQ8_EXPORT int gq8_q8_1_quantize(const uint16_t* x_bf16, int rows, int K, int8_t
 // ---------------------------------------------------------------------------------- workspace
 
 static bool q8_shape_ok(int T, int N, int K) {
-    return T >= 0 && T <= kMaxT && N >= 0 && K >= 0 && K % 32 == 0;
+    return T >= 0 && T <= kMaxT && N >= 0 && K >= 0 && K % 32 == 0 && N <= kMaxQ8Rows &&
+           K <= kMaxQ8Depth && (int64_t)N * K <= kMaxQ8Elems;
 }
 
 // x_q staging of the bf16-activation product when it runs as two kernels: x_q [M][K] at 0, then
@@ -281,13 +295,13 @@ GQ8_EXPORT int gq8_hc_bf16_pair(const uint16_t* w_down, const uint16_t* R, const
 // ---------------------------------------------------------------------------------- W8A8
 
 GQ8_EXPORT size_t gq8_w8a8_packed_bytes(int K, int N) {
-    if (K < 0 || N < 0) return 0;
-    return (size_t)((N + 15) / 16) * 16 * (size_t)((K + 63) / 64) * 64;
+    if (K < 0 || N < 0 || N > kMaxW8N) return 0;
+    return (size_t)((N + 15) / 16) * 16 * (size_t)(((int64_t)K + 63) / 64) * 64;
 }
 
 GQ8_EXPORT int gq8_w8a8_pack(const int8_t* W, int K, int N, int8_t* W_packed, void* stream) {
     if (K < 0 || N < 0) return GQ8_EINVAL;
-    if (K % 16 != 0) return GQ8_ESHAPE;
+    if (K % 16 != 0 || N > kMaxW8N || gq8_w8a8_packed_bytes(K, N) / 16 > kMaxItems) return GQ8_ESHAPE;
     if (K == 0 || N == 0) return GQ8_OK;
     if (W == nullptr || W_packed == nullptr) return GQ8_EINVAL;
     if (!aligned16(W_packed)) return GQ8_EALIGN;
@@ -298,7 +312,7 @@ GQ8_EXPORT int gq8_w8a8_pack(const int8_t* W, int K, int N, int8_t* W_packed, vo
 static int w8a8_common(const int8_t* xq, const float* xs, const int8_t* wp, const float* wsc,
                        void* out, bool i32, int M, int N, int K, void* stream) {
     if (M < 0 || N < 0 || K < 0) return GQ8_EINVAL;
-    if (M > kMaxM || K % 16 != 0 || K > kW8MaxK) return GQ8_ESHAPE;
+    if (M > kMaxM || K % 16 != 0 || K > kW8MaxK || N > kMaxW8N) return GQ8_ESHAPE;
     if (M == 0 || N == 0) return GQ8_OK;
     if (out == nullptr) return GQ8_EINVAL;
     if (K == 0) {
@@ -314,7 +328,7 @@ static int w8a8_common(const int8_t* xq, const float* xs, const int8_t* wp, cons
 GQ8_EXPORT int gq8_quantize_per_token(const uint16_t* x, int M, int K, int8_t* xq, float* xs,
                                       void* stream) {
     if (M < 0 || K < 0) return GQ8_EINVAL;
-    if (K % 16 != 0) return GQ8_ESHAPE;
+    if (K % 16 != 0 || M > kMaxRouteT || K > kMaxQ8Depth) return GQ8_ESHAPE;
     if (M == 0) return GQ8_OK;
     if (xs == nullptr || (K > 0 && (x == nullptr || xq == nullptr))) return GQ8_EINVAL;
     if (K > 0 && (!aligned16(x) || !aligned16(xq))) return GQ8_EALIGN;
@@ -327,7 +341,7 @@ GQ8_EXPORT int gq8_w8a8_gemm_bf16x(const uint16_t* x, const int8_t* W_packed, co
                                    uint16_t* out, int8_t* xq_out, float* xs_out, int M, int N,
                                    int K, void* ws, size_t ws_bytes, void* stream) {
     if (M < 0 || N < 0 || K < 0) return GQ8_EINVAL;
-    if (M > kMaxM || K % 16 != 0 || K > kW8MaxK) return GQ8_ESHAPE;
+    if (M > kMaxM || K % 16 != 0 || K > kW8MaxK || N > kMaxW8N) return GQ8_ESHAPE;
     if (M == 0 || N == 0) return GQ8_OK;
     if (out == nullptr) return GQ8_EINVAL;
     if (K == 0) {
@@ -381,7 +395,7 @@ GQ8_EXPORT int gq8_moe_route(const float* logits, int T, int E, int topk, int32_
                              float* weights, void* stream) {
     if (T < 0 || E < 0 || topk < 0) return GQ8_EINVAL;
     if (T == 0) return GQ8_OK;
-    if (topk < 1 || topk > 16 || E < topk || E > 4096) return GQ8_ESHAPE;
+    if (topk < 1 || topk > 16 || E < topk || E > 4096 || T > kMaxRouteT) return GQ8_ESHAPE;
     if (logits == nullptr || ids == nullptr || weights == nullptr) return GQ8_EINVAL;
     if (device_cus() == 0) return GQ8_ENODEV;
     return launch_moe_route(logits, T, E, topk, ids, weights, S(stream));
@@ -395,7 +409,7 @@ GQ8_EXPORT size_t gq8_moe_plan_words(int T, int topk) {
 GQ8_EXPORT int gq8_moe_plan(const int32_t* ids, int T, int topk, int E, int32_t* plan,
                             void* stream) {
     if (T < 0 || topk < 0 || E < 0) return GQ8_EINVAL;
-    if (T * topk > 256 || (T > 0 && topk < 1)) return GQ8_ESHAPE;
+    if ((int64_t)T * topk > 256 || (T > 0 && topk < 1)) return GQ8_ESHAPE;
     if (T == 0) return GQ8_OK;
     if (ids == nullptr || plan == nullptr) return GQ8_EINVAL;
     if (device_cus() == 0) return GQ8_ENODEV;
@@ -413,7 +427,7 @@ GQ8_EXPORT int gq8_moe_q8_0_routed(const int8_t* xq, const uint16_t* xd, const i
                                    size_t ws_bytes, void* stream) {
     if (T < 0 || topk < 0 || E < 0 || D < 0 || F < 0) return GQ8_EINVAL;
     if (T == 0) return GQ8_OK;
-    if (T > kMaxT || topk < 1 || T * topk > 256 || E < 1 || D < 32 || D % 32 != 0 || F < 32 ||
+    if (T > kMaxT || topk < 1 || (int64_t)T * topk > 256 || E < 1 || D < 32 || D % 32 != 0 || D > kMaxMoeD || F < 32 ||
         F % 32 != 0 || F > 1024)
         return GQ8_ESHAPE;
     if (xq == nullptr || xd == nullptr || ids == nullptr || weights == nullptr ||
@@ -433,7 +447,7 @@ GQ8_EXPORT int gq8_moe_q8_0_routed_bf16(const uint16_t* x, const int32_t* ids, c
                                         size_t ws_bytes, void* stream) {
     if (T < 0 || topk < 0 || E < 0 || D < 0 || F < 0) return GQ8_EINVAL;
     if (T == 0) return GQ8_OK;
-    if (T > kMaxT || topk < 1 || T * topk > 256 || E < 1 || D < 32 || D % 32 != 0 || F < 32 ||
+    if (T > kMaxT || topk < 1 || (int64_t)T * topk > 256 || E < 1 || D < 32 || D % 32 != 0 || D > kMaxMoeD || F < 32 ||
         F % 32 != 0 || F > 1024)
         return GQ8_ESHAPE;
     if (x == nullptr || ids == nullptr || weights == nullptr || w_gate_up == nullptr ||
@@ -456,7 +470,7 @@ GQ8_EXPORT int gq8_moe_q8_0_routed_flags(const void* x, const uint16_t* xd, cons
     if (flags & ~(GQ8_MOE_X_BF16 | GQ8_MOE_H_Q8_1)) return GQ8_EINVAL;
     if (T == 0) return GQ8_OK;
     const bool xb = (flags & GQ8_MOE_X_BF16) != 0, hq = (flags & GQ8_MOE_H_Q8_1) != 0;
-    if (T > kMaxT || topk < 1 || T * topk > 256 || E < 1 || D < 32 || D % 32 != 0 || F < 32 ||
+    if (T > kMaxT || topk < 1 || (int64_t)T * topk > 256 || E < 1 || D < 32 || D % 32 != 0 || D > kMaxMoeD || F < 32 ||
         F % 32 != 0 || F > 1024 || (hq && F != 256 && F != 512 && F != 1024))
         return GQ8_ESHAPE;
     if (x == nullptr || (!xb && xd == nullptr) || ids == nullptr || weights == nullptr ||
@@ -476,7 +490,7 @@ GQ8_EXPORT int gq8_moe_q8_0_routed_flags(const void* x, const uint16_t* xd, cons
 GQ8_EXPORT size_t gq8_read_probe_sink_floats(size_t bytes) { return read_probe_blocks(bytes); }
 
 GQ8_EXPORT int gq8_read_probe(const void* src, size_t bytes, float* sink, void* stream) {
-    if (bytes % 16 != 0) return GQ8_ESHAPE;
+    if (bytes % 16 != 0 || bytes / 16 > kMaxItems) return GQ8_ESHAPE;
     if (bytes == 0) return GQ8_OK;
     if (src == nullptr || sink == nullptr) return GQ8_EINVAL;
     if (!aligned16(src)) return GQ8_EALIGN;

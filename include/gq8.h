@@ -12,6 +12,21 @@
  * before anything is enqueued; on an error nothing has been launched and the
  * outputs are untouched. A HIP launch failure is reported as GQ8_EHIP.
  *
+ * Buffers: an output may not overlap any input, another output or the
+ * workspace (the kernels assume no aliasing). Threads: every entry point may
+ * be called from several host threads at once; the only state the library
+ * keeps is a per-device cache of the compute-unit count and once-per-process
+ * notes on stderr. Calls that can run at the same time (other streams) need
+ * workspaces of their own.
+ *
+ * Size limits, far above decode-time shapes, beyond which a call returns
+ * GQ8_ESHAPE (they keep every launch under 2^32 work-items and the index
+ * arithmetic in range): Q8_0 reads N <= 2^21 output rows, K <= 2^24 and
+ * N*K <= 2^38; W8A8 N <= 2^24; routed experts D <= 2^20; the top-k and the
+ * per-token quantizer at most 2^23 rows (per-token K <= 2^24); the
+ * quantizers and the packer at most 2^32 - 256 blocks, slots or 16-byte
+ * pieces; the read probe at most that many 16-byte pieces.
+ *
  * Pages cited (by title and section):
  *   HC-Q8 page  "sycl: STRATA_HC_Q8=1 reads the Q8_0 hyper-connection projections" (PR #2810)
  *   EP page     "sycl: --expert-parallel-device N, two Arc cards compute each layer's experts together" (PR #1798)

@@ -185,3 +185,40 @@ def test_per_token_argument_checks(lib):
                                    None, 0, None) == lib.EWORKSPACE
     assert raw.gq8_w8a8_gemm_bf16x(dummy, dummy, dummy, dummy, dummy, None, 16, 16, 64,
                                    dummy, 16 * 64, None) == lib.EWORKSPACE
+
+
+def test_size_limits_return_eshape(lib):
+    """Sizes past the documented limits are rejected before any device work (no int overflow in
+    the checks, no launch past 2^32 work-items)."""
+    raw = lib.raw()
+    dummy = 1 << 20  # never dereferenced
+    # Q8_0 reads: rows above 2^21, depth above 2^24, rows x depth above 2^38
+    assert raw.gq8_q8_0_gemv(dummy, dummy, dummy, 1, (1 << 21) + 32, 64, None, 0, None) == lib.ESHAPE
+    assert raw.gq8_q8_0_gemv(dummy, dummy, dummy, 1, 8, (1 << 24) + 32, None, 0, None) == lib.ESHAPE
+    assert raw.gq8_q8_0_gemv(dummy, dummy, dummy, 1, 1 << 21, 1 << 18, None, 0, None) == lib.ESHAPE
+    assert raw.gq8_hc_q8_down(dummy, dummy, dummy, 1e-6, dummy, None, 1, 320, (1 << 24) + 32,
+                              None, 0, None) == lib.ESHAPE
+    assert raw.gq8_hc_q8_up(dummy, dummy, dummy, 1, (1 << 21) + 16, 320, None, 0, None) == lib.ESHAPE
+    assert raw.gq8_hc_q8_pair(dummy, dummy, dummy, 1e-6, dummy, dummy, None, dummy, 1, 320,
+                              (1 << 24) + 32, None, 0, None) == lib.ESHAPE
+    # W8A8 columns above 2^24: product, packer and packed size
+    assert raw.gq8_w8a8_gemm(dummy, dummy, dummy, dummy, dummy, 4, (1 << 24) + 16, 64, None, 0,
+                             None) == lib.ESHAPE
+    assert raw.gq8_w8a8_pack(dummy, 64, (1 << 24) + 16, dummy, None) == lib.ESHAPE
+    assert lib.gq8_w8a8_packed_bytes(64, (1 << 24) + 16) == 0
+    assert lib.gq8_w8a8_packed_bytes(2**31 - 1, 16) == 16 * 2**31        # no overflow in K + 63
+    assert raw.gq8_w8a8_pack(dummy, 2**31 - 16, 1 << 12, dummy, None) == lib.ESHAPE
+    # quantizers: more than 2^32 - 256 blocks
+    assert raw.gq8_q8_0_quantize(dummy, 1 << 20, 1 << 18, dummy, None) == lib.ESHAPE
+    assert raw.gq8_q8_0_split_from_blocks(dummy, 1 << 20, 1 << 18, dummy, None) == lib.ESHAPE
+    assert raw.gq8_q8_1_quantize(dummy, 1 << 20, 1 << 18, dummy, dummy, None, None) == lib.ESHAPE
+    assert raw.gq8_quantize_per_token(dummy, (1 << 23) + 1, 64, dummy, dummy, None) == lib.ESHAPE
+    # routed experts: width above 2^20; T * topk that overflows 32 bits is still rejected
+    assert raw.gq8_moe_q8_0_routed(dummy, dummy, dummy, dummy, dummy, dummy, dummy,
+                                   4, 8, 512, (1 << 20) + 32, 512, None, 0, None) == lib.ESHAPE
+    assert raw.gq8_moe_q8_0_routed(dummy, dummy, dummy, dummy, dummy, dummy, dummy,
+                                   16, 1 << 28, 512, 2048, 512, None, 0, None) == lib.ESHAPE
+    assert raw.gq8_moe_plan(dummy, 1 << 16, 1 << 16, 512, dummy, None) == lib.ESHAPE
+    assert raw.gq8_moe_route(dummy, (1 << 23) + 1, 512, 8, dummy, dummy, None) == lib.ESHAPE
+    # read probe: more than 2^32 - 256 pieces of 16 bytes
+    assert raw.gq8_read_probe(dummy, 1 << 40, dummy, None) == lib.ESHAPE
