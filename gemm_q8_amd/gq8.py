@@ -1,7 +1,8 @@
 """Thin Python binding of libgq8.so (include/gq8.h), same names and argument order as the C ABI.
 
-Argument marshalling only: device-pointer arguments accept a torch tensor (its data_ptr()), an
-int address, or None (NULL); `stream` defaults to torch's current stream on the current device.
+Argument marshalling only: device-pointer arguments accept a contiguous torch tensor on the GPU
+(its data_ptr()), an int address, or None (NULL); the `_host` calls take C-contiguous numpy
+arrays or contiguous CPU tensors instead (anything else raises ValueError before the call); `stream` defaults to torch's current stream on the current device.
 A negative status raises GQ8Error. Every computation happens in the library's HIP kernels.
 
 Importing this module loads libgq8.so and fails loudly if it has not been built
@@ -80,14 +81,31 @@ class GQ8Error(RuntimeError):
         super().__init__(f"{fn}: status {status} ({gq8_status_str(status)})")
 
 
-def _ptr(x):
-    if x is None:
-        return None
-    if isinstance(x, int):
+def _dev(x):
+    """Device address: a contiguous torch tensor on the GPU, an int address, or None."""
+    if x is None or isinstance(x, int):
         return x
-    if hasattr(x, "__array_interface__"):        # numpy array on the host (the _host calls)
-        assert x.flags["C_CONTIGUOUS"], "host arrays must be contiguous"
+    if hasattr(x, "__array_interface__"):
+        raise ValueError("a host (numpy) array was given where device memory is required")
+    if not x.is_cuda:
+        raise ValueError("a CPU tensor was given where device memory is required")
+    if not x.is_contiguous():
+        raise ValueError("device tensors must be contiguous")
+    return x.data_ptr()
+
+
+def _host(x):
+    """Host address: a C-contiguous numpy array, a contiguous CPU torch tensor, an int, or None."""
+    if x is None or isinstance(x, int):
+        return x
+    if hasattr(x, "__array_interface__"):
+        if not x.flags["C_CONTIGUOUS"]:
+            raise ValueError("host arrays must be C-contiguous")
         return x.__array_interface__["data"][0]
+    if x.is_cuda:
+        raise ValueError("a GPU tensor was given where host memory is required")
+    if not x.is_contiguous():
+        raise ValueError("host tensors must be contiguous")
     return x.data_ptr()
 
 
@@ -125,17 +143,17 @@ def gq8_q8_0_bytes(rows, K):
 
 
 def gq8_q8_0_quantize(w, rows, K, w_split, stream=None):
-    return _check("gq8_q8_0_quantize", _lib.gq8_q8_0_quantize(_ptr(w), rows, K, _ptr(w_split), _stream(stream)))
+    return _check("gq8_q8_0_quantize", _lib.gq8_q8_0_quantize(_dev(w), rows, K, _dev(w_split), _stream(stream)))
 
 
 def gq8_q8_0_split_from_blocks(blocks34, rows, K, w_split, stream=None):
     return _check("gq8_q8_0_split_from_blocks",
-                  _lib.gq8_q8_0_split_from_blocks(_ptr(blocks34), rows, K, _ptr(w_split), _stream(stream)))
+                  _lib.gq8_q8_0_split_from_blocks(_dev(blocks34), rows, K, _dev(w_split), _stream(stream)))
 
 
 def gq8_q8_1_quantize(x_bf16, rows, K, q, d, s, stream=None):
     return _check("gq8_q8_1_quantize", _lib.gq8_q8_1_quantize(
-        _ptr(x_bf16), rows, K, _ptr(q), _ptr(d), _ptr(s), _stream(stream)))
+        _dev(x_bf16), rows, K, _dev(q), _dev(d), _dev(s), _stream(stream)))
 
 
 def gq8_workspace_bytes(op, rows, N, K):
@@ -147,37 +165,37 @@ def gq8_workspace_counter_bytes(op, rows, N, K):
 
 
 def gq8_workspace_init(ws, nbytes, stream=None):
-    return _check("gq8_workspace_init", _lib.gq8_workspace_init(_ptr(ws), nbytes, _stream(stream)))
+    return _check("gq8_workspace_init", _lib.gq8_workspace_init(_dev(ws), nbytes, _stream(stream)))
 
 
 def gq8_q8_0_gemv(w_split, x, y, T, N, K, ws, ws_bytes, stream=None):
     return _check("gq8_q8_0_gemv", _lib.gq8_q8_0_gemv(
-        _ptr(w_split), _ptr(x), _ptr(y), T, N, K, _ptr(ws), ws_bytes, _stream(stream)))
+        _dev(w_split), _dev(x), _dev(y), T, N, K, _dev(ws), ws_bytes, _stream(stream)))
 
 
 def gq8_hc_q8_down(w_split, R, w_norm, eps, lo, rs_out, T, N, K, ws, ws_bytes, stream=None):
     return _check("gq8_hc_q8_down", _lib.gq8_hc_q8_down(
-        _ptr(w_split), _ptr(R), _ptr(w_norm), eps, _ptr(lo), _ptr(rs_out), T, N, K, _ptr(ws), ws_bytes,
+        _dev(w_split), _dev(R), _dev(w_norm), eps, _dev(lo), _dev(rs_out), T, N, K, _dev(ws), ws_bytes,
         _stream(stream)))
 
 
 def gq8_hc_q8_up(w_split, lo, out, T, N, K, ws, ws_bytes, stream=None):
     return _check("gq8_hc_q8_up", _lib.gq8_hc_q8_up(
-        _ptr(w_split), _ptr(lo), _ptr(out), T, N, K, _ptr(ws), ws_bytes, _stream(stream)))
+        _dev(w_split), _dev(lo), _dev(out), T, N, K, _dev(ws), ws_bytes, _stream(stream)))
 
 
 def gq8_hc_q8_pair(w_down, R, w_norm, eps, w_up, lo, rs_out, out, T, Nlr, Khc, ws, ws_bytes,
                    stream=None):
     return _check("gq8_hc_q8_pair", _lib.gq8_hc_q8_pair(
-        _ptr(w_down), _ptr(R), _ptr(w_norm), eps, _ptr(w_up), _ptr(lo), _ptr(rs_out), _ptr(out),
-        T, Nlr, Khc, _ptr(ws), ws_bytes, _stream(stream)))
+        _dev(w_down), _dev(R), _dev(w_norm), eps, _dev(w_up), _dev(lo), _dev(rs_out), _dev(out),
+        T, Nlr, Khc, _dev(ws), ws_bytes, _stream(stream)))
 
 
 def gq8_hc_bf16_pair(w_down, R, w_norm, eps, w_up, lo, rs_out, out, T, Nlr, Khc, ws, ws_bytes,
                      stream=None):
     return _check("gq8_hc_bf16_pair", _lib.gq8_hc_bf16_pair(
-        _ptr(w_down), _ptr(R), _ptr(w_norm), eps, _ptr(w_up), _ptr(lo), _ptr(rs_out), _ptr(out),
-        T, Nlr, Khc, _ptr(ws), ws_bytes, _stream(stream)))
+        _dev(w_down), _dev(R), _dev(w_norm), eps, _dev(w_up), _dev(lo), _dev(rs_out), _dev(out),
+        T, Nlr, Khc, _dev(ws), ws_bytes, _stream(stream)))
 
 
 def gq8_w8a8_packed_bytes(K, N):
@@ -185,60 +203,60 @@ def gq8_w8a8_packed_bytes(K, N):
 
 
 def gq8_w8a8_pack(W, K, N, W_packed, stream=None):
-    return _check("gq8_w8a8_pack", _lib.gq8_w8a8_pack(_ptr(W), K, N, _ptr(W_packed), _stream(stream)))
+    return _check("gq8_w8a8_pack", _lib.gq8_w8a8_pack(_dev(W), K, N, _dev(W_packed), _stream(stream)))
 
 
 def gq8_w8a8_gemm(xq, x_scale, W_packed, w_scale, out, M, N, K, ws, ws_bytes, stream=None):
     return _check("gq8_w8a8_gemm", _lib.gq8_w8a8_gemm(
-        _ptr(xq), _ptr(x_scale), _ptr(W_packed), _ptr(w_scale), _ptr(out), M, N, K, _ptr(ws), ws_bytes,
+        _dev(xq), _dev(x_scale), _dev(W_packed), _dev(w_scale), _dev(out), M, N, K, _dev(ws), ws_bytes,
         _stream(stream)))
 
 
 def gq8_w8a8_gemm_i32(xq, W_packed, acc, M, N, K, ws, ws_bytes, stream=None):
     return _check("gq8_w8a8_gemm_i32", _lib.gq8_w8a8_gemm_i32(
-        _ptr(xq), _ptr(W_packed), _ptr(acc), M, N, K, _ptr(ws), ws_bytes, _stream(stream)))
+        _dev(xq), _dev(W_packed), _dev(acc), M, N, K, _dev(ws), ws_bytes, _stream(stream)))
 
 
 def gq8_q8_0_quantize_host(w, rows, K, split_out):
-    return _check("gq8_q8_0_quantize_host", _lib.gq8_q8_0_quantize_host(_ptr(w), rows, K, _ptr(split_out)))
+    return _check("gq8_q8_0_quantize_host", _lib.gq8_q8_0_quantize_host(_host(w), rows, K, _host(split_out)))
 
 
 def gq8_q8_0_split_from_blocks_host(blocks34, rows, K, split_out):
     return _check("gq8_q8_0_split_from_blocks_host",
-                  _lib.gq8_q8_0_split_from_blocks_host(_ptr(blocks34), rows, K, _ptr(split_out)))
+                  _lib.gq8_q8_0_split_from_blocks_host(_host(blocks34), rows, K, _host(split_out)))
 
 
 def gq8_q8_1_quantize_host(x_bf16, rows, K, q, d, s=None):
     return _check("gq8_q8_1_quantize_host",
-                  _lib.gq8_q8_1_quantize_host(_ptr(x_bf16), rows, K, _ptr(q), _ptr(d), _ptr(s)))
+                  _lib.gq8_q8_1_quantize_host(_host(x_bf16), rows, K, _host(q), _host(d), _host(s)))
 
 
 def gq8_w8a8_pack_host(W, K, N, W_packed):
-    return _check("gq8_w8a8_pack_host", _lib.gq8_w8a8_pack_host(_ptr(W), K, N, _ptr(W_packed)))
+    return _check("gq8_w8a8_pack_host", _lib.gq8_w8a8_pack_host(_host(W), K, N, _host(W_packed)))
 
 
 def gq8_workspace_check(ws, nbytes, stream=None):
     """Number of non-zero arrival counters of a workspace (no entry point keeps any: 0)."""
     out = ctypes.c_int(-1)
     _check("gq8_workspace_check", _lib.gq8_workspace_check(
-        _ptr(ws), nbytes, None if stream is None else _stream(stream), ctypes.addressof(out)))
+        _dev(ws), nbytes, None if stream is None else _stream(stream), ctypes.addressof(out)))
     return out.value
 
 
 def gq8_quantize_per_token(x, M, K, xq, xs, stream=None):
     return _check("gq8_quantize_per_token", _lib.gq8_quantize_per_token(
-        _ptr(x), M, K, _ptr(xq), _ptr(xs), _stream(stream)))
+        _dev(x), M, K, _dev(xq), _dev(xs), _stream(stream)))
 
 
 def gq8_w8a8_gemm_bf16x(x, W_packed, w_scale, out, xq_out, xs_out, M, N, K, ws, ws_bytes, stream=None):
     return _check("gq8_w8a8_gemm_bf16x", _lib.gq8_w8a8_gemm_bf16x(
-        _ptr(x), _ptr(W_packed), _ptr(w_scale), _ptr(out), _ptr(xq_out), _ptr(xs_out), M, N, K,
-        _ptr(ws), ws_bytes, _stream(stream)))
+        _dev(x), _dev(W_packed), _dev(w_scale), _dev(out), _dev(xq_out), _dev(xs_out), M, N, K,
+        _dev(ws), ws_bytes, _stream(stream)))
 
 
 def gq8_moe_route(logits, T, E, topk, ids, weights, stream=None):
     return _check("gq8_moe_route", _lib.gq8_moe_route(
-        _ptr(logits), T, E, topk, _ptr(ids), _ptr(weights), _stream(stream)))
+        _dev(logits), T, E, topk, _dev(ids), _dev(weights), _stream(stream)))
 
 
 def gq8_moe_plan_words(T, topk):
@@ -246,7 +264,7 @@ def gq8_moe_plan_words(T, topk):
 
 
 def gq8_moe_plan(ids, T, topk, E, plan, stream=None):
-    return _check("gq8_moe_plan", _lib.gq8_moe_plan(_ptr(ids), T, topk, E, _ptr(plan), _stream(stream)))
+    return _check("gq8_moe_plan", _lib.gq8_moe_plan(_dev(ids), T, topk, E, _dev(plan), _stream(stream)))
 
 
 def gq8_moe_workspace_bytes(T, topk, D, F):
@@ -256,22 +274,22 @@ def gq8_moe_workspace_bytes(T, topk, D, F):
 def gq8_moe_q8_0_routed(xq, xd, ids, weights, w_gate_up, w_down, out, T, topk, E, D, F, ws, ws_bytes,
                         stream=None):
     return _check("gq8_moe_q8_0_routed", _lib.gq8_moe_q8_0_routed(
-        _ptr(xq), _ptr(xd), _ptr(ids), _ptr(weights), _ptr(w_gate_up), _ptr(w_down), _ptr(out),
-        T, topk, E, D, F, _ptr(ws), ws_bytes, _stream(stream)))
+        _dev(xq), _dev(xd), _dev(ids), _dev(weights), _dev(w_gate_up), _dev(w_down), _dev(out),
+        T, topk, E, D, F, _dev(ws), ws_bytes, _stream(stream)))
 
 
 def gq8_moe_q8_0_routed_bf16(x, ids, weights, w_gate_up, w_down, out, T, topk, E, D, F, ws, ws_bytes,
                              stream=None):
     return _check("gq8_moe_q8_0_routed_bf16", _lib.gq8_moe_q8_0_routed_bf16(
-        _ptr(x), _ptr(ids), _ptr(weights), _ptr(w_gate_up), _ptr(w_down), _ptr(out),
-        T, topk, E, D, F, _ptr(ws), ws_bytes, _stream(stream)))
+        _dev(x), _dev(ids), _dev(weights), _dev(w_gate_up), _dev(w_down), _dev(out),
+        T, topk, E, D, F, _dev(ws), ws_bytes, _stream(stream)))
 
 
 def gq8_moe_q8_0_routed_flags(x, xd, ids, weights, w_gate_up, w_down, out, T, topk, E, D, F, flags,
                               ws, ws_bytes, stream=None):
     return _check("gq8_moe_q8_0_routed_flags", _lib.gq8_moe_q8_0_routed_flags(
-        _ptr(x), _ptr(xd), _ptr(ids), _ptr(weights), _ptr(w_gate_up), _ptr(w_down), _ptr(out),
-        T, topk, E, D, F, flags, _ptr(ws), ws_bytes, _stream(stream)))
+        _dev(x), _dev(xd), _dev(ids), _dev(weights), _dev(w_gate_up), _dev(w_down), _dev(out),
+        T, topk, E, D, F, flags, _dev(ws), ws_bytes, _stream(stream)))
 
 
 def gq8_read_probe_sink_floats(nbytes):
@@ -279,7 +297,7 @@ def gq8_read_probe_sink_floats(nbytes):
 
 
 def gq8_read_probe(src, nbytes, sink, stream=None):
-    return _check("gq8_read_probe", _lib.gq8_read_probe(_ptr(src), nbytes, _ptr(sink), _stream(stream)))
+    return _check("gq8_read_probe", _lib.gq8_read_probe(_dev(src), nbytes, _dev(sink), _stream(stream)))
 
 
 def raw():

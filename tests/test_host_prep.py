@@ -97,7 +97,18 @@ def test_host_prep_argument_checks(lib):
 def test_workspace_check_reports_no_counters(lib):
     assert lib.gq8_workspace_check(None, 0) == 0
     buf = np.zeros(256, np.uint8)
-    assert lib.gq8_workspace_check(buf, buf.nbytes) == 0
+    # the check reads no memory (no entry point keeps counters): any address will do
+    assert lib.gq8_workspace_check(buf.ctypes.data, buf.nbytes) == 0
+    # the binding refuses host arrays and CPU tensors where device memory is required, and GPU
+    # memory where host memory is required, before calling the library
+    with pytest.raises(ValueError):
+        lib.gq8_workspace_check(buf, buf.nbytes)
+    import torch
+    with pytest.raises(ValueError):
+        lib.gq8_q8_0_gemv(torch.zeros(64, dtype=torch.uint8), None, None, 1, 1, 32, None, 0, 0)
+    with pytest.raises(ValueError):
+        lib.gq8_q8_1_quantize_host(np.zeros((4, 64), np.uint16)[:, :32], 4, 32,
+                                   np.zeros(128, np.int8), np.zeros(4, np.uint16))
     raw = lib.raw()
     assert raw.gq8_workspace_check(None, 64, None, None) == lib.EINVAL
 
