@@ -20,8 +20,8 @@ Output: one JSON line on stdout (metric = weight bytes / time in GB/s), with
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload (host CPU model
                 and thread counts stated).
 --all-configs also times the other workloads (BF16 comparison pair, Q8_0 GEMV T sweep, W8A8
-sweep, routed MoE variants) and writes their lines to --report (default
-gpurun_out/bench_all.jsonl) and stderr; --only and --w8a8-ms select among them.
+sweep, routed MoE variants) and writes their lines to --report (default bench_all.jsonl) and
+stderr; --only and --w8a8-ms select among them.
 """
 from __future__ import annotations
 
@@ -447,7 +447,8 @@ def main():
     ap.add_argument("--only", default="probe,hcbf16,gemv,w8a8,moe",
                     help="with --all-configs: comma-separated subset of probe,hcbf16,gemv,w8a8,moe")
     ap.add_argument("--w8a8-ms", default="1,4,8,16,32", help="with --all-configs: W8A8 M values")
-    ap.add_argument("--report", default="gpurun_out/bench_all.jsonl")
+    ap.add_argument("--report", default="bench_all.jsonl",
+                    help="file for the --all-configs lines (JSON, one per line)")
     ap.add_argument("--reps", type=int, default=20,
                     help="replays of each per-call timing graph (per-T pair, down, up)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -455,7 +456,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU sharding is described, not run", file=sys.stderr)
         sys.exit(2)
 
