@@ -47,6 +47,23 @@ constexpr int64_t kMaxMoeD = int64_t(1) << 20;       // routed-expert model widt
 constexpr int64_t kMaxRouteT = int64_t(1) << 23;     // token rows of the top-k and the per-token quantizer
 constexpr uint64_t kMaxItems = (uint64_t(1) << 32) - 256;   // one-work-item-per-element launches
 
+// The largest grids these limits allow, in work-items (each must stay below 2^32):
+constexpr uint64_t kItemCap = uint64_t(1) << 32;
+// GEMV work-group kernel: up to 16 waves per output row
+static_assert(uint64_t(kMaxQ8Rows) * 16 * 64 < kItemCap, "GEMV grid");
+// 512-column slab kernels (down read, GEMV from T = 5): ceil(K/512) x ceil(N/64) groups of 256
+static_assert((uint64_t(kMaxQ8Elems) / (512 * 64) + uint64_t(kMaxQ8Rows) / 64 +
+               uint64_t(kMaxQ8Depth) / 512 + 1) * 256 < kItemCap, "slab grid");
+// up reads (N output rows = the pair's depth): ceil(N/64) groups of up to 512
+static_assert((uint64_t(kMaxQ8Depth) / 64 + 1) * 512 < kItemCap, "up-read grid");
+// W8A8: one group of up to 1024 per 16 columns
+static_assert((uint64_t(kMaxW8N) / 16 + 1) * 1024 < kItemCap, "W8A8 grid");
+// routed experts: 16 rows of D per group of 256 per token; the combine's T * D stays an int
+static_assert((uint64_t(kMaxMoeD) / 16 + 1) * 256 * kMaxT < kItemCap, "routed-expert grid");
+static_assert(uint64_t(kMaxMoeD) * kMaxT < (uint64_t(1) << 31), "routed-expert combine index");
+// top-k and per-token quantizer: one group of 256 per row
+static_assert(uint64_t(kMaxRouteT) * 256 < kItemCap, "per-row grids");
+
 static int check_ws(void* ws, size_t ws_bytes, size_t need) {
     if (need == 0) return GQ8_OK;
     if (ws == nullptr || ws_bytes < need) return GQ8_EWORKSPACE;
