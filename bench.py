@@ -21,7 +21,7 @@ Output: one JSON line on stdout (metric = weight bytes / time in GB/s), with
                 and thread counts stated).
 --all-configs also times the other workloads (BF16 comparison pair, Q8_0 GEMV T sweep, W8A8
 sweep, routed MoE variants) and writes their lines to --report (default bench_all.jsonl) and
-stderr; --only and --w8a8-ms select among them.
+stderr; --only, --w8a8-ms and --gemv-ts select among them.
 """
 from __future__ import annotations
 
@@ -241,7 +241,7 @@ def cpu_baseline(synth, budget_s):
 
 # ------------------------------------------------------------------------------------ other configs
 
-def bench_other_configs(torch, gq8, synth, dev, stream, report, only=None, w8a8_ms=None):
+def bench_other_configs(torch, gq8, synth, dev, stream, report, only=None, w8a8_ms=None, gemv_ts=None):
     from gemm_q8_amd.device import q8_0_from_f32, to_dev, workspace
     lines = []
     only = set(only or ("probe", "hcbf16", "gemv", "w8a8", "moe"))
@@ -273,7 +273,7 @@ def bench_other_configs(torch, gq8, synth, dev, stream, report, only=None, w8a8_
     if "hcbf16" in only:
         bench_hc_bf16(torch, gq8, synth, dev, timed, emit)
     if "gemv" in only:
-        bench_gemv_sweep(torch, gq8, synth, dev, timed, emit)
+        bench_gemv_sweep(torch, gq8, synth, dev, timed, emit, gemv_ts)
     if "w8a8" in only:
         bench_w8a8_sweep(torch, gq8, synth, dev, timed, emit, ms)
     if "moe" in only:
@@ -318,14 +318,14 @@ def bench_hc_bf16(torch, gq8, synth, dev, timed, emit):
     del bds, bus, qds, qus
 
 
-def bench_gemv_sweep(torch, gq8, synth, dev, timed, emit):
+def bench_gemv_sweep(torch, gq8, synth, dev, timed, emit, gemv_ts=None):
     from gemm_q8_amd.device import q8_0_from_f32, to_dev, workspace
     # Q8_0 GEMV N=1024 K=4096, T sweep
     d = synth.q8_0_gemv_inputs(T=16)
     w0 = q8_0_from_f32(to_dev(d["w"]))
     n = n_sets_for(w0.numel())
     ws_ = [w0] + [w0.clone() for _ in range(n - 1)]
-    for T in (1, 2, 4, 8, 16):
+    for T in tuple(gemv_ts or (1, 2, 4, 8, 16)):
         x = to_dev(np.ascontiguousarray(d["x"][:T]))
         y = torch.empty((T, 1024), dtype=torch.float32, device=dev)
         nb = gq8.gq8_workspace_bytes(gq8.OP_Q8_0_GEMV, T, 1024, 4096)
@@ -447,6 +447,7 @@ def main():
     ap.add_argument("--only", default="probe,hcbf16,gemv,w8a8,moe",
                     help="with --all-configs: comma-separated subset of probe,hcbf16,gemv,w8a8,moe")
     ap.add_argument("--w8a8-ms", default="1,4,8,16,32", help="with --all-configs: W8A8 M values")
+    ap.add_argument("--gemv-ts", default="1,2,4,8,16", help="token rows of the GEMV sweep")
     ap.add_argument("--report", default="bench_all.jsonl",
                     help="file for the --all-configs lines (JSON, one per line)")
     ap.add_argument("--reps", type=int, default=20,
@@ -577,7 +578,8 @@ def main():
         result["cpu_baseline"] = cpu_baseline(synth, args.cpu_seconds)
     if args.all_configs:
         bench_other_configs(torch, gq8, synth, dev, stream, args.report, only=args.only.split(","),
-                            w8a8_ms=[int(m) for m in args.w8a8_ms.split(",")])
+                            w8a8_ms=[int(m) for m in args.w8a8_ms.split(",")],
+                            gemv_ts=[int(t) for t in args.gemv_ts.split(",")])
     print(json.dumps(result), flush=True)
 
 

@@ -239,9 +239,16 @@ int launch_q8_0_gemv(GemvArgs a, void* ws, hipStream_t st) { GQ8_T_SWITCH(launch
 
 constexpr int kDnNB = kDownSlab / 32;      // Q8_0 blocks per slab
 constexpr int kDnStride = kDownSlab + 16;  // padded LDS row stride of a wave's weight tile (bytes)
-constexpr int kDnRows = 64;                // rows per work-group: four waves of 16
+constexpr int kDnRows = 64;                // rows per work-group: four row tiles of 16
 
-// One work-group: a slab of 512 columns x 64 rows, one 16-row MFMA tile per wave. Work-groups
+// Column parts of a work-group's slab: from T = 9 on (two A planes, so twice the staging and
+// MFMA work per wave) eight waves take the four row tiles x two column halves and add the halves
+// through LDS; up to T = 8 four waves take whole rows (the split is slower there, measured).
+template <int T, bool WB>
+constexpr int dn_parts() { return (WB || T <= 8) ? 1 : 2; }
+
+// One work-group: a slab of 512 columns x 64 rows, one 16-row MFMA tile per wave (from T = 9, two
+// waves per tile, one per 256-column half: see dn_parts). Work-groups
 // are dealt round-robin to the 8 XCDs (work-group i to XCD i % 8), each with its own L2; when the
 // slab count is a multiple of 8, XCD x gets slabs [x S/8, (x+1) S/8) for every row group, so the
 // activation columns and the 128-byte scale lines a slab group shares are fetched into one L2
@@ -264,17 +271,24 @@ constexpr int kDnRows = 64;                // rows per work-group: four waves of
 // MFMA B operand is 8 bf16 straight from the LDS tile and the block results chain in the MFMA
 // accumulator (A is zero past the slab end).
 template <int T, bool XF = false, bool WB = false>
-__global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
+__global__ void __launch_bounds__((256 * dn_parts<T, WB>())) hc_down_partial_kernel(GemvArgs a) {
+    constexpr int NCP = dn_parts<T, WB>();                         // column parts of the slab
+    constexpr int NWV = 4 * NCP;                                   // waves: 4 row tiles x NCP parts
+    constexpr int NTH = 64 * NWV;
+    constexpr int NQ = 4 / NCP;                                    // column quarters per wave
     constexpr bool PACK = T <= 8;
     constexpr int NPL = PACK ? 1 : 2;                              // A planes (hi, lo)
     constexpr int TR = PACK ? 8 : 16;                              // token rows per plane
-    constexpr int NI = kDnNB * 4 * TR / 256;                       // staging items per thread
-    constexpr int WS = WB ? 2 * kDownSlab + 16 : kDnStride;        // LDS tile row stride (bytes)
-    constexpr int NW = WB ? 16 : 8;                                // weight loads per lane
+    constexpr int NI = kDnNB * 4 * TR / NTH;                       // staging items per thread
+    constexpr int WS = WB ? 2 * kDownSlab + 16 : kDownSlab / NCP + 16;   // LDS tile row stride (bytes)
+    constexpr int NW = WB ? 16 : 8 / NCP;                          // weight loads per lane
+    constexpr int NSW = 8 / NCP;                                   // scale words (2 blocks each) per lane
     __shared__ u32x4 ua[NPL][kDnNB][64];                           // A operands, lane order
-    __shared__ float sqw[4][TR];                                   // per-wave sums of R^2
-    __shared__ __attribute__((aligned(16))) uint8_t wt[4][16 * WS];
+    __shared__ float sqw[NWV][TR];                                 // per-wave sums of R^2
+    __shared__ __attribute__((aligned(16))) uint8_t wt[NWV][16 * WS];
+    __shared__ f32x4 part1[NCP > 1 ? 4 : 1][64];                   // column part 1's sums per row tile
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rt = wave & 3, cp = wave >> 2;                       // row tile, column part
     const int N = a.N, K = a.K, nblk = K >> 5;
     const int S = a.S;
     int s, y;
@@ -289,17 +303,17 @@ __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
     const int k0 = s * kDownSlab;
     const int cw = imin(kDownSlab, K - k0);                        // multiple of 32
     const int cb = cw >> 5;
-    const int r0 = y * kDnRows + 16 * wave;                        // first row of this wave
+    const int r0 = y * kDnRows + 16 * rt;                          // first row of this wave
     const uint16_t* R = reinterpret_cast<const uint16_t*>(a.x);
 
-    // 0. activations: item it = 256 j + thread covers token t = it % TR (the same t for every
+    // 0. activations: item it = NTH j + thread covers token t = it % TR (the same t for every
     //    j), columns 32b + 8g .. +8 with b = it / (4 TR), g = (it / TR) % 4
     const int t = (int)threadIdx.x % TR;
     uint4 rv[NI], nv[NI];
     bool okv[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-        const int it = 256 * i + (int)threadIdx.x;
+        const int it = NTH * i + (int)threadIdx.x;
         const int b = it / (4 * TR), g = (it / TR) & 3;
         const int k = k0 + 32 * b + 8 * g;
         okv[i] = t < T && 32 * b < cw;
@@ -313,29 +327,32 @@ __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
             nv[i] = *reinterpret_cast<const uint4*>(a.wnorm + kc);
         }
     }
-    // block scales in the MFMA result layout: lane l needs the 16 scales of row r0 + l%16 (32
-    //    contiguous bytes when the slab is whole and scale rows are 16-byte aligned)
+    // block scales in the MFMA result layout: lane l needs the scales of row r0 + l%16 for the
+    //    wave's column part (16 contiguous bytes a part when the slab is whole and scale rows are
+    //    16-byte aligned)
     const int j = lane & 15, g = lane >> 4;
-    uint32_t sw[8];
+    const int b0 = (kDnNB / NCP) * cp;                             // first block of the part
+    uint32_t sw[NSW];
     if (!WB) {
         const int row = imin(r0 + j, N - 1);
-        const uint16_t* dr = a.d + (size_t)row * nblk + (k0 >> 5);
+        const uint16_t* dr = a.d + (size_t)row * nblk + (k0 >> 5) + b0;
         if (cb == kDnNB && (nblk & 7) == 0) {
-            const u32x4 s01 = *reinterpret_cast<const u32x4*>(dr);
-            const u32x4 s23 = *reinterpret_cast<const u32x4*>(dr + 8);
-            sw[0] = s01.x; sw[1] = s01.y; sw[2] = s01.z; sw[3] = s01.w;
-            sw[4] = s23.x; sw[5] = s23.y; sw[6] = s23.z; sw[7] = s23.w;
+#pragma unroll
+            for (int h = 0; h < NSW / 4; ++h) {
+                const u32x4 s4 = *reinterpret_cast<const u32x4*>(dr + 8 * h);
+                sw[4 * h] = s4.x; sw[4 * h + 1] = s4.y; sw[4 * h + 2] = s4.z; sw[4 * h + 3] = s4.w;
+            }
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t lo16 = 2 * i < cb ? dr[2 * i] : 0u;
-                const uint32_t hi16 = 2 * i + 1 < cb ? dr[2 * i + 1] : 0u;
+            for (int i = 0; i < NSW; ++i) {
+                const uint32_t lo16 = b0 + 2 * i < cb ? dr[2 * i] : 0u;
+                const uint32_t hi16 = b0 + 2 * i + 1 < cb ? dr[2 * i + 1] : 0u;
                 sw[i] = lo16 | (hi16 << 16);
             }
         }
     }
-    // 1. weights: quarter q = i / 2 covers columns 128q .. +128; load i covers rows 8(i%2) ..
-    //    +8 of it (8 lanes a row)
+    // 1. weights: the wave's quarter q = i / 2 (slab quarter NQ cp + q) covers columns
+    //    128 (NQ cp + q) .. +128; load i covers rows 8(i%2) .. +8 of it (8 lanes a row)
     u32x4 wv[NW];
     if constexpr (WB) {
         // quarter q = i / 4 covers bytes 256q .. +256 of the slab's 1024-byte rows; load i covers
@@ -350,7 +367,7 @@ __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
 #pragma unroll
         for (int i = 0; i < NW; ++i) {
             const int row = imin(r0 + 8 * (i & 1) + (lane >> 3), N - 1);
-            const int col = k0 + imin(128 * (i >> 1) + 16 * (lane & 7), cw - 16);
+            const int col = k0 + imin(128 * (NQ * cp + (i >> 1)) + 16 * (lane & 7), cw - 16);
             wv[i] = ld_nt16(a.q + (size_t)row * K + col);
         }
     }
@@ -361,7 +378,7 @@ __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
     float r2acc = 0.f;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-        const int it = 256 * i + (int)threadIdx.x;
+        const int it = NTH * i + (int)threadIdx.x;
         const int b = it / (4 * TR), g = (it / TR) & 3;
         const bool ok = okv[i];
         const uint32_t rw[4] = {rv[i].x, rv[i].y, rv[i].z, rv[i].w};
@@ -432,7 +449,7 @@ __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
     }
     if constexpr (!WB)
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
+    for (int qq = 0; qq < NQ; ++qq) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
             *reinterpret_cast<u32x4*>(tile + (8 * i + (lane >> 3)) * WS + 128 * qq + 16 * (lane & 7)) =
@@ -442,8 +459,8 @@ __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
         u32x4 x0[4], x1[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int b = 4 * qq + i;
-            q[i] = *reinterpret_cast<const uint2*>(tile + j * WS + 32 * b + 8 * g);
+            const int bl = 4 * qq + i, b = b0 + bl;             // block in the part, in the slab
+            q[i] = *reinterpret_cast<const uint2*>(tile + j * WS + 32 * bl + 8 * g);
             x0[i] = ua[0][b][lane];
             if (!PACK) x1[i] = ua[NPL - 1][b][lane];
         }
@@ -458,15 +475,24 @@ __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
         __builtin_amdgcn_sched_barrier(0);     // four MFMAs in flight, then their scales
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int b = 4 * qq + i;
-            const uint32_t sp = sw[b >> 1];
-            const float dsc = b < cb ? h2f((uint16_t)((b & 1) ? (sp >> 16) : (sp & 0xffffu))) : 0.f;
+            const int bl = 4 * qq + i, b = b0 + bl;
+            const uint32_t sp = sw[bl >> 1];
+            const float dsc = b < cb ? h2f((uint16_t)((bl & 1) ? (sp >> 16) : (sp & 0xffffu))) : 0.f;
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[v] = fmaf(dsc, D[i][v], acc[v]);
         }
     }
 
-    // 4. partial sums of this slab, part[s][t][n] (D lane l: column n = r0 + l%16, rows 4(l/16)+v)
+    // 4. the column parts' sums added in part order (part 1's through LDS), then the partial sums
+    //    of this slab, part[s][t][n] (D lane l: column n = r0 + l%16, rows 4(l/16)+v)
+    if constexpr (NCP > 1) {
+        if (cp == 1) part1[rt][lane] = acc;
+        __syncthreads();
+        if (cp == 1) return;
+        const f32x4 o = part1[rt][lane];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[v] = acc[v] + o[v];
+    }
     const int n = r0 + j;
     if (PACK) {
         // rows 8..15 (lanes 32..63) hold the lo parts of tokens 0..7: add them to rows 0..7
@@ -489,7 +515,10 @@ __global__ void __launch_bounds__(256) hc_down_partial_kernel(GemvArgs a) {
     }
     if (!XF && y == 0 && threadIdx.x < T) {
         const int tt = threadIdx.x;
-        a.ssq[(size_t)s * T + tt] = ((sqw[0][tt] + sqw[1][tt]) + sqw[2][tt]) + sqw[3][tt];
+        float v = sqw[0][tt];
+#pragma unroll
+        for (int w = 1; w < NWV; ++w) v += sqw[w][tt];
+        a.ssq[(size_t)s * T + tt] = v;
     }
 }
 
@@ -549,7 +578,7 @@ static int launch_down_t(GemvArgs a, void* ws, hipStream_t st) {
     a.S = S;
     a.part = reinterpret_cast<float*>(w);
     a.ssq = reinterpret_cast<float*>(w + round_up((size_t)S * T * a.N * sizeof(float), kCounterAlign));
-    hipLaunchKernelGGL((hc_down_partial_kernel<T>), dim3(S * ((a.N + kDnRows - 1) / kDnRows)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((hc_down_partial_kernel<T>), dim3(S * ((a.N + kDnRows - 1) / kDnRows)), dim3(256 * dn_parts<T, false>()), 0, st, a);
     int rc = launch_status();
     if (rc != GQ8_OK) return rc;
     hipLaunchKernelGGL(hc_down_combine_kernel<false>, dim3((a.N + 63) / 64, T), dim3(256), 0, st, a);
@@ -570,7 +599,7 @@ static int launch_gemv_mfma_t(GemvArgs a, void* ws, hipStream_t st) {
     a.S = S;
     a.part = static_cast<float*>(ws);
     a.ssq = nullptr;
-    hipLaunchKernelGGL((hc_down_partial_kernel<T, true>), dim3(S * ((a.N + kDnRows - 1) / kDnRows)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((hc_down_partial_kernel<T, true>), dim3(S * ((a.N + kDnRows - 1) / kDnRows)), dim3(256 * dn_parts<T, false>()), 0, st, a);
     int rc = launch_status();
     if (rc != GQ8_OK) return rc;
     hipLaunchKernelGGL(hc_down_combine_kernel<true>, dim3((a.N + 63) / 64, T), dim3(256), 0, st, a);
@@ -1027,7 +1056,7 @@ static int launch_pair_t(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st) {
         dn.S = S;
         dn.part = reinterpret_cast<float*>(w);
         dn.ssq = reinterpret_cast<float*>(w + round_up((size_t)S * T * dn.N * sizeof(float), kCounterAlign));
-        hipLaunchKernelGGL((hc_down_partial_kernel<T>), dim3(S * ((dn.N + kDnRows - 1) / kDnRows)), dim3(256), 0, st, dn);
+        hipLaunchKernelGGL((hc_down_partial_kernel<T>), dim3(S * ((dn.N + kDnRows - 1) / kDnRows)), dim3(256 * dn_parts<T, false>()), 0, st, dn);
         int rc = launch_status();
         if (rc != GQ8_OK) return rc;
         up.S = S; up.part = dn.part; up.ssq = dn.ssq; up.eps = dn.eps; up.kd = dn.K;
