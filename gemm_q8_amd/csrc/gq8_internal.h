@@ -89,6 +89,7 @@ struct W8Plan {
     int ksteps;        // K rounded up to 64, / 64
     int nw;            // waves per work-group (<= 16)
     int kpw;           // k-steps per wave
+    bool half;         // MFMA path, M <= 16, few tiles: two work-groups of 8 columns per tile
 };
 W8Plan plan_w8a8(int M, int N, int K);
 // xb != nullptr: bf16 x quantized per token inside the kernel (xq, xs unused; bf16x_fused(M, K));

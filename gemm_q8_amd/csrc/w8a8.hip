@@ -10,7 +10,10 @@
 // clamped to valid addresses, before the first MFMA / dot.
 //   M >= 2:  v_mfma_i32_16x16x64_i8 (rows past M are zero), one MFMA row tile for M <= 16 and
 //            two (sharing the weight fragment) for M <= 32. One x load per k-step per lane;
-//            the VALU dot needs M of them, which bound it from M = 4 on (measured).
+//            the VALU dot needs M of them, which bound it from M = 4 on (measured). With at most
+//            128 tiles and M <= 16, two work-groups share a tile, eight columns each, so that
+//            twice as many CUs stream the weight (measured: M = 16, N = 1536, K = 4096 5.16 ->
+//            5.00 us).
 //   M == 1:  v_dot4_i32_i8 on the VALU over the same fragments.
 // int32 sums are exact, so every order gives the one correct accumulator; the epilogue is
 // bf16( (fp32(acc) * x_scale[m]) * w_scale[n] ), two rounded fp32 products.
@@ -44,9 +47,9 @@ struct W8Scales {
     float xs, ws;
 };
 
-GQ8_DEV W8Scales w8a8_prefetch_scales(const W8Args& a, int nt) {
+GQ8_DEV W8Scales w8a8_prefetch_scales(const W8Args& a, int n0) {
     const int i = (int)threadIdx.x;
-    const int m = imin8(i >> 4, a.M - 1), n = imin8(nt * 16 + (i & 15), a.N - 1);
+    const int m = imin8(i >> 4, a.M - 1), n = imin8(n0 + (i & 15), a.N - 1);
     W8Scales sc;
     sc.xs = (a.i32_out || a.xs == nullptr) ? 0.f : a.xs[m];
     sc.ws = a.i32_out ? 0.f : a.wsc[n];
@@ -55,12 +58,13 @@ GQ8_DEV W8Scales w8a8_prefetch_scales(const W8Args& a, int nt) {
 
 // The WG's int32 tiles [NW][32][16] -> sum over waves (in wave order) -> epilogue. xs_lds: the
 // x scales computed in the work-group (the variant that quantizes x), else a.xs.
-GQ8_DEV void w8a8_finish(const W8Args& a, int nt, int nw, int (*tile)[32][16], W8Scales sc,
+GQ8_DEV void w8a8_finish(const W8Args& a, int n0, int ncols, int nw, int (*tile)[32][16], W8Scales sc,
                          const float* xs_lds = nullptr) {
     __syncthreads();
     for (int i = threadIdx.x; i < a.M * 16; i += blockDim.x) {
         const int m = i >> 4, nl = i & 15;
-        const int n = nt * 16 + nl;
+        if (nl >= ncols) continue;
+        const int n = n0 + nl;
         int p[16];
 #pragma unroll
         for (int w = 0; w < 16; ++w) p[w] = tile[w][m][nl];     // all reads in flight
@@ -137,16 +141,22 @@ GQ8_DEV uint32_t absmax8_bf16_bits(u32x4 r) {
 
 GQ8_DEV float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-template <int MT, int KPW>
+// HALF: two work-groups per 16-column tile, eight columns each (twice the work-groups when the
+// tiles are fewer than the CUs): lane l loads the fragment lane of column 8h + l%8, so lanes l
+// and l + 8 load the same bytes (one cache-line request) and the MFMA computes each of the
+// work-group's eight columns twice.
+template <int MT, int KPW, bool HALF = false>
 __global__ void __launch_bounds__(1024) w8a8_mfma_kernel(W8Args a) {
     __shared__ int tile[16][32][16];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nw = blockDim.x >> 6;
-    const int nt = blockIdx.x;
+    const int nt = HALF ? (int)blockIdx.x >> 1 : (int)blockIdx.x;
+    const int hf = HALF ? (int)blockIdx.x & 1 : 0;
+    const int n0 = nt * 16 + 8 * hf;
     v4i b[KPW];
     bool ok[KPW];
-    load_frags<KPW>(a, nt, wave, nw, lane, b, ok);
-    const W8Scales sc = w8a8_prefetch_scales(a, nt);
+    load_frags<KPW>(a, nt, wave, nw, HALF ? ((lane & 48) | (8 * hf + (lane & 7))) : lane, b, ok);
+    const W8Scales sc = w8a8_prefetch_scales(a, n0);
     const int mrow = lane & 15;
     v4i x0[KPW], x1[KPW];
 #pragma unroll
@@ -176,7 +186,7 @@ __global__ void __launch_bounds__(1024) w8a8_mfma_kernel(W8Args a) {
         tile[wave][r0 + v][col] = acc0[v];
         if (MT == 2) tile[wave][16 + r0 + v][col] = acc1[v];
     }
-    w8a8_finish(a, nt, nw, tile, sc);
+    w8a8_finish(a, n0, HALF ? 8 : 16, nw, tile, sc);
 }
 
 // x is bf16 [M][K], M <= 8, M * K <= 16384 (the variant that quantizes x per token in the
@@ -258,7 +268,7 @@ __global__ void __launch_bounds__(1024) w8a8_bf16x_kernel(W8Args a) {
     const int col = lane & 15, r0 = 4 * (lane >> 4);
 #pragma unroll
     for (int v = 0; v < 4; ++v) tile[wave][r0 + v][col] = acc[v];
-    w8a8_finish(a, nt, nw, tile, sc, xs_s);
+    w8a8_finish(a, nt * 16, 16, nw, tile, sc, xs_s);
 }
 
 template <int MC, int KPW>
@@ -270,7 +280,7 @@ __global__ void __launch_bounds__(1024) w8a8_dot_kernel(W8Args a) {
     v4i b[KPW];
     bool ok[KPW];
     load_frags<KPW>(a, nt, wave, nw, lane, b, ok);
-    const W8Scales sc = w8a8_prefetch_scales(a, nt);
+    const W8Scales sc = w8a8_prefetch_scales(a, nt * 16);
     int acc[MC];
 #pragma unroll
     for (int m = 0; m < MC; ++m) acc[m] = 0;
@@ -301,7 +311,7 @@ __global__ void __launch_bounds__(1024) w8a8_dot_kernel(W8Args a) {
         t += (int)lane_xor32((uint32_t)t);
         if (lane < 16 && m < a.M) tile[wave][m][lane] = t;
     }
-    w8a8_finish(a, nt, nw, tile, sc);
+    w8a8_finish(a, nt * 16, 16, nw, tile, sc);
 }
 
 // ------------------------------------------------------------------------------------ planning
@@ -310,6 +320,7 @@ W8Plan plan_w8a8(int M, int N, int K) {
     W8Plan p{};
     p.mfma = M >= 2;
     p.ntiles = (N + 15) / 16;
+    p.half = p.mfma && M <= 16 && 2 * p.ntiles <= 256;
     p.ksteps = (K + 63) / 64;
     p.nw = p.ksteps < 16 ? p.ksteps : 16;
     p.kpw = (p.ksteps + p.nw - 1) / p.nw;
@@ -318,14 +329,15 @@ W8Plan plan_w8a8(int M, int N, int K) {
 
 template <int KPW>
 static int launch_w8a8_kpw(const W8Plan& p, W8Args a, hipStream_t st) {
-    const dim3 g(p.ntiles), b(64 * p.nw);
+    const dim3 g(p.ntiles), g2(2 * p.ntiles), b(64 * p.nw);
     if (a.xb != nullptr) {                 // bf16 x quantized in the work-group
         const int nch = a.M * (a.K >> 3), nthr = 64 * p.nw, xc = (nch + nthr - 1) / nthr;
         if (xc <= 1) hipLaunchKernelGGL((w8a8_bf16x_kernel<KPW, 1>), g, b, 0, st, a);
         else if (xc <= 2) hipLaunchKernelGGL((w8a8_bf16x_kernel<KPW, 2>), g, b, 0, st, a);
         else return GQ8_ESHAPE;
     } else if (p.mfma) {
-        if (a.M <= 16) hipLaunchKernelGGL((w8a8_mfma_kernel<1, KPW>), g, b, 0, st, a);
+        if (p.half) hipLaunchKernelGGL((w8a8_mfma_kernel<1, KPW, true>), g2, b, 0, st, a);
+        else if (a.M <= 16) hipLaunchKernelGGL((w8a8_mfma_kernel<1, KPW>), g, b, 0, st, a);
         else hipLaunchKernelGGL((w8a8_mfma_kernel<2, KPW>), g, b, 0, st, a);
     } else if (a.M <= 1) {
         hipLaunchKernelGGL((w8a8_dot_kernel<1, KPW>), g, b, 0, st, a);
