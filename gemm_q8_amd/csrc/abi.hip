@@ -41,7 +41,7 @@ static inline hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
 // the kernels' int index arithmetic in range; a call beyond them returns GQ8_ESHAPE.
 constexpr int64_t kMaxQ8Rows = int64_t(1) << 21;     // output rows of a Q8_0 read
 constexpr int64_t kMaxQ8Depth = int64_t(1) << 24;    // depth of a Q8_0 read
-constexpr int64_t kMaxQ8Elems = int64_t(1) << 38;    // rows x depth of a Q8_0 read
+constexpr int64_t kMaxQ8Elems = int64_t(1) << 36;    // rows x depth of a Q8_0 read
 constexpr int64_t kMaxW8N = int64_t(1) << 24;        // W8A8 output columns
 constexpr int64_t kMaxMoeD = int64_t(1) << 20;       // routed-expert model width
 constexpr int64_t kMaxRouteT = int64_t(1) << 23;     // token rows of the top-k and the per-token quantizer
@@ -51,9 +51,10 @@ constexpr uint64_t kMaxItems = (uint64_t(1) << 32) - 256;   // one-work-item-per
 constexpr uint64_t kItemCap = uint64_t(1) << 32;
 // GEMV work-group kernel: up to 16 waves per output row
 static_assert(uint64_t(kMaxQ8Rows) * 16 * 64 < kItemCap, "GEMV grid");
-// 512-column slab kernels (down read, GEMV from T = 5): ceil(K/512) x ceil(N/64) groups of 256
-static_assert((uint64_t(kMaxQ8Elems) / (512 * 64) + uint64_t(kMaxQ8Rows) / 64 +
-               uint64_t(kMaxQ8Depth) / 512 + 1) * 256 < kItemCap, "slab grid");
+// slab kernels (down read: 512 columns; GEMV from T = 5: 256): ceil(K/256) x ceil(N/64) groups
+// of up to 512
+static_assert((uint64_t(kMaxQ8Elems) / (256 * 64) + uint64_t(kMaxQ8Rows) / 64 +
+               uint64_t(kMaxQ8Depth) / 256 + 1) * 512 < kItemCap, "slab grid");
 // up reads (N output rows = the pair's depth): ceil(N/64) groups of up to 512
 static_assert((uint64_t(kMaxQ8Depth) / 64 + 1) * 512 < kItemCap, "up-read grid");
 // W8A8: one group of up to 1024 per 16 columns

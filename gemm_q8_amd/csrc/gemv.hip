@@ -190,8 +190,8 @@ constexpr int kGemvWaveMaxK = 4096;
 template <int T> constexpr int gemv_rw() { return T == 2 ? 4 : (T <= 4 ? 2 : 1); }
 
 // From this many token rows on, the GEMV runs on MFMA (the down read's slab kernel with x as the
-// A operand, then its combine): the VALU dot re-reads x from cache for every 16 weight bytes,
-// which binds once T grows.
+// A operand and 256-column slabs, then its combine): the VALU dot re-reads x from cache for
+// every 16 weight bytes, which binds once T grows.
 constexpr int kGemvMfmaT = 5;
 
 template <int T>
@@ -270,20 +270,22 @@ constexpr int dn_parts() { return (WB || T <= 8) ? 1 : 2; }
 // 16 x 1024 bytes, read in four quarters of four 1 KiB loads (four rows x 256 bytes each); the
 // MFMA B operand is 8 bf16 straight from the LDS tile and the block results chain in the MFMA
 // accumulator (A is zero past the slab end).
-template <int T, bool XF = false, bool WB = false>
+template <int T, bool XF = false, bool WB = false, int SLAB = kDownSlab>
 __global__ void __launch_bounds__((256 * dn_parts<T, WB>())) hc_down_partial_kernel(GemvArgs a) {
+    static_assert(!WB || SLAB == kDownSlab, "the BF16 read uses 512-column slabs");
+    constexpr int NB = SLAB / 32;                                  // Q8_0 blocks per slab
     constexpr int NCP = dn_parts<T, WB>();                         // column parts of the slab
     constexpr int NWV = 4 * NCP;                                   // waves: 4 row tiles x NCP parts
     constexpr int NTH = 64 * NWV;
-    constexpr int NQ = 4 / NCP;                                    // column quarters per wave
+    constexpr int NQ = SLAB / 128 / NCP;                           // 128-column quarters per wave
     constexpr bool PACK = T <= 8;
     constexpr int NPL = PACK ? 1 : 2;                              // A planes (hi, lo)
     constexpr int TR = PACK ? 8 : 16;                              // token rows per plane
-    constexpr int NI = kDnNB * 4 * TR / NTH;                       // staging items per thread
-    constexpr int WS = WB ? 2 * kDownSlab + 16 : kDownSlab / NCP + 16;   // LDS tile row stride (bytes)
-    constexpr int NW = WB ? 16 : 8 / NCP;                          // weight loads per lane
-    constexpr int NSW = 8 / NCP;                                   // scale words (2 blocks each) per lane
-    __shared__ u32x4 ua[NPL][kDnNB][64];                           // A operands, lane order
+    constexpr int NI = NB * 4 * TR / NTH;                          // staging items per thread
+    constexpr int WS = WB ? 2 * kDownSlab + 16 : SLAB / NCP + 16;  // LDS tile row stride (bytes)
+    constexpr int NW = WB ? 16 : 2 * NQ;                           // weight loads per lane
+    constexpr int NSW = NB / 2 / NCP;                              // scale words (2 blocks each) per lane
+    __shared__ u32x4 ua[NPL][NB][64];                              // A operands, lane order
     __shared__ float sqw[NWV][TR];                                 // per-wave sums of R^2
     __shared__ __attribute__((aligned(16))) uint8_t wt[NWV][16 * WS];
     __shared__ f32x4 part1[NCP > 1 ? 4 : 1][64];                   // column part 1's sums per row tile
@@ -300,8 +302,8 @@ __global__ void __launch_bounds__((256 * dn_parts<T, WB>())) hc_down_partial_ker
         s = blockIdx.x % S;
         y = blockIdx.x / S;
     }
-    const int k0 = s * kDownSlab;
-    const int cw = imin(kDownSlab, K - k0);                        // multiple of 32
+    const int k0 = s * SLAB;
+    const int cw = imin(SLAB, K - k0);                             // multiple of 32
     const int cb = cw >> 5;
     const int r0 = y * kDnRows + 16 * rt;                          // first row of this wave
     const uint16_t* R = reinterpret_cast<const uint16_t*>(a.x);
@@ -331,16 +333,21 @@ __global__ void __launch_bounds__((256 * dn_parts<T, WB>())) hc_down_partial_ker
     //    wave's column part (16 contiguous bytes a part when the slab is whole and scale rows are
     //    16-byte aligned)
     const int j = lane & 15, g = lane >> 4;
-    const int b0 = (kDnNB / NCP) * cp;                             // first block of the part
+    const int b0 = (NB / NCP) * cp;                                // first block of the part
     uint32_t sw[NSW];
     if (!WB) {
         const int row = imin(r0 + j, N - 1);
         const uint16_t* dr = a.d + (size_t)row * nblk + (k0 >> 5) + b0;
-        if (cb == kDnNB && (nblk & 7) == 0) {
+        if (cb == NB && (nblk & 7) == 0) {
+            if constexpr (NSW >= 4) {
 #pragma unroll
-            for (int h = 0; h < NSW / 4; ++h) {
-                const u32x4 s4 = *reinterpret_cast<const u32x4*>(dr + 8 * h);
-                sw[4 * h] = s4.x; sw[4 * h + 1] = s4.y; sw[4 * h + 2] = s4.z; sw[4 * h + 3] = s4.w;
+                for (int h = 0; h < NSW / 4; ++h) {
+                    const u32x4 s4 = *reinterpret_cast<const u32x4*>(dr + 8 * h);
+                    sw[4 * h] = s4.x; sw[4 * h + 1] = s4.y; sw[4 * h + 2] = s4.z; sw[4 * h + 3] = s4.w;
+                }
+            } else {
+                const uint2 s2 = *reinterpret_cast<const uint2*>(dr);
+                sw[0] = s2.x; sw[1] = s2.y;
             }
         } else {
 #pragma unroll
@@ -587,19 +594,25 @@ static int launch_down_t(GemvArgs a, void* ws, hipStream_t st) {
 
 int launch_hc_down(GemvArgs a, void* ws, hipStream_t st) { GQ8_T_SWITCH(launch_down_t, a, ws, st) }
 
+// The GEMV's slabs are 256 columns wide (the down read's are 512): twice the work-groups on the
+// weight stream (the 1024 x 4096 read has 16 row groups), for twice the partial planes.
+constexpr int kGemvSlab = 256;
+
+static int gemv_slabs(int K) { return (K + kGemvSlab - 1) / kGemvSlab; }
+
 size_t gemv_workspace_bytes(int T, int N, int K) {
     if (T < kGemvMfmaT || N == 0 || K == 0) return 0;
-    const size_t S = hc_down_slabs(K);
+    const size_t S = gemv_slabs(K);
     return round_up(S * T * N * sizeof(float), kCounterAlign);
 }
 
 template <int T>
 static int launch_gemv_mfma_t(GemvArgs a, void* ws, hipStream_t st) {
-    const int S = hc_down_slabs(a.K);
+    const int S = gemv_slabs(a.K);
     a.S = S;
     a.part = static_cast<float*>(ws);
     a.ssq = nullptr;
-    hipLaunchKernelGGL((hc_down_partial_kernel<T, true>), dim3(S * ((a.N + kDnRows - 1) / kDnRows)), dim3(256 * dn_parts<T, false>()), 0, st, a);
+    hipLaunchKernelGGL((hc_down_partial_kernel<T, true, false, kGemvSlab>), dim3(S * ((a.N + kDnRows - 1) / kDnRows)), dim3(256 * dn_parts<T, false>()), 0, st, a);
     int rc = launch_status();
     if (rc != GQ8_OK) return rc;
     hipLaunchKernelGGL(hc_down_combine_kernel<true>, dim3((a.N + 63) / 64, T), dim3(256), 0, st, a);

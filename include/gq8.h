@@ -22,7 +22,7 @@
  * Size limits, far above decode-time shapes, beyond which a call returns
  * GQ8_ESHAPE (they keep every launch under 2^32 work-items and the index
  * arithmetic in range): Q8_0 reads N <= 2^21 output rows, K <= 2^24 and
- * N*K <= 2^38; W8A8 N <= 2^24; routed experts D <= 2^20; the top-k and the
+ * N*K <= 2^36; W8A8 N <= 2^24; routed experts D <= 2^20; the top-k and the
  * per-token quantizer at most 2^23 rows (per-token K <= 2^24); the
  * quantizers and the packer at most 2^32 - 256 blocks, slots or 16-byte
  * pieces; the read probe at most that many 16-byte pieces.

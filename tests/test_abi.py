@@ -192,7 +192,7 @@ def test_size_limits_return_eshape(lib):
     the checks, no launch past 2^32 work-items)."""
     raw = lib.raw()
     dummy = 1 << 20  # never dereferenced
-    # Q8_0 reads: rows above 2^21, depth above 2^24, rows x depth above 2^38
+    # Q8_0 reads: rows above 2^21, depth above 2^24, rows x depth above 2^36
     assert raw.gq8_q8_0_gemv(dummy, dummy, dummy, 1, (1 << 21) + 32, 64, None, 0, None) == lib.ESHAPE
     assert raw.gq8_q8_0_gemv(dummy, dummy, dummy, 1, 8, (1 << 24) + 32, None, 0, None) == lib.ESHAPE
     assert raw.gq8_q8_0_gemv(dummy, dummy, dummy, 1, 1 << 21, 1 << 18, None, 0, None) == lib.ESHAPE
