@@ -241,11 +241,12 @@ constexpr int kDnNB = kDownSlab / 32;      // Q8_0 blocks per slab
 constexpr int kDnStride = kDownSlab + 16;  // padded LDS row stride of a wave's weight tile (bytes)
 constexpr int kDnRows = 64;                // rows per work-group: four row tiles of 16
 
-// Column parts of a work-group's slab: from T = 9 on (two A planes, so twice the staging and
-// MFMA work per wave) eight waves take the four row tiles x two column halves and add the halves
-// through LDS; up to T = 8 four waves take whole rows (the split is slower there, measured).
-template <int T, bool WB>
-constexpr int dn_parts() { return (WB || T <= 8) ? 1 : 2; }
+// Column parts of a work-group's 512-column slab: from T = 9 on (two A planes, so twice the
+// staging and MFMA work per wave) eight waves take the four row tiles x two column halves and add
+// the halves through LDS; up to T = 8, and on the GEMV's narrower slabs, four waves take whole
+// rows (the split is slower there, measured).
+template <int T, bool WB, int SLAB = kDownSlab>
+constexpr int dn_parts() { return (WB || T <= 8 || SLAB < kDownSlab) ? 1 : 2; }
 
 // One work-group: a slab of 512 columns x 64 rows, one 16-row MFMA tile per wave (from T = 9, two
 // waves per tile, one per 256-column half: see dn_parts). Work-groups
@@ -271,10 +272,10 @@ constexpr int dn_parts() { return (WB || T <= 8) ? 1 : 2; }
 // MFMA B operand is 8 bf16 straight from the LDS tile and the block results chain in the MFMA
 // accumulator (A is zero past the slab end).
 template <int T, bool XF = false, bool WB = false, int SLAB = kDownSlab>
-__global__ void __launch_bounds__((256 * dn_parts<T, WB>())) hc_down_partial_kernel(GemvArgs a) {
+__global__ void __launch_bounds__((256 * dn_parts<T, WB, SLAB>())) hc_down_partial_kernel(GemvArgs a) {
     static_assert(!WB || SLAB == kDownSlab, "the BF16 read uses 512-column slabs");
     constexpr int NB = SLAB / 32;                                  // Q8_0 blocks per slab
-    constexpr int NCP = dn_parts<T, WB>();                         // column parts of the slab
+    constexpr int NCP = dn_parts<T, WB, SLAB>();                   // column parts of the slab
     constexpr int NWV = 4 * NCP;                                   // waves: 4 row tiles x NCP parts
     constexpr int NTH = 64 * NWV;
     constexpr int NQ = SLAB / 128 / NCP;                           // 128-column quarters per wave
@@ -612,7 +613,7 @@ static int launch_gemv_mfma_t(GemvArgs a, void* ws, hipStream_t st) {
     a.S = S;
     a.part = static_cast<float*>(ws);
     a.ssq = nullptr;
-    hipLaunchKernelGGL((hc_down_partial_kernel<T, true, false, kGemvSlab>), dim3(S * ((a.N + kDnRows - 1) / kDnRows)), dim3(256 * dn_parts<T, false>()), 0, st, a);
+    hipLaunchKernelGGL((hc_down_partial_kernel<T, true, false, kGemvSlab>), dim3(S * ((a.N + kDnRows - 1) / kDnRows)), dim3(256 * dn_parts<T, false, kGemvSlab>()), 0, st, a);
     int rc = launch_status();
     if (rc != GQ8_OK) return rc;
     hipLaunchKernelGGL(hc_down_combine_kernel<true>, dim3((a.N + 63) / 64, T), dim3(256), 0, st, a);
