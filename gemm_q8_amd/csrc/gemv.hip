@@ -12,10 +12,12 @@
 //    partials over its chunks, one wave sum, no LDS.
 //    Other T <= 4 (gemv_rows_kernel): a work-group owns RW rows and all of K; wave w reads
 //    1024-column chunks w, w+NW, ...; lane partials are reduced over the wave (DPP) and the
-//    waves' sums are added through LDS in wave order. T >= 5: the down read's slab kernel with
-//    x split into bf16 hi + lo as the MFMA A operand, then the combine kernel without rs.
+//    waves' sums are added through LDS in wave order. T >= 5: the down read's slab kernel on
+//    256-column slabs with x split into bf16 hi + lo as the MFMA A operand, then the combine
+//    kernel without rs.
 //  * down read (hc_down_partial_kernel): a work-group takes a 512-column slab x 64 rows, one
-//    16-row 16x16x32 bf16 MFMA tile per wave. u = R * w_norm is exact in fp32 (8-bit x 8-bit
+//    16-row 16x16x32 bf16 MFMA tile per wave (from T = 9 two waves per tile, one per column
+//    half). u = R * w_norm is exact in fp32 (8-bit x 8-bit
 //    significands) and splits exactly into bf16 hi + lo, so the MFMA products are exact; it is
 //    staged once per work-group in LDS. The wave's weight tile goes through an LDS transpose in
 //    four column quarters. The slab partial sums and sums of R^2 go to the workspace, and a
