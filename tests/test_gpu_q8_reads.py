@@ -26,7 +26,10 @@ def _gemv(gpu, wbuf, x, T, N, K):
 @pytest.mark.parametrize("T,N,K", [(1, 96, 4096), (3, 37, 1056), (5, 130, 2080), (8, 64, 96),
                                    (11, 33, 320), (16, 70, 4096), (2, 5, 32), (4, 300, 1024),
                                    (2, 77, 3104), (3, 9, 2080), (1, 1, 64), (2, 1, 4096),
-                                   (1, 333, 4064), (3, 130, 4096)])
+                                   (1, 333, 4064), (3, 130, 4096),
+                                   # 256-column slabs from T = 5: slab counts off a multiple of 8
+                                   # (general work-group mapping), a 32- or 64-column last slab
+                                   (6, 64, 288), (12, 70, 2080), (9, 129, 4160), (16, 16, 8224)])
 def test_gemv_matches_oracle(gpu, T, N, K):
     w = synth.normal_f32(10, "gpu.gemv.w", (N, K), 0.0, 0.02)
     x = synth.normal_f32(10, "gpu.gemv.x", (T, K))
