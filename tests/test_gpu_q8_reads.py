@@ -184,7 +184,10 @@ def _up(gpu, wbuf, lo, T, N, K):
 
 
 @pytest.mark.parametrize("T,N,K", [(1, 37, 2048), (4, 10, 1056), (6, 64, 96), (16, 9, 4096),
-                                   (8, 70, 1536), (9, 33, 544)])
+                                   (8, 70, 1536), (9, 33, 544),
+                                   # from T = 9 two waves per tile, one per 256-column half: a
+                                   # 32-column last slab (its second half empty), ragged row groups
+                                   (12, 70, 1056), (16, 130, 2112)])
 def test_down_matches_oracle_small(gpu, T, N, K):
     d = synth.hc_inputs(T, K=K, N=N, seed=20)
     lo, rs = _down(gpu, q8_0_from_f32(to_dev(d["w_down"])), to_dev(d["R"]), to_dev(d["w_norm"]), T, N, K)
