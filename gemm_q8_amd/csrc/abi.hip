@@ -489,7 +489,7 @@ GQ8_EXPORT int gq8_moe_q8_0_routed_flags(const void* x, const uint16_t* xd, cons
     if (T == 0) return GQ8_OK;
     const bool xb = (flags & GQ8_MOE_X_BF16) != 0, hq = (flags & GQ8_MOE_H_Q8_1) != 0;
     if (T > kMaxT || topk < 1 || (int64_t)T * topk > 256 || E < 1 || D < 32 || D % 32 != 0 || D > kMaxMoeD || F < 32 ||
-        F % 32 != 0 || F > 1024 || (hq && F != 256 && F != 512 && F != 1024))
+        F % 32 != 0 || F > 1024 || (hq && ((F != 256 && F != 512 && F != 1024) || topk > 16)))
         return GQ8_ESHAPE;
     if (x == nullptr || (!xb && xd == nullptr) || ids == nullptr || weights == nullptr ||
         w_gate_up == nullptr || w_down == nullptr || out == nullptr)

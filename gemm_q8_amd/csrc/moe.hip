@@ -774,7 +774,7 @@ size_t moe_workspace_bytes(int T, int topk, int D, int F) {
 int launch_moe_routed(const int8_t* xq, const uint16_t* xd, const uint16_t* xb, const int32_t* ids,
                       const float* w, const void* wgu, const void* wdn, uint16_t* out, int T,
                       int topk, int E, int D, int F, bool hq, void* ws, hipStream_t st) {
-    if (hq && F != 256 && F != 512 && F != 1024) return GQ8_ESHAPE;
+    if (hq && ((F != 256 && F != 512 && F != 1024) || topk > kMoeMaxTopk)) return GQ8_ESHAPE;
     MoeArgs a{};
     a.xq = xq; a.xd = xd; a.xb = xb; a.w = w;
     a.wgu = static_cast<const int8_t*>(wgu);
@@ -804,7 +804,8 @@ int launch_moe_routed(const int8_t* xq, const uint16_t* xd, const uint16_t* xb, 
     // the plan is needed only by the fallback kernels (D > 4096 gate/up; F outside
     // {256, 512, 1024} down)
     // (the q8_1(h) down read exists only as the token kernel: the switch leaves it there)
-    const bool token_dn = (F == 256 || F == 512 || F == 1024) && (!general || hq);
+    // (the token kernel keeps one result row per slot in LDS: at most kMoeMaxTopk slots)
+    const bool token_dn = (F == 256 || F == 512 || F == 1024) && topk <= kMoeMaxTopk && (!general || hq);
     if (!rows_gu || !token_dn) {
         GQ8_NOTE_GENERAL("routed experts: plan-based general kernels: D > 4096, F not in {256, 512, 1024}, or forced");
         hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(256), 0, st, ids, a.P, E, plan);

@@ -303,8 +303,8 @@ int gq8_moe_q8_0_routed_bf16(const uint16_t* x, const int32_t* ids, const float*
  *                   quantized per 32-block with the input's rule, and the down read's blocks are
  *                   integer dots of those codes with the weight quants, scaled by both scales.
  *                   A different, slightly less exact read than the default (h in fp32), within
- *                   the same pass rule of the oracle's variant. Needs F in {256, 512, 1024}, else
- *                   GQ8_ESHAPE.
+ *                   the same pass rule of the oracle's variant. Needs F in {256, 512, 1024} and
+ *                   topk <= 16, else GQ8_ESHAPE.
  * Other flag bits: GQ8_EINVAL. Shapes, weights, workspace and errors otherwise as
  * gq8_moe_q8_0_routed; flags = 0 is gq8_moe_q8_0_routed and GQ8_MOE_X_BF16 alone is
  * gq8_moe_q8_0_routed_bf16, bit for bit. */

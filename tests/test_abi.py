@@ -146,6 +146,9 @@ def test_moe_flags_argument_checks(lib):
     # q8_1(h) needs F in {256, 512, 1024}
     assert raw.gq8_moe_q8_0_routed_flags(dummy, dummy, dummy, dummy, dummy, dummy, dummy,
                                          4, 8, 512, 2048, 96, lib.MOE_H_Q8_1, None, 0, None) == lib.ESHAPE
+    # q8_1(h) keeps one result row per slot on chip: at most 16 slots
+    assert raw.gq8_moe_q8_0_routed_flags(dummy, dummy, dummy, dummy, dummy, dummy, dummy,
+                                         1, 17, 512, 2048, 512, lib.MOE_H_Q8_1, None, 0, None) == lib.ESHAPE
     # the int8 input needs its scales; the bf16 input does not
     assert raw.gq8_moe_q8_0_routed_flags(dummy, None, dummy, dummy, dummy, dummy, dummy,
                                          4, 8, 512, 2048, 512, 0, None, 0, None) == lib.EINVAL

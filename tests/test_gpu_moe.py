@@ -149,6 +149,34 @@ def test_moe_crowded_expert(gpu, D, F):
     check_bf16(to_host(out, np.uint16), y_ref, S, f"moe crowded D={D} F={F}")
 
 
+@pytest.mark.parametrize("T,topk,E,D,F", [(1, 32, 64, 2048, 512), (2, 17, 40, 544, 256),
+                                          (1, 20, 20, 160, 1024)])
+def test_moe_more_than_16_slots(gpu, T, topk, E, D, F):
+    """topk > 16 (ids given directly: the routing call stops at 16): more slots per token than
+    the on-chip per-slot rows of the fused down read, so the plan-based kernels run; the output
+    still passes the rule against the oracle."""
+    seed = 49
+    inp = synth.moe_inputs(T=T, E=E, D=D, seed=seed)
+    g = np.random.default_rng(seed)
+    ids_ref = np.stack([g.choice(E, size=topk, replace=False) for _ in range(T)]).astype(np.int32)
+    p_ref = synth.uniform_f32(seed, "moe.many.w", (T, topk), 0.01, 0.1)
+    experts = lambda e: synth.moe_expert_weights(e, D=D, F=F, seed=seed)  # noqa: E731
+    agu, adn = _arena(gpu, experts, E, D, F, sorted(set(ids_ref.ravel().tolist())), seed)
+    xq = torch.empty((T, D), dtype=torch.int8, device="cuda")
+    xd = torch.empty((T, D // 32), dtype=torch.int16, device="cuda")
+    gpu.gq8_q8_1_quantize(to_dev(inp["x"]), T, D, xq, xd, None)
+    nb = gpu.gq8_moe_workspace_bytes(T, topk, D, F)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, D), dtype=torch.int16, device="cuda")
+    gpu.gq8_moe_q8_0_routed(xq, xd, to_dev(ids_ref), to_dev(p_ref), agu, adn, out, T, topk, E, D,
+                            F, ws, nb)
+    torch.cuda.synchronize()
+    x81 = quantize_q8_1_bf16(inp["x"])
+    blocks = lambda e: (quantize_q8_0(experts(e)["gate_up"]), quantize_q8_0(experts(e)["down"]))  # noqa: E731
+    y_ref, S = moe_forward(x81, ids_ref, p_ref, blocks)
+    check_bf16(to_host(out, np.uint16), y_ref, S, f"moe topk={topk} T={T} D={D} F={F}")
+
+
 @pytest.mark.parametrize("T,E,topk,D,F", [(4, 512, 8, 2048, 512),      # the full workload
                                           (3, 20, 4, 128, 64),         # VALU down + plan
                                           (6, 40, 6, 1056, 96),        # ragged last chunk
