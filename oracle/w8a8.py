@@ -28,9 +28,15 @@ def w8a8_acc(xq, W):
     return acc
 
 
+def acc_to_f32(acc):
+    """The epilogue's first step: the int32 accumulator as the nearest fp32, ties to even (above
+    2^24 not every integer is an fp32)."""
+    return np.asarray(acc, dtype=np.int64).astype(np.float32)
+
+
 def w8a8_epilogue(acc, x_scale, w_scale):
     """bf16 bits of (fp32(acc) * x_scale[m]) * w_scale[n], each product rounded in fp32."""
-    a = np.asarray(acc, dtype=np.int64).astype(np.float32)      # int -> fp32, nearest even
+    a = acc_to_f32(acc)
     v = (a * f32(x_scale)[:, None]).astype(np.float32)
     v = (v * f32(w_scale)[None, :]).astype(np.float32)
     return bf16_bits(v)

@@ -115,3 +115,45 @@ def test_requantized_forward_passes_the_flag_through():
     for t in range(2):
         want = sum(p[t, j] * expert_rows(x81, t, *blocks(ids[t, j]), h_q8_1=True)[0] for j in range(2))
         assert np.allclose(yq[t], want, rtol=1e-13, atol=1e-16)
+
+
+def test_expert_rows_gate_up_split_and_silu_closed_forms():
+    """One 32-column block, hand-built so every dot product is one exact term: x is the one-hot
+    q8_1 block (q = e_0, d = 1), gate/up row n holds d_n * e_0, and the down weight is the
+    identity (row m = e_m, d = 1), so the routed row is h itself. Gate rows are 0..F-1 and up rows
+    F..2F-1 (h = SiLU(g) * u with SiLU(g) = g * sigma(g)); the expected values are closed forms:
+      sigma(0) = 1/2 so SiLU(0) = 0;  sigma(ln 3) = 3/4;  sigma(-ln 3) = 1/4;  SiLU(40) = 40 to
+      1e-16.  g = fp16(ln 3) misses ln 3 by |delta| < 2^-11, and |SiLU'| < 1.1 there.
+    Swapping the gate and up halves, or taking sigma(g) * u (no factor g), fails every case with
+    g != u; dropping u fails the u = 0 rows."""
+    from oracle.numerics import fp16_bits, fp16_to_f32
+    from oracle.q8 import Q81Blocks, Q8Blocks
+    F = D = 32
+    one = fp16_bits(np.float32(1.0))
+    xq = np.zeros((1, 1, 32), np.int8)
+    xq[0, 0, 0] = 1
+    x81 = Q81Blocks(d=np.array([[one]], np.uint16), s=np.array([[one]], np.uint16), q=xq)
+    ln3 = float(np.log(3.0))
+    # (g, u) per row n; rows 6.. are zero
+    gu_vals = [(0.0, 2.0), (ln3, 2.0), (-ln3, 2.0), (40.0, 0.5), (-40.0, 0.5), (ln3, 0.0)]
+    gd = np.zeros((2 * F, 1), np.uint16)
+    gq = np.zeros((2 * F, 1, 32), np.int8)
+    for n, (g, u) in enumerate(gu_vals):
+        for row, v in ((n, g), (F + n, u)):
+            gd[row, 0] = fp16_bits(np.float32(abs(v)))
+            gq[row, 0, 0] = 1 if v >= 0 else -1
+    gu = Q8Blocks(d=gd, q=gq)
+    dq = np.zeros((D, 1, 32), np.int8)
+    dq[np.arange(D), 0, np.arange(D)] = 1
+    dn = Q8Blocks(d=np.full((D, 1), one, np.uint16), q=dq)
+    r, S = expert_rows(x81, 0, gu, dn)
+    g_ln3 = float(fp16_to_f32(fp16_bits(np.float32(ln3))))
+    delta = abs(g_ln3 - ln3)
+    assert 0 < delta < 2.0 ** -11
+    assert r[0] == 0.0                                          # SiLU(0) = 0
+    assert abs(r[1] - ln3 * 0.75 * 2.0) <= 1.1 * delta * 2.0     # ln 3 * 3/4 * u
+    assert abs(r[2] - (-ln3) * 0.25 * 2.0) <= 1.1 * delta * 2.0  # -ln 3 * 1/4 * u
+    assert abs(r[3] - 40.0 * 0.5) <= 1e-13                      # SiLU(40) = 40
+    assert abs(r[4]) <= 1e-15                                   # SiLU(-40) ~ -1.7e-16
+    assert r[5] == 0.0 and np.all(r[6:] == 0.0)                  # u = 0, or nothing routed
+    assert np.array_equal(S, np.abs(r))                           # one term per output

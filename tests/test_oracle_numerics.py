@@ -2,7 +2,7 @@
 import numpy as np
 import pytest
 
-from oracle.numerics import bf16_bits, bf16_to_f32, fp16_bits, fp16_to_f32, round_half_away
+from oracle.numerics import bf16_bits, bf16_to_f32, bf16_ulp, fp16_bits, fp16_to_f32, round_half_away
 
 
 def test_fp16_known_encodings():
@@ -40,3 +40,23 @@ def test_round_half_away():
     v = np.array([0.5, -0.5, 1.5, 2.5, -2.5, 0.49999997, -0.49999997, 126.5, -127.49998, 8388607.5],
                  dtype=np.float32)
     assert round_half_away(v).tolist() == [1, -1, 2, 3, -3, 0, 0, 127, -127, 8388608]
+
+
+def test_bf16_ulp_known_spacings():
+    """bf16 keeps 8 significant bits: the spacing in [2^e, 2^(e+1)) is 2^(e-7); below the smallest
+    normal the spacing of the smallest normal binade is used."""
+    v = np.array([1.0, 1.99, 2.0, -3.0, 0.75, 2.0 ** -126, 0.0, 2.0 ** -130, 3.0e38], np.float64)
+    want = [2.0 ** -7, 2.0 ** -7, 2.0 ** -6, 2.0 ** -6, 2.0 ** -8, 2.0 ** -133, 2.0 ** -133,
+            2.0 ** -133, 2.0 ** 120]
+    assert bf16_ulp(v).tolist() == want
+
+
+def test_bf16_ulp_is_the_gap_to_the_next_bf16():
+    """For every positive normal finite bf16 value b (all 32,512 bit patterns below the largest),
+    bf16_ulp(b) equals the distance to the next bf16 up (bit pattern + 1): the spacing as the
+    format itself defines it."""
+    bits = np.arange(0x0080, 0x7F7F, dtype=np.uint32)
+    b = bf16_to_f32(bits.astype(np.uint16)).astype(np.float64)
+    nxt = bf16_to_f32((bits + 1).astype(np.uint16)).astype(np.float64)
+    assert np.array_equal(bf16_ulp(b), nxt - b)
+    assert np.array_equal(bf16_ulp(-b), nxt - b)

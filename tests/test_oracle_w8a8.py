@@ -84,3 +84,28 @@ def test_per_token_quantization_ties_go_away_from_zero():
     q, xs = quantize_per_token(bf16_bits(row)[None, :])
     assert xs[0] == np.float32(1.0)
     assert q[0].tolist() == [127, 1, -1, 3, -3, 127, -127, 3]
+
+
+def test_accumulator_to_fp32_rounds_to_nearest_even():
+    """Above 2^24 the int32 accumulator is rounded to the nearest fp32, ties to even:
+    2^24 + 1 -> 16777216, 2^24 + 3 -> 16777220 (not 16777218, which truncation gives), and at
+    2^25 (spacing 4) 2^25 + 2 -> 2^25, 2^25 + 6 -> 2^25 + 8; below 2^24 every integer is exact."""
+    from oracle.w8a8 import acc_to_f32
+    acc = np.array([2 ** 24 + 1, 2 ** 24 + 3, -(2 ** 24 + 1), -(2 ** 24 + 3), 2 ** 25 + 2,
+                    2 ** 25 + 6, 2 ** 24 - 1, 66064384, -66064383], np.int64)
+    want = [16777216, 16777220, -16777216, -16777220, 2 ** 25, 2 ** 25 + 8, 2 ** 24 - 1,
+            66064384, -66064384]
+    assert acc_to_f32(acc).astype(np.int64).tolist() == want
+
+
+def test_epilogue_sees_the_accumulator_rounding():
+    """Cases where the bf16 output depends on how the accumulator became an fp32 (x_scale chosen
+    so the scaled value lands on or next to a bf16 rounding boundary at 2^24 (1 + 2^-8)):
+      acc = 2^24 + 1, x_scale = 1 + 2^-8: fp32(acc) = 2^24, times x_scale is exactly the bf16
+        midpoint, which ties to even: 2^24 (0x4B80); an exact conversion would give 0x4B81;
+      acc = 2^24 + 3, x_scale = the fp32 just below 1 + 2^-8: 16777220 * x_scale lies above the
+        midpoint (0x4B81); a truncated 16777218 would land below it (0x4B80)."""
+    xs_below = np.array([np.float32(1 + 2.0 ** -8).view(np.uint32) - 1], np.uint32).view(np.float32)
+    out = w8a8_epilogue(np.array([[2 ** 24 + 1], [2 ** 24 + 3]], np.int64),
+                        np.array([1 + 2.0 ** -8, xs_below[0]], np.float32), np.ones(1, np.float32))
+    assert out[:, 0].tolist() == [0x4B80, 0x4B81]
