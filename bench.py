@@ -17,11 +17,18 @@ Output: one JSON line on stdout (metric = weight bytes / time in GB/s), with
   config        per-T pair call times: the mean, the median and p90 over --reps samples of one
                 rotation each, and a hot-cache run (one weight set: cache, not HBM, context only);
                 the sha256 of the library that ran;
-  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload (host CPU model
-                and thread counts stated).
---all-configs also times the other workloads (BF16 comparison pair, Q8_0 GEMV T sweep, W8A8
-sweep, routed MoE variants) and writes their lines to --report (default bench_all.jsonl) and
-stderr; --only, --w8a8-ms and --gemv-ts select among them.
+  configs       one record per workload shape of the five configurations (Q8_0 GEMV
+                1024 x 4096 at T = 1, 2, 4, 8, 16; the HC pair at T = 1, 4, 6; W8A8 M = 16,
+                N = 1536, K = 4096; W8A8 M in {1, 4, 8, 16, 32} x (2560, 4096), (4096, 2048); the
+                routed MoE): median / p90 / mean us per call over samples of back-to-back graph
+                replays on rotated weight copies, weight GB/s, the fraction of 8 TB/s and of a
+                same-byte read probe timed the same way, and the oracle's host time (one BLAS
+                thread and the whole pool; a stated sample where the whole call would be slow);
+  cpu_baseline  the CPU oracle timed on a bounded sample of the step's workload, at one thread and
+                at the whole BLAS pool (host CPU model and thread counts stated).
+--all-configs also times comparison reads and variants (BF16 pair, W8A8 on a bf16 x, MoE options,
+the read-probe curve) and writes their lines to --report (default bench_all.jsonl) and stderr;
+--only, --w8a8-ms and --gemv-ts select among them.
 """
 from __future__ import annotations
 
@@ -99,6 +106,20 @@ def time_region(torch, stream, fn):
     e1.record(stream)
     e1.synchronize()
     return e0.elapsed_time(e1) * 1e-3       # seconds
+
+
+def timed_dist(torch, stream, fn_for_set, n_sets, reps=30, min_calls=400):
+    """Per-call microseconds of fn_for_set(i) (i = 0 .. n_sets-1 rotates over the weight copies)
+    captured serially into one hipGraph: one warm-up rotation, then `reps` samples, each of enough
+    whole rotations for >= min_calls calls (so the graph launch itself is amortized). Returns the
+    median, p90 and mean over the samples."""
+    rot = max(1, -(-min_calls // n_sets))
+    gs = GraphSteps(torch, stream, lambda step: [fn_for_set(step)], n_sets)
+    gs.run(n_sets)
+    us = np.array([time_region(torch, stream, lambda: gs.run(n_sets * rot)) / (n_sets * rot) * 1e6
+                   for _ in range(reps)])
+    return {"median": float(np.median(us)), "p90": float(np.percentile(us, 90)),
+            "mean": float(np.mean(us)), "calls_per_sample": n_sets * rot, "samples": reps}
 
 
 def code_digest(root, files):
@@ -200,13 +221,20 @@ def lib_sha256(path):
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it: model name, then family / model / stepping."""
+    f = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            k, _, v = line.partition(":")
+            k = k.strip()
+            if k in ("model name", "cpu family", "model", "stepping") and k not in f:
+                f[k] = v.strip()
+            if len(f) == 4:
+                break
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    return (f"{f.get('model name', 'unknown')} (family {f.get('cpu family', '?')}, model "
+            f"{f.get('model', '?')}, stepping {f.get('stepping', '?')})")
 
 
 def cpu_baseline(synth, budget_s):
@@ -214,29 +242,32 @@ def cpu_baseline(synth, budget_s):
     step, repeated until about `budget_s` seconds have been spent."""
     import oracle
     from oracle.q8 import quantize_q8_0
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # noqa: BLE001
-        cores = 1
+    from threadpoolctl import threadpool_info, threadpool_limits
+    cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     base = synth.hc_inputs(6)
     bd, bu = quantize_q8_0(base["w_down"]), quantize_q8_0(base["w_up"])
     from oracle.numerics import bf16_bits
     ins = {T: synth.hc_inputs(T) for T in TS}
-    steps, t0 = 0, time.perf_counter()
-    while True:
-        for T in TS:
-            lo, _, _ = oracle.hc.hc_down(ins[T]["R"], ins[T]["w_norm"], bd)
-            oracle.hc.hc_up(bf16_bits(lo.astype(np.float32)), bu)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    wbytes = steps * len(TS) * 2 * (K_HC * N_LR + K_HC * N_LR // 32 * 2)
-    return {"value": round(wbytes / el / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+
+    def run(budget):
+        steps, t0 = 0, time.perf_counter()
+        while True:
+            for T in TS:
+                lo, _, _ = oracle.hc.hc_down(ins[T]["R"], ins[T]["w_norm"], bd)
+                oracle.hc.hc_up(bf16_bits(lo.astype(np.float32)), bu)
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return steps, el
+    step_bytes = len(TS) * 2 * (K_HC * N_LR + K_HC * N_LR // 32 * 2)
+    with threadpool_limits(limits=1):
+        s1, e1 = run(budget_s / 3)
+    sa, ea = run(budget_s * 2 / 3)
+    return {"value": round(sa * step_bytes / ea / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle", "value_1thread": round(s1 * step_bytes / e1 / 1e9, 4),
             "cpu_model": cpu_model(), "host_threads": os.cpu_count(),
-            "sample": f"{steps} oracle steps (down+up read at T=1,4,6 each, full size) in {el:.1f} s; "
-                      f"numpy float64 on the host, BLAS threads={cores}"}
+            "sample": f"{sa} oracle steps (down+up read at T=1,4,6 each, full size) in {ea:.1f} s at "
+                      f"{cores} BLAS threads, {s1} steps in {e1:.1f} s at 1 thread; numpy float64"}
 
 
 # ------------------------------------------------------------------------------------ other configs
@@ -380,28 +411,12 @@ def bench_w8a8_sweep(torch, gq8, synth, dev, timed, emit, ms):
 def bench_moe(torch, gq8, synth, dev, timed, emit):
     from gemm_q8_amd.device import to_dev
     # routed MoE: 512 experts, T=4, top-8, D=2048, F=512
-    T, E, topk, D, F = 4, 512, 8, 2048, 512
-    gu_b, dn_b = gq8.gq8_q8_0_bytes(2 * F, D), gq8.gq8_q8_0_bytes(D, F)
-    agu = torch.empty(E * gu_b, dtype=torch.uint8, device=dev)
-    adn = torch.empty(E * dn_b, dtype=torch.uint8, device=dev)
-    for e in range(E):
-        w = synth.moe_expert_weights(e, D=D, F=F)
-        gq8.gq8_q8_0_quantize(to_dev(w["gate_up"]), 2 * F, D, agu[e * gu_b:(e + 1) * gu_b])
-        gq8.gq8_q8_0_quantize(to_dev(w["down"]), D, F, adn[e * dn_b:(e + 1) * dn_b])
-    n = 8
-    agus = [agu] + [agu.clone() for _ in range(n - 1)]
-    adns = [adn] + [adn.clone() for _ in range(n - 1)]
-    inp = synth.moe_inputs(T=T, E=E, D=D)
-    ids = torch.empty((T, topk), dtype=torch.int32, device=dev)
-    wts = torch.empty((T, topk), dtype=torch.float32, device=dev)
-    gq8.gq8_moe_route(to_dev(inp["logits"]), T, E, topk, ids, wts)
-    xq = torch.empty((T, D), dtype=torch.int8, device=dev)
-    xd = torch.empty((T, D // 32), dtype=torch.int16, device=dev)
-    gq8.gq8_q8_1_quantize(to_dev(inp["x"]), T, D, xq, xd, None)
-    nb = gq8.gq8_moe_workspace_bytes(T, topk, D, F)
-    wsp = torch.empty(nb, dtype=torch.uint8, device=dev)
-    out = torch.empty((T, D), dtype=torch.int16, device=dev)
-    U = len(set(to_host_ids(ids)))
+    m = setup_moe(torch, gq8, synth, dev)
+    T, E, topk, D, F = m["T"], m["E"], m["topk"], m["D"], m["F"]
+    gu_b, dn_b, n, agus, adns = m["gu_b"], m["dn_b"], m["n"], m["agus"], m["adns"]
+    inp, ids, wts, xq, xd, nb, wsp, out = (m["inp"], m["ids"], m["wts"], m["xq"], m["xd"], m["nb"],
+                                           m["ws"], m["out"])
+    U = len(m["routed"])
     us = timed(lambda i: (lambda s, a=agus[i % n], b=adns[i % n]: gq8.gq8_moe_q8_0_routed(
         xq, xd, ids, wts, a, b, out, T, topk, E, D, F, wsp, nb, s)), n, reps=50)
     emit({"workload": "routed MoE T=4 E=512 top-8 D=2048 F=512", "unique_experts": U,
@@ -430,8 +445,236 @@ def bench_moe(torch, gq8, synth, dev, timed, emit):
           "unique_experts": U, "us_per_call": round(us, 3), "weight_GBps": round(U * (gu_b + dn_b) / us / 1e3, 1)})
 
 
+def probe_sweep(torch, gq8, dev, stream, report, sizes=(4_456_448, 5_570_560, 6_291_456, 8_388_608,
+                                                        10_485_760, 33_554_432)):
+    """The read probe over launch shapes at the byte counts of the reads: loads per lane 1/2/4/8,
+    256/512/1024 threads, one work-group per chunk or a fixed grid of 1, 2, 4 or 8 work-groups per
+    CU striding over the chunks, non-temporal or plain loads; graphs of back-to-back launches over
+    rotated buffers (>= 640 MiB). One JSON line per (size, shape); the fastest shape per size is
+    logged."""
+    cus = gq8.gq8_device_cus()
+    lines = []
+    for nbytes in sizes:
+        n = n_sets_for(nbytes)
+        bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(n)]
+        sink = torch.empty(gq8.gq8_read_probe_sink_floats(nbytes), dtype=torch.float32, device=dev)
+        best = None
+        for lpt in (1, 2, 4, 8):
+            for threads in (256, 512, 1024):
+                for wg in (0, cus, 2 * cus, 4 * cus, 8 * cus):
+                    for nt in (1, 0):
+                        d = timed_dist(torch, stream, lambda i, lpt=lpt, threads=threads, wg=wg, nt=nt: (
+                            lambda s, b=bufs[i % n]: gq8.gq8_read_probe_ex(b, nbytes, sink, lpt, threads, wg, nt, s)),
+                            n, reps=5, min_calls=200)
+                        r = {"workload": "read probe sweep", "bytes": nbytes, "loads_per_lane": lpt,
+                             "threads": threads, "work_groups": wg or "one per chunk", "nontemporal": nt,
+                             "us_median": round(d["median"], 3), "GBps": round(nbytes / d["median"] / 1e3, 1)}
+                        lines.append(r)
+                        if best is None or r["us_median"] < best["us_median"]:
+                            best = r
+        log("[probe sweep] best " + json.dumps(best))
+        del bufs
+    if report:
+        with open(report, "w") as f:
+            for r in lines:
+                f.write(json.dumps(r) + "\n")
+    return lines
+
+
 def to_host_ids(ids):
     return ids.cpu().numpy().ravel().tolist()
+
+
+# ------------------------------------------------------------------------------------ the five workloads
+
+class ProbeCache:
+    """Same-byte read-probe times: one call = gq8_read_probe launches of the given sizes in
+    sequence (a read of two launches is compared with two probe launches), over rotated buffers
+    (>= 640 MiB), timed like the reads. Median us per call, cached by the launch sizes."""
+
+    def __init__(self, torch, gq8, dev, stream, reps):
+        self.torch, self.gq8, self.dev, self.stream, self.reps = torch, gq8, dev, stream, reps
+        self.cache = {}
+
+    def us(self, sizes):
+        key = tuple(int(b) for b in sizes)
+        if key not in self.cache:
+            torch, gq8 = self.torch, self.gq8
+            n = n_sets_for(sum(key))
+            bufs = [[torch.ones(b, dtype=torch.uint8, device=self.dev) for b in key] for _ in range(n)]
+            sink = torch.empty(max(gq8.gq8_read_probe_sink_floats(b) for b in key),
+                               dtype=torch.float32, device=self.dev)
+
+            def fn(i):
+                bs = bufs[i % n]
+
+                def f(s):
+                    for b, nb in zip(bs, key):
+                        gq8.gq8_read_probe(b, nb, sink, s)
+                return f
+            self.cache[key] = timed_dist(torch, self.stream, fn, n, reps=self.reps)["median"]
+            del bufs
+        return self.cache[key]
+
+
+def oracle_times(fn, scale=1.0):
+    """The oracle (test infrastructure) timed on the host: once with the BLAS pool at one thread,
+    once at its default size. Returns (us at 1 thread, us at all threads, threads of the pool),
+    each scaled by `scale` (a sample of 1/scale of the call)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    fn()                                                   # first-touch / allocation warm-up
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        fn()
+        t1 = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    fn()
+    ta = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return t1 * 1e6 * scale, ta * 1e6 * scale, threads
+
+
+def config_record(cfg, workload, shape, d, wbytes, probe_us, orc, orc_sample):
+    gbs = wbytes / d["median"] / 1e3
+    r = {"config": cfg, "workload": workload, **shape,
+         "us_median": round(d["median"], 3), "us_p90": round(d["p90"], 3), "us_mean": round(d["mean"], 3),
+         "weight_bytes": int(wbytes), "weight_GBps": round(gbs, 1),
+         "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4),
+         "probe_us": round(probe_us, 3), "frac_of_probe": round(probe_us / d["median"], 4)}
+    if orc is not None:
+        r["oracle_us_1thread"] = round(orc[0], 1)
+        r["oracle_us_all_threads"] = round(orc[1], 1)
+        r["oracle_threads"] = orc[2]
+        r["oracle_sample"] = orc_sample
+    return r
+
+
+def setup_moe(torch, gq8, synth, dev, T=4, E=512, topk=8, D=2048, F=512, n_copies=8):
+    """The routed-expert workload: routing from N(0,1) logits on the device, arenas of E experts
+    (gate/up Q8_0 [2F, D] and down Q8_0 [D, F] each), n_copies copies rotated. Only the routed
+    experts' bytes are ever read, so only they are drawn and quantized (the others are zero);
+    every arena has the full E-expert size and layout."""
+    from gemm_q8_amd.device import to_dev
+    gu_b, dn_b = gq8.gq8_q8_0_bytes(2 * F, D), gq8.gq8_q8_0_bytes(D, F)
+    inp = synth.moe_inputs(T=T, E=E, D=D)
+    ids = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, topk), dtype=torch.float32, device=dev)
+    gq8.gq8_moe_route(to_dev(inp["logits"]), T, E, topk, ids, wts)
+    routed = sorted(set(to_host_ids(ids)))
+    agu = torch.zeros(E * gu_b, dtype=torch.uint8, device=dev)
+    adn = torch.zeros(E * dn_b, dtype=torch.uint8, device=dev)
+    for e in routed:
+        w = synth.moe_expert_weights(e, D=D, F=F)
+        gq8.gq8_q8_0_quantize(to_dev(w["gate_up"]), 2 * F, D, agu[e * gu_b:(e + 1) * gu_b])
+        gq8.gq8_q8_0_quantize(to_dev(w["down"]), D, F, adn[e * dn_b:(e + 1) * dn_b])
+    xq = torch.empty((T, D), dtype=torch.int8, device=dev)
+    xd = torch.empty((T, D // 32), dtype=torch.int16, device=dev)
+    gq8.gq8_q8_1_quantize(to_dev(inp["x"]), T, D, xq, xd, None)
+    nb = gq8.gq8_moe_workspace_bytes(T, topk, D, F)
+    return dict(T=T, E=E, topk=topk, D=D, F=F, gu_b=gu_b, dn_b=dn_b, inp=inp, ids=ids, wts=wts,
+                routed=routed, agus=[agu] + [agu.clone() for _ in range(n_copies - 1)],
+                adns=[adn] + [adn.clone() for _ in range(n_copies - 1)], n=n_copies, xq=xq, xd=xd,
+                nb=nb, ws=torch.empty(nb, dtype=torch.uint8, device=dev),
+                out=torch.empty((T, D), dtype=torch.int16, device=dev))
+
+
+def bench_configs(torch, gq8, synth, dev, stream, hc_dist, reps, with_oracle=True,
+                  gemv_ts=(1, 2, 4, 8, 16)):
+    """One record per workload shape of the five configurations: median / p90 / mean us per call
+    (graphs of back-to-back calls over rotated weight copies, inputs in HBM), weight GB/s, the
+    fraction of 8 TB/s and of the same-byte read probe, and the oracle's time on the host."""
+    from gemm_q8_amd.device import q8_0_from_f32, to_dev, workspace
+    import oracle
+    from oracle.numerics import bf16_bits
+    from oracle.q8 import quantize_q8_0, quantize_q8_1_bf16
+    probe = ProbeCache(torch, gq8, dev, stream, reps)
+    recs = []
+
+    def emit(r):
+        recs.append(r)
+        log("[config] " + json.dumps(r))
+
+    # 1: Q8_0 GEMV N = 1024, K = 4096 (T = 1 is the configuration; the metric spans T = 1..16)
+    d = synth.q8_0_gemv_inputs(T=16)
+    w0 = q8_0_from_f32(to_dev(d["w"]))
+    n = n_sets_for(w0.numel())
+    wset = [w0] + [w0.clone() for _ in range(n - 1)]
+    b = quantize_q8_0(d["w"]) if with_oracle else None
+    for T in gemv_ts:
+        x = to_dev(np.ascontiguousarray(d["x"][:T]))
+        y = torch.empty((T, 1024), dtype=torch.float32, device=dev)
+        nb = gq8.gq8_workspace_bytes(gq8.OP_Q8_0_GEMV, T, 1024, 4096)
+        wsp = workspace(nb)
+        dist = timed_dist(torch, stream, lambda i, T=T, x=x, y=y, nb=nb, wsp=wsp: (
+            lambda s, w=wset[i % n]: gq8.gq8_q8_0_gemv(w, x, y, T, 1024, 4096, wsp, nb, s)), n, reps)
+        xs = d["x"][:T]
+        orc = oracle_times(lambda: oracle.q8.q8_0_gemv(b, xs)) if with_oracle else None
+        emit(config_record(1, "Q8_0 GEMV N=1024 K=4096", {"T": T}, dist, w0.numel(),
+                           probe.us([w0.numel()]), orc, "the whole call (numpy float64)"))
+    del wset
+
+    # 2: the HC pair (timed with the step's own graphs)
+    pair_w = 2 * (K_HC * N_LR + K_HC * N_LR // 32 * 2)
+    if with_oracle:
+        base = synth.hc_inputs(6)
+        bd, bu = quantize_q8_0(base["w_down"]), quantize_q8_0(base["w_up"])
+    for T in TS:
+        if with_oracle:
+            ins = synth.hc_inputs(T)
+
+            def pair_oracle(ins=ins):
+                lo, _, _ = oracle.hc.hc_down(ins["R"], ins["w_norm"], bd)
+                oracle.hc.hc_up(bf16_bits(lo.astype(np.float32)), bu)
+            orc = oracle_times(pair_oracle)
+        else:
+            orc = None
+        emit(config_record(2, "HC pair: RMSNorm + Q8_0 down [320 x 16384], Q8_0 up [16384 x 320]",
+                           {"T": T}, hc_dist[T], pair_w, probe.us([pair_w // 2, pair_w // 2]), orc,
+                           "the whole call: down then up read (numpy float64)"))
+
+    # 3 and 4: W8A8
+    for cfg, (M, N, K) in [(3, (16, 1536, 4096))] + [(4, (m, 2560, 4096)) for m in (1, 4, 8, 16, 32)] + \
+                          [(4, (m, 4096, 2048)) for m in (1, 4, 8, 16, 32)]:
+        dd = synth.w8a8_inputs(M, N, K)
+        wp0 = torch.empty(gq8.gq8_w8a8_packed_bytes(K, N), dtype=torch.int8, device=dev)
+        gq8.gq8_w8a8_pack(to_dev(dd["W"]), K, N, wp0)
+        n = n_sets_for(wp0.numel())
+        wps = [wp0] + [wp0.clone() for _ in range(n - 1)]
+        xq, xs, wsc = to_dev(dd["xq"]), to_dev(dd["x_scale"]), to_dev(dd["w_scale"])
+        out = torch.empty((M, N), dtype=torch.int16, device=dev)
+        dist = timed_dist(torch, stream, lambda i: (lambda s, w=wps[i % n]: gq8.gq8_w8a8_gemm(
+            xq, xs, w, wsc, out, M, N, K, None, 0, s)), n, reps)
+        ns = 256
+        orc = (oracle_times(lambda: oracle.w8a8.w8a8_gemm(dd["xq"], dd["x_scale"], dd["W"][:, :ns],
+                                                          dd["w_scale"][:ns]), scale=N / ns)
+               if with_oracle else None)
+        emit(config_record(cfg, "W8A8 int8 x int8 -> int32 -> bf16", {"M": M, "N": N, "K": K}, dist,
+                           N * K, probe.us([wp0.numel()]), orc,
+                           f"{ns} of {N} columns, scaled by N/{ns} (numpy int64, single-threaded)"))
+        del wps
+
+    # 5: routed MoE
+    m = setup_moe(torch, gq8, synth, dev)
+    T, E, topk, D, F = m["T"], m["E"], m["topk"], m["D"], m["F"]
+    U = len(m["routed"])
+    dist = timed_dist(torch, stream, lambda i: (lambda s, a=m["agus"][i % m["n"]], b=m["adns"][i % m["n"]]:
+                                                 gq8.gq8_moe_q8_0_routed(m["xq"], m["xd"], m["ids"], m["wts"], a, b,
+                                                                         m["out"], T, topk, E, D, F, m["ws"], m["nb"], s)),
+                      m["n"], reps)
+    orc = None
+    if with_oracle:
+        ids_h = m["ids"].cpu().numpy().astype(np.int64)
+        p_h = m["wts"].cpu().numpy().astype(np.float64)
+        cache = {e: (quantize_q8_0(synth.moe_expert_weights(e, D=D, F=F)["gate_up"]),
+                     quantize_q8_0(synth.moe_expert_weights(e, D=D, F=F)["down"])) for e in m["routed"]}
+        x81 = quantize_q8_1_bf16(m["inp"]["x"])
+        orc = oracle_times(lambda: oracle.moe.moe_forward(x81, ids_h, p_h, lambda e: cache[e]))
+    emit(config_record(5, "routed MoE: T=4, 512 experts, top-8, gate/up [1024 x 2048], down [2048 x 512]",
+                       {"T": T, "E": E, "topk": topk, "unique_experts": U}, dist,
+                       U * (m["gu_b"] + m["dn_b"]), probe.us([U * m["gu_b"], U * m["dn_b"]]), orc,
+                       "the whole call (numpy float64, weights already quantized)"))
+    del m
+    return recs
 
 
 # ------------------------------------------------------------------------------------ main
@@ -443,7 +686,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=42)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--all-configs", action="store_true")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="also the comparison reads and variants (BF16 pair, W8A8 on a bf16 x, MoE "
+                         "options, the probe curve) on stderr and in --report")
+    ap.add_argument("--probe-sweep", default="",
+                    help="sweep the read probe's launch shapes and write the lines to this file, "
+                         "then exit")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="leave out the per-configuration records (the five workloads)")
     ap.add_argument("--only", default="probe,hcbf16,gemv,w8a8,moe",
                     help="with --all-configs: comma-separated subset of probe,hcbf16,gemv,w8a8,moe")
     ap.add_argument("--w8a8-ms", default="1,4,8,16,32", help="with --all-configs: W8A8 M values")
@@ -468,6 +718,9 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
     log(f"[bench] device {torch.cuda.get_device_name(0)}, {gq8.gq8_device_cus()} CUs; lib {gq8.LIB_PATH}")
+    if args.probe_sweep:
+        probe_sweep(torch, gq8, dev, stream, args.probe_sweep)
+        return
 
     h = setup_hc(torch, gq8, synth, dev)
     steps_per_graph = h["n_sets"] // len(TS)
@@ -489,10 +742,12 @@ def main():
     # back-to-back calls over the rotated weight sets
     n = h["n_sets"]
     per_call = {}
+    calls = {}
     kern = {}
     reps = max(1, args.reps)
     dist = {}
     hot = {}
+    hc_dist = {}
     for T in TS:
         for kind, mk in (("pair", hc_pair_fn), ("down", hc_down_fn), ("up", hc_up_fn)):
             g = GraphSteps(torch, stream, lambda i, T=T, mk=mk: [mk(gq8, h, T, i)], n)
@@ -507,9 +762,9 @@ def main():
             k["launches"] += n * reps
             if kind == "pair":
                 per_call[f"T{T}"] = round(tk / (n * reps) * 1e6, 3)
-                us = np.array(ts) / n * 1e6
-                dist[f"T{T}"] = {"median": round(float(np.median(us)), 3),
-                                 "p90": round(float(np.percentile(us, 90)), 3)}
+            else:
+                calls[f"{kind}_T{T}"] = round(tk / (n * reps) * 1e6, 3)
+        hc_dist[T] = timed_dist(torch, stream, lambda i, T=T: hc_pair_fn(gq8, h, T, i), n, reps)
         # hot cache: the same call on one weight set (5.6 MB per read stays in the 256 MB MALL)
         g = GraphSteps(torch, stream, lambda i, T=T: [hc_pair_fn(gq8, h, T, 0)], n)
         g.run(n)
@@ -518,6 +773,8 @@ def main():
     kd = kern[dom]
     avg_us = kd["t"] / kd["launches"] * 1e6
     achieved = kd["bytes"] / kd["t"] / 1e9
+    dist = {f"T{T}": {"median": round(hc_dist[T]["median"], 3), "p90": round(hc_dist[T]["p90"], 3)}
+            for T in TS}
     log(f"[bench] per-call pair us {per_call}; median/p90 {dist}; hot cache {hot}")
     log(f"[bench] per-call pair us {per_call}; calls: " + ", ".join(
         f"{k} {v['t'] / v['launches'] * 1e6:.3f} us" for k, v in kern.items()))
@@ -556,6 +813,7 @@ def main():
             "us_per_pair": per_call,
             "us_per_pair_median_p90": dist,
             "us_per_pair_hot_cache": hot,
+            "us_per_separate_call": calls,
             "hot_cache_note": "one weight set replayed: cache, not HBM (context only)",
             "lib_sha256": lib_sha256(gq8.LIB_PATH),
             "baseline_note": "vs_baseline divides by the HC-Q8 page's Arc Pro B70 Q8_0 read times "
@@ -574,6 +832,10 @@ def main():
             "avg_call_us": round(avg_us, 3),
         },
     }
+    if not args.no_configs:
+        result["configs"] = bench_configs(torch, gq8, synth, dev, stream, hc_dist, reps,
+                                          with_oracle=not args.no_cpu_baseline,
+                                          gemv_ts=[int(t) for t in args.gemv_ts.split(",")])
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(synth, args.cpu_seconds)
     if args.all_configs:

@@ -507,6 +507,21 @@ GQ8_EXPORT int gq8_moe_q8_0_routed_flags(const void* x, const uint16_t* xd, cons
 
 GQ8_EXPORT size_t gq8_read_probe_sink_floats(size_t bytes) { return read_probe_blocks(bytes); }
 
+GQ8_EXPORT int gq8_read_probe_ex(const void* src, size_t bytes, float* sink, int loads_per_lane,
+                                 int threads, int work_groups, int nontemporal, void* stream) {
+    if (bytes % 16 != 0 || bytes / 16 > kMaxItems) return GQ8_ESHAPE;
+    if (!(loads_per_lane == 1 || loads_per_lane == 2 || loads_per_lane == 4 || loads_per_lane == 8) ||
+        !(threads == 256 || threads == 512 || threads == 1024) || work_groups < 0 ||
+        !(nontemporal == 0 || nontemporal == 1))
+        return GQ8_ESHAPE;
+    if (bytes == 0) return GQ8_OK;
+    if (src == nullptr || sink == nullptr) return GQ8_EINVAL;
+    if (!aligned16(src)) return GQ8_EALIGN;
+    if (device_cus() == 0) return GQ8_ENODEV;
+    return launch_read_probe_ex(src, bytes, sink, loads_per_lane, threads, work_groups,
+                                nontemporal != 0, S(stream));
+}
+
 GQ8_EXPORT int gq8_read_probe(const void* src, size_t bytes, float* sink, void* stream) {
     if (bytes % 16 != 0 || bytes / 16 > kMaxItems) return GQ8_ESHAPE;
     if (bytes == 0) return GQ8_OK;

@@ -112,6 +112,8 @@ int launch_q8_1_quantize(const uint16_t* x, int rows, int K, int8_t* q, uint16_t
                          hipStream_t st);
 int launch_w8a8_pack(const int8_t* W, int K, int N, int8_t* Wp, hipStream_t st);
 int launch_read_probe(const void* src, size_t bytes, float* sink, hipStream_t st);
+int launch_read_probe_ex(const void* src, size_t bytes, float* sink, int lpt, int threads,
+                         int work_groups, bool nt, hipStream_t st);
 size_t read_probe_blocks(size_t bytes);
 
 // ---------------------------------------------------------------- MoE

@@ -162,28 +162,65 @@ int launch_w8a8_pack(const int8_t* W, int K, int N, int8_t* Wp, hipStream_t st) 
 }
 
 // -------------------------------------------------------------------------------- read probe
-// 256 threads per work-group, one 16-byte non-temporal load each (4 KiB per work-group): the
-// launch shape that streams a few MiB fastest on this chip.
+// A plain stream of 16-byte loads: lane l of a work-group of NT threads takes pieces
+// c * NT * LPT + j * NT + l (j < LPT) of chunk c, so each load instruction covers NT * 16
+// contiguous bytes. With one work-group per chunk the grid covers the buffer in one pass; with
+// fewer work-groups each one strides over the chunks (grid-stride). The loaded words are folded
+// into one value that is stored only for an impossible bit pattern, so no load can be elided.
 
-constexpr size_t kProbeChunk = 4096;
+constexpr size_t kProbeChunk = 4096;     // smallest chunk: 256 threads x one 16-byte load
 
 size_t read_probe_blocks(size_t bytes) { return (bytes + kProbeChunk - 1) / kProbeChunk; }
 
-__global__ void __launch_bounds__(256) read_probe_kernel(const u32x4* __restrict__ src, size_t n16,
-                                                         float* __restrict__ sink) {
-    size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    i = i < n16 ? i : n16 - 1;
-    const u32x4 v = __builtin_nontemporal_load(src + i);
-    const uint32_t x = v.x ^ v.y ^ v.z ^ v.w;
-    if (x == 0x9E3779B9u && threadIdx.x == 0) sink[blockIdx.x] = 1.0f;   // keeps the load alive
+template <int LPT, bool NTL>
+__global__ void __launch_bounds__(1024) read_probe_kernel(const u32x4* __restrict__ src, size_t n16,
+                                                          size_t nchunks, float* __restrict__ sink) {
+    const size_t nt = blockDim.x;
+    uint32_t acc = 0;
+    for (size_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        u32x4 v[LPT];
+#pragma unroll
+        for (int j = 0; j < LPT; ++j) {
+            size_t i = (c * LPT + j) * nt + threadIdx.x;
+            i = i < n16 ? i : n16 - 1;
+            v[j] = NTL ? __builtin_nontemporal_load(src + i) : src[i];
+        }
+#pragma unroll
+        for (int j = 0; j < LPT; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+    }
+    if (acc == 0x9E3779B9u && threadIdx.x == 0) sink[blockIdx.x] = 1.0f;   // keeps the loads alive
+}
+
+// The default shape (gq8_read_probe): one 16-byte non-temporal load per lane, 256 threads, one
+// work-group per 4 KiB chunk.
+constexpr int kProbeLpt = 1, kProbeThreads = 256, kProbeNt = 1;
+
+template <int LPT>
+static void launch_probe_lpt(const void* src, size_t n16, size_t nchunks, unsigned grid, int threads,
+                             bool nt, float* sink, hipStream_t st) {
+    const u32x4* s = static_cast<const u32x4*>(src);
+    if (nt) hipLaunchKernelGGL((read_probe_kernel<LPT, true>), dim3(grid), dim3(threads), 0, st, s, n16, nchunks, sink);
+    else hipLaunchKernelGGL((read_probe_kernel<LPT, false>), dim3(grid), dim3(threads), 0, st, s, n16, nchunks, sink);
+}
+
+int launch_read_probe_ex(const void* src, size_t bytes, float* sink, int lpt, int threads,
+                         int work_groups, bool nt, hipStream_t st) {
+    const size_t n16 = bytes / 16;
+    if (n16 == 0) return GQ8_OK;
+    const size_t per = (size_t)threads * lpt;                        // pieces per chunk
+    const size_t nchunks = (n16 + per - 1) / per;                    // <= read_probe_blocks(bytes)
+    const unsigned grid = (unsigned)(work_groups > 0 && (size_t)work_groups < nchunks ? (size_t)work_groups : nchunks);
+    switch (lpt) {
+        case 1: launch_probe_lpt<1>(src, n16, nchunks, grid, threads, nt, sink, st); break;
+        case 2: launch_probe_lpt<2>(src, n16, nchunks, grid, threads, nt, sink, st); break;
+        case 4: launch_probe_lpt<4>(src, n16, nchunks, grid, threads, nt, sink, st); break;
+        default: launch_probe_lpt<8>(src, n16, nchunks, grid, threads, nt, sink, st); break;
+    }
+    return launch_status();
 }
 
 int launch_read_probe(const void* src, size_t bytes, float* sink, hipStream_t st) {
-    const size_t blocks = read_probe_blocks(bytes);
-    if (blocks == 0) return GQ8_OK;
-    hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
-                       static_cast<const u32x4*>(src), bytes / 16, sink);
-    return launch_status();
+    return launch_read_probe_ex(src, bytes, sink, kProbeLpt, kProbeThreads, 0, kProbeNt != 0, st);
 }
 
 }  // namespace gq8

@@ -67,6 +67,7 @@ _SIGS = {
     "gq8_moe_q8_0_routed_flags": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _SZ, _P]),
     "gq8_read_probe_sink_floats": (_SZ, [_SZ]),
     "gq8_read_probe": (_I, [_P, _SZ, _P, _P]),
+    "gq8_read_probe_ex": (_I, [_P, _SZ, _P, _I, _I, _I, _I, _P]),
 }
 
 for _name, (_res, _args) in _SIGS.items():
@@ -298,6 +299,13 @@ def gq8_read_probe_sink_floats(nbytes):
 
 def gq8_read_probe(src, nbytes, sink, stream=None):
     return _check("gq8_read_probe", _lib.gq8_read_probe(_dev(src), nbytes, _dev(sink), _stream(stream)))
+
+
+def gq8_read_probe_ex(src, nbytes, sink, loads_per_lane, threads, work_groups, nontemporal,
+                      stream=None):
+    return _check("gq8_read_probe_ex", _lib.gq8_read_probe_ex(
+        _dev(src), nbytes, _dev(sink), loads_per_lane, threads, work_groups, nontemporal,
+        _stream(stream)))
 
 
 def raw():

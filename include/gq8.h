@@ -325,6 +325,15 @@ int gq8_moe_q8_0_routed_flags(const void* x, const uint16_t* xd, const int32_t* 
 size_t gq8_read_probe_sink_floats(size_t bytes);
 int gq8_read_probe(const void* src, size_t bytes, float* sink, void* stream);
 
+/* The same stream with its launch shape chosen: loads_per_lane 16-byte loads per lane per chunk
+ * (1, 2, 4 or 8), threads per work-group (256, 512 or 1024), work_groups = 0 for one work-group per
+ * chunk of threads * loads_per_lane * 16 bytes, else at most that many work-groups striding over
+ * the chunks; nontemporal 1 for non-temporal loads, 0 for plain ones. The sink is as above (its
+ * size covers every shape). Other values: GQ8_ESHAPE. For sweeping the shapes that bound how fast
+ * a read of a given size can be. */
+int gq8_read_probe_ex(const void* src, size_t bytes, float* sink, int loads_per_lane, int threads,
+                      int work_groups, int nontemporal, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,3 +21,19 @@ def gpu():
         pytest.fail("gpu-marked test run without a visible GPU")
     from gemm_q8_amd import gq8
     return gq8
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """With GQ8_PARITY_REPORT=<path>, write every parity check's worst ratios (tests/helpers.py)
+    as JSON lines."""
+    path = os.environ.get("GQ8_PARITY_REPORT")
+    if not path:
+        return
+    import json
+    try:
+        from tests.helpers import RECORDS
+    except ImportError:
+        return
+    with open(path, "w") as f:
+        for r in RECORDS:
+            f.write(json.dumps(r) + "\n")

@@ -76,7 +76,8 @@ def test_forced_general_moe(gpu, forced, T, E, topk, D, F):
     experts = lambda e: synth.moe_expert_weights(e, D=D, F=F, seed=seed)  # noqa: E731
     blocks = lambda e: (quantize_q8_0(experts(e)["gate_up"]), quantize_q8_0(experts(e)["down"]))  # noqa: E731
     y_ref, S = moe_forward(quantize_q8_1_bf16(inp["x"]), ids_ref, p_ref, blocks, h_q8_1=True)
-    check_bf16(to_host(o3, np.uint16), y_ref, S, f"forced moe q8_1(h) T={T} D={D} F={F}")
+    check_bf16(to_host(o3, np.uint16), y_ref, S, f"forced moe q8_1(h) T={T} D={D} F={F}",
+               page=False)   # its own rule: h re-quantized on both sides, codes may flip
 
 
 def test_unknown_switch_value_is_ignored(gpu, monkeypatch):

@@ -273,7 +273,8 @@ def test_moe_flags(gpu, T, E, topk, D, F):
     experts = lambda e: synth.moe_expert_weights(e, D=D, F=F, seed=seed)  # noqa: E731
     blocks = lambda e: (quantize_q8_0(experts(e)["gate_up"]), quantize_q8_0(experts(e)["down"]))  # noqa: E731
     y_ref, S = moe_forward(quantize_q8_1_bf16(inp["x"]), ids_ref, p_ref, blocks, h_q8_1=True)
-    check_bf16(to_host(o[2], np.uint16), y_ref, S, f"moe q8_1(h) T={T} D={D} F={F}")
+    check_bf16(to_host(o[2], np.uint16), y_ref, S, f"moe q8_1(h) T={T} D={D} F={F}",
+               page=False)   # its own rule: h re-quantized on both sides, codes may flip
     assert not torch.equal(o[2], out)                           # a different read
 
 

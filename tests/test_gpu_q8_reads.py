@@ -223,7 +223,8 @@ def test_hc_pair_full_size(gpu, T):
     Wu = np.abs(dequantize(bu))
     dlo = 2e-3 * S + bf16_ulp(np.abs(lo_ref) + 2e-3 * S)
     S_chain = S_up + dlo @ Wu.T / 2e-3
-    check_bf16(to_host(out2, np.uint16), ref_chain, S_chain, f"hc chain T={T}")
+    check_bf16(to_host(out2, np.uint16), ref_chain, S_chain, f"hc chain T={T}",
+               page=False)   # lo differs by bf16 roundings on the two sides: widened rule above
 
 
 @pytest.mark.parametrize("T,N,K", [(1, 100, 320), (4, 77, 320), (6, 5, 64), (9, 40, 1024), (16, 33, 320),
@@ -356,3 +357,98 @@ def test_gemv_mfma_graph_replay(gpu):
             g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, y0)
+
+
+# ------------------------------------------------------------------------------ exact, full size
+
+def _one_hot_cols(T, K, stride_mix):
+    """T distinct columns spread over K (different blocks and slabs for each token)."""
+    return [int((t * K // T + stride_mix * (t + 1) + 37 * t) % K) for t in range(T)]
+
+
+_CS = [1.0, -1.5, 0.75, -3.0]
+
+
+@pytest.mark.parametrize("general", [False, True])
+@pytest.mark.parametrize("T", [1, 4, 6, 16])
+def test_up_one_hot_full_size_is_exact(gpu, T, general, monkeypatch):
+    """lo[t] = c_t e_{k_t} at the full 16384 x 320 up read: every output is one product
+    d q c (11 + 7 + 2 significant bits: exact in fp32) and the other 319 terms are exact zeros, so
+    out[t] = bf16(d q c) bit for bit, on the direct kernel and on the general (LDS-staged) one. A
+    dropped or misread Q8_0 block shows as a wrong row. Values are compared, so a quant of 0 with
+    c < 0 may come out as +0 (the sum of the 320 terms) where the single product is -0."""
+    from oracle.numerics import bf16_bits
+    N, K = 16384, 320
+    w = synth.normal_f32(30, "gpu.up.onehot", (N, K), 0.0, 0.02)
+    b = quantize_q8_0(w)
+    ks = _one_hot_cols(T, K, 7)
+    lo = np.zeros((T, K), np.uint16)
+    for t, k in enumerate(ks):
+        lo[t, k] = bf16_bits(np.float32(_CS[t % 4]))
+    if general:
+        monkeypatch.setenv("GQ8_FORCE_GENERIC", "1")
+    out = to_host(_up(gpu, q8_0_from_f32(to_dev(w)), to_dev(lo), T, N, K), np.uint16)
+    for t, k in enumerate(ks):
+        prod = (fp16_to_f32(b.d[:, k // 32]) * b.q[:, k // 32, k % 32].astype(np.float32)
+                * np.float32(_CS[t % 4])).astype(np.float32)
+        assert np.array_equal(bf16_to_f32(out[t]), bf16_to_f32(bf16_bits(prod))), f"T={T} t={t} k={k}"
+
+
+def _down_one_hot_ref(b, ks, cs, K, eps=1e-6):
+    """lo[t][n] = rs_t c_t d[n][k_t/32] q[n][k_t] and rs_t = 1/sqrt(c_t^2 / K + eps) (fp64)."""
+    rs = np.array([1.0 / np.sqrt(c * c / K + eps) for c in cs])
+    lo = np.stack([rs[t] * cs[t] * fp16_to_f32(b.d[:, k // 32]).astype(np.float64)
+                   * b.q[:, k // 32, k % 32].astype(np.float64) for t, k in enumerate(ks)])
+    return lo, rs
+
+
+def _one_hot_R(T, K, ks, cs):
+    from oracle.numerics import bf16_bits
+    R = np.zeros((T, K), np.uint16)
+    for t, k in enumerate(ks):
+        R[t, k] = bf16_bits(np.float32(cs[t]))
+    return R
+
+
+@pytest.mark.parametrize("T", [1, 4, 6, 16])
+def test_down_one_hot_full_size(gpu, T):
+    """R[t] = c_t e_{k_t}, w_norm = 1, at the full 320 x 16384 down read: each lo is one product
+    rs c d q, so lo is within one bf16 spacing of the fp64 value for all 320 rows (rs is an fp32
+    value on the GPU), and rs within fp32 rounding. The k_t fall in different 512-column slabs; a
+    dropped or misread block gives a wrong (or zero) row."""
+    N, K = 320, 16384
+    w = synth.normal_f32(31, "gpu.down.onehot", (N, K), 0.0, 0.02)
+    b = quantize_q8_0(w)
+    ks = _one_hot_cols(T, K, 515)
+    cs = [_CS[t % 4] for t in range(T)]
+    wn = np.full(K, 0x3F80, np.uint16)                           # bf16 1.0
+    lo, rs = _down(gpu, q8_0_from_f32(to_dev(w)), to_dev(_one_hot_R(T, K, ks, cs)), to_dev(wn), T, N, K)
+    lo_ref, rs_ref = _down_one_hot_ref(b, ks, cs, K)
+    from oracle.numerics import bf16_ulp
+    v = bf16_to_f32(to_host(lo, np.uint16)).astype(np.float64)
+    assert np.all(np.abs(v - lo_ref) <= bf16_ulp(lo_ref)), f"T={T} ks={ks}"
+    assert np.allclose(to_host(rs), rs_ref, rtol=2e-7, atol=0)
+
+
+@pytest.mark.parametrize("T", [1, 4, 6, 16])
+def test_pair_one_hot_full_size(gpu, T):
+    """The pair (the down's combine inside the up kernel for T <= 4, three kernels above) on the
+    one-hot R of the test above: lo within one bf16 spacing of rs c d q, and the up output against
+    the oracle's up read of the pair's own lo under both rules."""
+    Nlr, Khc = 320, 16384
+    wd_f = synth.normal_f32(32, "gpu.pair.onehot.d", (Nlr, Khc), 0.0, 0.02)
+    wu_f = synth.normal_f32(32, "gpu.pair.onehot.u", (Khc, Nlr), 0.0, 0.02)
+    ks = _one_hot_cols(T, Khc, 301)
+    cs = [_CS[(t + 1) % 4] for t in range(T)]
+    wn = np.full(Khc, 0x3F80, np.uint16)
+    lo, rs, out = _pair(gpu, q8_0_from_f32(to_dev(wd_f)), to_dev(_one_hot_R(T, Khc, ks, cs)),
+                        to_dev(wn), q8_0_from_f32(to_dev(wu_f)), T, Nlr, Khc)
+    torch.cuda.synchronize()
+    lo_ref, rs_ref = _down_one_hot_ref(quantize_q8_0(wd_f), ks, cs, Khc)
+    from oracle.numerics import bf16_ulp
+    lo_h = to_host(lo, np.uint16)
+    v = bf16_to_f32(lo_h).astype(np.float64)
+    assert np.all(np.abs(v - lo_ref) <= bf16_ulp(lo_ref)), f"T={T} ks={ks}"
+    assert np.allclose(to_host(rs), rs_ref, rtol=2e-7, atol=0)
+    out_ref, S_up = hc_up(lo_h, quantize_q8_0(wu_f))
+    check_bf16(to_host(out, np.uint16), out_ref, S_up, f"pair one-hot up T={T}")
