@@ -282,6 +282,56 @@ GQ8_EXPORT int gq8_hc_q8_pair(const void* w_down, const uint16_t* R, const uint1
     return launch_hc_pair(dn, up, ws, S(stream));
 }
 
+// ---------------------------------------------------------------------------------- no allocation
+// The pair's workspace in a file-scope device array, for callers that cannot allocate (code
+// under graph capture, allocation-free serving loops). Each device the library runs on holds
+// its own copy of the array until the process ends; host code never uses the array's name (on
+// the host it is only a stand-in), only the device address that hipGetSymbolAddress returns,
+// fetched once per device with that device current and kept per device.
+
+static __device__ __align__(256) unsigned char scratch[GQ8_NOALLOC_SCRATCH_BYTES];
+
+static void* scratch_address() {
+    static std::atomic<void*> addr[64];     // per device id; null = not yet fetched
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (p != nullptr) return p;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    addr[dev].store(p, std::memory_order_release);   // every thread that races here gets the same address
+    return p;
+}
+
+GQ8_EXPORT int gq8_hc_q8_pair_noalloc(const void* w_down, const uint16_t* R, const uint16_t* w_norm,
+                                      float eps, const void* w_up, uint16_t* lo, float* rs_out,
+                                      uint16_t* out, int T, int Nlr, int Khc, void* stream) {
+    if (T < 0 || Nlr < 0 || Khc < 0) return GQ8_EINVAL;
+    if (!q8_shape_ok(T, Nlr, Khc) || Nlr % 32 != 0 || Nlr > 1024 || Khc == 0 || Nlr == 0)
+        return GQ8_ESHAPE;
+    if (T == 0) return GQ8_OK;
+    if (hc_down_workspace_bytes(T, Nlr, Khc) > (size_t)GQ8_NOALLOC_SCRATCH_BYTES) return GQ8_ESHAPE;
+    if (w_down == nullptr || R == nullptr || w_norm == nullptr || w_up == nullptr ||
+        lo == nullptr || out == nullptr)
+        return GQ8_EINVAL;
+    if (!aligned16(w_down) || !aligned16(R) || !aligned16(w_norm) || !aligned16(w_up) ||
+        !aligned16(lo))
+        return GQ8_EALIGN;
+    if (!(eps >= 0.f)) return GQ8_EINVAL;
+    if (device_cus() == 0) return GQ8_ENODEV;
+    void* ws = scratch_address();
+    if (ws == nullptr) return GQ8_EHIP;
+    GemvArgs dn{};
+    dn.q = static_cast<const int8_t*>(w_down);
+    dn.d = reinterpret_cast<const uint16_t*>(dn.q + (size_t)Nlr * Khc);
+    dn.x = R; dn.wnorm = w_norm; dn.T = T; dn.N = Nlr; dn.K = Khc; dn.out = lo;
+    dn.rs_out = rs_out; dn.eps = eps;
+    GemvArgs up{};
+    up.q = static_cast<const int8_t*>(w_up);
+    up.d = reinterpret_cast<const uint16_t*>(up.q + (size_t)Khc * Nlr);
+    up.x = lo; up.T = T; up.N = Khc; up.K = Nlr; up.out = out;
+    return launch_hc_pair(dn, up, ws, S(stream));
+}
+
 GQ8_EXPORT int gq8_hc_bf16_pair(const uint16_t* w_down, const uint16_t* R, const uint16_t* w_norm,
                                 float eps, const uint16_t* w_up, uint16_t* lo, float* rs_out,
                                 uint16_t* out, int T, int Nlr, int Khc, void* ws, size_t ws_bytes,

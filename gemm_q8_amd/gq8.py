@@ -21,6 +21,7 @@ _lib = ctypes.CDLL(_LIB_PATH)
 LIB_PATH = _LIB_PATH
 
 OK, EINVAL, ESHAPE, EALIGN, EWORKSPACE, ECAPTURE, EHIP, ENODEV = 0, -1, -2, -3, -4, -5, -6, -7
+NOALLOC_SCRATCH_BYTES = 4 << 20
 MOE_X_BF16, MOE_H_Q8_1 = 1, 2
 OP_Q8_0_GEMV, OP_HC_DOWN, OP_HC_UP, OP_W8A8, OP_HC_PAIR, OP_W8A8_BF16X = 1, 2, 3, 4, 5, 6
 
@@ -46,6 +47,7 @@ _SIGS = {
     "gq8_hc_q8_down": (_I, [_P, _P, _P, _F, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_hc_q8_up": (_I, [_P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_hc_q8_pair": (_I, [_P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "gq8_hc_q8_pair_noalloc": (_I, [_P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _P]),
     "gq8_hc_bf16_pair": (_I, [_P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_w8a8_packed_bytes": (_SZ, [_I, _I]),
     "gq8_w8a8_pack": (_I, [_P, _I, _I, _P, _P]),
@@ -306,6 +308,12 @@ def gq8_read_probe_ex(src, nbytes, sink, loads_per_lane, threads, work_groups, n
     return _check("gq8_read_probe_ex", _lib.gq8_read_probe_ex(
         _dev(src), nbytes, _dev(sink), loads_per_lane, threads, work_groups, nontemporal,
         _stream(stream)))
+
+
+def gq8_hc_q8_pair_noalloc(w_down, R, w_norm, eps, w_up, lo, rs_out, out, T, Nlr, Khc, stream=None):
+    return _check("gq8_hc_q8_pair_noalloc", _lib.gq8_hc_q8_pair_noalloc(
+        _dev(w_down), _dev(R), _dev(w_norm), eps, _dev(w_up), _dev(lo), _dev(rs_out), _dev(out),
+        T, Nlr, Khc, _stream(stream)))
 
 
 def raw():

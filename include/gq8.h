@@ -188,6 +188,22 @@ int gq8_hc_q8_pair(const void* w_down, const uint16_t* R, const uint16_t* w_norm
                    const void* w_up, uint16_t* lo, float* rs_out, uint16_t* out,
                    int T, int Nlr, int Khc, void* ws, size_t ws_bytes, void* stream);
 
+/* gq8_hc_q8_pair without a workspace argument, for callers that cannot allocate memory (code
+ * under hipGraph capture that may not call hipMalloc, allocation-free serving loops, harnesses
+ * that forbid allocation): the workspace is a fixed device array inside the library, of
+ * GQ8_NOALLOC_SCRATCH_BYTES, one per device, held until the process ends. The call itself
+ * allocates nothing. Inputs, outputs, shapes and results are those of gq8_hc_q8_pair (bitwise);
+ * a shape whose workspace, gq8_workspace_bytes(GQ8_OP_HC_PAIR, T, Nlr, Khc), exceeds the array
+ * returns GQ8_ESHAPE (T = 16, Nlr = 320, Khc = 16384 needs 642 KiB; at T = 16 and Nlr = 1024,
+ * Khc up to 32256 fits). Every call on one device shares that device's array and every call
+ * rewrites all of it that it reads (no clearing needed), so calls that may run at the same time
+ * on one device (several streams, host threads or concurrent graph replays) race and must not
+ * overlap. GQ8_EHIP if the array's device address cannot be obtained. */
+#define GQ8_NOALLOC_SCRATCH_BYTES (4u << 20)
+int gq8_hc_q8_pair_noalloc(const void* w_down, const uint16_t* R, const uint16_t* w_norm, float eps,
+                           const void* w_up, uint16_t* lo, float* rs_out, uint16_t* out, int T,
+                           int Nlr, int Khc, void* stream);
+
 /* The same pair on BF16 weights: the read the Q8_0 pair replaces (HC-Q8 page, "Summary": the
  * kernel-level BF16 -> Q8_0 read times), kept as an in-library comparison read measured with the
  * same harness. w_down bf16 [Nlr][Khc] and w_up bf16 [Khc][Nlr], row-major, 16-byte aligned; every
