@@ -191,9 +191,10 @@ __global__ void __launch_bounds__(1024) read_probe_kernel(const u32x4* __restric
     if (acc == 0x9E3779B9u && threadIdx.x == 0) sink[blockIdx.x] = 1.0f;   // keeps the loads alive
 }
 
-// The default shape (gq8_read_probe): one 16-byte non-temporal load per lane, 256 threads, one
-// work-group per 4 KiB chunk.
-constexpr int kProbeLpt = 1, kProbeThreads = 256, kProbeNt = 1;
+// The default shape (gq8_read_probe), the fastest of a sweep over loads per lane, threads,
+// grid and load kind at 4.5 to 34 MB: one 16-byte non-temporal load per lane, 256 threads, eight
+// work-groups per compute unit striding over the 4 KiB chunks.
+constexpr int kProbeLpt = 1, kProbeThreads = 256, kProbeNt = 1, kProbeWgPerCu = 8;
 
 template <int LPT>
 static void launch_probe_lpt(const void* src, size_t n16, size_t nchunks, unsigned grid, int threads,
@@ -220,7 +221,8 @@ int launch_read_probe_ex(const void* src, size_t bytes, float* sink, int lpt, in
 }
 
 int launch_read_probe(const void* src, size_t bytes, float* sink, hipStream_t st) {
-    return launch_read_probe_ex(src, bytes, sink, kProbeLpt, kProbeThreads, 0, kProbeNt != 0, st);
+    return launch_read_probe_ex(src, bytes, sink, kProbeLpt, kProbeThreads, kProbeWgPerCu * device_cus(),
+                                kProbeNt != 0, st);
 }
 
 }  // namespace gq8

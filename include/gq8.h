@@ -334,7 +334,9 @@ int gq8_moe_q8_0_routed_flags(const void* x, const uint16_t* xd, const int32_t* 
  * Diagnostics
  * ------------------------------------------------------------------------------------------ */
 
-/* Streaming read of `bytes` (multiple of 16) from src, 4 KiB per work-group; sink holds
+/* Streaming read of `bytes` (multiple of 16) from src, one 16-byte non-temporal load per lane,
+ * 256 threads per work-group, eight work-groups per compute unit over 4 KiB chunks (the fastest
+ * shape of a sweep of gq8_read_probe_ex at 4.5 to 34 MB); sink holds
  * gq8_read_probe_sink_floats(bytes) floats, written only for a bit pattern that keeps the loads
  * from being elided (its contents are unspecified). Measures the read bandwidth reachable for a
  * given byte count in one launch. */
