@@ -150,11 +150,13 @@ def test_moe_crowded_expert(gpu, D, F):
 
 
 @pytest.mark.parametrize("T,topk,E,D,F", [(1, 32, 64, 2048, 512), (2, 17, 40, 544, 256),
-                                          (1, 20, 20, 160, 1024)])
+                                          (1, 20, 20, 160, 1024),
+                                          # more entries x F than the grouped down read stages
+                                          (2, 32, 80, 256, 512), (3, 20, 64, 96, 1024)])
 def test_moe_more_than_16_slots(gpu, T, topk, E, D, F):
     """topk > 16 (ids given directly: the routing call stops at 16): more slots per token than
-    the on-chip per-slot rows of the fused down read, so the plan-based kernels run; the output
-    still passes the rule against the oracle."""
+    the per-token down kernel keeps on chip, so the plan-based kernels run; the output passes the
+    rules against the oracle."""
     seed = 49
     inp = synth.moe_inputs(T=T, E=E, D=D, seed=seed)
     g = np.random.default_rng(seed)
