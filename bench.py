@@ -238,36 +238,36 @@ def cpu_model():
 
 
 def cpu_baseline(synth, budget_s):
-    """The oracle (test infrastructure) on the same workload: down + up for T = 1, 4, 6 per
-    step, repeated until about `budget_s` seconds have been spent."""
-    import oracle
+    """The C++ oracle (test infrastructure: float64 loops, OpenMP over output rows) on the step's
+    workload, down + up read at full size for T = 1, 4, 6 per step, repeated for about a third of
+    `budget_s` on one thread and two thirds on every host core."""
+    from oracle import c_oracle as C
     from oracle.q8 import quantize_q8_0
-    from threadpoolctl import threadpool_info, threadpool_limits
-    cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     base = synth.hc_inputs(6)
     bd, bu = quantize_q8_0(base["w_down"]), quantize_q8_0(base["w_up"])
-    from oracle.numerics import bf16_bits
     ins = {T: synth.hc_inputs(T) for T in TS}
+    cores = C.threads_available()
 
-    def run(budget):
+    def run(budget, threads):
         steps, t0 = 0, time.perf_counter()
         while True:
             for T in TS:
-                lo, _, _ = oracle.hc.hc_down(ins[T]["R"], ins[T]["w_norm"], bd)
-                oracle.hc.hc_up(bf16_bits(lo.astype(np.float32)), bu)
+                lo, _, _ = C.hc_down(ins[T]["R"], ins[T]["w_norm"], bd, threads=threads)
+                C.hc_up(C.bf16_bits(lo.astype(np.float32)), bu, threads=threads)
             steps += 1
             el = time.perf_counter() - t0
             if el >= budget:
                 return steps, el
     step_bytes = len(TS) * 2 * (K_HC * N_LR + K_HC * N_LR // 32 * 2)
-    with threadpool_limits(limits=1):
-        s1, e1 = run(budget_s / 3)
-    sa, ea = run(budget_s * 2 / 3)
+    run(0.2, 0)                                                    # warm-up
+    s1, e1 = run(budget_s / 3, 1)
+    sa, ea = run(budget_s * 2 / 3, 0)
     return {"value": round(sa * step_bytes / ea / 1e9, 4), "unit": "GB/s", "cores": int(cores),
             "kind": "oracle", "value_1thread": round(s1 * step_bytes / e1 / 1e9, 4),
             "cpu_model": cpu_model(), "host_threads": os.cpu_count(),
-            "sample": f"{sa} oracle steps (down+up read at T=1,4,6 each, full size) in {ea:.1f} s at "
-                      f"{cores} BLAS threads, {s1} steps in {e1:.1f} s at 1 thread; numpy float64"}
+            "sample": f"C++ oracle (float64 loops, OpenMP over output rows): {sa} steps (down+up read "
+                      f"at T=1,4,6 each, full size) in {ea:.1f} s on {cores} threads, {s1} steps in "
+                      f"{e1:.1f} s on 1 thread"}
 
 
 # ------------------------------------------------------------------------------------ other configs
@@ -517,21 +517,19 @@ class ProbeCache:
         return self.cache[key]
 
 
-def oracle_times(fn, scale=1.0):
-    """The oracle (test infrastructure) timed on the host: once with the BLAS pool at one thread,
-    once at its default size. Returns (us at 1 thread, us at all threads, threads of the pool),
-    each scaled by `scale` (a sample of 1/scale of the call)."""
-    from threadpoolctl import threadpool_info, threadpool_limits
-    fn()                                                   # first-touch / allocation warm-up
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        fn()
-        t1 = time.perf_counter() - t0
+def oracle_times(fn):
+    """The C++ oracle (test infrastructure) timed on the host: fn(threads) runs the whole call,
+    once on one thread and once on every host core, after a warm-up call. Returns (us at 1
+    thread, us at all cores, cores)."""
+    from oracle import c_oracle as C
+    fn(0)                                                  # first-touch / allocation warm-up
     t0 = time.perf_counter()
-    fn()
+    fn(1)
+    t1 = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    fn(0)
     ta = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return t1 * 1e6 * scale, ta * 1e6 * scale, threads
+    return t1 * 1e6, ta * 1e6, C.threads_available()
 
 
 def config_record(cfg, workload, shape, d, wbytes, probe_us, orc, orc_sample):
@@ -584,8 +582,7 @@ def bench_configs(torch, gq8, synth, dev, stream, hc_dist, reps, with_oracle=Tru
     (graphs of back-to-back calls over rotated weight copies, inputs in HBM), weight GB/s, the
     fraction of 8 TB/s and of the same-byte read probe, and the oracle's time on the host."""
     from gemm_q8_amd.device import q8_0_from_f32, to_dev, workspace
-    import oracle
-    from oracle.numerics import bf16_bits
+    from oracle import c_oracle as C
     from oracle.q8 import quantize_q8_0, quantize_q8_1_bf16
     probe = ProbeCache(torch, gq8, dev, stream, reps)
     recs = []
@@ -608,9 +605,9 @@ def bench_configs(torch, gq8, synth, dev, stream, hc_dist, reps, with_oracle=Tru
         dist = timed_dist(torch, stream, lambda i, T=T, x=x, y=y, nb=nb, wsp=wsp: (
             lambda s, w=wset[i % n]: gq8.gq8_q8_0_gemv(w, x, y, T, 1024, 4096, wsp, nb, s)), n, reps)
         xs = d["x"][:T]
-        orc = oracle_times(lambda: oracle.q8.q8_0_gemv(b, xs)) if with_oracle else None
+        orc = oracle_times(lambda th: C.q8_0_gemv(b, xs, threads=th)) if with_oracle else None
         emit(config_record(1, "Q8_0 GEMV N=1024 K=4096", {"T": T}, dist, w0.numel(),
-                           probe.us([w0.numel()]), orc, "the whole call (numpy float64)"))
+                           probe.us([w0.numel()]), orc, "the whole call (C++ oracle, float64)"))
     del wset
 
     # 2: the HC pair (timed with the step's own graphs)
@@ -622,15 +619,15 @@ def bench_configs(torch, gq8, synth, dev, stream, hc_dist, reps, with_oracle=Tru
         if with_oracle:
             ins = synth.hc_inputs(T)
 
-            def pair_oracle(ins=ins):
-                lo, _, _ = oracle.hc.hc_down(ins["R"], ins["w_norm"], bd)
-                oracle.hc.hc_up(bf16_bits(lo.astype(np.float32)), bu)
+            def pair_oracle(th, ins=ins):
+                lo, _, _ = C.hc_down(ins["R"], ins["w_norm"], bd, threads=th)
+                C.hc_up(C.bf16_bits(lo.astype(np.float32)), bu, threads=th)
             orc = oracle_times(pair_oracle)
         else:
             orc = None
         emit(config_record(2, "HC pair: RMSNorm + Q8_0 down [320 x 16384], Q8_0 up [16384 x 320]",
                            {"T": T}, hc_dist[T], pair_w, probe.us([pair_w // 2, pair_w // 2]), orc,
-                           "the whole call: down then up read (numpy float64)"))
+                           "the whole call: down then up read (C++ oracle, float64)"))
 
     # 3 and 4: W8A8
     for cfg, (M, N, K) in [(3, (16, 1536, 4096))] + [(4, (m, 2560, 4096)) for m in (1, 4, 8, 16, 32)] + \
@@ -644,13 +641,10 @@ def bench_configs(torch, gq8, synth, dev, stream, hc_dist, reps, with_oracle=Tru
         out = torch.empty((M, N), dtype=torch.int16, device=dev)
         dist = timed_dist(torch, stream, lambda i: (lambda s, w=wps[i % n]: gq8.gq8_w8a8_gemm(
             xq, xs, w, wsc, out, M, N, K, None, 0, s)), n, reps)
-        ns = 256
-        orc = (oracle_times(lambda: oracle.w8a8.w8a8_gemm(dd["xq"], dd["x_scale"], dd["W"][:, :ns],
-                                                          dd["w_scale"][:ns]), scale=N / ns)
-               if with_oracle else None)
+        orc = (oracle_times(lambda th: C.w8a8_gemm(dd["xq"], dd["x_scale"], dd["W"], dd["w_scale"],
+                                                   threads=th)) if with_oracle else None)
         emit(config_record(cfg, "W8A8 int8 x int8 -> int32 -> bf16", {"M": M, "N": N, "K": K}, dist,
-                           N * K, probe.us([wp0.numel()]), orc,
-                           f"{ns} of {N} columns, scaled by N/{ns} (numpy int64, single-threaded)"))
+                           N * K, probe.us([wp0.numel()]), orc, "the whole call (C++ oracle, int64)"))
         del wps
 
     # 5: routed MoE
@@ -668,11 +662,12 @@ def bench_configs(torch, gq8, synth, dev, stream, hc_dist, reps, with_oracle=Tru
         cache = {e: (quantize_q8_0(synth.moe_expert_weights(e, D=D, F=F)["gate_up"]),
                      quantize_q8_0(synth.moe_expert_weights(e, D=D, F=F)["down"])) for e in m["routed"]}
         x81 = quantize_q8_1_bf16(m["inp"]["x"])
-        orc = oracle_times(lambda: oracle.moe.moe_forward(x81, ids_h, p_h, lambda e: cache[e]))
+        prep = C.moe_prepare(x81, ids_h, p_h, lambda e: cache[e])
+        orc = oracle_times(lambda th: C.moe_run(prep, threads=th))
     emit(config_record(5, "routed MoE: T=4, 512 experts, top-8, gate/up [1024 x 2048], down [2048 x 512]",
                        {"T": T, "E": E, "topk": topk, "unique_experts": U}, dist,
                        U * (m["gu_b"] + m["dn_b"]), probe.us([U * m["gu_b"], U * m["dn_b"]]), orc,
-                       "the whole call (numpy float64, weights already quantized)"))
+                       "the whole call (C++ oracle, float64; weights already quantized)"))
     del m
     return recs
 
