@@ -275,7 +275,7 @@ def cpu_baseline(synth, budget_s):
 def bench_other_configs(torch, gq8, synth, dev, stream, report, only=None, w8a8_ms=None, gemv_ts=None):
     from gemm_q8_amd.device import q8_0_from_f32, to_dev, workspace
     lines = []
-    only = set(only or ("probe", "hcbf16", "gemv", "w8a8", "moe"))
+    only = set(only or ("probe", "combine", "hcbf16", "gemv", "w8a8", "moe"))
     ms = tuple(w8a8_ms or (1, 4, 8, 16, 32))
 
     def emit(d):
@@ -301,6 +301,8 @@ def bench_other_configs(torch, gq8, synth, dev, stream, report, only=None, w8a8_
               "GBps": round(nbytes / us / 1e3, 1)})
         del bufs
 
+    if "combine" in only:
+        bench_combine(torch, gq8, synth, dev, stream, emit)
     if "hcbf16" in only:
         bench_hc_bf16(torch, gq8, synth, dev, timed, emit)
     if "gemv" in only:
@@ -314,6 +316,49 @@ def bench_other_configs(torch, gq8, synth, dev, stream, report, only=None, w8a8_
         with open(report, "w") as f:
             for d in lines:
                 f.write(json.dumps(d) + "\n")
+
+
+def bench_combine(torch, gq8, synth, dev, stream, emit, rounds=3):
+    """The split reads' two combines in the same run: a kernel of its own (the default) against
+    the last-arriving work-group of each row group (GQ8_COMBINE=last), alternating, for the GEMV
+    at T = 5, 8, 16 (1024 x 4096), the down read at T = 1, 4, 8 and the pair at T = 1, 4
+    (320 x 16384). Median us per call over graphs of back-to-back calls on rotated weights."""
+    from gemm_q8_amd.device import q8_0_from_f32, to_dev, workspace
+    h = setup_hc(torch, gq8, synth, dev)
+    d = synth.q8_0_gemv_inputs(T=16)
+    w0 = q8_0_from_f32(to_dev(d["w"]))
+    ng = n_sets_for(w0.numel())
+    wg = [w0] + [w0.clone() for _ in range(ng - 1)]
+    cases = []
+    for T in (5, 8, 16):
+        x = to_dev(np.ascontiguousarray(d["x"][:T]))
+        y = torch.empty((T, 1024), dtype=torch.float32, device=dev)
+        nb = gq8.gq8_workspace_bytes(gq8.OP_Q8_0_GEMV, T, 1024, 4096)
+        wsp = workspace(nb)
+        cases.append((f"Q8_0 GEMV 1024x4096 T={T}", ng, lambda i, T=T, x=x, y=y, nb=nb, wsp=wsp: (
+            lambda s, w=wg[i % ng]: gq8.gq8_q8_0_gemv(w, x, y, T, 1024, 4096, wsp, nb, s))))
+    for T in (1, 4, 8):
+        dd = synth.hc_inputs(T)
+        R, wn = to_dev(dd["R"]), to_dev(dd["w_norm"])
+        lo = torch.empty((T, N_LR), dtype=torch.int16, device=dev)
+        rs = torch.empty((T,), dtype=torch.float32, device=dev)
+        nb = gq8.gq8_workspace_bytes(gq8.OP_HC_DOWN, T, N_LR, K_HC)
+        wsp = workspace(nb)
+        cases.append((f"HC down read 320x16384 T={T}", h["n_sets"], lambda i, T=T, R=R, wn=wn, lo=lo, rs=rs, nb=nb, wsp=wsp: (
+            lambda s, w=h["wds"][i % h["n_sets"]]: gq8.gq8_hc_q8_down(w, R, wn, 1e-6, lo, rs, T, N_LR, K_HC, wsp, nb, s))))
+    for T in (1, 4):
+        cases.append((f"HC pair T={T}", h["n_sets"], lambda i, T=T: hc_pair_fn(gq8, h, T, i)))
+    for name, n, mk in cases:
+        t = {"kernel": [], "last": []}
+        for _ in range(rounds):
+            for mode in ("kernel", "last"):
+                os.environ["GQ8_COMBINE"] = mode
+                t[mode].append(timed_dist(torch, stream, mk, n, reps=10)["median"])
+        os.environ.pop("GQ8_COMBINE", None)
+        emit({"workload": "combine of split partial sums: " + name,
+              "kernel_combine_us": round(min(t["kernel"]), 3), "last_arriver_us": round(min(t["last"]), 3),
+              "rounds": rounds})
+    del wg
 
 
 def bench_hc_bf16(torch, gq8, synth, dev, timed, emit):
@@ -689,8 +734,8 @@ def main():
                          "then exit")
     ap.add_argument("--no-configs", action="store_true",
                     help="leave out the per-configuration records (the five workloads)")
-    ap.add_argument("--only", default="probe,hcbf16,gemv,w8a8,moe",
-                    help="with --all-configs: comma-separated subset of probe,hcbf16,gemv,w8a8,moe")
+    ap.add_argument("--only", default="probe,combine,hcbf16,gemv,w8a8,moe",
+                    help="with --all-configs: comma-separated subset of probe,combine,hcbf16,gemv,w8a8,moe")
     ap.add_argument("--w8a8-ms", default="1,4,8,16,32", help="with --all-configs: W8A8 M values")
     ap.add_argument("--gemv-ts", default="1,2,4,8,16", help="token rows of the GEMV sweep")
     ap.add_argument("--report", default="bench_all.jsonl",

@@ -33,6 +33,15 @@ bool force_general() {
     return false;
 }
 
+bool combine_last_arriver() {
+    const char* v = getenv("GQ8_COMBINE");
+    if (v == nullptr || v[0] == '\0' || strcmp(v, "kernel") == 0) return false;
+    if (strcmp(v, "last") == 0) return true;
+    static std::atomic<bool> said{false};
+    if (!said.exchange(true)) fprintf(stderr, "gq8: GQ8_COMBINE=%s not understood (kernel or last); ignored\n", v);
+    return false;
+}
+
 }  // namespace gq8
 
 static inline hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
@@ -147,8 +156,17 @@ static size_t bf16x_stage_bytes(int M, int K) {
 }
 
 GQ8_EXPORT size_t gq8_workspace_counter_bytes(int op, int rows, int N, int K) {
-    (void)op; (void)rows; (void)N; (void)K;
-    return 0;   // no operation keeps arrival counters: split sums are combined by a second kernel
+    switch (op) {
+        case GQ8_OP_HC_DOWN:
+        case GQ8_OP_HC_PAIR:
+            if (!q8_shape_ok(rows, N, K) || rows == 0 || N == 0 || K == 0) return 0;
+            return hc_down_counter_bytes(N);
+        case GQ8_OP_Q8_0_GEMV:
+            if (!q8_shape_ok(rows, N, K)) return 0;
+            return gemv_counter_bytes(rows, N, K);
+        default:
+            return 0;
+    }
 }
 
 GQ8_EXPORT size_t gq8_workspace_bytes(int op, int rows, int N, int K) {
@@ -181,10 +199,30 @@ GQ8_EXPORT int gq8_workspace_init(void* ws, size_t bytes, void* stream) {
     return launch_fill_zero(ws, bytes, S(stream));
 }
 
-GQ8_EXPORT int gq8_workspace_check(const void* ws, size_t bytes, void* stream, int* nonzero_counters) {
-    (void)stream;
-    if (nonzero_counters == nullptr || (ws == nullptr && bytes > 0)) return GQ8_EINVAL;
-    *nonzero_counters = 0;      // gq8_workspace_counter_bytes() is 0 for every operation
+GQ8_EXPORT int gq8_workspace_check(int op, int rows, int N, int K, const void* ws, size_t bytes,
+                                   void* stream, int* nonzero_counters) {
+    if (nonzero_counters == nullptr) return GQ8_EINVAL;
+    const size_t need = gq8_workspace_bytes(op, rows, N, K);
+    const size_t cb = gq8_workspace_counter_bytes(op, rows, N, K);
+    *nonzero_counters = 0;
+    if (cb == 0) return GQ8_OK;
+    if (ws == nullptr || bytes < need) return GQ8_EWORKSPACE;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(S(stream), &cs) != hipSuccess) return GQ8_EHIP;
+    if (cs != hipStreamCaptureStatusNone) return GQ8_ECAPTURE;
+    unsigned host[1024];
+    const size_t words = cb / sizeof(unsigned);
+    const char* src = static_cast<const char*>(ws) + (need - cb);
+    int nz = 0;
+    for (size_t w0 = 0; w0 < words; w0 += 1024) {
+        const size_t nw = words - w0 < 1024 ? words - w0 : 1024;
+        if (hipMemcpyAsync(host, src + w0 * sizeof(unsigned), nw * sizeof(unsigned),
+                           hipMemcpyDeviceToHost, S(stream)) != hipSuccess ||
+            hipStreamSynchronize(S(stream)) != hipSuccess)
+            return GQ8_EHIP;
+        for (size_t i = 0; i < nw; ++i) nz += host[i] != 0u;
+    }
+    *nonzero_counters = nz;
     return GQ8_OK;
 }
 

@@ -273,8 +273,18 @@ constexpr int dn_parts() { return (WB || T <= 8 || SLAB < kDownSlab) ? 1 : 2; }
 // 16 x 1024 bytes, read in four quarters of four 1 KiB loads (four rows x 256 bytes each); the
 // MFMA B operand is 8 bf16 straight from the LDS tile and the block results chain in the MFMA
 // accumulator (A is zero past the slab end).
-template <int T, bool XF = false, bool WB = false, int SLAB = kDownSlab>
+//
+// LA (the last-arriver combine, one column part only): every work-group also keeps its own copy
+// of its slab's sums of squares (per row group), and after its partial sums are stored (every
+// wave waiting for its stores, then a work-group barrier), thread 0 adds one to the row group's
+// counter with an agent-scope release atomic (the one that sees S - 1 then takes an agent-scope
+// acquire fence: the arrivals form a release sequence on the counter). The work-group that sees S - 1 was
+// the last: it adds the row group's S partial planes and applies rs exactly as
+// hc_down_combine_kernel does (same order: bitwise the same outputs) and resets the counter.
+// No work-group waits for another, so nothing assumes that they are resident together.
+template <int T, bool XF = false, bool WB = false, int SLAB = kDownSlab, bool LA = false>
 __global__ void __launch_bounds__((256 * dn_parts<T, WB, SLAB>())) hc_down_partial_kernel(GemvArgs a) {
+    static_assert(!LA || dn_parts<T, WB, SLAB>() == 1, "the last-arriver combine takes one column part");
     static_assert(!WB || SLAB == kDownSlab, "the BF16 read uses 512-column slabs");
     constexpr int NB = SLAB / 32;                                  // Q8_0 blocks per slab
     constexpr int NCP = dn_parts<T, WB, SLAB>();                   // column parts of the slab
@@ -523,12 +533,72 @@ __global__ void __launch_bounds__((256 * dn_parts<T, WB, SLAB>())) hc_down_parti
             if (tt < T && n < N) a.part[((size_t)s * T + tt) * N + n] = acc[v];
         }
     }
-    if (!XF && y == 0 && threadIdx.x < T) {
+    if (!XF && (y == 0 || LA) && threadIdx.x < T) {
         const int tt = threadIdx.x;
         float v = sqw[0][tt];
 #pragma unroll
         for (int w = 1; w < NWV; ++w) v += sqw[w][tt];
-        a.ssq[(size_t)s * T + tt] = v;
+        a.ssq[((size_t)y * S + s) * T + tt] = v;           // row group 0's copy is [S][T]
+    }
+    if constexpr (LA) {
+        __shared__ int s_last;
+        __shared__ float s_rs[16];
+        // every wave's partial-sum stores complete in L2 (vmcnt 0) before the barrier, so that
+        // thread 0's agent-scope release (an L2 writeback) covers all of them, not only its own
+        // wave's (the barrier alone does not wait for other waves' global stores)
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            // release: this work-group's partial sums before the arrival; only the last arriver
+            // needs the acquire (an L2 invalidate), so the others skip it
+            const unsigned old = __hip_atomic_fetch_add(a.cnt + y, 1u, __ATOMIC_RELEASE,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
+            s_last = old == (unsigned)(S - 1);
+            if (s_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+        __syncthreads();
+        if (!s_last) return;
+        // the last work-group of row group y: rs per token (the combine kernel's lane-strided
+        // sums and wave sum), then the 64 rows x T outputs over the S planes
+        if (!XF && wave == 0) {
+            for (int tt = 0; tt < T; ++tt) {
+                float ss = 0.f;
+                for (int s2 = lane; s2 < S; s2 += 64) ss += a.ssq[((size_t)y * S + s2) * T + tt];
+                ss = wave_sum(ss);
+                if (lane == 0) {
+                    const float rs = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+                    s_rs[tt] = rs;
+                    if (y == 0 && a.rs_out != nullptr) a.rs_out[tt] = rs;
+                }
+            }
+        }
+        __syncthreads();
+        const int per = (S + 3) / 4;
+        for (int o = threadIdx.x; o < 64 * T; o += NTH) {
+            const int nl = o & 63, tt = o >> 6;
+            const int nn = y * kDnRows + nl;
+            if (nn >= N) continue;
+            float gs[4];
+#pragma unroll
+            for (int sg = 0; sg < 4; ++sg) {
+                const int s0 = sg * per, s1 = imin(S, s0 + per);
+                float v = 0.f;
+                for (int sb = s0; sb < s1; sb += 8) {
+                    float p[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) p[i] = a.part[((size_t)imin(sb + i, S - 1) * T + tt) * N + nn];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) v += sb + i < s1 ? p[i] : 0.f;
+                }
+                gs[sg] = v;
+            }
+            const float tot = ((gs[0] + gs[1]) + gs[2]) + gs[3];
+            if (XF)
+                reinterpret_cast<float*>(a.out)[(size_t)tt * N + nn] = tot;
+            else
+                reinterpret_cast<uint16_t*>(a.out)[(size_t)tt * N + nn] = f2bf_bits(s_rs[tt] * tot);
+        }
+        if (threadIdx.x == 0) __hip_atomic_store(a.cnt + y, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -575,19 +645,44 @@ __global__ void __launch_bounds__(256) hc_down_combine_kernel(GemvArgs a) {
     }
 }
 
+// Down-read workspace: partial sums [S][T][N], then the sums of squares [G][S][T] (G = 64-row
+// groups; the kernel combine reads row group 0's copy, the last-arriver combine each group's
+// own), then one arrival counter per row group (zero between calls).
+static size_t dn_groups(int N) { return (size_t)(N + kDnRows - 1) / kDnRows; }
+
+size_t hc_down_counter_bytes(int N) { return round_up(dn_groups(N) * sizeof(unsigned), kCounterAlign); }
+
 size_t hc_down_workspace_bytes(int T, int N, int K) {
     const size_t S = hc_down_slabs(K);
     return round_up(S * T * N * sizeof(float), kCounterAlign) +
-           round_up(S * T * sizeof(float), kCounterAlign);
+           round_up(dn_groups(N) * S * T * sizeof(float), kCounterAlign) + hc_down_counter_bytes(N);
 }
+
+static void dn_workspace(GemvArgs& a, int T, void* ws) {
+    const int S = hc_down_slabs(a.K);
+    char* w = static_cast<char*>(ws);
+    const size_t pb = round_up((size_t)S * T * a.N * sizeof(float), kCounterAlign);
+    const size_t sb = round_up(dn_groups(a.N) * S * T * sizeof(float), kCounterAlign);
+    a.S = S;
+    a.part = reinterpret_cast<float*>(w);
+    a.ssq = reinterpret_cast<float*>(w + pb);
+    a.cnt = reinterpret_cast<unsigned*>(w + pb + sb);
+}
+
+// the last-arriver combine where the slab kernel has one column part (T <= 8 for 512 columns)
+template <int T>
+static bool dn_last_arriver() { return dn_parts<T, false>() == 1 && combine_last_arriver(); }
 
 template <int T>
 static int launch_down_t(GemvArgs a, void* ws, hipStream_t st) {
-    const int S = hc_down_slabs(a.K);
-    char* w = static_cast<char*>(ws);
-    a.S = S;
-    a.part = reinterpret_cast<float*>(w);
-    a.ssq = reinterpret_cast<float*>(w + round_up((size_t)S * T * a.N * sizeof(float), kCounterAlign));
+    dn_workspace(a, T, ws);
+    const int S = a.S;
+    if constexpr (dn_parts<T, false>() == 1) {
+        if (combine_last_arriver()) {
+            hipLaunchKernelGGL((hc_down_partial_kernel<T, false, false, kDownSlab, true>), dim3(S * ((a.N + kDnRows - 1) / kDnRows)), dim3(256), 0, st, a);
+            return launch_status();
+        }
+    }
     hipLaunchKernelGGL((hc_down_partial_kernel<T>), dim3(S * ((a.N + kDnRows - 1) / kDnRows)), dim3(256 * dn_parts<T, false>()), 0, st, a);
     int rc = launch_status();
     if (rc != GQ8_OK) return rc;
@@ -603,10 +698,16 @@ constexpr int kGemvSlab = 256;
 
 static int gemv_slabs(int K) { return (K + kGemvSlab - 1) / kGemvSlab; }
 
+// GEMV workspace (T >= 5): partial sums [S][T][N], then one arrival counter per row group
+size_t gemv_counter_bytes(int T, int N, int K) {
+    if (T < kGemvMfmaT || N == 0 || K == 0) return 0;
+    return round_up(dn_groups(N) * sizeof(unsigned), kCounterAlign);
+}
+
 size_t gemv_workspace_bytes(int T, int N, int K) {
     if (T < kGemvMfmaT || N == 0 || K == 0) return 0;
     const size_t S = gemv_slabs(K);
-    return round_up(S * T * N * sizeof(float), kCounterAlign);
+    return round_up(S * T * N * sizeof(float), kCounterAlign) + gemv_counter_bytes(T, N, K);
 }
 
 template <int T>
@@ -615,6 +716,12 @@ static int launch_gemv_mfma_t(GemvArgs a, void* ws, hipStream_t st) {
     a.S = S;
     a.part = static_cast<float*>(ws);
     a.ssq = nullptr;
+    a.cnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) +
+                                        round_up((size_t)S * T * a.N * sizeof(float), kCounterAlign));
+    if (combine_last_arriver()) {
+        hipLaunchKernelGGL((hc_down_partial_kernel<T, true, false, kGemvSlab, true>), dim3(S * ((a.N + kDnRows - 1) / kDnRows)), dim3(256), 0, st, a);
+        return launch_status();
+    }
     hipLaunchKernelGGL((hc_down_partial_kernel<T, true, false, kGemvSlab>), dim3(S * ((a.N + kDnRows - 1) / kDnRows)), dim3(256 * dn_parts<T, false, kGemvSlab>()), 0, st, a);
     int rc = launch_status();
     if (rc != GQ8_OK) return rc;
@@ -1067,11 +1174,12 @@ static int launch_pair_t(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st) {
         const int rc = launch_down_t<T>(dn, ws, st);
         return rc != GQ8_OK ? rc : launch_up_t<T>(up, st);
     } else {
-        const int S = hc_down_slabs(dn.K);
-        char* w = static_cast<char*>(ws);
-        dn.S = S;
-        dn.part = reinterpret_cast<float*>(w);
-        dn.ssq = reinterpret_cast<float*>(w + round_up((size_t)S * T * dn.N * sizeof(float), kCounterAlign));
+        if (dn_last_arriver<T>()) {        // the down call (its own combine), then the up read
+            const int rc = launch_down_t<T>(dn, ws, st);
+            return rc != GQ8_OK ? rc : launch_up_t<T>(up, st);
+        }
+        dn_workspace(dn, T, ws);
+        const int S = dn.S;
         hipLaunchKernelGGL((hc_down_partial_kernel<T>), dim3(S * ((dn.N + kDnRows - 1) / kDnRows)), dim3(256 * dn_parts<T, false>()), 0, st, dn);
         int rc = launch_status();
         if (rc != GQ8_OK) return rc;
@@ -1096,11 +1204,8 @@ int launch_hc_pair(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st) {
 
 template <int T>
 static int launch_bf16_pair_t(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st) {
-    const int S = hc_down_slabs(dn.K);
-    char* w = static_cast<char*>(ws);
-    dn.S = S;
-    dn.part = reinterpret_cast<float*>(w);
-    dn.ssq = reinterpret_cast<float*>(w + round_up((size_t)S * T * dn.N * sizeof(float), kCounterAlign));
+    dn_workspace(dn, T, ws);
+    const int S = dn.S;
     hipLaunchKernelGGL((hc_down_partial_kernel<T, false, true>), dim3(S * ((dn.N + kDnRows - 1) / kDnRows)), dim3(256), 0, st, dn);
     int rc = launch_status();
     if (rc != GQ8_OK) return rc;

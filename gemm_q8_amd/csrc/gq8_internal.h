@@ -57,7 +57,12 @@ struct GemvArgs {
     float eps;
     void* lo_out;           // fused pair: bf16 [T][K] down output written by work-group 0
     int kd;                 // fused pair: depth of the down read (the RMS mean's divisor)
+    unsigned* cnt;          // last-arriver combine: one arrival counter per 64-row group
 };
+
+// Combine of split partial sums: a kernel of its own (default), or the last-arriving work-group
+// of each row group (GQ8_COMBINE=last, read on every call; other values: default, said once).
+bool combine_last_arriver();
 
 // Q8_0 GEMV (fp32 x): T < 5 one work-group per RW rows and all of K on the VALU, no workspace;
 // T >= 5 MFMA over 512-column slabs into S partial planes [S][T][N] (the workspace), then a
@@ -69,6 +74,8 @@ size_t gemv_workspace_bytes(int T, int N, int K);
 constexpr int kDownSlab = 512;                 // columns per slab (16 Q8_0 blocks)
 inline int hc_down_slabs(int K) { return (K + kDownSlab - 1) / kDownSlab; }
 size_t hc_down_workspace_bytes(int T, int N, int K);
+size_t hc_down_counter_bytes(int N);                 // counters at the workspace's end (down, pair)
+size_t gemv_counter_bytes(int T, int N, int K);      // the GEMV's (T >= 5), 0 otherwise
 int launch_hc_down(GemvArgs a, void* ws, hipStream_t st);
 
 // Q8_0 up read (bf16 x, K <= 1024): MFMA, one wave per 16 output rows, no workspace.

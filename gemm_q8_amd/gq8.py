@@ -58,7 +58,7 @@ _SIGS = {
     "gq8_q8_0_split_from_blocks_host": (_I, [_P, _I, _I, _P]),
     "gq8_q8_1_quantize_host": (_I, [_P, _I, _I, _P, _P, _P]),
     "gq8_w8a8_pack_host": (_I, [_P, _I, _I, _P]),
-    "gq8_workspace_check": (_I, [_P, _SZ, _P, _P]),
+    "gq8_workspace_check": (_I, [_I, _I, _I, _I, _P, _SZ, _P, _P]),
     "gq8_w8a8_gemm_bf16x": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_moe_route": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "gq8_moe_plan_words": (_SZ, [_I, _I]),
@@ -238,11 +238,13 @@ def gq8_w8a8_pack_host(W, K, N, W_packed):
     return _check("gq8_w8a8_pack_host", _lib.gq8_w8a8_pack_host(_host(W), K, N, _host(W_packed)))
 
 
-def gq8_workspace_check(ws, nbytes, stream=None):
-    """Number of non-zero arrival counters of a workspace (no entry point keeps any: 0)."""
+def gq8_workspace_check(op, rows, N, K, ws, nbytes, stream=None):
+    """Number of non-zero words in a workspace's arrival-counter region (synchronizes the stream
+    when the operation has counters)."""
     out = ctypes.c_int(-1)
     _check("gq8_workspace_check", _lib.gq8_workspace_check(
-        _dev(ws), nbytes, None if stream is None else _stream(stream), ctypes.addressof(out)))
+        op, rows, N, K, _dev(ws), nbytes, None if stream is None else _stream(stream),
+        ctypes.addressof(out)))
     return out.value
 
 

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define GQ8_ABI_VERSION 1
+#define GQ8_ABI_VERSION 2
 
 enum gq8_status {
     GQ8_OK = 0,
@@ -120,27 +120,36 @@ int gq8_w8a8_pack_host(const int8_t* W, int K, int N, int8_t* W_packed);
  * Workspace: device scratch that a compute call needs beyond its inputs and outputs.
  *   - size it with gq8_workspace_bytes() for the exact (op, rows, N, K) of the call; 0 means the
  *     call needs none (pass NULL, 0). The down read and the down/up pair use one (fp32 partial
- *     sums of the K slabs [S][T][N], then the slabs' sums of squares [S][T]), and so does the
- *     GEMV at T >= 5 (the partial sums only) (HC-Q8 page, "What changed": one scratch per queue,
- *     allocated outside any capture);
- *   - every call rewrites every workspace value it later reads, so a workspace needs no clearing
- *     and can be reused by any later call on the same stream (W8A8 page, "Split-K requirements":
- *     planes fully rewritten, no memset in the timed region); calls that may run concurrently
- *     (different streams, or a graph replayed concurrently with itself) need separate workspaces;
- *   - gq8_workspace_counter_bytes() is 0 for every operation (no call keeps arrival counters: the
- *     partial sums are combined by a kernel of their own, or inside the up read's kernel);
- *     gq8_workspace_init() zero-fills a workspace (harmless, never required).
+ *     sums of the K slabs [S][T][N], the slabs' sums of squares per 64-row group [G][S][T], then
+ *     one 32-bit arrival counter per 64-row group), and so does the GEMV at T >= 5 (the partial
+ *     sums and the counters) (HC-Q8 page, "What changed": one scratch per queue, allocated and
+ *     zeroed outside any capture);
+ *   - the partial sums are combined in a fixed order either by a kernel of their own (the
+ *     default) or by the last-arriving work-group of each row group (environment variable
+ *     GQ8_COMBINE=last, read on every call; "kernel" or unset: the default; other values: the
+ *     default, said once on stderr). The results are bitwise the same. The last-arriver combine
+ *     (HC-Q8 page, "What changed"; W8A8 page, "Split-K requirements") counts arrivals in the
+ *     counters, which must be zero before a call and which every call leaves at zero: zero a new
+ *     workspace once with gq8_workspace_init(); the partial sums themselves are always rewritten
+ *     before they are read (W8A8 page, "Split-K requirements": planes fully rewritten, no memset
+ *     in the timed region);
+ *   - calls that may run concurrently (different streams, or a graph replayed concurrently with
+ *     itself) need separate workspaces;
+ *   - gq8_workspace_counter_bytes() is the size of the counter region at the end of the
+ *     workspace (0 when the operation has none).
  * rows = T for the Q8_0 calls, M for W8A8.
  * ------------------------------------------------------------------------------------------ */
 size_t gq8_workspace_bytes(int op, int rows, int N, int K);
 size_t gq8_workspace_counter_bytes(int op, int rows, int N, int K);
 int gq8_workspace_init(void* ws, size_t bytes, void* stream);
-/* Debug check of a workspace's arrival counters: *nonzero_counters = how many are not zero. No
- * entry point keeps arrival counters (split sums are combined by a second kernel or inside the
- * consuming kernel, in a fixed order), so the count is 0 and nothing is read; it is kept for
- * callers written against a counter-based workspace contract. Errors: GQ8_EINVAL (null
- * nonzero_counters, or null ws with bytes > 0). */
-int gq8_workspace_check(const void* ws, size_t bytes, void* stream, int* nonzero_counters);
+/* Debug check of a workspace's arrival counters: *nonzero_counters = the number of non-zero 32-bit
+ * words in the counter region of a workspace sized for (op, rows, N, K) (0 after any complete
+ * call; non-zero means a call was interrupted or the workspace was not zeroed). Copies the region
+ * to the host and synchronizes the stream; 0 without a read when the operation has no counters.
+ * Errors: GQ8_EINVAL (null nonzero_counters), GQ8_EWORKSPACE (ws null or smaller than
+ * gq8_workspace_bytes), GQ8_ECAPTURE (capturing stream), GQ8_EHIP. */
+int gq8_workspace_check(int op, int rows, int N, int K, const void* ws, size_t bytes, void* stream,
+                        int* nonzero_counters);
 
 /* Q8_0 matrix-vector product for T = 1..16 token rows (HC-Q8 page, "What changed": w = d*q,
  * exact in fp32):
@@ -149,8 +158,9 @@ int gq8_workspace_check(const void* ws, size_t bytes, void* stream, int* nonzero
  * K % 32 == 0. Accumulation is fp32 in a fixed order: the result is deterministic for a given
  * device and shape (replays are bitwise identical). T == 0 or N == 0: nothing to do.
  * K == 0: y is zero-filled. T <= 4: VALU dots, one kernel, no workspace. T >= 5: bf16 MFMA on
- * x split into bf16 hi + lo (|x - hi - lo| <= 2^-17 |x|) over 512-column slabs, then a combine
- * of the slab sums in a fixed order; workspace gq8_workspace_bytes(GQ8_OP_Q8_0_GEMV, T, N, K). */
+ * x split into bf16 hi + lo (|x - hi - lo| <= 2^-17 |x|) over 256-column slabs, then a combine
+ * of the slab sums in a fixed order (a kernel, or the last-arriving work-group: see Workspace);
+ * workspace gq8_workspace_bytes(GQ8_OP_Q8_0_GEMV, T, N, K), its counters zeroed once. */
 int gq8_q8_0_gemv(const void* w_split, const float* x, float* y, int T, int N, int K,
                   void* ws, size_t ws_bytes, void* stream);
 
@@ -161,8 +171,10 @@ int gq8_q8_0_gemv(const void* w_split, const float* x, float* y, int T, int N, i
  *   lo[t][n] = bf16( rs[t] * sum_k d[n][k/32] * q[n][k] * (R[t][k] * w_norm[k]) )
  * w_split: Q8_0 [N][K]; R bf16 [T][K]; w_norm bf16 [K]; lo bf16 [T][N]; rs_out fp32 [T]
  * (nullable). T = 1..16, K % 32 == 0, K > 0. Workspace: gq8_workspace_bytes(GQ8_OP_HC_DOWN, T,
- * N, K). Two kernels: per 512-column slab partial sums (bf16 MFMA on exact hi/lo operands), then
- * the combine (slab groups in ascending order) with rs and the bf16 rounding. */
+ * N, K), its counters zeroed once. Two kernels: per 512-column slab partial sums (bf16 MFMA on
+ * exact hi/lo operands), then the combine (slab groups in ascending order) with rs and the bf16
+ * rounding; with GQ8_COMBINE=last and T <= 8 one kernel, whose last-arriving work-group per row
+ * group combines in the same order. */
 int gq8_hc_q8_down(const void* w_split, const uint16_t* R, const uint16_t* w_norm, float eps,
                    uint16_t* lo, float* rs_out, int T, int N, int K,
                    void* ws, size_t ws_bytes, void* stream);

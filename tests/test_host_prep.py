@@ -94,15 +94,19 @@ def test_host_prep_argument_checks(lib):
     assert raw.gq8_q8_1_quantize_host(dummy, 2, 64, dummy, None, None) == lib.EINVAL
 
 
-def test_workspace_check_reports_no_counters(lib):
-    assert lib.gq8_workspace_check(None, 0) == 0
+def test_workspace_check_without_counters(lib):
+    # operations without arrival counters: nothing to read, 0
+    assert lib.gq8_workspace_check(lib.OP_W8A8, 16, 1536, 4096, None, 0) == 0
+    assert lib.gq8_workspace_check(lib.OP_HC_UP, 4, 16384, 320, None, 0) == 0
     buf = np.zeros(256, np.uint8)
-    # the check reads no memory (no entry point keeps counters): any address will do
-    assert lib.gq8_workspace_check(buf.ctypes.data, buf.nbytes) == 0
     # the binding refuses host arrays and CPU tensors where device memory is required, and GPU
     # memory where host memory is required, before calling the library
     with pytest.raises(ValueError):
-        lib.gq8_workspace_check(buf, buf.nbytes)
+        lib.gq8_workspace_check(lib.OP_HC_DOWN, 1, 320, 16384, buf, buf.nbytes)
+    # a workspace smaller than the operation's: refused before any read
+    raw = lib.raw()
+    st = raw.gq8_workspace_check(lib.OP_HC_DOWN, 1, 320, 16384, 1 << 20, 16, None, buf.ctypes.data)
+    assert st == lib.EWORKSPACE
     import torch
     with pytest.raises(ValueError):
         lib.gq8_q8_0_gemv(torch.zeros(64, dtype=torch.uint8), None, None, 1, 1, 32, None, 0, 0)
@@ -110,7 +114,7 @@ def test_workspace_check_reports_no_counters(lib):
         lib.gq8_q8_1_quantize_host(np.zeros((4, 64), np.uint16)[:, :32], 4, 32,
                                    np.zeros(128, np.int8), np.zeros(4, np.uint16))
     raw = lib.raw()
-    assert raw.gq8_workspace_check(None, 64, None, None) == lib.EINVAL
+    assert raw.gq8_workspace_check(lib.OP_HC_DOWN, 1, 320, 16384, None, 64, None, None) == lib.EINVAL
 
 
 @pytest.mark.parametrize("K,N", [(4096, 48), (80, 17), (16, 1)])
