@@ -320,6 +320,63 @@ GQ8_EXPORT int gq8_hc_q8_pair(const void* w_down, const uint16_t* R, const uint1
     return launch_hc_pair(dn, up, ws, S(stream));
 }
 
+// ---------------------------------------------------------------------------------- pending write
+
+GQ8_EXPORT int gq8_hc_q8_down_pending(const void* w_split, const uint16_t* R, const uint16_t* P,
+                                      const uint16_t* w_norm, float eps, uint16_t* R_out,
+                                      uint16_t* lo, float* rs_out, int T, int N, int K, void* ws,
+                                      size_t ws_bytes, void* stream) {
+    if (T < 0 || N < 0 || K < 0) return GQ8_EINVAL;
+    if (!q8_shape_ok(T, N, K) || K == 0) return GQ8_ESHAPE;
+    if (T == 0 || N == 0) return GQ8_OK;
+    if (w_split == nullptr || R == nullptr || P == nullptr || w_norm == nullptr || R_out == nullptr ||
+        lo == nullptr)
+        return GQ8_EINVAL;
+    if (!aligned16(R) || !aligned16(P) || !aligned16(R_out) || !aligned16(w_norm) || !aligned16(w_split))
+        return GQ8_EALIGN;
+    if (!(eps >= 0.f)) return GQ8_EINVAL;
+    int rc = check_ws(ws, ws_bytes, hc_down_workspace_bytes(T, N, K));
+    if (rc != GQ8_OK) return rc;
+    if (device_cus() == 0) return GQ8_ENODEV;
+    GemvArgs a{};
+    a.q = static_cast<const int8_t*>(w_split);
+    a.d = reinterpret_cast<const uint16_t*>(a.q + (size_t)N * K);
+    a.x = R; a.wnorm = w_norm; a.T = T; a.N = N; a.K = K; a.out = lo; a.rs_out = rs_out; a.eps = eps;
+    a.pw = P; a.r_out = R_out;
+    return launch_hc_down_pending(a, ws, S(stream));
+}
+
+GQ8_EXPORT int gq8_hc_q8_pair_pending(const void* w_down, const uint16_t* R, const uint16_t* P,
+                                      const uint16_t* w_norm, float eps, const void* w_up,
+                                      uint16_t* R_out, uint16_t* lo, float* rs_out, uint16_t* out,
+                                      int T, int Nlr, int Khc, void* ws, size_t ws_bytes,
+                                      void* stream) {
+    if (T < 0 || Nlr < 0 || Khc < 0) return GQ8_EINVAL;
+    if (!q8_shape_ok(T, Nlr, Khc) || Nlr % 32 != 0 || Nlr > 1024 || Khc == 0 || Nlr == 0)
+        return GQ8_ESHAPE;
+    if (T == 0) return GQ8_OK;
+    if (w_down == nullptr || R == nullptr || P == nullptr || w_norm == nullptr || w_up == nullptr ||
+        R_out == nullptr || lo == nullptr || out == nullptr)
+        return GQ8_EINVAL;
+    if (!aligned16(w_down) || !aligned16(R) || !aligned16(P) || !aligned16(R_out) ||
+        !aligned16(w_norm) || !aligned16(w_up) || !aligned16(lo))
+        return GQ8_EALIGN;
+    if (!(eps >= 0.f)) return GQ8_EINVAL;
+    int rc = check_ws(ws, ws_bytes, hc_down_workspace_bytes(T, Nlr, Khc));
+    if (rc != GQ8_OK) return rc;
+    if (device_cus() == 0) return GQ8_ENODEV;
+    GemvArgs dn{};
+    dn.q = static_cast<const int8_t*>(w_down);
+    dn.d = reinterpret_cast<const uint16_t*>(dn.q + (size_t)Nlr * Khc);
+    dn.x = R; dn.wnorm = w_norm; dn.T = T; dn.N = Nlr; dn.K = Khc; dn.out = lo;
+    dn.rs_out = rs_out; dn.eps = eps; dn.pw = P; dn.r_out = R_out;
+    GemvArgs up{};
+    up.q = static_cast<const int8_t*>(w_up);
+    up.d = reinterpret_cast<const uint16_t*>(up.q + (size_t)Khc * Nlr);
+    up.x = lo; up.T = T; up.N = Khc; up.K = Nlr; up.out = out;
+    return launch_hc_pair_pending(dn, up, ws, S(stream));
+}
+
 // ---------------------------------------------------------------------------------- no allocation
 // The pair's workspace in a file-scope device array, for callers that cannot allocate (code
 // under graph capture, allocation-free serving loops). Each device the library runs on holds

@@ -282,8 +282,13 @@ constexpr int dn_parts() { return (WB || T <= 8 || SLAB < kDownSlab) ? 1 : 2; }
 // the last: it adds the row group's S partial planes and applies rs exactly as
 // hc_down_combine_kernel does (same order: bitwise the same outputs) and resets the counter.
 // No work-group waits for another, so nothing assumes that they are resident together.
-template <int T, bool XF = false, bool WB = false, int SLAB = kDownSlab, bool LA = false>
+//
+// PW (the pending write, HC-Q8 page "Summary"): the staging reads P beside R and takes
+// R' = bf16(R + P) in place of R (the fp32 sum of two bf16 values, rounded to nearest even);
+// the work-groups of row group 0 also write R' to R_out for their slab.
+template <int T, bool XF = false, bool WB = false, int SLAB = kDownSlab, bool LA = false, bool PW = false>
 __global__ void __launch_bounds__((256 * dn_parts<T, WB, SLAB>())) hc_down_partial_kernel(GemvArgs a) {
+    static_assert(!PW || !XF, "the pending write belongs to the down read");
     static_assert(!LA || dn_parts<T, WB, SLAB>() == 1, "the last-arriver combine takes one column part");
     static_assert(!WB || SLAB == kDownSlab, "the BF16 read uses 512-column slabs");
     constexpr int NB = SLAB / 32;                                  // Q8_0 blocks per slab
@@ -324,7 +329,7 @@ __global__ void __launch_bounds__((256 * dn_parts<T, WB, SLAB>())) hc_down_parti
     // 0. activations: item it = NTH j + thread covers token t = it % TR (the same t for every
     //    j), columns 32b + 8g .. +8 with b = it / (4 TR), g = (it / TR) % 4
     const int t = (int)threadIdx.x % TR;
-    uint4 rv[NI], nv[NI];
+    uint4 rv[NI], nv[NI], pv[PW ? NI : 1];
     bool okv[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -340,6 +345,7 @@ __global__ void __launch_bounds__((256 * dn_parts<T, WB, SLAB>())) hc_down_parti
         } else {
             rv[i] = *reinterpret_cast<const uint4*>(R + (size_t)tc * K + kc);
             nv[i] = *reinterpret_cast<const uint4*>(a.wnorm + kc);
+            if constexpr (PW) pv[PW ? i : 0] = *reinterpret_cast<const uint4*>(a.pw + (size_t)tc * K + kc);
         }
     }
     // block scales in the MFMA result layout: lane l needs the scales of row r0 + l%16 for the
@@ -401,7 +407,21 @@ __global__ void __launch_bounds__((256 * dn_parts<T, WB, SLAB>())) hc_down_parti
         const int it = NTH * i + (int)threadIdx.x;
         const int b = it / (4 * TR), g = (it / TR) & 3;
         const bool ok = okv[i];
-        const uint32_t rw[4] = {rv[i].x, rv[i].y, rv[i].z, rv[i].w};
+        uint32_t rw[4] = {rv[i].x, rv[i].y, rv[i].z, rv[i].w};
+        if constexpr (PW) {
+            // R' = bf16(R + P) (the fp32 sum, rounded to nearest even), written out by row group 0
+            const uint32_t pw4[4] = {pv[PW ? i : 0].x, pv[PW ? i : 0].y, pv[PW ? i : 0].z, pv[PW ? i : 0].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float s0 = __uint_as_float(rw[e] << 16) + __uint_as_float(pw4[e] << 16);
+                const float s1 = __uint_as_float(rw[e] & 0xffff0000u) + __uint_as_float(pw4[e] & 0xffff0000u);
+                rw[e] = (uint32_t)f2bf_bits(s0) | ((uint32_t)f2bf_bits(s1) << 16);
+            }
+            if (y == 0 && ok) {
+                const int k = k0 + 32 * b + 8 * g;
+                *reinterpret_cast<uint4*>(a.r_out + (size_t)t * K + k) = make_uint4(rw[0], rw[1], rw[2], rw[3]);
+            }
+        }
         const uint32_t ww[4] = {nv[i].x, nv[i].y, nv[i].z, nv[i].w};
         uint32_t hi[4], lo[4];
         float r2 = 0.f;
@@ -691,6 +711,19 @@ static int launch_down_t(GemvArgs a, void* ws, hipStream_t st) {
 }
 
 int launch_hc_down(GemvArgs a, void* ws, hipStream_t st) { GQ8_T_SWITCH(launch_down_t, a, ws, st) }
+
+// the down read with the pending write: the slab kernel with PW, then the combine kernel
+template <int T>
+static int launch_down_pending_t(GemvArgs a, void* ws, hipStream_t st) {
+    dn_workspace(a, T, ws);
+    hipLaunchKernelGGL((hc_down_partial_kernel<T, false, false, kDownSlab, false, true>), dim3(a.S * ((a.N + kDnRows - 1) / kDnRows)), dim3(256 * dn_parts<T, false>()), 0, st, a);
+    const int rc = launch_status();
+    if (rc != GQ8_OK) return rc;
+    hipLaunchKernelGGL(hc_down_combine_kernel<false>, dim3((a.N + 63) / 64, T), dim3(256), 0, st, a);
+    return launch_status();
+}
+
+int launch_hc_down_pending(GemvArgs a, void* ws, hipStream_t st) { GQ8_T_SWITCH(launch_down_pending_t, a, ws, st) }
 
 // The GEMV's slabs are 256 columns wide (the down read's are 512): twice the work-groups on the
 // weight stream (the 1024 x 4096 read has 16 row groups), for twice the partial planes.
@@ -1189,6 +1222,35 @@ static int launch_pair_t(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st) {
         hipLaunchKernelGGL((hc_pair_up_kernel<T>), dim3((ntile + 3) / 4), dim3(512), 0, st, up);
         return launch_status();
     }
+}
+
+// the pair with the pending write: as launch_pair_t, the down read's slab kernel with PW
+template <int T>
+static int launch_pair_pending_t(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st) {
+    if constexpr (T > kPairMaxT) {
+        const int rc = launch_down_pending_t<T>(dn, ws, st);
+        return rc != GQ8_OK ? rc : launch_up_t<T>(up, st);
+    } else {
+        if (up.K != kUpCW || force_general()) {
+            const int rc = launch_down_pending_t<T>(dn, ws, st);
+            return rc != GQ8_OK ? rc : launch_up_t<T>(up, st);
+        }
+        dn_workspace(dn, T, ws);
+        const int S = dn.S;
+        hipLaunchKernelGGL((hc_down_partial_kernel<T, false, false, kDownSlab, false, true>), dim3(S * ((dn.N + kDnRows - 1) / kDnRows)), dim3(256 * dn_parts<T, false>()), 0, st, dn);
+        int rc = launch_status();
+        if (rc != GQ8_OK) return rc;
+        up.S = S; up.part = dn.part; up.ssq = dn.ssq; up.eps = dn.eps; up.kd = dn.K;
+        up.rs_out = dn.rs_out; up.lo_out = dn.out;
+        const int ntile = (up.N + 15) / 16;
+        hipLaunchKernelGGL((hc_pair_up_kernel<T>), dim3((ntile + 3) / 4), dim3(512), 0, st, up);
+        return launch_status();
+    }
+}
+
+int launch_hc_pair_pending(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st) {
+    GemvArgs& a = dn;
+    GQ8_T_SWITCH(launch_pair_pending_t, dn, up, ws, st)
 }
 
 int launch_hc_pair(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st) {

@@ -58,6 +58,8 @@ struct GemvArgs {
     void* lo_out;           // fused pair: bf16 [T][K] down output written by work-group 0
     int kd;                 // fused pair: depth of the down read (the RMS mean's divisor)
     unsigned* cnt;          // last-arriver combine: one arrival counter per 64-row group
+    const uint16_t* pw;     // down read with the pending write: bf16 P [T][K] ...
+    uint16_t* r_out;        //   ... and R_out = bf16(R + P) [T][K], the stream the read takes
 };
 
 // Combine of split partial sums: a kernel of its own (default), or the last-arriving work-group
@@ -77,6 +79,9 @@ size_t hc_down_workspace_bytes(int T, int N, int K);
 size_t hc_down_counter_bytes(int N);                 // counters at the workspace's end (down, pair)
 size_t gemv_counter_bytes(int T, int N, int K);      // the GEMV's (T >= 5), 0 otherwise
 int launch_hc_down(GemvArgs a, void* ws, hipStream_t st);
+// the down read (a.pw, a.r_out set) and the pair with the pending write folded into the staging
+int launch_hc_down_pending(GemvArgs a, void* ws, hipStream_t st);
+int launch_hc_pair_pending(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st);
 
 // Q8_0 up read (bf16 x, K <= 1024): MFMA, one wave per 16 output rows, no workspace.
 int launch_hc_up(GemvArgs a, hipStream_t st);

@@ -47,6 +47,8 @@ _SIGS = {
     "gq8_hc_q8_down": (_I, [_P, _P, _P, _F, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_hc_q8_up": (_I, [_P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_hc_q8_pair": (_I, [_P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "gq8_hc_q8_down_pending": (_I, [_P, _P, _P, _P, _F, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "gq8_hc_q8_pair_pending": (_I, [_P, _P, _P, _P, _F, _P, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_hc_q8_pair_noalloc": (_I, [_P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _P]),
     "gq8_hc_bf16_pair": (_I, [_P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_w8a8_packed_bytes": (_SZ, [_I, _I]),
@@ -310,6 +312,20 @@ def gq8_read_probe_ex(src, nbytes, sink, loads_per_lane, threads, work_groups, n
     return _check("gq8_read_probe_ex", _lib.gq8_read_probe_ex(
         _dev(src), nbytes, _dev(sink), loads_per_lane, threads, work_groups, nontemporal,
         _stream(stream)))
+
+
+def gq8_hc_q8_down_pending(w_split, R, P, w_norm, eps, R_out, lo, rs_out, T, N, K, ws, ws_bytes,
+                           stream=None):
+    return _check("gq8_hc_q8_down_pending", _lib.gq8_hc_q8_down_pending(
+        _dev(w_split), _dev(R), _dev(P), _dev(w_norm), eps, _dev(R_out), _dev(lo), _dev(rs_out),
+        T, N, K, _dev(ws), ws_bytes, _stream(stream)))
+
+
+def gq8_hc_q8_pair_pending(w_down, R, P, w_norm, eps, w_up, R_out, lo, rs_out, out, T, Nlr, Khc, ws,
+                           ws_bytes, stream=None):
+    return _check("gq8_hc_q8_pair_pending", _lib.gq8_hc_q8_pair_pending(
+        _dev(w_down), _dev(R), _dev(P), _dev(w_norm), eps, _dev(w_up), _dev(R_out), _dev(lo),
+        _dev(rs_out), _dev(out), T, Nlr, Khc, _dev(ws), ws_bytes, _stream(stream)))
 
 
 def gq8_hc_q8_pair_noalloc(w_down, R, w_norm, eps, w_up, lo, rs_out, out, T, Nlr, Khc, stream=None):

@@ -200,6 +200,25 @@ int gq8_hc_q8_pair(const void* w_down, const uint16_t* R, const uint16_t* w_norm
                    const void* w_up, uint16_t* lo, float* rs_out, uint16_t* out,
                    int T, int Nlr, int Khc, void* ws, size_t ws_bytes, void* stream);
 
+/* The down read and the pair with the pending write folded in (HC-Q8 page, "Summary": R_out, the
+ * pending write between the two reads, bitwise the default read's; the page does not define it
+ * further, and this is a reading of it): a pending residual update P is added to the stream
+ * before the down read,
+ *   R_out[t][k] = bf16( R[t][k] + P[t][k] )    (fp32 sum of the two bf16 values, round to nearest even)
+ * and the RMSNorm and the down read take R_out in place of R; lo, rs_out and out are then what
+ * gq8_hc_q8_down / gq8_hc_q8_pair give on R_out (bitwise). P and R_out bf16 [T][K] (K = Khc),
+ * 16-byte aligned; R_out may not overlap R or P. The up read's own epilogue on the page (gate,
+ * stream mean) is not defined there and not part of these calls. Shapes, workspace and errors as
+ * the calls without the pending write; the partial sums are combined by the combine kernel. */
+int gq8_hc_q8_down_pending(const void* w_split, const uint16_t* R, const uint16_t* P,
+                           const uint16_t* w_norm, float eps, uint16_t* R_out, uint16_t* lo,
+                           float* rs_out, int T, int N, int K, void* ws, size_t ws_bytes,
+                           void* stream);
+int gq8_hc_q8_pair_pending(const void* w_down, const uint16_t* R, const uint16_t* P,
+                           const uint16_t* w_norm, float eps, const void* w_up, uint16_t* R_out,
+                           uint16_t* lo, float* rs_out, uint16_t* out, int T, int Nlr, int Khc,
+                           void* ws, size_t ws_bytes, void* stream);
+
 /* gq8_hc_q8_pair without a workspace argument, for callers that cannot allocate memory (code
  * under hipGraph capture that may not call hipMalloc, allocation-free serving loops, harnesses
  * that forbid allocation): the workspace is a fixed device array inside the library, of

@@ -9,7 +9,7 @@ up projection (its rows are K = 320 long) by the down read's output.
 Readings taken where the page is not explicit:
   * rs is one value per token row over the whole row: rs = 1/sqrt(mean(R^2) + eps),
     eps = 1e-6, with the mean over the K columns of R (not of R * w_norm);
-  * R' is R itself (no pending write is modelled);
+  * R' is R itself, or R + P rounded to bf16 when a pending write P is given (pending_write);
   * the down output lo is rs * dot, stored as bf16; rs is also returned;
   * the up read's own epilogue (pending write, gate, stream mean) is not
     defined on the page and is left out: the up output is the plain product,
@@ -20,7 +20,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .numerics import bf16_to_f32
+from .numerics import bf16_bits, bf16_to_f32
 from .q8 import dequantize, q8_0_gemv
 
 
@@ -36,6 +36,18 @@ def _down(R_bits, wnorm_bits, W, eps):
     lo = rs[:, None] * dot
     S = rs[:, None] * (np.abs(u) @ np.abs(W).T)
     return lo, rs, S
+
+
+def pending_write(R_bits, P_bits):
+    """The pending write (HC-Q8 page, "Summary": R_out, the pending write, is bitwise the default
+    read's, written between the two reads; the page does not define it further). Reading: a
+    pending residual update P is added to the stream before the down read, R' = R + P rounded to
+    bf16 (to nearest, ties to even), and R' is both R_out and the down read's input. Two bf16
+    values are added exactly in float64 here; rounding their sum to fp32 first gives the same
+    bf16 (their fp32 sum is inexact only when the exponents differ by 16 or more, and then the
+    smaller is below half a bf16 spacing of the larger). Returns bf16 bits [T, K]."""
+    s = bf16_to_f32(R_bits).astype(np.float64) + bf16_to_f32(P_bits).astype(np.float64)
+    return bf16_bits(s.astype(np.float32))
 
 
 def hc_down(R_bits, wnorm_bits, blocks, eps=1e-6):

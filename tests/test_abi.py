@@ -119,6 +119,23 @@ def test_argument_checks_return_before_device_work(lib):
                                    4, 8, 512, 2048, 2048, None, 0, None) == lib.ESHAPE
 
 
+def test_pending_write_argument_checks(lib):
+    raw = lib.raw()
+    dummy = 1 << 20  # never dereferenced
+    # R_out and P are required
+    assert raw.gq8_hc_q8_down_pending(dummy, dummy, None, dummy, 1e-6, dummy, dummy, None, 1, 320,
+                                      16384, dummy, 1 << 30, None) == lib.EINVAL
+    assert raw.gq8_hc_q8_pair_pending(dummy, dummy, dummy, dummy, 1e-6, dummy, None, dummy, None,
+                                      dummy, 1, 320, 16384, dummy, 1 << 30, None) == lib.EINVAL
+    # misaligned R_out, shapes as the calls without the pending write
+    assert raw.gq8_hc_q8_down_pending(dummy, dummy, dummy, dummy, 1e-6, dummy + 2, dummy, None, 1,
+                                      320, 16384, dummy, 1 << 30, None) == lib.EALIGN
+    assert raw.gq8_hc_q8_pair_pending(dummy, dummy, dummy, dummy, 1e-6, dummy, dummy, dummy, None,
+                                      dummy, 1, 330, 16384, dummy, 1 << 30, None) == lib.ESHAPE
+    assert raw.gq8_hc_q8_down_pending(dummy, dummy, dummy, dummy, 1e-6, dummy, dummy, None, 17,
+                                      320, 16384, dummy, 1 << 30, None) == lib.ESHAPE
+
+
 def test_moe_bf16_input_argument_checks(lib):
     raw = lib.raw()
     dummy = 1 << 20  # never dereferenced

@@ -157,3 +157,56 @@ def test_bf16_up_one_hot_picks_a_weight_column():
         o, S = hc_up_bf16(e, W)
         assert np.array_equal(o[0], bf16_to_f32(W[:, k]).astype(np.float64))
         assert np.array_equal(S[0], np.abs(o[0]))
+
+
+def test_pending_write_closed_forms_and_ties():
+    """R' = R + P rounded once to bf16: P = 0 gives R; R = -P gives 0; sums of small integers are
+    exact; 1 + 2^-8 is a tie between 1 and 1 + 2^-7 (even: 1); 1 + 3 * 2^-8 is a tie between
+    1 + 2^-7 and 1 + 2^-6 (even: 1 + 2^-6); -0 + -0 is -0 and -0 + 0 is +0."""
+    from oracle.hc import pending_write
+    from oracle.numerics import bf16_bits
+    f = lambda v: bf16_bits(np.array(v, np.float32))                         # noqa: E731
+    R = f([[1.5, -3.0, 7.0, 1.0, 1.0, -0.0, -0.0, 100.0]])
+    P = f([[0.0, 3.0, 5.0, 2.0 ** -8, 3 * 2.0 ** -8, -0.0, 0.0, -36.0]])
+    want = f([[1.5, 0.0, 12.0, 1.0, 1.0 + 2.0 ** -6, -0.0, 0.0, 64.0]])
+    assert pending_write(R, P).tolist() == want.tolist()
+
+
+def test_pending_write_is_the_once_rounded_exact_sum():
+    """Against exact rational sums rounded to nearest-even bf16 by hand (8-bit significands), over
+    random bf16 pairs whose exponents differ by up to 30 (so the fp32 sum is sometimes inexact)."""
+    from fractions import Fraction
+    from oracle.hc import pending_write
+    g = np.random.default_rng(5)
+    n = 4000
+    e1 = g.integers(-20, 20, n)
+    e2 = e1 - g.integers(-30, 30, n)
+    m1 = g.integers(128, 256, n) * g.choice([-1, 1], n)
+    m2 = g.integers(128, 256, n) * g.choice([-1, 1], n)
+    r = (m1 * np.ldexp(1.0, e1 - 7)).astype(np.float32)
+    p = (m2 * np.ldexp(1.0, e2 - 7)).astype(np.float32)
+    Rb = (r.view(np.uint32) >> 16).astype(np.uint16)
+    Pb = (p.view(np.uint32) >> 16).astype(np.uint16)
+    got = bf16_to_f32(pending_write(Rb[None], Pb[None])[0]).astype(np.float64)
+
+    def rne_bf16(x):
+        if x == 0:
+            return Fraction(0)
+        sgn = -1 if x < 0 else 1
+        a = abs(x)
+        e = 0
+        while a >= 2:
+            a /= 2
+            e += 1
+        while a < 1:
+            a *= 2
+            e -= 1
+        m = a * 128                                   # 7 fraction bits
+        lo = m.numerator // m.denominator
+        rem = m - lo
+        if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+            lo += 1
+        return sgn * Fraction(lo, 128) * Fraction(2) ** e
+    for i in range(n):
+        exact = Fraction(float(r[i])) + Fraction(float(p[i]))
+        assert Fraction(float(got[i])) == rne_bf16(exact), i
