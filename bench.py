@@ -870,6 +870,14 @@ def main():
             "traffic": recorded_traffic(),
             "traffic_unit": "bytes per pair call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
             "avg_call_us": round(avg_us, 3),
+            # the same fraction per T, and for the standalone down and up calls (their own kernels:
+            # partial sums + combine kernel, and the up read alone), each over its own bytes
+            "frac_per_T": {f"T{T}": round(hc_kernel_bytes("pair", T) / (per_call[f"T{T}"] * 1e3)
+                                          / HBM_PEAK_GBS, 4) for T in TS},
+            "separate_calls": {k: {"avg_us": round(v["t"] / v["launches"] * 1e6, 3),
+                                   "achieved": round(v["bytes"] / v["t"] / 1e9, 2),
+                                   "frac": round(v["bytes"] / v["t"] / 1e9 / HBM_PEAK_GBS, 4)}
+                               for k, v in kern.items() if k != dom},
         },
     }
     if not args.no_configs:

@@ -212,7 +212,7 @@ GQ8_EXPORT int gq8_workspace_check(int op, int rows, int N, int K, const void* w
     if (cs != hipStreamCaptureStatusNone) return GQ8_ECAPTURE;
     unsigned host[1024];
     const size_t words = cb / sizeof(unsigned);
-    const char* src = static_cast<const char*>(ws) + (need - cb);
+    const char* src = static_cast<const char*>(ws);         // the counters open the workspace
     int nz = 0;
     for (size_t w0 = 0; w0 < words; w0 += 1024) {
         const size_t nw = words - w0 < 1024 ? words - w0 : 1024;

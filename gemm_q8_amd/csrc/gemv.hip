@@ -665,28 +665,29 @@ __global__ void __launch_bounds__(256) hc_down_combine_kernel(GemvArgs a) {
     }
 }
 
-// Down-read workspace: partial sums [S][T][N], then the sums of squares [G][S][T] (G = 64-row
-// groups; the kernel combine reads row group 0's copy, the last-arriver combine each group's
-// own), then one arrival counter per row group (zero between calls).
+// Down-read workspace: one arrival counter per 64-row group first (zero between calls; 256
+// bytes for every N <= 4096, so calls of different shapes find their counters at the same
+// zeroed bytes), then the partial sums [S][T][N], then the sums of squares [G][S][T] (G = row
+// groups; the kernel combine reads row group 0's copy, the last-arriver combine each group's own).
 static size_t dn_groups(int N) { return (size_t)(N + kDnRows - 1) / kDnRows; }
 
 size_t hc_down_counter_bytes(int N) { return round_up(dn_groups(N) * sizeof(unsigned), kCounterAlign); }
 
 size_t hc_down_workspace_bytes(int T, int N, int K) {
     const size_t S = hc_down_slabs(K);
-    return round_up(S * T * N * sizeof(float), kCounterAlign) +
-           round_up(dn_groups(N) * S * T * sizeof(float), kCounterAlign) + hc_down_counter_bytes(N);
+    return hc_down_counter_bytes(N) + round_up(S * T * N * sizeof(float), kCounterAlign) +
+           round_up(dn_groups(N) * S * T * sizeof(float), kCounterAlign);
 }
 
 static void dn_workspace(GemvArgs& a, int T, void* ws) {
     const int S = hc_down_slabs(a.K);
     char* w = static_cast<char*>(ws);
+    const size_t cb = hc_down_counter_bytes(a.N);
     const size_t pb = round_up((size_t)S * T * a.N * sizeof(float), kCounterAlign);
-    const size_t sb = round_up(dn_groups(a.N) * S * T * sizeof(float), kCounterAlign);
     a.S = S;
-    a.part = reinterpret_cast<float*>(w);
-    a.ssq = reinterpret_cast<float*>(w + pb);
-    a.cnt = reinterpret_cast<unsigned*>(w + pb + sb);
+    a.cnt = reinterpret_cast<unsigned*>(w);
+    a.part = reinterpret_cast<float*>(w + cb);
+    a.ssq = reinterpret_cast<float*>(w + cb + pb);
 }
 
 // the last-arriver combine where the slab kernel has one column part (T <= 8 for 512 columns)
@@ -731,7 +732,8 @@ constexpr int kGemvSlab = 256;
 
 static int gemv_slabs(int K) { return (K + kGemvSlab - 1) / kGemvSlab; }
 
-// GEMV workspace (T >= 5): partial sums [S][T][N], then one arrival counter per row group
+// GEMV workspace (T >= 5): one arrival counter per row group first (as the down read's), then
+// the partial sums [S][T][N]
 size_t gemv_counter_bytes(int T, int N, int K) {
     if (T < kGemvMfmaT || N == 0 || K == 0) return 0;
     return round_up(dn_groups(N) * sizeof(unsigned), kCounterAlign);
@@ -740,17 +742,16 @@ size_t gemv_counter_bytes(int T, int N, int K) {
 size_t gemv_workspace_bytes(int T, int N, int K) {
     if (T < kGemvMfmaT || N == 0 || K == 0) return 0;
     const size_t S = gemv_slabs(K);
-    return round_up(S * T * N * sizeof(float), kCounterAlign) + gemv_counter_bytes(T, N, K);
+    return gemv_counter_bytes(T, N, K) + round_up(S * T * N * sizeof(float), kCounterAlign);
 }
 
 template <int T>
 static int launch_gemv_mfma_t(GemvArgs a, void* ws, hipStream_t st) {
     const int S = gemv_slabs(a.K);
     a.S = S;
-    a.part = static_cast<float*>(ws);
+    a.cnt = static_cast<unsigned*>(ws);
+    a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + gemv_counter_bytes(T, a.N, a.K));
     a.ssq = nullptr;
-    a.cnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) +
-                                        round_up((size_t)S * T * a.N * sizeof(float), kCounterAlign));
     if (combine_last_arriver()) {
         hipLaunchKernelGGL((hc_down_partial_kernel<T, true, false, kGemvSlab, true>), dim3(S * ((a.N + kDnRows - 1) / kDnRows)), dim3(256), 0, st, a);
         return launch_status();

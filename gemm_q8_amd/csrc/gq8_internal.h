@@ -76,7 +76,7 @@ size_t gemv_workspace_bytes(int T, int N, int K);
 constexpr int kDownSlab = 512;                 // columns per slab (16 Q8_0 blocks)
 inline int hc_down_slabs(int K) { return (K + kDownSlab - 1) / kDownSlab; }
 size_t hc_down_workspace_bytes(int T, int N, int K);
-size_t hc_down_counter_bytes(int N);                 // counters at the workspace's end (down, pair)
+size_t hc_down_counter_bytes(int N);                 // counters at the workspace's start (down, pair)
 size_t gemv_counter_bytes(int T, int N, int K);      // the GEMV's (T >= 5), 0 otherwise
 int launch_hc_down(GemvArgs a, void* ws, hipStream_t st);
 // the down read (a.pw, a.r_out set) and the pair with the pending write folded into the staging

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define GQ8_ABI_VERSION 2
+#define GQ8_ABI_VERSION 3
 
 enum gq8_status {
     GQ8_OK = 0,
@@ -119,23 +119,26 @@ int gq8_w8a8_pack_host(const int8_t* W, int K, int N, int8_t* W_packed);
 /* ------------------------------------------------------------------------------------------
  * Workspace: device scratch that a compute call needs beyond its inputs and outputs.
  *   - size it with gq8_workspace_bytes() for the exact (op, rows, N, K) of the call; 0 means the
- *     call needs none (pass NULL, 0). The down read and the down/up pair use one (fp32 partial
- *     sums of the K slabs [S][T][N], the slabs' sums of squares per 64-row group [G][S][T], then
- *     one 32-bit arrival counter per 64-row group), and so does the GEMV at T >= 5 (the partial
- *     sums and the counters) (HC-Q8 page, "What changed": one scratch per queue, allocated and
- *     zeroed outside any capture);
+ *     call needs none (pass NULL, 0). The down read and the down/up pair use one (one 32-bit
+ *     arrival counter per 64-row group first, then the fp32 partial sums of the K slabs
+ *     [S][T][N], then the slabs' sums of squares per row group [G][S][T]), and so does the GEMV
+ *     at T >= 5 (the counters, then the partial sums) (HC-Q8 page, "What changed": one scratch
+ *     per queue, allocated and zeroed outside any capture);
  *   - the partial sums are combined in a fixed order either by a kernel of their own (the
  *     default) or by the last-arriving work-group of each row group (environment variable
  *     GQ8_COMBINE=last, read on every call; "kernel" or unset: the default; other values: the
  *     default, said once on stderr). The results are bitwise the same. The last-arriver combine
  *     (HC-Q8 page, "What changed"; W8A8 page, "Split-K requirements") counts arrivals in the
- *     counters, which must be zero before a call and which every call leaves at zero: zero a new
- *     workspace once with gq8_workspace_init(); the partial sums themselves are always rewritten
- *     before they are read (W8A8 page, "Split-K requirements": planes fully rewritten, no memset
- *     in the timed region);
+ *     counters, which must be zero before a call and which every complete call leaves at zero:
+ *     zero a new workspace once with gq8_workspace_init(); the partial sums themselves are always
+ *     rewritten before they are read (W8A8 page, "Split-K requirements": planes fully rewritten,
+ *     no memset in the timed region). The counters open the workspace and take
+ *     gq8_workspace_counter_bytes() bytes, 256 for every N <= 4096, so one zeroed workspace
+ *     serves calls of any shapes it is large enough for; only a call whose counter region is
+ *     larger than every earlier call's since the zeroing (N > 4096 growing) needs it zeroed again;
  *   - calls that may run concurrently (different streams, or a graph replayed concurrently with
  *     itself) need separate workspaces;
- *   - gq8_workspace_counter_bytes() is the size of the counter region at the end of the
+ *   - gq8_workspace_counter_bytes() is the size of the counter region at the start of the
  *     workspace (0 when the operation has none).
  * rows = T for the Q8_0 calls, M for W8A8.
  * ------------------------------------------------------------------------------------------ */
@@ -226,10 +229,13 @@ int gq8_hc_q8_pair_pending(const void* w_down, const uint16_t* R, const uint16_t
  * allocates nothing. Inputs, outputs, shapes and results are those of gq8_hc_q8_pair (bitwise);
  * a shape whose workspace, gq8_workspace_bytes(GQ8_OP_HC_PAIR, T, Nlr, Khc), exceeds the array
  * returns GQ8_ESHAPE (T = 16, Nlr = 320, Khc = 16384 needs 642 KiB; at T = 16 and Nlr = 1024,
- * Khc up to 32256 fits). Every call on one device shares that device's array and every call
- * rewrites all of it that it reads (no clearing needed), so calls that may run at the same time
- * on one device (several streams, host threads or concurrent graph replays) race and must not
- * overlap. GQ8_EHIP if the array's device address cannot be obtained. */
+ * Khc up to 32256 fits). Every call on one device shares that device's array, which keeps the
+ * last call's contents. Nothing needs clearing: the array starts zeroed, every call writes the
+ * partial sums before it reads them, and the one part that must be zero before a call, the
+ * 256-byte block of arrival counters at its start (read only with GQ8_COMBINE=last; 256 bytes
+ * for every pair shape), is left at zero by every complete call. Calls that may run at the same
+ * time on one device (several streams, host threads or concurrent graph replays) race and must
+ * not overlap. GQ8_EHIP if the array's device address cannot be obtained. */
 #define GQ8_NOALLOC_SCRATCH_BYTES (4u << 20)
 int gq8_hc_q8_pair_noalloc(const void* w_down, const uint16_t* R, const uint16_t* w_norm, float eps,
                            const void* w_up, uint16_t* lo, float* rs_out, uint16_t* out, int T,

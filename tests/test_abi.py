@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.gq8_abi_version() == 2
+    assert lib.gq8_abi_version() == 3
     assert lib.gq8_status_str(0) == "ok"
     assert lib.gq8_status_str(-4).startswith("workspace")
     assert lib.gq8_status_str(12345) == "unknown status"
@@ -61,13 +61,15 @@ def test_workspace_sizes(lib):
                            (lib.OP_W8A8, 16, 1536, 4096), (99, 1, 1, 32)]:
         assert lib.gq8_workspace_bytes(op, rows, n, k) == 0
         assert lib.gq8_workspace_counter_bytes(op, rows, n, k) == 0
-    # the split reads end their workspace with one arrival counter per 64-row group (the
-    # last-arriver combine), inside gq8_workspace_bytes
+    # the split reads open their workspace with one arrival counter per 64-row group (the
+    # last-arriver combine), inside gq8_workspace_bytes: 256 bytes for every N <= 4096
     for op, rows, n, k in [(lib.OP_HC_DOWN, 4, 320, 16384), (lib.OP_HC_PAIR, 16, 320, 16384),
                            (lib.OP_Q8_0_GEMV, 8, 1024, 4096)]:
         cb = lib.gq8_workspace_counter_bytes(op, rows, n, k)
         assert cb >= 4 * ((n + 63) // 64) and cb % 256 == 0
         assert lib.gq8_workspace_bytes(op, rows, n, k) > cb
+        assert cb == (256 if n <= 4096 else -(-4 * ((n + 63) // 64) // 256) * 256)
+    assert lib.gq8_workspace_counter_bytes(lib.OP_HC_DOWN, 1, 4160, 64) == 512
     # the GEMV takes a workspace from T = 5 on (MFMA over slabs, then a combine)
     assert lib.gq8_workspace_bytes(lib.OP_Q8_0_GEMV, 4, 1024, 4096) == 0
     assert lib.gq8_workspace_bytes(lib.OP_Q8_0_GEMV, 8, 1024, 4096) >= 8 * 8 * 1024 * 4

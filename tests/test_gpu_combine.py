@@ -87,6 +87,36 @@ def test_pair_last_arriver_is_the_default_pair(gpu, monkeypatch, T):
         assert gpu.gq8_workspace_check(gpu.OP_HC_PAIR, T, Nlr, Khc, ws, nb) == 0
 
 
+def test_last_arriver_workspace_reused_for_a_smaller_call(gpu, monkeypatch):
+    """One workspace, zeroed once and sized for the larger call, serves a down read at T = 8 and
+    then smaller down reads and a GEMV: the counters open the workspace, so each call finds them
+    at the same zeroed bytes (the larger call's partial sums lie past them)."""
+    big = (8, 320, 16384)
+    nb = gpu.gq8_workspace_bytes(gpu.OP_HC_DOWN, *big)
+    ws = workspace(nb)
+    cases = [("down", big), ("down", (2, 320, 4096)), ("down", (5, 64, 2048)), ("gemv", (6, 1024, 2048))]
+    want, got = [], []
+    for mode, out in (("kernel", want), ("last", got)):
+        monkeypatch.setenv("GQ8_COMBINE", mode)
+        for i, (op, (T, N, K)) in enumerate(cases):
+            if op == "down":
+                d = synth.hc_inputs(T, K=K, N=N, seed=74 + i)
+                wd = q8_0_from_f32(to_dev(d["w_down"]))
+                lo, rs = _down(gpu, wd, to_dev(d["R"]), to_dev(d["w_norm"]), T, N, K, ws, nb)
+                out.append((lo, rs))
+            else:
+                wg = q8_0_from_f32(to_dev(synth.normal_f32(74, "gpu.comb.r.w", (N, K), 0.0, 0.02)))
+                xg = to_dev(synth.normal_f32(74, "gpu.comb.r.x", (T, K)))
+                y = torch.full((T, N), 7.0, dtype=torch.float32, device="cuda")
+                gpu.gq8_q8_0_gemv(wg, xg, y, T, N, K, ws, nb)
+                out.append((y,))
+            torch.cuda.synchronize()
+    for (op, shape), a, b in zip(cases, want, got):
+        for x, y in zip(a, b):
+            assert torch.equal(x, y), f"{op} {shape}"
+    assert gpu.gq8_workspace_check(gpu.OP_HC_DOWN, *big, ws, nb) == 0
+
+
 def test_last_arriver_graph_replay(gpu, monkeypatch):
     """The down read and the GEMV (T = 8) with the last-arriver combine captured into one graph and
     replayed five times, with eager work and a poisoned partial-sum region (not the counters)
@@ -118,7 +148,7 @@ def test_last_arriver_graph_replay(gpu, monkeypatch):
             gpu.gq8_q8_0_gemv(wg, xg, y, Tg, Ng, Kg, wsg, nbg, s)
     for _ in range(5):
         lo.zero_(); rs.zero_(); y.zero_()
-        ws[: nb - cb].fill_(0xFF)                        # partial sums poisoned, counters kept
+        ws[cb:].fill_(0xFF)                              # partial sums poisoned, counters kept
         torch.cuda.synchronize()
         with torch.cuda.stream(s):
             g.replay()

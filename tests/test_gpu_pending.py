@@ -86,7 +86,7 @@ def test_pair_pending_graph_replay(gpu):
     for _ in range(3):
         for b in bufs:
             b.zero_()
-        ws[: nb - cb].fill_(0xFF)
+        ws[cb:].fill_(0xFF)
         torch.cuda.synchronize()
         with torch.cuda.stream(s):
             g.replay()

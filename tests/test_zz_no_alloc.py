@@ -40,6 +40,18 @@ def test_noalloc_pair_matches_the_workspace_pair(gpu, first, second):
     _both(gpu, *second, seed=61)
 
 
+@pytest.mark.parametrize("first,second", [((8, 320, 16384), (1, 320, 8192)),
+                                          ((4, 1024, 4096), (2, 64, 1056))])
+def test_noalloc_pair_last_arriver_after_a_larger_call(gpu, monkeypatch, first, second):
+    """With the last-arriver combine the array's arrival counters must be zero before each call:
+    they open the array (the same 256 bytes for every pair shape) and every call leaves them at
+    zero, so a smaller call after a larger one, whose partial sums cover the bytes that follow,
+    still finds them zero."""
+    monkeypatch.setenv("GQ8_COMBINE", "last")
+    _both(gpu, *first, seed=62)
+    _both(gpu, *second, seed=63)
+
+
 def test_noalloc_pair_limit(gpu):
     """A shape whose workspace exceeds the library's array is refused before any launch."""
     T, Nlr, Khc = 16, 1024, 32768
