@@ -327,8 +327,9 @@ GQ8_EXPORT int gq8_hc_q8_down_pending(const void* w_split, const uint16_t* R, co
                                       uint16_t* lo, float* rs_out, int T, int N, int K, void* ws,
                                       size_t ws_bytes, void* stream) {
     if (T < 0 || N < 0 || K < 0) return GQ8_EINVAL;
-    if (!q8_shape_ok(T, N, K) || K == 0) return GQ8_ESHAPE;
-    if (T == 0 || N == 0) return GQ8_OK;
+    // the down read's row group 0 performs the pending write: N = 0 would leave R_out unwritten
+    if (!q8_shape_ok(T, N, K) || K == 0 || N == 0) return GQ8_ESHAPE;
+    if (T == 0) return GQ8_OK;
     if (w_split == nullptr || R == nullptr || P == nullptr || w_norm == nullptr || R_out == nullptr ||
         lo == nullptr)
         return GQ8_EINVAL;

@@ -173,8 +173,9 @@ int gq8_q8_0_gemv(const void* w_split, const float* x, float* y, int T, int N, i
  *   rs[t]    = 1 / sqrt(mean_k R[t][k]^2 + eps)
  *   lo[t][n] = bf16( rs[t] * sum_k d[n][k/32] * q[n][k] * (R[t][k] * w_norm[k]) )
  * w_split: Q8_0 [N][K]; R bf16 [T][K]; w_norm bf16 [K]; lo bf16 [T][N]; rs_out fp32 [T]
- * (nullable). T = 1..16, K % 32 == 0, K > 0. Workspace: gq8_workspace_bytes(GQ8_OP_HC_DOWN, T,
- * N, K), its counters zeroed once. Two kernels: per 512-column slab partial sums (bf16 MFMA on
+ * (nullable). T = 1..16, K % 32 == 0, K > 0; T == 0 or N == 0: nothing to do (rs_out is not
+ * written either). Workspace: gq8_workspace_bytes(GQ8_OP_HC_DOWN, T, N, K), its counters zeroed
+ * once. Two kernels: per 512-column slab partial sums (bf16 MFMA on
  * exact hi/lo operands), then the combine (slab groups in ascending order) with rs and the bf16
  * rounding; with GQ8_COMBINE=last and T <= 8 one kernel, whose last-arriving work-group per row
  * group combines in the same order. */
@@ -212,7 +213,8 @@ int gq8_hc_q8_pair(const void* w_down, const uint16_t* R, const uint16_t* w_norm
  * gq8_hc_q8_down / gq8_hc_q8_pair give on R_out (bitwise). P and R_out bf16 [T][K] (K = Khc),
  * 16-byte aligned; R_out may not overlap R or P. The up read's own epilogue on the page (gate,
  * stream mean) is not defined there and not part of these calls. Shapes, workspace and errors as
- * the calls without the pending write; the partial sums are combined by the combine kernel. */
+ * the calls without the pending write, except that N == 0 returns GQ8_ESHAPE (the write is done
+ * by the down read's work-groups); the partial sums are combined by the combine kernel. */
 int gq8_hc_q8_down_pending(const void* w_split, const uint16_t* R, const uint16_t* P,
                            const uint16_t* w_norm, float eps, uint16_t* R_out, uint16_t* lo,
                            float* rs_out, int T, int N, int K, void* ws, size_t ws_bytes,

@@ -136,6 +136,12 @@ def test_pending_write_argument_checks(lib):
                                       dummy, 1, 330, 16384, dummy, 1 << 30, None) == lib.ESHAPE
     assert raw.gq8_hc_q8_down_pending(dummy, dummy, dummy, dummy, 1e-6, dummy, dummy, None, 17,
                                       320, 16384, dummy, 1 << 30, None) == lib.ESHAPE
+    # N == 0: the plain down read has nothing to do; the pending write needs the down read's
+    # work-groups, so the pending call refuses it rather than leave R_out unwritten
+    assert raw.gq8_hc_q8_down(dummy, dummy, dummy, 1e-6, dummy, None, 1, 0, 16384, None, 0,
+                              None) == lib.OK
+    assert raw.gq8_hc_q8_down_pending(dummy, dummy, dummy, dummy, 1e-6, dummy, dummy, None, 1, 0,
+                                      16384, None, 0, None) == lib.ESHAPE
 
 
 def test_moe_bf16_input_argument_checks(lib):
