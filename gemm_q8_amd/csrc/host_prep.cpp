@@ -69,7 +69,9 @@ uint16_t quantize_block(const float* v, int8_t* q) {
             continue;
         }
         const float r = roundf(v[i] / d);               // C round: half away from zero
-        q[i] = (int8_t)(r > 127.f ? 127 : (r < -127.f ? -127 : (int)r));
+        // a NaN quotient (only from non-finite input) gives 0, as the device conversion does,
+        // instead of an undefined float -> int conversion
+        q[i] = (int8_t)(r != r ? 0 : (r > 127.f ? 127 : (r < -127.f ? -127 : (int)r)));
     }
     return dbits;
 }

@@ -90,7 +90,8 @@ size_t gq8_q8_0_bytes(int64_t rows, int64_t K);
  * rounding). Per block: d = fp16(amax / 127) (fp32 quotient, round to nearest even);
  * q = round(w / d) with the fp32 quotient by the stored fp16 d, ties away from zero, clamped to
  * [-127, 127]; a block whose fp16 d is 0 gets zero quants. Weight preparation, not a hot-path
- * call. w: 16-byte aligned; K % 32 == 0. */
+ * call. w: 16-byte aligned, finite (a block holding an infinity or a NaN gets unspecified
+ * quants); K % 32 == 0. */
 int gq8_q8_0_quantize(const float* w, int rows, int K, void* w_split, void* stream);
 
 /* Reorder ggml 34-byte blocks {fp16 d; int8 q[32]} (row-major blocks, [rows][K/32]) into the
