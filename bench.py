@@ -275,7 +275,7 @@ def cpu_baseline(synth, budget_s):
 def bench_other_configs(torch, gq8, synth, dev, stream, report, only=None, w8a8_ms=None, gemv_ts=None):
     from gemm_q8_amd.device import q8_0_from_f32, to_dev, workspace
     lines = []
-    only = set(only or ("probe", "combine", "hcbf16", "gemv", "w8a8", "moe"))
+    only = set(only or ("probe", "combine", "hcbf16", "gemv", "w8a8", "w8a8kern", "moe"))
     ms = tuple(w8a8_ms or (1, 4, 8, 16, 32))
 
     def emit(d):
@@ -306,6 +306,8 @@ def bench_other_configs(torch, gq8, synth, dev, stream, report, only=None, w8a8_
         bench_gemv_sweep(torch, gq8, synth, dev, timed, emit, gemv_ts)
     if "w8a8" in only:
         bench_w8a8_sweep(torch, gq8, synth, dev, timed, emit, ms)
+    if "w8a8kern" in only:
+        bench_w8a8_kernels(torch, gq8, synth, dev, timed, emit)
     if "moe" in only:
         bench_moe(torch, gq8, synth, dev, timed, emit)
     if report:
@@ -448,6 +450,39 @@ def bench_w8a8_sweep(torch, gq8, synth, dev, timed, emit, ms):
         emit({"workload": "W8A8 on a bf16 x (quantize kernel, then the product)", "M": M, "N": N,
               "K": K, "us_per_call": round(us, 3), "weight_GBps": round(N * K / us / 1e3, 1)})
         del wps
+
+
+def bench_w8a8_kernels(torch, gq8, synth, dev, timed, emit, ms=(1, 2, 4, 8)):
+    """The VALU dot4 kernel against the int8 MFMA kernel (the default) at the M where both exist,
+    each forced with GQ8_W8A8_KERNEL (read by the library on every call, so at graph capture),
+    the same inputs and rotated weight copies."""
+    from gemm_q8_amd.device import to_dev, workspace
+    for (N, K) in ((1536, 4096), (2560, 4096), (4096, 2048)):
+        for M in ms:
+            dd = synth.w8a8_inputs(M, N, K)
+            wp0 = torch.empty(gq8.gq8_w8a8_packed_bytes(K, N), dtype=torch.int8, device=dev)
+            gq8.gq8_w8a8_pack(to_dev(dd["W"]), K, N, wp0)
+            n = n_sets_for(wp0.numel())
+            wps = [wp0] + [wp0.clone() for _ in range(n - 1)]
+            xq, xs, wsc = to_dev(dd["xq"]), to_dev(dd["x_scale"]), to_dev(dd["w_scale"])
+            out = torch.empty((M, N), dtype=torch.int16, device=dev)
+            nb = gq8.gq8_workspace_bytes(gq8.OP_W8A8, M, N, K)
+            wsp = workspace(nb)
+            rec = {"workload": "W8A8 kernel choice: VALU dot4 against int8 MFMA", "M": M, "N": N, "K": K,
+                   "default": "mfma"}
+            prev = os.environ.get("GQ8_W8A8_KERNEL")
+            try:
+                for kern in ("dot", "mfma"):
+                    os.environ["GQ8_W8A8_KERNEL"] = kern
+                    rec[f"{kern}_us"] = round(timed(lambda i: (lambda s, w=wps[i % n]: gq8.gq8_w8a8_gemm(
+                        xq, xs, w, wsc, out, M, N, K, wsp, nb, s)), n), 3)
+            finally:
+                if prev is None:
+                    os.environ.pop("GQ8_W8A8_KERNEL", None)
+                else:
+                    os.environ["GQ8_W8A8_KERNEL"] = prev
+            emit(rec)
+            del wps
 
 
 def bench_moe(torch, gq8, synth, dev, timed, emit):
@@ -734,8 +769,8 @@ def main():
                          "then exit")
     ap.add_argument("--no-configs", action="store_true",
                     help="leave out the per-configuration records (the five workloads)")
-    ap.add_argument("--only", default="probe,combine,hcbf16,gemv,w8a8,moe",
-                    help="with --all-configs: comma-separated subset of probe,combine,hcbf16,gemv,w8a8,moe")
+    ap.add_argument("--only", default="probe,combine,hcbf16,gemv,w8a8,w8a8kern,moe",
+                    help="with --all-configs: comma-separated subset of probe,combine,hcbf16,gemv,w8a8,w8a8kern,moe")
     ap.add_argument("--w8a8-ms", default="1,4,8,16,32", help="with --all-configs: W8A8 M values")
     ap.add_argument("--gemv-ts", default="1,2,4,8,16", help="token rows of the GEMV sweep")
     ap.add_argument("--report", default="bench_all.jsonl",

@@ -42,6 +42,16 @@ bool combine_last_arriver() {
     return false;
 }
 
+int w8a8_kernel_choice() {
+    const char* v = getenv("GQ8_W8A8_KERNEL");
+    if (v == nullptr || v[0] == '\0') return 0;
+    if (strcmp(v, "dot") == 0) return 1;
+    if (strcmp(v, "mfma") == 0) return 2;
+    static std::atomic<bool> said{false};
+    if (!said.exchange(true)) fprintf(stderr, "gq8: GQ8_W8A8_KERNEL=%s not understood (dot or mfma); ignored\n", v);
+    return 0;
+}
+
 }  // namespace gq8
 
 static inline hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }

@@ -95,8 +95,14 @@ int launch_hc_bf16_pair(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st);
 
 // ---------------------------------------------------------------- W8A8
 
+// The W8A8 kernel: int8 MFMA at every M by default; GQ8_W8A8_KERNEL=dot forces the VALU dot4
+// kernel where it exists (M <= 15), "mfma" the default (read on every call; other values: the
+// default, said once). int32 sums are exact, so both give bitwise the same results. Returns 0
+// default, 1 dot, 2 mfma.
+int w8a8_kernel_choice();
+
 struct W8Plan {
-    bool mfma;         // int8 MFMA path (M >= 2) or VALU dot4 path (M == 1)
+    bool mfma;         // int8 MFMA path (the default) or VALU dot4 path (forced, M <= 15)
     int ntiles;        // N rounded up to 16, / 16: one work-group each
     int ksteps;        // K rounded up to 64, / 64
     int nw;            // waves per work-group (<= 16)

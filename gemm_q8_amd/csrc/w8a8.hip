@@ -8,13 +8,15 @@
 // across blocks because its chip had 120 CUs per 40-160 tiles; here a work-group of 16 waves
 // has the same bytes in flight without the combine round trip). Every load of a wave is issued,
 // clamped to valid addresses, before the first MFMA / dot.
-//   M >= 2:  v_mfma_i32_16x16x64_i8 (rows past M are zero), one MFMA row tile for M <= 16 and
-//            two (sharing the weight fragment) for M <= 32. One x load per k-step per lane;
-//            the VALU dot needs M of them, which bound it from M = 4 on (measured). With at most
-//            128 tiles and M <= 16, two work-groups share a tile, eight columns each, so that
-//            twice as many CUs stream the weight (measured: M = 16, N = 1536, K = 4096 5.16 ->
-//            5.00 us).
-//   M == 1:  v_dot4_i32_i8 on the VALU over the same fragments.
+//   every M: v_mfma_i32_16x16x64_i8 (rows past M are zero), one MFMA row tile for M <= 16 and
+//            two (sharing the weight fragment) for M <= 32. One x load per k-step per lane. With
+//            at most 128 tiles and M <= 16, two work-groups share a tile, eight columns each, so
+//            that twice as many CUs stream the weight (measured: M = 16, N = 1536, K = 4096
+//            5.16 -> 5.00 us).
+//   the alternative for M <= 15: v_dot4_i32_i8 on the VALU over the same fragments, which needs
+//            M x loads per k-step per lane. The environment variable GQ8_W8A8_KERNEL=dot forces
+//            it, for comparison (the results are bitwise the same); measured slower at every M,
+//            by 0.05 to 0.3 us at M = 1 and from 1.8x at M = 8.
 // int32 sums are exact, so every order gives the one correct accumulator; the epilogue is
 // bf16( (fp32(acc) * x_scale[m]) * w_scale[n] ), two rounded fp32 products.
 #include "gq8_device.h"
@@ -318,7 +320,8 @@ __global__ void __launch_bounds__(1024) w8a8_dot_kernel(W8Args a) {
 
 W8Plan plan_w8a8(int M, int N, int K) {
     W8Plan p{};
-    p.mfma = M >= 2;
+    const int choice = w8a8_kernel_choice();
+    p.mfma = !(choice == 1 && M <= 15);            // MFMA by default, at every M (measured)
     p.ntiles = (N + 15) / 16;
     p.half = p.mfma && M <= 16 && 2 * p.ntiles <= 256;
     p.ksteps = (K + 63) / 64;

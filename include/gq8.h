@@ -266,7 +266,10 @@ size_t gq8_w8a8_packed_bytes(int K, int N);
 int gq8_w8a8_pack(const int8_t* W, int K, int N, int8_t* W_packed, void* stream);
 
 /* out[m][n] = bf16( (fp32(acc[m][n]) * x_scale[m]) * w_scale[n] ), acc = exact int32 sum,
- * two separately rounded fp32 products, round to nearest even. Exactly one correct output. */
+ * two separately rounded fp32 products, round to nearest even. Exactly one correct output.
+ * Every M runs on int8 MFMA; the environment variable GQ8_W8A8_KERNEL=dot (read on every call)
+ * forces a VALU dot4 kernel where it exists (M <= 15), for comparison: the output is the same
+ * either way. */
 int gq8_w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* W_packed,
                   const float* w_scale, uint16_t* out, int M, int N, int K,
                   void* ws, size_t ws_bytes, void* stream);

@@ -1,6 +1,6 @@
 """GPU parity of the W8A8 product: int32 accumulators and bf16 outputs bit-exact against the
-oracle, for M = 1..32 (VALU dot4 below 16 rows, int8 MFMA from 16), ragged N and K, the full
-workload shapes, rounding ties, and graph replay."""
+oracle, for M = 1..32 (int8 MFMA; the VALU dot4 kernel forced where it exists, M <= 15),
+ragged N and K, the full workload shapes, rounding ties, and graph replay."""
 import numpy as np
 import pytest
 import torch
@@ -49,6 +49,20 @@ def test_w8a8_full_size_exact(gpu, M, N, K):
     acc_ref, out_ref = w8a8_gemm(d["xq"], d["x_scale"], d["W"], d["w_scale"])
     assert np.array_equal(_run(gpu, d, M, N, K, i32=True), acc_ref)
     assert np.array_equal(_run(gpu, d, M, N, K), out_ref)
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 15])
+@pytest.mark.parametrize("N,K", [(37, 80), (160, 4096), (40, 8192)])
+def test_w8a8_forced_kernels_exact(gpu, monkeypatch, M, N, K):
+    """GQ8_W8A8_KERNEL=dot and =mfma force the VALU dot4 kernel and the int8 MFMA kernel where both
+    exist (M <= 15): each is bit-exact against the oracle, so the choice between them is speed
+    only."""
+    d = synth.w8a8_inputs(M, N, K, seed=90 + M)
+    acc_ref, out_ref = w8a8_gemm(d["xq"], d["x_scale"], d["W"], d["w_scale"])
+    for kern in ("dot", "mfma"):
+        monkeypatch.setenv("GQ8_W8A8_KERNEL", kern)
+        assert np.array_equal(_run(gpu, d, M, N, K, i32=True), acc_ref), kern
+        assert np.array_equal(_run(gpu, d, M, N, K), out_ref), kern
 
 
 def test_w8a8_extreme_accumulators(gpu):
