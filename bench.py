@@ -845,9 +845,12 @@ def main():
         g.run(n)
         hot[f"T{T}"] = round(time_region(torch, stream, lambda: g.run(n * reps)) / (n * reps) * 1e6, 3)
     dom = "pair"
-    kd = kern[dom]
-    avg_us = kd["t"] / kd["launches"] * 1e6
-    achieved = kd["bytes"] / kd["t"] / 1e9
+    # the roofline unit is the pair call, timed over the timed region itself: K steps of one
+    # call per T, so the average call is t / (K * len(TS)) and its algorithmic bytes are the mean
+    # of the T's
+    n_calls = args.steps * len(TS)
+    avg_us = t / n_calls * 1e6
+    achieved = sum(hc_kernel_bytes("pair", T) for T in TS) * args.steps / t / 1e9
     dist = {f"T{T}": {"median": round(hc_dist[T]["median"], 3), "p90": round(hc_dist[T]["p90"], 3)}
             for T in TS}
     log(f"[bench] per-call pair us {per_call}; median/p90 {dist}; hot cache {hot}")
@@ -905,8 +908,10 @@ def main():
             "traffic": recorded_traffic(),
             "traffic_unit": "bytes per pair call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
             "avg_call_us": round(avg_us, 3),
-            # the same fraction per T, and for the standalone down and up calls (their own kernels:
-            # partial sums + combine kernel, and the up read alone), each over its own bytes
+            "measured_over": f"the timed region: {args.steps} steps x {len(TS)} pair calls",
+            # the same fraction per T (graphs of back-to-back calls of one T after the timed
+            # region), and for the standalone down and up calls (their own kernels: partial sums +
+            # combine kernel, and the up read alone), each over its own bytes
             "frac_per_T": {f"T{T}": round(hc_kernel_bytes("pair", T) / (per_call[f"T{T}"] * 1e3)
                                           / HBM_PEAK_GBS, 4) for T in TS},
             "separate_calls": {k: {"avg_us": round(v["t"] / v["launches"] * 1e6, 3),
