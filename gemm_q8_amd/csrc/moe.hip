@@ -568,7 +568,9 @@ __global__ void __launch_bounds__(256) moe_down_kernel(MoeArgs a) {
 // as bf16 hi and lo (|h - hi - lo| <= 2^-17 |h|); A rows 0..7 take hi and rows 8..15 lo, so
 // result rows 0 and 8 hold the two parts. The per-entry results r_j go to LDS and one wave
 // forms out[t] = bf16( sum_j w[t][j] r_j ), j in order (the combine's order). An expert that
-// two tokens route to is read by both tokens' work-groups.
+// two tokens route to is read by both tokens' work-groups. The expert ids are loaded once per
+// lane (they are validated and give each entry's expert by a cross-lane read), so the weight
+// loads start after one round trip to the ids.
 GQ8_DEV int dn_koff(int g) { return 16 * (g & 1) + 8 * (g >> 1); }
 GQ8_DEV int imin_m(int x, int y) { return x < y ? x : y; }
 
@@ -596,16 +598,18 @@ __global__ void __launch_bounds__(256) moe_down_token_kernel(MoeArgs a) {
     const int r0 = blockIdx.x * 16;
     const int row = r0 + j < D ? r0 + j : D - 1;
 
-    bool bad = false;
-    for (int k = lane; k < a.P; k += 64) {
-        const int e = a.ids[k];
-        bad = bad || e < 0 || e >= a.E;
-    }
-    const bool ok = __ballot(bad) == 0;            // wave-uniform; the same in every wave
+    // every entry's expert id, one load per lane per 64 entries (P <= 256): they validate the
+    // ids and give each entry's expert by a cross-lane read, so the weight loads wait for one
+    // round trip only (the h loads of the first round are issued before that wait)
+    int idv[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) idv[c] = a.ids[imin_m(64 * c + lane, a.P - 1)];   // clamped: P >= 1
+    bool ok = true;                                // wave-uniform; the same in every wave
+    bool checked = false;
     const int ko = 2 * dn_koff(g);                 // byte offset of the lane's k-group in a bf16 row
     const int hl = j < 8 ? 0 : 1;                  // A rows 0..7 hi, 8..15 lo
 
-    for (int j0 = wave; ok && j0 < topk; j0 += 4 * EG) {
+    for (int j0 = wave; j0 < topk; j0 += 4 * EG) {
         int ent[EG];
         bool on[EG];
         float4 hv[EG][HC][2];
@@ -615,7 +619,7 @@ __global__ void __launch_bounds__(256) moe_down_token_kernel(MoeArgs a) {
         for (int u = 0; u < EG; ++u) {
             const int jj = j0 + 4 * u;
             on[u] = jj < topk;
-            ent[u] = t * topk + (on[u] ? jj : j0);
+            ent[u] = __builtin_amdgcn_readfirstlane(t * topk + (on[u] ? jj : j0));
             const float4* hp = reinterpret_cast<const float4*>(a.h + (size_t)ent[u] * F);
 #pragma unroll
             for (int c = 0; c < HC; ++c) {
@@ -624,9 +628,24 @@ __global__ void __launch_bounds__(256) moe_down_token_kernel(MoeArgs a) {
                 hv[u][c][1] = hp[2 * pc + 1];
             }
         }
+        if (!checked) {
+            // the ids are used only from here on, after the h loads are issued (an empty
+            // statement that the compiler may not move across memory accesses)
+            __asm__ volatile("" : "+v"(idv[0]), "+v"(idv[1]), "+v"(idv[2]), "+v"(idv[3]) :: "memory");
+            bool bad = false;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                bad = bad || (64 * c + lane < a.P && (idv[c] < 0 || idv[c] >= a.E));
+            ok = __ballot(bad) == 0;
+            checked = true;
+        }
+        if (!ok) break;
 #pragma unroll
         for (int u = 0; u < EG; ++u) {
-            const int8_t* q = a.wdn + (size_t)a.ids[ent[u]] * a.dn_bytes;
+            const int cw = ent[u] >> 6;
+            const int sel = cw == 0 ? idv[0] : cw == 1 ? idv[1] : cw == 2 ? idv[2] : idv[3];
+            const int eid = __builtin_amdgcn_readlane(sel, ent[u] & 63);
+            const int8_t* q = a.wdn + (size_t)eid * a.dn_bytes;
             const uint32_t* dp = reinterpret_cast<const uint32_t*>(q + (size_t)D * F) + (size_t)row * (NB / 2);
 #pragma unroll
             for (int i = 0; i < NL; i += 4) {

@@ -336,7 +336,9 @@ int gq8_moe_plan(const int32_t* ids, int T, int topk, int E, int32_t* plan, void
  * and out[t] = bf16( sum_{j=0..topk-1} weights[t][j] * r_{t,j} ), in slot order.
  * xq int8 [T][D], xd fp16 [T][D/32] (the q8_1 quants and scales); ids int32 [T][topk];
  * weights fp32 [T][topk]; out bf16 [T][D]. D % 32 == 0, F % 32 == 0, F <= 1024,
- * T*topk <= 256. Only the routed experts' bytes are read. */
+ * T*topk <= 256. Only the routed experts' bytes are read. An id outside [0, E) anywhere in
+ * ids (gq8_moe_route writes -1 for a row of NaN logits) makes the call write zeros to out and
+ * read no expert. */
 size_t gq8_moe_workspace_bytes(int T, int topk, int D, int F);
 int gq8_moe_q8_0_routed(const int8_t* xq, const uint16_t* xd, const int32_t* ids,
                         const float* weights, const void* w_gate_up, const void* w_down,

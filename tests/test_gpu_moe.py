@@ -280,6 +280,34 @@ def test_moe_flags(gpu, T, E, topk, D, F):
     assert not torch.equal(o[2], out)                           # a different read
 
 
+@pytest.mark.parametrize("bad", [8, -1, 1 << 30])
+@pytest.mark.parametrize("D,F", [(64, 256), (96, 64)])
+@pytest.mark.parametrize("general", [False, True])
+def test_moe_invalid_id_writes_zeros(gpu, monkeypatch, bad, D, F, general):
+    """An id outside [0, E) anywhere in ids: every routed call writes an all-zero output (bf16
+    +0) and reads no expert (the arenas hold junk). Every flag combination, the token down read
+    (F = 256) and the plan-based kernels (F = 64, or forced)."""
+    if general:
+        monkeypatch.setenv("GQ8_FORCE_GENERIC", "1")
+    T, E, topk = 2, 8, 2
+    agu, adn = _arena(gpu, None, E, D, F, [], seed=0)
+    ids = to_dev(np.array([[1, 3], [bad, 5]], np.int32))
+    w = to_dev(np.full((T, topk), 0.5, np.float32))
+    x = to_dev(np.full((T, D), 0x3F80, np.uint16))                # bf16 1.0
+    xq = to_dev(np.ones((T, D), np.int8))
+    xd = to_dev(np.full((T, D // 32), 0x2000, np.uint16))
+    nb = gpu.gq8_moe_workspace_bytes(T, topk, D, F)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    for flags in (0, gpu.MOE_X_BF16, gpu.MOE_H_Q8_1, gpu.MOE_X_BF16 | gpu.MOE_H_Q8_1):
+        if (flags & gpu.MOE_H_Q8_1) and F not in (256, 512, 1024):
+            continue
+        out = torch.full((T, D), 0x5555, dtype=torch.int16, device="cuda")
+        xx, xs = (x, None) if flags & gpu.MOE_X_BF16 else (xq, xd)
+        gpu.gq8_moe_q8_0_routed_flags(xx, xs, ids, w, agu, adn, out, T, topk, E, D, F, flags, ws, nb)
+        torch.cuda.synchronize()
+        assert not out.any(), f"flags={flags}"
+
+
 def test_moe_graph_replay(gpu):
     """The routed calls (each flag combination) captured into one hipGraph and replayed, with
     eager work and a poisoned workspace between replays: every replay equals the eager output."""
