@@ -216,14 +216,19 @@ GQ8_DEV EntrySet entry_set(const int32_t* ids, int P, int E, int i) {
     const int lane = threadIdx.x & 63;
     int v[4];
     bool bad = false;
+    // four loads in flight at once (clamped, no branches: P >= 1), one wait; entry i's own id
+    // is lane i % 64 of word i / 64, read across lanes rather than loaded again
+#pragma unroll
+    for (int w = 0; w < 4; ++w) v[w] = ids[64 * w + lane < P ? 64 * w + lane : P - 1];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
         const int k = 64 * w + lane;
-        v[w] = k < P ? ids[k] : -1;
+        if (k >= P) v[w] = -1;
         bad = bad || (k < P && (v[w] < 0 || v[w] >= E));
     }
     EntrySet r;
-    r.e = ids[i];
+    const int iw = i >> 6;
+    r.e = __builtin_amdgcn_readlane(iw == 0 ? v[0] : iw == 1 ? v[1] : iw == 2 ? v[2] : v[3], i & 63);
     r.ok = __ballot(bad) == 0;
 #pragma unroll
     for (int w = 0; w < 4; ++w) r.m[w] = __ballot(64 * w + lane < P && v[w] == r.e);
