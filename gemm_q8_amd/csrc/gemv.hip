@@ -636,6 +636,9 @@ __global__ void __launch_bounds__(256) hc_down_combine_kernel(GemvArgs a) {
     const int per = (S + 3) / 4;
     const int s0 = sg * per, s1 = imin(S, s0 + per);
     const int nc = imin(n, N - 1);
+    // the first sum-of-squares term of each rs lane (the only one while S <= 64) is loaded ahead
+    // of the partial sums, clamped rather than behind a branch, so it shares their round trip
+    const float sq0 = XF ? 0.f : a.ssq[(size_t)imin((int)threadIdx.x & 63, S - 1) * a.T + t];
     float v = 0.f;
     for (int s = s0; s < s1; s += 8) {
         float p[8];
@@ -645,8 +648,8 @@ __global__ void __launch_bounds__(256) hc_down_combine_kernel(GemvArgs a) {
         for (int i = 0; i < 8; ++i) v += s + i < s1 ? p[i] : 0.f;
     }
     if (!XF && threadIdx.x < 64) {     // rs[t]: lane-strided sums, then the wave sum
-        float ss = 0.f;
-        for (int s = threadIdx.x; s < S; s += 64) ss += a.ssq[(size_t)s * a.T + t];
+        float ss = (int)threadIdx.x < S ? 0.f + sq0 : 0.f;
+        for (int s = threadIdx.x + 64; s < S; s += 64) ss += a.ssq[(size_t)s * a.T + t];
         ss = wave_sum(ss);
         if (threadIdx.x == 0) {
             const float rs = 1.0f / sqrtf(ss / (float)a.K + a.eps);
