@@ -369,12 +369,17 @@ __global__ void __launch_bounds__((256 * dn_parts<T, WB, SLAB>())) hc_down_parti
                 sw[0] = s2.x; sw[1] = s2.y;
             }
         } else {
+            // a ragged slab: clamped loads, all in flight at once (no branch and wait per load);
+            // the MFMA loop gives the blocks past the slab's end scale 0
+            const uint16_t* ds = a.d + (size_t)row * nblk + (k0 >> 5);
+            uint32_t lo16[NSW], hi16[NSW];
 #pragma unroll
             for (int i = 0; i < NSW; ++i) {
-                const uint32_t lo16 = b0 + 2 * i < cb ? dr[2 * i] : 0u;
-                const uint32_t hi16 = b0 + 2 * i + 1 < cb ? dr[2 * i + 1] : 0u;
-                sw[i] = lo16 | (hi16 << 16);
+                lo16[i] = ds[imin(b0 + 2 * i, cb - 1)];
+                hi16[i] = ds[imin(b0 + 2 * i + 1, cb - 1)];
             }
+#pragma unroll
+            for (int i = 0; i < NSW; ++i) sw[i] = lo16[i] | (hi16[i] << 16);
         }
     }
     // 1. weights: the wave's quarter q = i / 2 (slab quarter NQ cp + q) covers columns
