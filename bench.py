@@ -272,7 +272,8 @@ def cpu_baseline(synth, budget_s):
 
 # ------------------------------------------------------------------------------------ other configs
 
-def bench_other_configs(torch, gq8, synth, dev, stream, report, only=None, w8a8_ms=None, gemv_ts=None):
+def bench_other_configs(torch, gq8, synth, dev, stream, report, only=None, w8a8_ms=None, gemv_ts=None,
+                        samples=None):
     from gemm_q8_amd.device import q8_0_from_f32, to_dev, workspace
     lines = []
     only = set(only or ("probe", "combine", "hcbf16", "gemv", "w8a8", "w8a8kern", "moe"))
@@ -284,7 +285,7 @@ def bench_other_configs(torch, gq8, synth, dev, stream, report, only=None, w8a8_
 
     def timed(fn_for_set, n_sets, reps=30):
         # the per-configuration records' method: median over samples of >= 400 calls each
-        return timed_dist(torch, stream, fn_for_set, n_sets, reps=max(5, reps // 5))["median"]
+        return timed_dist(torch, stream, fn_for_set, n_sets, reps=samples or max(5, reps // 5))["median"]
 
     # read-bandwidth probe at the same byte counts
     # (4 KiB: one work-group, the launch floor; the large sizes: how close a plain stream gets)
@@ -772,6 +773,9 @@ def main():
     ap.add_argument("--only", default="probe,combine,hcbf16,gemv,w8a8,w8a8kern,moe",
                     help="with --all-configs: comma-separated subset of probe,combine,hcbf16,gemv,w8a8,w8a8kern,moe")
     ap.add_argument("--w8a8-ms", default="1,4,8,16,32", help="with --all-configs: W8A8 M values")
+    ap.add_argument("--sweep-samples", type=int, default=0,
+                    help="with --all-configs: samples of >= 400 calls per sweep line (0: the default, 6 for most; 1 keeps "
+                         "profiler runs short)")
     ap.add_argument("--gemv-ts", default="1,2,4,8,16", help="token rows of the GEMV sweep")
     ap.add_argument("--report", default="bench_all.jsonl",
                     help="file for the --all-configs lines (JSON, one per line)")
@@ -929,7 +933,8 @@ def main():
     if args.all_configs:
         bench_other_configs(torch, gq8, synth, dev, stream, args.report, only=args.only.split(","),
                             w8a8_ms=[int(m) for m in args.w8a8_ms.split(",")],
-                            gemv_ts=[int(t) for t in args.gemv_ts.split(",")])
+                            gemv_ts=[int(t) for t in args.gemv_ts.split(",")],
+                            samples=args.sweep_samples or None)
     print(json.dumps(result), flush=True)
 
 
