@@ -903,7 +903,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "gq8_hc_q8_pair: hc_down_partial_kernel + hc_pair_up_kernel (T = 1, 4); "
+            "kernel": "gq8_hc_q8_pair: hc_down_rows_kernel + hc_up_direct_kernel (T = 1); "
+                      "hc_down_partial_kernel + hc_pair_up_kernel (T = 4); hc_down_partial_kernel "
                       "+ hc_down_combine_kernel + hc_up_direct_kernel (T = 6)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,

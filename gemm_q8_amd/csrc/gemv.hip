@@ -15,7 +15,10 @@
 //    waves' sums are added through LDS in wave order. T >= 5: the down read's slab kernel on
 //    256-column slabs with x split into bf16 hi + lo as the MFMA A operand, then the combine
 //    kernel without rs.
-//  * down read (hc_down_partial_kernel): a work-group takes a 512-column slab x 64 rows, one
+//  * down read at T = 1 (hc_down_rows_kernel): a work-group owns two whole rows and all of K,
+//    VALU dots on u = R * w_norm formed in fp32, its own sum of squares for rs: one kernel, no
+//    partial sums; the pair then takes the direct up kernel (two launches).
+//  * down read, T >= 2 (hc_down_partial_kernel): a work-group takes a 512-column slab x 64 rows, one
 //    16-row 16x16x32 bf16 MFMA tile per wave (from T = 9 two waves per tile, one per column
 //    half). u = R * w_norm is exact in fp32 (8-bit x 8-bit
 //    significands) and splits exactly into bf16 hi + lo, so the MFMA products are exact; it is
@@ -673,6 +676,155 @@ __global__ void __launch_bounds__(256) hc_down_combine_kernel(GemvArgs a) {
     }
 }
 
+// Down read on whole rows (small T): a work-group owns RW rows and all of K, so no partial sums
+// and no combine. Wave w takes the 1024-column chunks w, w + NW, ... (CPW of them per pass, all
+// loaded before the first arithmetic: activations first, then the weights, as the GEMV's
+// work-group kernel does with x); lane l takes columns
+// 16l .. 16l + 15 of a chunk. u = R * w_norm is formed in fp32 (exact: two 8-bit significands)
+// and each lane adds q * u for its 16 columns (each product exact in fp32), times the block
+// scale, in chunk order; the sums of R^2 ride along. Each work-group reads all of R and w_norm
+// (from L2 after the first), adds the waves' sums through LDS in wave order, forms rs from its
+// own sum of squares (the same order in every work-group, so every work-group gets the same rs)
+// and rounds lo = bf16(rs * y). PW: the pending write, R' = bf16(R + P) in place of R, written
+// to R_out by work-group 0.
+template <int T, int RW, int CPW, bool PW = false>
+__global__ void __launch_bounds__(1024) hc_down_rows_kernel(GemvArgs a) {
+    __shared__ float red[16][RW * T + T];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int NW = blockDim.x >> 6;
+    const int N = a.N, K = a.K, nblk = K >> 5;
+    const int row0 = blockIdx.x * RW;
+    const int nchunk = (K + 1023) >> 10;
+    const uint16_t* R = reinterpret_cast<const uint16_t*>(a.x);
+
+    float acc[RW][T], r2[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        r2[t] = 0.f;
+#pragma unroll
+        for (int r = 0; r < RW; ++r) acc[r][t] = 0.f;
+    }
+    for (int c0 = wave; c0 < nchunk; c0 += NW * CPW) {
+        int kc[CPW];
+        bool kok[CPW];
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+            const int k = (c0 + c * NW) * 1024 + lane * 16;
+            kok[c] = k < K;                                     // K % 32 == 0: k + 16 <= K
+            kc[c] = kok[c] ? k : K - 16;
+        }
+        uint4 rv[CPW][T][2], nv[CPW][2], pv[CPW][PW ? T : 1][2];
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const uint4* rp = reinterpret_cast<const uint4*>(R + (size_t)t * K + kc[c]);
+                rv[c][t][0] = rp[0];
+                rv[c][t][1] = rp[1];
+                if constexpr (PW) {
+                    const uint4* pp = reinterpret_cast<const uint4*>(a.pw + (size_t)t * K + kc[c]);
+                    pv[c][t][0] = pp[0];
+                    pv[c][t][1] = pp[1];
+                }
+            }
+            const uint4* np = reinterpret_cast<const uint4*>(a.wnorm + kc[c]);
+            nv[c][0] = np[0];
+            nv[c][1] = np[1];
+        }
+        u32x4 wq[CPW][RW];
+        uint16_t wd[CPW][RW];
+#pragma unroll
+        for (int c = 0; c < CPW; ++c)
+#pragma unroll
+            for (int r = 0; r < RW; ++r) {
+                const int row = imin(row0 + r, N - 1);
+                wd[c][r] = a.d[(size_t)row * nblk + (kc[c] >> 5)];
+                wq[c][r] = ld_nt16(a.q + (size_t)row * K + kc[c]);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+            const uint32_t nw[8] = {nv[c][0].x, nv[c][0].y, nv[c][0].z, nv[c][0].w,
+                                    nv[c][1].x, nv[c][1].y, nv[c][1].z, nv[c][1].w};
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                uint32_t rw[8] = {rv[c][t][0].x, rv[c][t][0].y, rv[c][t][0].z, rv[c][t][0].w,
+                                  rv[c][t][1].x, rv[c][t][1].y, rv[c][t][1].z, rv[c][t][1].w};
+                if constexpr (PW) {
+                    const uint32_t pw8[8] = {pv[c][PW ? t : 0][0].x, pv[c][PW ? t : 0][0].y,
+                                             pv[c][PW ? t : 0][0].z, pv[c][PW ? t : 0][0].w,
+                                             pv[c][PW ? t : 0][1].x, pv[c][PW ? t : 0][1].y,
+                                             pv[c][PW ? t : 0][1].z, pv[c][PW ? t : 0][1].w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float s0 = __uint_as_float(rw[e] << 16) + __uint_as_float(pw8[e] << 16);
+                        const float s1 = __uint_as_float(rw[e] & 0xffff0000u) + __uint_as_float(pw8[e] & 0xffff0000u);
+                        rw[e] = (uint32_t)f2bf_bits(s0) | ((uint32_t)f2bf_bits(s1) << 16);
+                    }
+                    if (blockIdx.x == 0 && kok[c]) {
+                        uint4* op = reinterpret_cast<uint4*>(a.r_out + (size_t)t * K + kc[c]);
+                        op[0] = make_uint4(rw[0], rw[1], rw[2], rw[3]);
+                        op[1] = make_uint4(rw[4], rw[5], rw[6], rw[7]);
+                    }
+                }
+                float u[16], s2 = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float q0 = __uint_as_float(rw[e] << 16), q1 = __uint_as_float(rw[e] & 0xffff0000u);
+                    u[2 * e] = q0 * __uint_as_float(nw[e] << 16);              // exact products
+                    u[2 * e + 1] = q1 * __uint_as_float(nw[e] & 0xffff0000u);
+                    s2 = fmaf(q0, q0, s2);
+                    s2 = fmaf(q1, q1, s2);
+                }
+                r2[t] += kok[c] ? s2 : 0.f;
+#pragma unroll
+                for (int r = 0; r < RW; ++r)
+                    acc[r][t] = fmaf(dot16_i8_f32(wq[c][r], u), kok[c] ? h2f(wd[c][r]) : 0.f, acc[r][t]);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+#pragma unroll
+        for (int r = 0; r < RW; ++r) {
+            const float v = wave_sum(acc[r][t]);
+            if (lane == 0) red[wave][r * T + t] = v;
+        }
+        const float s = wave_sum(r2[t]);
+        if (lane == 0) red[wave][RW * T + t] = s;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < RW * T) {
+        const int t = (int)threadIdx.x / RW, r = (int)threadIdx.x - t * RW;
+        float y = 0.f, ss = 0.f;
+        for (int w = 0; w < NW; ++w) {
+            y += red[w][r * T + t];
+            ss += red[w][RW * T + t];
+        }
+        const float rs = 1.0f / sqrtf(ss / (float)K + a.eps);
+        if (blockIdx.x == 0 && r == 0 && a.rs_out != nullptr) a.rs_out[t] = rs;
+        const int row = row0 + r;
+        if (row < N && a.out != nullptr) reinterpret_cast<uint16_t*>(a.out)[(size_t)t * N + row] = f2bf_bits(rs * y);
+    }
+}
+
+// Whole-row down reads up to this many tokens. At T = 1 this kernel is VALU-bound (its dots, and
+// the activation arithmetic that every work-group repeats) but needs no combine: measured on
+// MI355X at 320 x 16384, the down call 5.90 -> 4.25 us and the pair (then with the direct up
+// kernel) 8.24 -> 8.00 us. At T = 2 and 3 the down call gains too but the pair loses against the
+// fused combine, and the pair must stay bitwise the two separate calls.
+constexpr int kDownRowsMaxT = 1;
+constexpr int kDownRowsRW = 2;     // rows per work-group: 160 work-groups at N = 320 (1 and 4: slower)
+
+template <int T, bool PW>
+static int launch_down_rows_t(GemvArgs a, hipStream_t st) {
+    constexpr int RW = kDownRowsRW;
+    const int nchunk = (a.K + 1023) / 1024;
+    const int nw = nchunk > 16 ? 16 : nchunk;
+    hipLaunchKernelGGL((hc_down_rows_kernel<T, RW, 1, PW>), dim3((a.N + RW - 1) / RW), dim3(64 * nw), 0, st, a);
+    return launch_status();
+}
+
 // Down-read workspace: one arrival counter per 64-row group first (zero between calls; 256
 // bytes for every N <= 4096, so calls of different shapes find their counters at the same
 // zeroed bytes), then the partial sums [S][T][N], then the sums of squares [G][S][T] (G = row
@@ -703,7 +855,13 @@ template <int T>
 static bool dn_last_arriver() { return dn_parts<T, false>() == 1 && combine_last_arriver(); }
 
 template <int T>
+static bool down_rows() { return T <= kDownRowsMaxT && !force_general(); }
+
+template <int T>
 static int launch_down_t(GemvArgs a, void* ws, hipStream_t st) {
+    if constexpr (T <= kDownRowsMaxT) {
+        if (down_rows<T>()) return launch_down_rows_t<T, false>(a, st);
+    }
     dn_workspace(a, T, ws);
     const int S = a.S;
     if constexpr (dn_parts<T, false>() == 1) {
@@ -724,6 +882,9 @@ int launch_hc_down(GemvArgs a, void* ws, hipStream_t st) { GQ8_T_SWITCH(launch_d
 // the down read with the pending write: the slab kernel with PW, then the combine kernel
 template <int T>
 static int launch_down_pending_t(GemvArgs a, void* ws, hipStream_t st) {
+    if constexpr (T <= kDownRowsMaxT) {
+        if (down_rows<T>()) return launch_down_rows_t<T, true>(a, st);
+    }
     dn_workspace(a, T, ws);
     hipLaunchKernelGGL((hc_down_partial_kernel<T, false, false, kDownSlab, false, true>), dim3(a.S * ((a.N + kDnRows - 1) / kDnRows)), dim3(256 * dn_parts<T, false>()), 0, st, a);
     const int rc = launch_status();
@@ -1216,7 +1377,7 @@ static int launch_pair_t(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st) {
         const int rc = launch_down_t<T>(dn, ws, st);
         return rc != GQ8_OK ? rc : launch_up_t<T>(up, st);
     } else {
-        if (dn_last_arriver<T>()) {        // the down call (its own combine), then the up read
+        if (down_rows<T>() || dn_last_arriver<T>()) {   // the down call, then the up read
             const int rc = launch_down_t<T>(dn, ws, st);
             return rc != GQ8_OK ? rc : launch_up_t<T>(up, st);
         }
@@ -1240,7 +1401,7 @@ static int launch_pair_pending_t(GemvArgs dn, GemvArgs up, void* ws, hipStream_t
         const int rc = launch_down_pending_t<T>(dn, ws, st);
         return rc != GQ8_OK ? rc : launch_up_t<T>(up, st);
     } else {
-        if (up.K != kUpCW || force_general()) {
+        if (up.K != kUpCW || force_general() || down_rows<T>()) {
             const int rc = launch_down_pending_t<T>(dn, ws, st);
             return rc != GQ8_OK ? rc : launch_up_t<T>(up, st);
         }

@@ -176,7 +176,9 @@ int gq8_q8_0_gemv(const void* w_split, const float* x, float* y, int T, int N, i
  * w_split: Q8_0 [N][K]; R bf16 [T][K]; w_norm bf16 [K]; lo bf16 [T][N]; rs_out fp32 [T]
  * (nullable). T = 1..16, K % 32 == 0, K > 0; T == 0 or N == 0: nothing to do (rs_out is not
  * written either). Workspace: gq8_workspace_bytes(GQ8_OP_HC_DOWN, T, N, K), its counters zeroed
- * once. Two kernels: per 512-column slab partial sums (bf16 MFMA on
+ * once. T = 1: one kernel, each work-group owning two whole rows over all of K (fp32 VALU dots,
+ * rs from the work-group's own sum of squares, the same in every work-group); the workspace is
+ * passed but not touched. T >= 2: two kernels, per 512-column slab partial sums (bf16 MFMA on
  * exact hi/lo operands), then the combine (slab groups in ascending order) with rs and the bf16
  * rounding; with GQ8_COMBINE=last and T <= 8 one kernel, whose last-arriving work-group per row
  * group combines in the same order. */
@@ -197,8 +199,9 @@ int gq8_hc_q8_up(const void* w_split, const uint16_t* lo, uint16_t* out, int T, 
  *   lo  = gq8_hc_q8_down(w_down [Nlr][Khc], R [T][Khc], w_norm [Khc])     bf16 [T][Nlr]
  *   out = gq8_hc_q8_up(w_up [Khc][Nlr], lo)                                bf16 [T][Khc]
  * lo, rs_out and out are bitwise what the two separate calls produce. For Nlr == 320 and
- * T <= 4 the down read's combine of its split partial sums runs inside the up kernel (two kernel
- * launches instead of three); otherwise the two calls' kernels run in sequence. lo is written (bf16
+ * 2 <= T <= 4 the down read's combine of its split partial sums runs inside the up kernel (two
+ * kernel launches instead of three); otherwise (T = 1: the whole-row down kernel, no combine)
+ * the two calls' kernels run in sequence. lo is written (bf16
  * [T][Nlr], 16-byte aligned, required); rs_out fp32 [T] is nullable. T = 1..16, Khc % 32 == 0,
  * Nlr % 32 == 0, 0 < Nlr <= 1024. Workspace: gq8_workspace_bytes(GQ8_OP_HC_PAIR, T, Nlr, Khc). */
 int gq8_hc_q8_pair(const void* w_down, const uint16_t* R, const uint16_t* w_norm, float eps,
@@ -215,7 +218,7 @@ int gq8_hc_q8_pair(const void* w_down, const uint16_t* R, const uint16_t* w_norm
  * 16-byte aligned; R_out may not overlap R or P. The up read's own epilogue on the page (gate,
  * stream mean) is not defined there and not part of these calls. Shapes, workspace and errors as
  * the calls without the pending write, except that N == 0 returns GQ8_ESHAPE (the write is done
- * by the down read's work-groups); the partial sums are combined by the combine kernel. */
+ * by the down read's work-groups); at T >= 2 the partial sums are combined by the combine kernel. */
 int gq8_hc_q8_down_pending(const void* w_split, const uint16_t* R, const uint16_t* P,
                            const uint16_t* w_norm, float eps, uint16_t* R_out, uint16_t* lo,
                            float* rs_out, int T, int N, int K, void* ws, size_t ws_bytes,

@@ -22,7 +22,7 @@ def _down(gpu, wd, R, wn, T, N, K, ws, nb, stream=None, lo=None, rs=None):
     return lo, rs
 
 
-@pytest.mark.parametrize("T,N,K", [(1, 320, 16384), (4, 320, 16384), (6, 320, 16384), (8, 320, 16384),
+@pytest.mark.parametrize("T,N,K", [(2, 320, 16384), (4, 320, 16384), (6, 320, 16384), (8, 320, 16384),
                                    (3, 70, 1056), (8, 130, 4128), (5, 64, 96)])
 def test_down_last_arriver_is_the_kernel_combine(gpu, monkeypatch, T, N, K):
     d = synth.hc_inputs(T, K=K, N=N, seed=70)
@@ -62,7 +62,7 @@ def test_gemv_last_arriver_is_the_kernel_combine(gpu, monkeypatch, T, N, K):
     check_f32(to_host(y), y_ref, S, f"gemv last-arriver T={T} N={N} K={K}")
 
 
-@pytest.mark.parametrize("T", [1, 4, 6])
+@pytest.mark.parametrize("T", [1, 2, 4, 6])
 def test_pair_last_arriver_is_the_default_pair(gpu, monkeypatch, T):
     Nlr, Khc = 320, 16384
     d = synth.hc_inputs(T, seed=72)

@@ -104,10 +104,12 @@ def test_gemv_repeat_calls_bitwise(gpu):
         assert torch.equal(y0, y1)
 
 
-def test_down_workspace_poison_and_replay(gpu):
+@pytest.mark.parametrize("T", [1, 6])
+def test_down_workspace_poison_and_replay(gpu, T):
     """Every call rewrites every partial sum it reads: poisoning the workspace between calls
-    (NaN bit patterns) changes nothing, and a captured graph replays bitwise."""
-    T, N, K = 6, 320, 16384
+    (NaN bit patterns) changes nothing, and a captured graph replays bitwise (T = 1: the
+    whole-row kernel, which does not touch the workspace)."""
+    N, K = 320, 16384
     d = synth.hc_inputs(T)
     wd = q8_0_from_f32(to_dev(d["w_down"]))
     R, wn = to_dev(d["R"]), to_dev(d["w_norm"])
@@ -193,6 +195,24 @@ def test_down_matches_oracle_small(gpu, T, N, K):
     lo, rs = _down(gpu, q8_0_from_f32(to_dev(d["w_down"])), to_dev(d["R"]), to_dev(d["w_norm"]), T, N, K)
     lo_ref, rs_ref, S = hc_down(d["R"], d["w_norm"], quantize_q8_0(d["w_down"]))
     check_bf16(to_host(lo, np.uint16), lo_ref, S, f"down T={T} N={N} K={K}")
+    assert np.allclose(to_host(rs), rs_ref, rtol=1e-5, atol=0)
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (37, 96), (65, 1056), (320, 16384), (9, 20512), (130, 33792)])
+def test_down_whole_rows(gpu, N, K):
+    """T = 1 runs the whole-row down kernel (a work-group owns two rows and all of K, 1024-column
+    chunks per wave): an odd row count (the last work-group's second row clamped), K below one
+    chunk, a chunk cut short (K % 1024 != 0), and more than sixteen chunks (waves taking a second
+    and third chunk), against the oracle; repeated calls are bitwise equal."""
+    T = 1
+    d = synth.hc_inputs(T, K=K, N=N, seed=21)
+    wd, R, wn = q8_0_from_f32(to_dev(d["w_down"])), to_dev(d["R"]), to_dev(d["w_norm"])
+    lo, rs = _down(gpu, wd, R, wn, T, N, K)
+    lo2, rs2 = _down(gpu, wd, R, wn, T, N, K)
+    torch.cuda.synchronize()
+    assert torch.equal(lo, lo2) and torch.equal(rs, rs2)
+    lo_ref, rs_ref, S = hc_down(d["R"], d["w_norm"], quantize_q8_0(d["w_down"]))
+    check_bf16(to_host(lo, np.uint16), lo_ref, S, f"down rows N={N} K={K}")
     assert np.allclose(to_host(rs), rs_ref, rtol=1e-5, atol=0)
 
 

@@ -40,7 +40,7 @@ def test_noalloc_pair_matches_the_workspace_pair(gpu, first, second):
     _both(gpu, *second, seed=61)
 
 
-@pytest.mark.parametrize("first,second", [((8, 320, 16384), (1, 320, 8192)),
+@pytest.mark.parametrize("first,second", [((8, 320, 16384), (2, 320, 8192)),
                                           ((4, 1024, 4096), (2, 64, 1056))])
 def test_noalloc_pair_last_arriver_after_a_larger_call(gpu, monkeypatch, first, second):
     """With the last-arriver combine the array's arrival counters must be zero before each call:
