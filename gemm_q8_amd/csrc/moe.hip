@@ -565,7 +565,10 @@ __global__ void __launch_bounds__(256) moe_down_kernel(MoeArgs a) {
 }
 
 // Down projection with the combine folded in (F = 64 NL): one work-group per (16 output rows,
-// token t). Wave w takes the token's entries j = w, w + 4, ... (up to two at a time in flight):
+// token t), eight waves. Wave w takes the token's entries j = w, w + 8, ..., one at a time (eight
+// waves of one entry each measured faster than four waves of two: the q8_1(h) option's per-entry
+// quantization spreads over twice the waves, 23.16 -> 22.46 us per call; the default 23.11 ->
+// 23.02 us):
 // the entry's expert tile of 16 rows x F bytes is read straight into MFMA operands -- load i
 // gives lane l the 16 bytes of row l%16 at column 64i + 16(l/16) (Q8_0 block 2i in lanes 0..31,
 // 2i+1 in lanes 32..63), and v_permlane32_swap makes both blocks' operands, so lane (row j,
@@ -587,15 +590,18 @@ constexpr int kMoeMaxTopk = 16;
 // and each block is one v_mfma_i32_16x16x32_i8 of those codes with the weight quants as the
 // loads give them (no conversion); its int32 result times d_w * d_h (exact in fp32) accumulates
 // in fp32.
+constexpr int kMoeDnWaves = 8;
+
 template <int NL, bool HQ>
-__global__ void __launch_bounds__(256) moe_down_token_kernel(MoeArgs a) {
+__global__ void __launch_bounds__(64 * kMoeDnWaves) moe_down_token_kernel(MoeArgs a) {
+    constexpr int NWV = kMoeDnWaves;
     constexpr int NB = 2 * NL;                     // Q8_0 blocks per row
     constexpr int F = 64 * NL;
-    constexpr int EG = NL >= 16 ? 1 : 2;           // entries in flight per wave
+    constexpr int EG = 1;                          // entries in flight per wave
     constexpr int HC = (F / 8 + 63) / 64;          // 8-float pieces of h per lane
-    __shared__ __attribute__((aligned(16))) uint16_t hs[HQ ? 1 : 4][EG][2][HQ ? 8 : F];
-    __shared__ __attribute__((aligned(16))) int8_t hq[HQ ? 4 : 1][EG][HQ ? F : 16];
-    __shared__ uint16_t hdq[HQ ? 4 : 1][EG][HQ ? NB : 1];
+    __shared__ __attribute__((aligned(16))) uint16_t hs[HQ ? 1 : NWV][EG][2][HQ ? 8 : F];
+    __shared__ __attribute__((aligned(16))) int8_t hq[HQ ? NWV : 1][EG][HQ ? F : 16];
+    __shared__ uint16_t hdq[HQ ? NWV : 1][EG][HQ ? NB : 1];
     __shared__ float rr[kMoeMaxTopk][16];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j = lane & 15, g = lane >> 4;
@@ -614,7 +620,7 @@ __global__ void __launch_bounds__(256) moe_down_token_kernel(MoeArgs a) {
     const int ko = 2 * dn_koff(g);                 // byte offset of the lane's k-group in a bf16 row
     const int hl = j < 8 ? 0 : 1;                  // A rows 0..7 hi, 8..15 lo
 
-    for (int j0 = wave; j0 < topk; j0 += 4 * EG) {
+    for (int j0 = wave; j0 < topk; j0 += NWV * EG) {
         int ent[EG];
         bool on[EG];
         float4 hv[EG][HC][2];
@@ -622,7 +628,7 @@ __global__ void __launch_bounds__(256) moe_down_token_kernel(MoeArgs a) {
         v4i wv[EG][NL];
 #pragma unroll
         for (int u = 0; u < EG; ++u) {
-            const int jj = j0 + 4 * u;
+            const int jj = j0 + NWV * u;
             on[u] = jj < topk;
             ent[u] = __builtin_amdgcn_readfirstlane(t * topk + (on[u] ? jj : j0));
             const float4* hp = reinterpret_cast<const float4*>(a.h + (size_t)ent[u] * F);
@@ -734,7 +740,7 @@ __global__ void __launch_bounds__(256) moe_down_token_kernel(MoeArgs a) {
                 }
             }
             // result row 0 (lanes 0..15, v = 0): every A row holds the same codes
-            if (on[u] && lane < 16) rr[j0 + 4 * u][j] = acc0;
+            if (on[u] && lane < 16) rr[j0 + NWV * u][j] = acc0;
         }
 #pragma unroll
         for (int u = 0; u < EG && !HQ; ++u) {
@@ -758,7 +764,7 @@ __global__ void __launch_bounds__(256) moe_down_token_kernel(MoeArgs a) {
             }
             // result row 8 (lanes 32..47, v = 0) holds the lo part: add it to row 0 (lanes 0..15)
             const float tot = acc[0] + lane_xor32f(acc[0]);     // lanes < 32: l + 32
-            if (on[u] && lane < 16) rr[j0 + 4 * u][j] = tot;
+            if (on[u] && lane < 16) rr[j0 + NWV * u][j] = tot;
         }
         // the next round overwrites this wave's hs slot: every lane's reads come first
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -851,13 +857,13 @@ int launch_moe_routed(const int8_t* xq, const uint16_t* xd, const uint16_t* xb, 
     if (token_dn) {                        // down + combine in one kernel
         const dim3 gt((D + 15) / 16, T);
         if (hq) {
-            if (F == 256) hipLaunchKernelGGL((moe_down_token_kernel<4, true>), gt, dim3(256), 0, st, a);
-            else if (F == 512) hipLaunchKernelGGL((moe_down_token_kernel<8, true>), gt, dim3(256), 0, st, a);
-            else hipLaunchKernelGGL((moe_down_token_kernel<16, true>), gt, dim3(256), 0, st, a);
+            if (F == 256) hipLaunchKernelGGL((moe_down_token_kernel<4, true>), gt, dim3(64 * kMoeDnWaves), 0, st, a);
+            else if (F == 512) hipLaunchKernelGGL((moe_down_token_kernel<8, true>), gt, dim3(64 * kMoeDnWaves), 0, st, a);
+            else hipLaunchKernelGGL((moe_down_token_kernel<16, true>), gt, dim3(64 * kMoeDnWaves), 0, st, a);
         } else {
-            if (F == 256) hipLaunchKernelGGL((moe_down_token_kernel<4, false>), gt, dim3(256), 0, st, a);
-            else if (F == 512) hipLaunchKernelGGL((moe_down_token_kernel<8, false>), gt, dim3(256), 0, st, a);
-            else hipLaunchKernelGGL((moe_down_token_kernel<16, false>), gt, dim3(256), 0, st, a);
+            if (F == 256) hipLaunchKernelGGL((moe_down_token_kernel<4, false>), gt, dim3(64 * kMoeDnWaves), 0, st, a);
+            else if (F == 512) hipLaunchKernelGGL((moe_down_token_kernel<8, false>), gt, dim3(64 * kMoeDnWaves), 0, st, a);
+            else hipLaunchKernelGGL((moe_down_token_kernel<16, false>), gt, dim3(64 * kMoeDnWaves), 0, st, a);
         }
         return launch_status();
     }
