@@ -1195,20 +1195,29 @@ constexpr int kPairQuads = kUpCW / 4;       // float4 quads of a 320-wide row
 
 // WB (the BF16 comparison read): bf16 weights [N][320]; lane l loads the 16 bytes of row l%16 at
 // column 32b + 8(l/16) for block b, which is the MFMA B operand as it stands (no scales).
+// Waves of the fused kernel: kPairNup up waves (16 rows each) and kPairNcw combine waves.
+// Measured on MI355X (pair at T = 2 / 3 / 4): 4 + 4 8.74 / 9.28 / 10.02 us; 8 + 4 9.29 / 9.76 /
+// 10.61; 8 + 8 9.71 / 9.96 / 10.81; 12 + 4 10.6 / 12.2 / 16.4. Fewer, larger work-groups halve
+// the partial-sum reads in total but not the combine on each work-group's critical path, and put
+// the weight stream on fewer CUs.
+constexpr int kPairNup = 4;
+constexpr int kPairNcw = 4;
+
 template <int T, bool WB = false>
-__global__ void __launch_bounds__(512) hc_pair_up_kernel(GemvArgs a) {
+__global__ void __launch_bounds__(64 * (kPairNup + kPairNcw)) hc_pair_up_kernel(GemvArgs a) {
     constexpr int NQ = T * kPairQuads;                            // float4 quads of lo
-    constexpr int NIT = (4 * NQ + 255) / 256;                     // (quad, slab group) items per thread
+    constexpr int NTC = 64 * kPairNcw;                            // combine threads
+    constexpr int NIT = (4 * NQ + NTC - 1) / NTC;                 // (quad, slab group) items per thread
     __shared__ __attribute__((aligned(16))) uint8_t xl[kMaxT][kUpLoStride];
     __shared__ float4 red[4][NQ];                                 // slab-group sums
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int N = a.N, K = a.K;                                   // up rows, up depth (== 320)
     const int j = lane & 15, g = lane >> 4;
-    if (wave < 4) {
+    if (wave < kPairNup) {
         // weights and scales of this wave's 16 rows, issued once the combine waves have issued
         // their partial-sum loads (those are few and on the critical path; issued behind the
         // weight stream they wait in the same memory queues), then in flight across the combine
-        const int r0 = (blockIdx.x * 4 + wave) * 16;
+        const int r0 = (blockIdx.x * kPairNup + wave) * 16;
         __syncthreads();                                          // partial-sum loads issued
         const int row = imin(r0 + j, N - 1);
         const u32x4 z = {0u, 0u, 0u, 0u};
@@ -1265,12 +1274,12 @@ __global__ void __launch_bounds__(512) hc_pair_up_kernel(GemvArgs a) {
         }
         return;
     }
-    // combine waves. Item it = ct + 256 m is (quad it % NQ, slab group it / NQ): the group's
+    // combine waves. Item it = ct + NTC m is (quad it % NQ, slab group it / NQ): the group's
     // ceil(S/4) consecutive slabs added in ascending order; every item's loads are issued before
     // the first wait. Then rs[t] from the slab sums of squares (lane-strided, then the wave sum),
     // and lo = bf16(rs * (((g0 + g1) + g2) + g3)) -- hc_down_combine_kernel's order.
     const int S = a.S;
-    const int ct = (int)threadIdx.x - 256;
+    const int ct = (int)threadIdx.x - 64 * kPairNup;
     const int per = (S + 3) / 4;
     const size_t plane = (size_t)T * K / 4;                       // float4s per slab plane
     float4 gs[NIT];
@@ -1279,7 +1288,7 @@ __global__ void __launch_bounds__(512) hc_pair_up_kernel(GemvArgs a) {
         float4 pv[NIT][8];
 #pragma unroll
         for (int m = 0; m < NIT; ++m) {
-            const int it = imin(ct + 256 * m, 4 * NQ - 1);
+            const int it = imin(ct + NTC * m, 4 * NQ - 1);
             const int qd = it % NQ, sg = it / NQ;
             const int t = qd / kPairQuads, n = 4 * (qd - t * kPairQuads);
             const float4* p = reinterpret_cast<const float4*>(a.part + (size_t)t * K + n) + (size_t)8 * sg * plane;
@@ -1303,7 +1312,7 @@ __global__ void __launch_bounds__(512) hc_pair_up_kernel(GemvArgs a) {
         __syncthreads();
 #pragma unroll
         for (int m = 0; m < NIT; ++m) {
-            const int it = imin(ct + 256 * m, 4 * NQ - 1);
+            const int it = imin(ct + NTC * m, 4 * NQ - 1);
             const int qd = it % NQ, sg = it / NQ;
             const int t = qd / kPairQuads, n = 4 * (qd - t * kPairQuads);
             const float4* p = reinterpret_cast<const float4*>(a.part + (size_t)t * K + n);
@@ -1337,7 +1346,7 @@ __global__ void __launch_bounds__(512) hc_pair_up_kernel(GemvArgs a) {
     }
 #pragma unroll
     for (int m = 0; m < NIT; ++m) {
-        const int it = ct + 256 * m;
+        const int it = ct + NTC * m;
         if (it < 4 * NQ) red[it / NQ][it % NQ] = gs[m];
     }
     if (blockIdx.x == 0 && ct < T && a.rs_out != nullptr) {
@@ -1346,7 +1355,7 @@ __global__ void __launch_bounds__(512) hc_pair_up_kernel(GemvArgs a) {
             if (t == ct) a.rs_out[t] = rs[t];
     }
     __syncthreads();
-    for (int qd = ct; qd < NQ; qd += 256) {
+    for (int qd = ct; qd < NQ; qd += NTC) {
         const int t = qd / kPairQuads, n = 4 * (qd - t * kPairQuads);
         float r = rs[0];
 #pragma unroll
@@ -1389,7 +1398,7 @@ static int launch_pair_t(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st) {
         up.S = S; up.part = dn.part; up.ssq = dn.ssq; up.eps = dn.eps; up.kd = dn.K;
         up.rs_out = dn.rs_out; up.lo_out = dn.out;
         const int ntile = (up.N + 15) / 16;
-        hipLaunchKernelGGL((hc_pair_up_kernel<T>), dim3((ntile + 3) / 4), dim3(512), 0, st, up);
+        hipLaunchKernelGGL((hc_pair_up_kernel<T>), dim3((ntile + kPairNup - 1) / kPairNup), dim3(64 * (kPairNup + kPairNcw)), 0, st, up);
         return launch_status();
     }
 }
@@ -1413,7 +1422,7 @@ static int launch_pair_pending_t(GemvArgs dn, GemvArgs up, void* ws, hipStream_t
         up.S = S; up.part = dn.part; up.ssq = dn.ssq; up.eps = dn.eps; up.kd = dn.K;
         up.rs_out = dn.rs_out; up.lo_out = dn.out;
         const int ntile = (up.N + 15) / 16;
-        hipLaunchKernelGGL((hc_pair_up_kernel<T>), dim3((ntile + 3) / 4), dim3(512), 0, st, up);
+        hipLaunchKernelGGL((hc_pair_up_kernel<T>), dim3((ntile + kPairNup - 1) / kPairNup), dim3(64 * (kPairNup + kPairNcw)), 0, st, up);
         return launch_status();
     }
 }
@@ -1446,7 +1455,7 @@ static int launch_bf16_pair_t(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st
         if (up.K == kUpCW) {               // the combine inside the up kernel
             up.S = S; up.part = dn.part; up.ssq = dn.ssq; up.eps = dn.eps; up.kd = dn.K;
             up.rs_out = dn.rs_out; up.lo_out = dn.out;
-            hipLaunchKernelGGL((hc_pair_up_kernel<T, true>), dim3((ntile + 3) / 4), dim3(512), 0, st, up);
+            hipLaunchKernelGGL((hc_pair_up_kernel<T, true>), dim3((ntile + kPairNup - 1) / kPairNup), dim3(64 * (kPairNup + kPairNcw)), 0, st, up);
             return launch_status();
         }
     }
