@@ -515,6 +515,18 @@ def bench_moe(torch, gq8, synth, dev, timed, emit):
         emit({"workload": name + " T=4 E=512 top-8 D=2048 F=512", "unique_experts": U,
               "us_per_call": round(us, 3), "weight_GBps": round(U * (gu_b + dn_b) / us / 1e3, 1)})
 
+    # the down weights in the tiled layout (bitwise the same outputs)
+    adns_t = tiled_down_arenas(torch, gq8, m)
+    for flags, name in ((gq8.MOE_DOWN_TILED, "routed MoE, down weights tiled"),
+                        (gq8.MOE_X_BF16 | gq8.MOE_DOWN_TILED, "routed MoE on the bf16 input, down weights tiled"),
+                        (gq8.MOE_H_Q8_1 | gq8.MOE_DOWN_TILED, "routed MoE, down read on q8_1(h), down weights tiled")):
+        xx, xs = (xb, None) if flags & gq8.MOE_X_BF16 else (xq, xd)
+        us = timed(lambda i: (lambda s, a=agus[i % n], b=adns_t[i % n]: gq8.gq8_moe_q8_0_routed_flags(
+            xx, xs, ids, wts, a, b, out, T, topk, E, D, F, flags, wsp, nb, s)), n, reps=50)
+        emit({"workload": name + " T=4 E=512 top-8 D=2048 F=512", "unique_experts": U,
+              "us_per_call": round(us, 3), "weight_GBps": round(U * (gu_b + dn_b) / us / 1e3, 1)})
+    del adns_t
+
     def two_calls(s, a, b):
         gq8.gq8_q8_1_quantize(xb, T, D, xq, xd, None, s)
         gq8.gq8_moe_q8_0_routed(xq, xd, ids, wts, a, b, out, T, topk, E, D, F, wsp, nb, s)
@@ -657,6 +669,17 @@ def setup_moe(torch, gq8, synth, dev, T=4, E=512, topk=8, D=2048, F=512, n_copie
                 out=torch.empty((T, D), dtype=torch.int16, device=dev))
 
 
+def tiled_down_arenas(torch, gq8, m):
+    """The down arenas of setup_moe in the tiled layout (gq8_q8_0_tile16: same size and expert
+    stride, quants in 1 KiB operand-order tiles), one per rotated copy."""
+    out = []
+    for a in m["adns"]:
+        t = torch.empty_like(a)
+        gq8.gq8_q8_0_tile16(a, m["D"], m["F"], m["E"], t)
+        out.append(t)
+    return out
+
+
 def bench_configs(torch, gq8, synth, dev, stream, hc_dist, reps, with_oracle=True,
                   gemv_ts=(1, 2, 4, 8, 16)):
     """One record per workload shape of the five configurations: median / p90 / mean us per call
@@ -749,7 +772,19 @@ def bench_configs(torch, gq8, synth, dev, stream, hc_dist, reps, with_oracle=Tru
                        {"T": T, "E": E, "topk": topk, "unique_experts": U}, dist,
                        U * (m["gu_b"] + m["dn_b"]), probe.us([U * m["gu_b"], U * m["dn_b"]]), orc,
                        "the whole call (C++ oracle, float64; weights already quantized)"))
-    del m
+    # the same call on the down weights in the tiled layout (bitwise the same output)
+    adns_t = tiled_down_arenas(torch, gq8, m)
+    dist = timed_dist(torch, stream, lambda i: (lambda s, a=m["agus"][i % m["n"]], b=adns_t[i % m["n"]]:
+                                                 gq8.gq8_moe_q8_0_routed_flags(m["xq"], m["xd"], m["ids"], m["wts"], a, b,
+                                                                               m["out"], T, topk, E, D, F, gq8.MOE_DOWN_TILED,
+                                                                               m["ws"], m["nb"], s)),
+                      m["n"], reps)
+    emit(config_record(5, "routed MoE, down weights tiled (gq8_q8_0_tile16): T=4, 512 experts, top-8, "
+                          "gate/up [1024 x 2048], down [2048 x 512]",
+                       {"T": T, "E": E, "topk": topk, "unique_experts": U}, dist,
+                       U * (m["gu_b"] + m["dn_b"]), probe.us([U * m["gu_b"], U * m["dn_b"]]), orc,
+                       "the whole call (C++ oracle, float64; weights already quantized)"))
+    del m, adns_t
     return recs
 
 

@@ -142,6 +142,22 @@ GQ8_EXPORT int gq8_q8_0_split_from_blocks(const void* blocks34, int rows, int K,
     return launch_q8_0_split_from_blocks(blocks34, rows, K, w_split, S(stream));
 }
 
+GQ8_EXPORT int gq8_q8_0_tile16(const void* w_split, int rows, int K, int count, void* w_tiled,
+                               void* stream) {
+    if (rows < 0 || K < 0 || count < 0) return GQ8_EINVAL;
+    if (rows % 16 != 0 || K % 64 != 0) return GQ8_ESHAPE;
+    const uint64_t bytes = (uint64_t)rows * (uint64_t)K / 16 * 17;         // one matrix
+    if (rows != 0 && K != 0 && (uint64_t)count > kMaxItems / (bytes / 16)) return GQ8_ESHAPE;
+    if (rows == 0 || K == 0 || count == 0) return GQ8_OK;
+    if (w_split == nullptr || w_tiled == nullptr) return GQ8_EINVAL;
+    if (!aligned16(w_split) || !aligned16(w_tiled)) return GQ8_EALIGN;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(w_split), b = reinterpret_cast<uintptr_t>(w_tiled);
+    const uint64_t n = bytes * (uint64_t)count;
+    if (a < b + n && b < a + n) return GQ8_EINVAL;                         // overlapping buffers
+    if (device_cus() == 0) return GQ8_ENODEV;
+    return launch_q8_0_tile16(w_split, rows, K, count, w_tiled, S(stream));
+}
+
 GQ8_EXPORT int gq8_q8_1_quantize(const uint16_t* x_bf16, int rows, int K, int8_t* q, uint16_t* d,
                                  uint16_t* s, void* stream) {
     if (rows < 0 || K < 0) return GQ8_EINVAL;
@@ -612,7 +628,7 @@ GQ8_EXPORT int gq8_moe_q8_0_routed(const int8_t* xq, const uint16_t* xd, const i
     if (rc != GQ8_OK) return rc;
     if (device_cus() == 0) return GQ8_ENODEV;
     return launch_moe_routed(xq, xd, nullptr, ids, weights, w_gate_up, w_down, out, T, topk, E, D,
-                             F, false, ws, S(stream));
+                             F, false, false, ws, S(stream));
 }
 
 GQ8_EXPORT int gq8_moe_q8_0_routed_bf16(const uint16_t* x, const int32_t* ids, const float* weights,
@@ -632,7 +648,7 @@ GQ8_EXPORT int gq8_moe_q8_0_routed_bf16(const uint16_t* x, const int32_t* ids, c
     if (rc != GQ8_OK) return rc;
     if (device_cus() == 0) return GQ8_ENODEV;
     return launch_moe_routed(nullptr, nullptr, x, ids, weights, w_gate_up, w_down, out, T, topk, E,
-                             D, F, false, ws, S(stream));
+                             D, F, false, false, ws, S(stream));
 }
 
 GQ8_EXPORT int gq8_moe_q8_0_routed_flags(const void* x, const uint16_t* xd, const int32_t* ids,
@@ -641,11 +657,13 @@ GQ8_EXPORT int gq8_moe_q8_0_routed_flags(const void* x, const uint16_t* xd, cons
                                          int D, int F, int flags, void* ws, size_t ws_bytes,
                                          void* stream) {
     if (T < 0 || topk < 0 || E < 0 || D < 0 || F < 0) return GQ8_EINVAL;
-    if (flags & ~(GQ8_MOE_X_BF16 | GQ8_MOE_H_Q8_1)) return GQ8_EINVAL;
+    if (flags & ~(GQ8_MOE_X_BF16 | GQ8_MOE_H_Q8_1 | GQ8_MOE_DOWN_TILED)) return GQ8_EINVAL;
     if (T == 0) return GQ8_OK;
     const bool xb = (flags & GQ8_MOE_X_BF16) != 0, hq = (flags & GQ8_MOE_H_Q8_1) != 0;
+    const bool tl = (flags & GQ8_MOE_DOWN_TILED) != 0;
     if (T > kMaxT || topk < 1 || (int64_t)T * topk > 256 || E < 1 || D < 32 || D % 32 != 0 || D > kMaxMoeD || F < 32 ||
-        F % 32 != 0 || F > 1024 || (hq && ((F != 256 && F != 512 && F != 1024) || topk > 16)))
+        F % 32 != 0 || F > 1024 || ((hq || tl) && ((F != 256 && F != 512 && F != 1024) || topk > 16)) ||
+        (tl && D % 16 != 0))
         return GQ8_ESHAPE;
     if (x == nullptr || (!xb && xd == nullptr) || ids == nullptr || weights == nullptr ||
         w_gate_up == nullptr || w_down == nullptr || out == nullptr)
@@ -656,7 +674,7 @@ GQ8_EXPORT int gq8_moe_q8_0_routed_flags(const void* x, const uint16_t* xd, cons
     if (device_cus() == 0) return GQ8_ENODEV;
     return launch_moe_routed(xb ? nullptr : static_cast<const int8_t*>(x), xb ? nullptr : xd,
                              xb ? static_cast<const uint16_t*>(x) : nullptr, ids, weights,
-                             w_gate_up, w_down, out, T, topk, E, D, F, hq, ws, S(stream));
+                             w_gate_up, w_down, out, T, topk, E, D, F, hq, tl, ws, S(stream));
 }
 
 // ---------------------------------------------------------------------------------- probe

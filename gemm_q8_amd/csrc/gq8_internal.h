@@ -129,6 +129,7 @@ int launch_q8_0_split_from_blocks(const void* b34, int rows, int K, void* w_spli
 int launch_q8_1_quantize(const uint16_t* x, int rows, int K, int8_t* q, uint16_t* d, uint16_t* s,
                          hipStream_t st);
 int launch_w8a8_pack(const int8_t* W, int K, int N, int8_t* Wp, hipStream_t st);
+int launch_q8_0_tile16(const void* w_split, int rows, int K, int count, void* w_tiled, hipStream_t st);
 int launch_read_probe(const void* src, size_t bytes, float* sink, hipStream_t st);
 int launch_read_probe_ex(const void* src, size_t bytes, float* sink, int lpt, int threads,
                          int work_groups, bool nt, hipStream_t st);
@@ -142,8 +143,10 @@ int launch_moe_plan(const int32_t* ids, int T, int topk, int E, int32_t* plan, h
 size_t moe_workspace_bytes(int T, int topk, int D, int F);
 // xb != nullptr: bf16 input quantized to q8_1 on the device (xq, xd unused); hq: the down read
 // takes q8_1(h) (F in {256, 512, 1024}, else GQ8_ESHAPE)
+// tl: the down weights are in the tiled layout (launch_q8_0_tile16; D % 16 == 0, F in {256, 512,
+// 1024}, topk <= 16: the token kernel reads them, whatever GQ8_FORCE_GENERIC says)
 int launch_moe_routed(const int8_t* xq, const uint16_t* xd, const uint16_t* xb, const int32_t* ids,
                       const float* w, const void* wgu, const void* wdn, uint16_t* out, int T,
-                      int topk, int E, int D, int F, bool hq, void* ws, hipStream_t st);
+                      int topk, int E, int D, int F, bool hq, bool tl, void* ws, hipStream_t st);
 
 }  // namespace gq8

@@ -592,7 +592,7 @@ constexpr int kMoeMaxTopk = 16;
 // in fp32.
 constexpr int kMoeDnWaves = 8;
 
-template <int NL, bool HQ>
+template <int NL, bool HQ, bool TL = false>
 __global__ void __launch_bounds__(64 * kMoeDnWaves) moe_down_token_kernel(MoeArgs a) {
     constexpr int NWV = kMoeDnWaves;
     constexpr int NB = 2 * NL;                     // Q8_0 blocks per row
@@ -663,9 +663,13 @@ __global__ void __launch_bounds__(64 * kMoeDnWaves) moe_down_token_kernel(MoeArg
                 const u32x4 s4 = *reinterpret_cast<const u32x4*>(dp + i);
                 sc[u][i] = s4.x; sc[u][i + 1] = s4.y; sc[u][i + 2] = s4.z; sc[u][i + 3] = s4.w;
             }
-            const int8_t* wp = q + (size_t)row * F + 16 * g;
+            // split layout: 64-byte pieces of 16 rows; tiled layout: the same 16 bytes a lane,
+            // stored as one contiguous 1 KiB tile per load (row group blockIdx.x, column group i)
+            const int8_t* wp = TL ? q + (size_t)blockIdx.x * (NL * 1024) + 16 * lane
+                                  : q + (size_t)row * F + 16 * g;
 #pragma unroll
-            for (int i = 0; i < NL; ++i) wv[u][i] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wp + 64 * i));
+            for (int i = 0; i < NL; ++i)
+                wv[u][i] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wp + (TL ? 1024 : 64) * i));
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -801,10 +805,18 @@ size_t moe_workspace_bytes(int T, int topk, int D, int F) {
            round_up((size_t)T * D, kCounterAlign) + round_up((size_t)T * (D / 32) * sizeof(uint16_t), kCounterAlign);
 }
 
+template <int NL, bool HQ>
+static void launch_down_token(const MoeArgs& a, bool tl, hipStream_t st) {
+    const dim3 gt((a.D + 15) / 16, a.T);
+    if (tl) hipLaunchKernelGGL((moe_down_token_kernel<NL, HQ, true>), gt, dim3(64 * kMoeDnWaves), 0, st, a);
+    else hipLaunchKernelGGL((moe_down_token_kernel<NL, HQ, false>), gt, dim3(64 * kMoeDnWaves), 0, st, a);
+}
+
 int launch_moe_routed(const int8_t* xq, const uint16_t* xd, const uint16_t* xb, const int32_t* ids,
                       const float* w, const void* wgu, const void* wdn, uint16_t* out, int T,
-                      int topk, int E, int D, int F, bool hq, void* ws, hipStream_t st) {
-    if (hq && ((F != 256 && F != 512 && F != 1024) || topk > kMoeMaxTopk)) return GQ8_ESHAPE;
+                      int topk, int E, int D, int F, bool hq, bool tl, void* ws, hipStream_t st) {
+    if ((hq || tl) && ((F != 256 && F != 512 && F != 1024) || topk > kMoeMaxTopk)) return GQ8_ESHAPE;
+    if (tl && D % 16 != 0) return GQ8_ESHAPE;
     MoeArgs a{};
     a.xq = xq; a.xd = xd; a.xb = xb; a.w = w;
     a.wgu = static_cast<const int8_t*>(wgu);
@@ -833,9 +845,10 @@ int launch_moe_routed(const int8_t* xq, const uint16_t* xd, const uint16_t* xb, 
     }
     // the plan is needed only by the fallback kernels (D > 4096 gate/up; F outside
     // {256, 512, 1024} down)
-    // (the q8_1(h) down read exists only as the token kernel: the switch leaves it there)
+    // (the q8_1(h) down read and the tiled down weights exist only as the token kernel: the switch
+    // leaves them there)
     // (the token kernel keeps one result row per slot in LDS: at most kMoeMaxTopk slots)
-    const bool token_dn = (F == 256 || F == 512 || F == 1024) && topk <= kMoeMaxTopk && (!general || hq);
+    const bool token_dn = (F == 256 || F == 512 || F == 1024) && topk <= kMoeMaxTopk && (!general || hq || tl);
     if (!rows_gu || !token_dn) {
         GQ8_NOTE_GENERAL("routed experts: plan-based general kernels: D > 4096, F not in {256, 512, 1024}, or forced");
         hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(256), 0, st, ids, a.P, E, plan);
@@ -855,15 +868,14 @@ int launch_moe_routed(const int8_t* xq, const uint16_t* xd, const uint16_t* xb, 
     else hipLaunchKernelGGL((moe_gate_up_rows_kernel<4, false>), ggu, dim3(256), 0, st, a);
     if ((rc = launch_status()) != GQ8_OK) return rc;
     if (token_dn) {                        // down + combine in one kernel
-        const dim3 gt((D + 15) / 16, T);
         if (hq) {
-            if (F == 256) hipLaunchKernelGGL((moe_down_token_kernel<4, true>), gt, dim3(64 * kMoeDnWaves), 0, st, a);
-            else if (F == 512) hipLaunchKernelGGL((moe_down_token_kernel<8, true>), gt, dim3(64 * kMoeDnWaves), 0, st, a);
-            else hipLaunchKernelGGL((moe_down_token_kernel<16, true>), gt, dim3(64 * kMoeDnWaves), 0, st, a);
+            if (F == 256) launch_down_token<4, true>(a, tl, st);
+            else if (F == 512) launch_down_token<8, true>(a, tl, st);
+            else launch_down_token<16, true>(a, tl, st);
         } else {
-            if (F == 256) hipLaunchKernelGGL((moe_down_token_kernel<4, false>), gt, dim3(64 * kMoeDnWaves), 0, st, a);
-            else if (F == 512) hipLaunchKernelGGL((moe_down_token_kernel<8, false>), gt, dim3(64 * kMoeDnWaves), 0, st, a);
-            else hipLaunchKernelGGL((moe_down_token_kernel<16, false>), gt, dim3(64 * kMoeDnWaves), 0, st, a);
+            if (F == 256) launch_down_token<4, false>(a, tl, st);
+            else if (F == 512) launch_down_token<8, false>(a, tl, st);
+            else launch_down_token<16, false>(a, tl, st);
         }
         return launch_status();
     }

@@ -161,6 +161,40 @@ int launch_w8a8_pack(const int8_t* W, int K, int N, int8_t* Wp, hipStream_t st) 
     return launch_status();
 }
 
+// ------------------------------------------------------------------------ Q8_0 tiled layout
+// Split layout -> tiled layout, matrix by matrix (count matrices back to back, each
+// mat_bytes = rows * K + rows * K / 16 bytes). Each matrix keeps its size and its scales; its
+// quants are reordered into 1 KiB tiles, one per (16-row group G, 64-column group c), tile (G, c)
+// at byte (G * K / 64 + c) * 1024, whose 16-byte piece l is row 16 G + l % 16, columns
+// 64 c + 16 (l / 16) .. + 16. One work-item per 16-byte piece.
+__global__ void q8_0_tile16_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                   int K, size_t qunits, size_t units, size_t total) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const size_t m = i / units, u = i - m * units;
+    const size_t base = m * units * 16;
+    size_t from = base + u * 16;                                // scales: in place
+    if (u < qunits) {
+        const size_t t = u >> 6;
+        const int l = (int)(u & 63);
+        const size_t cg = (size_t)K / 64;
+        const size_t G = t / cg, c = t - G * cg;
+        from = base + (16 * G + (l & 15)) * (size_t)K + 64 * c + 16 * (l >> 4);
+    }
+    *reinterpret_cast<uint4*>(dst + base + u * 16) = *reinterpret_cast<const uint4*>(src + from);
+}
+
+int launch_q8_0_tile16(const void* w_split, int rows, int K, int count, void* w_tiled, hipStream_t st) {
+    const size_t qunits = (size_t)rows * K / 16;
+    const size_t units = qunits + (size_t)rows * (K / 32) * 2 / 16;
+    const size_t total = units * (size_t)count;
+    if (total == 0) return GQ8_OK;
+    hipLaunchKernelGGL(q8_0_tile16_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                       static_cast<const uint8_t*>(w_split), static_cast<uint8_t*>(w_tiled), K,
+                       qunits, units, total);
+    return launch_status();
+}
+
 // -------------------------------------------------------------------------------- read probe
 // A plain stream of 16-byte loads: lane l of a work-group of NT threads takes pieces
 // c * NT * LPT + j * NT + l (j < LPT) of chunk c, so each load instruction covers NT * 16

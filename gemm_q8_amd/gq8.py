@@ -22,7 +22,7 @@ LIB_PATH = _LIB_PATH
 
 OK, EINVAL, ESHAPE, EALIGN, EWORKSPACE, ECAPTURE, EHIP, ENODEV = 0, -1, -2, -3, -4, -5, -6, -7
 NOALLOC_SCRATCH_BYTES = 4 << 20
-MOE_X_BF16, MOE_H_Q8_1 = 1, 2
+MOE_X_BF16, MOE_H_Q8_1, MOE_DOWN_TILED = 1, 2, 4
 OP_Q8_0_GEMV, OP_HC_DOWN, OP_HC_UP, OP_W8A8, OP_HC_PAIR, OP_W8A8_BF16X = 1, 2, 3, 4, 5, 6
 
 _P = ctypes.c_void_p
@@ -39,6 +39,7 @@ _SIGS = {
     "gq8_q8_0_bytes": (_SZ, [_I64, _I64]),
     "gq8_q8_0_quantize": (_I, [_P, _I, _I, _P, _P]),
     "gq8_q8_0_split_from_blocks": (_I, [_P, _I, _I, _P, _P]),
+    "gq8_q8_0_tile16": (_I, [_P, _I, _I, _I, _P, _P]),
     "gq8_q8_1_quantize": (_I, [_P, _I, _I, _P, _P, _P, _P]),
     "gq8_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "gq8_workspace_counter_bytes": (_SZ, [_I, _I, _I, _I]),
@@ -154,6 +155,11 @@ def gq8_q8_0_quantize(w, rows, K, w_split, stream=None):
 def gq8_q8_0_split_from_blocks(blocks34, rows, K, w_split, stream=None):
     return _check("gq8_q8_0_split_from_blocks",
                   _lib.gq8_q8_0_split_from_blocks(_dev(blocks34), rows, K, _dev(w_split), _stream(stream)))
+
+
+def gq8_q8_0_tile16(w_split, rows, K, count, w_tiled, stream=None):
+    return _check("gq8_q8_0_tile16",
+                  _lib.gq8_q8_0_tile16(_dev(w_split), rows, K, count, _dev(w_tiled), _stream(stream)))
 
 
 def gq8_q8_1_quantize(x_bf16, rows, K, q, d, s, stream=None):

@@ -98,6 +98,20 @@ int gq8_q8_0_quantize(const float* w, int rows, int K, void* w_split, void* stre
  * split layout: the same bytes, reordered (HC-Q8 page, "What changed"). */
 int gq8_q8_0_split_from_blocks(const void* blocks34, int rows, int K, void* w_split, void* stream);
 
+/* Tiled layout, for the routed down weights (gq8_moe_q8_0_routed_flags, GQ8_MOE_DOWN_TILED):
+ * `count` split-layout matrices [rows][K] stored back to back (each gq8_q8_0_bytes(rows, K)
+ * bytes, e.g. an expert arena) are copied to w_tiled, each matrix at the same offset and of the
+ * same size, with its scales unchanged and its quants reordered into 1 KiB tiles: tile (G, c)
+ * of row group G (16 rows) and column group c (64 columns) sits at byte (G * K/64 + c) * 1024,
+ * and its 16-byte piece l (l < 64) is row 16G + l%16, columns 64c + 16(l/16) .. +16. These are
+ * the 16 bytes that lane l of the routed down read's MFMA tile takes for that row and column
+ * group, so a tile is one contiguous 1 KiB load instead of sixteen 64-byte row pieces. Weight
+ * preparation, not a hot-path call (the layout is a choice for MI355X; the pages' blocks hold
+ * the same bytes). rows % 16 == 0, K % 64 == 0 (else GQ8_ESHAPE); both buffers 16-byte
+ * aligned (GQ8_EALIGN) and not overlapping (GQ8_EINVAL); count == 0, rows == 0 or K == 0: no
+ * work. */
+int gq8_q8_0_tile16(const void* w_split, int rows, int K, int count, void* w_tiled, void* stream);
+
 /* q8_1 quantization of bf16 rows x[rows][K] (EP page, "What changed": the q8_1 MoE input).
  * Per 32-block, the Q8_0 rule above plus s = fp16(d * sum(q)).
  * Outputs: q int8 [rows][K], d fp16 [rows][K/32], s fp16 [rows][K/32] (s may be null). */
@@ -369,10 +383,15 @@ int gq8_moe_q8_0_routed_bf16(const uint16_t* x, const int32_t* ids, const float*
  *                   A different, slightly less exact read than the default (h in fp32), within
  *                   the same pass rule of the oracle's variant. Needs F in {256, 512, 1024} and
  *                   topk <= 16, else GQ8_ESHAPE.
+ *   GQ8_MOE_DOWN_TILED  w_down holds the experts' down weights in the tiled layout
+ *                   (gq8_q8_0_tile16 with rows = D, K = F, count = E; same size and expert
+ *                   stride as the split layout). The results are bitwise those on the split
+ *                   layout; the read is faster (contiguous 1 KiB loads). Needs F in
+ *                   {256, 512, 1024}, topk <= 16 and D % 16 == 0, else GQ8_ESHAPE.
  * Other flag bits: GQ8_EINVAL. Shapes, weights, workspace and errors otherwise as
  * gq8_moe_q8_0_routed; flags = 0 is gq8_moe_q8_0_routed and GQ8_MOE_X_BF16 alone is
  * gq8_moe_q8_0_routed_bf16, bit for bit. */
-enum { GQ8_MOE_X_BF16 = 1, GQ8_MOE_H_Q8_1 = 2 };
+enum { GQ8_MOE_X_BF16 = 1, GQ8_MOE_H_Q8_1 = 2, GQ8_MOE_DOWN_TILED = 4 };
 int gq8_moe_q8_0_routed_flags(const void* x, const uint16_t* xd, const int32_t* ids,
                               const float* weights, const void* w_gate_up, const void* w_down,
                               uint16_t* out, int T, int topk, int E, int D, int F, int flags,

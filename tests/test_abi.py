@@ -171,10 +171,18 @@ def test_moe_bf16_input_argument_checks(lib):
 def test_moe_flags_argument_checks(lib):
     raw = lib.raw()
     dummy = 1 << 20  # never dereferenced
-    assert lib.MOE_X_BF16 == 1 and lib.MOE_H_Q8_1 == 2
+    assert lib.MOE_X_BF16 == 1 and lib.MOE_H_Q8_1 == 2 and lib.MOE_DOWN_TILED == 4
     # unknown flag bits
     assert raw.gq8_moe_q8_0_routed_flags(dummy, dummy, dummy, dummy, dummy, dummy, dummy,
-                                         4, 8, 512, 2048, 512, 4, None, 0, None) == lib.EINVAL
+                                         4, 8, 512, 2048, 512, 8, None, 0, None) == lib.EINVAL
+    # tiled down weights: the token kernel's shapes only (F in {256, 512, 1024}, topk <= 16)
+    for flags in (lib.MOE_DOWN_TILED, lib.MOE_DOWN_TILED | lib.MOE_H_Q8_1 | lib.MOE_X_BF16):
+        assert raw.gq8_moe_q8_0_routed_flags(dummy, dummy, dummy, dummy, dummy, dummy, dummy,
+                                             4, 8, 512, 2048, 320, flags, None, 0, None) == lib.ESHAPE
+        assert raw.gq8_moe_q8_0_routed_flags(dummy, dummy, dummy, dummy, dummy, dummy, dummy,
+                                             1, 17, 512, 2048, 512, flags, None, 0, None) == lib.ESHAPE
+        assert raw.gq8_moe_q8_0_routed_flags(dummy, dummy, dummy, dummy, dummy, dummy, dummy,
+                                             4, 8, 512, 2048, 512, flags, None, 0, None) == lib.EWORKSPACE
     # q8_1(h) needs F in {256, 512, 1024}
     assert raw.gq8_moe_q8_0_routed_flags(dummy, dummy, dummy, dummy, dummy, dummy, dummy,
                                          4, 8, 512, 2048, 96, lib.MOE_H_Q8_1, None, 0, None) == lib.ESHAPE
@@ -186,6 +194,26 @@ def test_moe_flags_argument_checks(lib):
                                          4, 8, 512, 2048, 512, 0, None, 0, None) == lib.EINVAL
     assert raw.gq8_moe_q8_0_routed_flags(dummy, None, dummy, dummy, dummy, dummy, dummy,
                                          4, 8, 512, 2048, 512, lib.MOE_X_BF16, None, 0, None) == lib.EWORKSPACE
+
+
+def test_tile16_argument_checks(lib):
+    """gq8_q8_0_tile16 refuses shapes that are not whole tiles, misaligned or overlapping buffers
+    and null pointers before any device work; empty inputs are no work."""
+    raw = lib.raw()
+    a, b = 1 << 20, 1 << 24          # never dereferenced
+    assert raw.gq8_q8_0_tile16(a, -16, 64, 1, b, None) == lib.EINVAL
+    assert raw.gq8_q8_0_tile16(a, 16, 64, -1, b, None) == lib.EINVAL
+    assert raw.gq8_q8_0_tile16(a, 24, 64, 1, b, None) == lib.ESHAPE        # rows % 16
+    assert raw.gq8_q8_0_tile16(a, 16, 96, 1, b, None) == lib.ESHAPE        # K % 64
+    assert raw.gq8_q8_0_tile16(a, 16, 64, 1 << 30, b, None) == lib.ESHAPE  # too many pieces
+    assert raw.gq8_q8_0_tile16(None, 16, 64, 0, None, None) == lib.OK
+    assert raw.gq8_q8_0_tile16(None, 0, 64, 5, None, None) == lib.OK
+    assert raw.gq8_q8_0_tile16(None, 16, 64, 1, b, None) == lib.EINVAL
+    assert raw.gq8_q8_0_tile16(a + 8, 16, 64, 1, b, None) == lib.EALIGN
+    # one matrix of 16 x 64 is 1088 bytes: buffers 1088 bytes apart do not overlap, closer do
+    assert raw.gq8_q8_0_tile16(a, 16, 64, 1, a + 1072, None) == lib.EINVAL
+    assert raw.gq8_q8_0_tile16(a + 1072, 16, 64, 1, a, None) == lib.EINVAL
+    assert raw.gq8_q8_0_tile16(a, 16, 64, 2, a + 1088, None) == lib.EINVAL
 
 
 def test_per_token_argument_checks(lib):

@@ -280,6 +280,54 @@ def test_moe_flags(gpu, T, E, topk, D, F):
     assert not torch.equal(o[2], out)                           # a different read
 
 
+def _tile16_ref(split, rows, K, count):
+    """The tiled layout by index arithmetic: per matrix, quants [rows][K] as 1 KiB tiles (row
+    group G, column group c), piece l of a tile = row 16G + l%16, columns 64c + 16(l/16)..+16;
+    scales unchanged."""
+    mb = rows * K + rows * K // 16
+    out = np.empty_like(split)
+    for m in range(count):
+        q = split[m * mb:m * mb + rows * K].reshape(rows // 16, 16, K // 64, 4, 16)
+        out[m * mb:m * mb + rows * K] = q.transpose(0, 2, 3, 1, 4).reshape(-1)
+        out[m * mb + rows * K:(m + 1) * mb] = split[m * mb + rows * K:(m + 1) * mb]
+    return out
+
+
+@pytest.mark.parametrize("rows,K,count", [(16, 64, 1), (32, 128, 3), (2048, 512, 2), (48, 1024, 2)])
+def test_tile16_layout(gpu, rows, K, count):
+    """gq8_q8_0_tile16 against the layout's definition written as index arithmetic, on random
+    bytes (every byte distinct in position, so a misplaced piece shows)."""
+    n = count * gpu.gq8_q8_0_bytes(rows, K)
+    split = np.random.default_rng(rows + K + count).integers(0, 256, n, dtype=np.uint8)
+    tiled = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")
+    gpu.gq8_q8_0_tile16(to_dev(split), rows, K, count, tiled)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(tiled), _tile16_ref(split, rows, K, count))
+
+
+@pytest.mark.parametrize("T,E,topk,D,F", [(4, 512, 8, 2048, 512), (3, 20, 4, 544, 256),
+                                          (5, 12, 3, 1056, 1024), (16, 40, 16, 160, 512)])
+def test_moe_down_tiled_is_the_split_read(gpu, T, E, topk, D, F):
+    """GQ8_MOE_DOWN_TILED with the down arena tiled by gq8_q8_0_tile16: bitwise the output of the
+    same call on the split-layout arena, for every combination of the other flags."""
+    seed = 49
+    out, (xq, xd, ids, w, agu, adn, ws, nb) = _moe_case(gpu, T, E, topk, D, F, seed=seed)
+    xb = to_dev(synth.moe_inputs(T=T, E=E, D=D, seed=seed)["x"])
+    adn_t = torch.empty_like(adn)
+    gpu.gq8_q8_0_tile16(adn, D, F, E, adn_t)
+    for flags in (0, gpu.MOE_X_BF16, gpu.MOE_H_Q8_1, gpu.MOE_X_BF16 | gpu.MOE_H_Q8_1):
+        xx, xs = (xb, None) if flags & gpu.MOE_X_BF16 else (xq, xd)
+        o_s = torch.full_like(out, 0x5555)
+        o_t = torch.full_like(out, 0x2222)
+        gpu.gq8_moe_q8_0_routed_flags(xx, xs, ids, w, agu, adn, o_s, T, topk, E, D, F, flags, ws, nb)
+        gpu.gq8_moe_q8_0_routed_flags(xx, xs, ids, w, agu, adn_t, o_t, T, topk, E, D, F,
+                                      flags | gpu.MOE_DOWN_TILED, ws, nb)
+        torch.cuda.synchronize()
+        assert torch.equal(o_t, o_s), f"flags={flags}"
+        if flags in (0, gpu.MOE_X_BF16):
+            assert torch.equal(o_t, out), f"flags={flags}"
+
+
 @pytest.mark.parametrize("bad", [8, -1, 1 << 30])
 @pytest.mark.parametrize("D,F", [(64, 256), (96, 64)])
 @pytest.mark.parametrize("general", [False, True])
@@ -298,8 +346,8 @@ def test_moe_invalid_id_writes_zeros(gpu, monkeypatch, bad, D, F, general):
     xd = to_dev(np.full((T, D // 32), 0x2000, np.uint16))
     nb = gpu.gq8_moe_workspace_bytes(T, topk, D, F)
     ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
-    for flags in (0, gpu.MOE_X_BF16, gpu.MOE_H_Q8_1, gpu.MOE_X_BF16 | gpu.MOE_H_Q8_1):
-        if (flags & gpu.MOE_H_Q8_1) and F not in (256, 512, 1024):
+    for flags in range(8):           # every combination of X_BF16, H_Q8_1 and DOWN_TILED
+        if (flags & (gpu.MOE_H_Q8_1 | gpu.MOE_DOWN_TILED)) and F not in (256, 512, 1024):
             continue
         out = torch.full((T, D), 0x5555, dtype=torch.int16, device="cuda")
         xx, xs = (x, None) if flags & gpu.MOE_X_BF16 else (xq, xd)
