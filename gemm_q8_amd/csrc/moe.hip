@@ -360,6 +360,7 @@ template <int NCH, bool XB>
 __global__ void __launch_bounds__(256) moe_gate_up_rows_kernel(MoeArgs a) {
     __shared__ __attribute__((aligned(16))) int8_t xq_s[XB ? 1024 * NCH : 16];   // q8_1 of the row
     __shared__ uint16_t xd_s[XB ? 32 * NCH : 1];
+    __shared__ uint32_t scs[4][64 * NCH];      // per wave: its gate rows' scales, then its up rows'
     const int i0 = blockIdx.y;
     const EntrySet es = entry_set(a.ids, a.P, a.E, i0);
     if (!es.ok || entry_first(es) != i0) return;
@@ -370,6 +371,20 @@ __global__ void __launch_bounds__(256) moe_gate_up_rows_kernel(MoeArgs a) {
     const int pr0 = (blockIdx.x * 4 + wave) * kGuRpw;
     const int nblk = D >> 5;
 
+    // block scales: the wave's two gate rows (pr0, pr0 + 1, even pr0 < F - 1 since F % 8 == 0)
+    // are one run of nblk dwords, its two up rows another; lane l loads dwords l, l + 64, ... of
+    // the two runs (NCH loads a lane instead of one 2-byte load per row and chunk: the weight
+    // loads wait behind far fewer instructions), ahead of the weights
+    static_assert(kGuRpw == 2, "two rows a wave: one dword run per gate or up row pair");
+    const uint32_t* d32 = reinterpret_cast<const uint32_t*>(d);
+    const size_t g0 = (size_t)pr0 * nblk / 2, u0 = (size_t)(F + pr0) * nblk / 2;
+    uint32_t sv[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int idx = lane + 64 * i;
+        const int ic = idx < 2 * nblk ? idx : 2 * nblk - 1;
+        sv[i] = __builtin_nontemporal_load(d32 + (ic < nblk ? g0 + ic : u0 + (ic - nblk)));
+    }
     v4i qg[kGuRpw][NCH], qu[kGuRpw][NCH];
     uint16_t dg[kGuRpw][NCH], du[kGuRpw][NCH];
 #pragma unroll
@@ -378,11 +393,29 @@ __global__ void __launch_bounds__(256) moe_gate_up_rows_kernel(MoeArgs a) {
         const int kc = k < D ? k : D - 16;
 #pragma unroll
         for (int r = 0; r < kGuRpw; ++r) {
-            const int n = pr0 + r < F ? pr0 + r : F - 1;
+            const int n = pr0 + r;
             qg[r][j] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(q + (size_t)n * D + kc));
             qu[r][j] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(q + (size_t)(F + n) * D + kc));
-            dg[r][j] = d[(size_t)n * nblk + (kc >> 5)];
-            du[r][j] = d[(size_t)(F + n) * nblk + (kc >> 5)];
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+        if (lane + 64 * i < 2 * nblk) scs[wave][lane + 64 * i] = sv[i];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    {
+        const uint16_t* sc16 = reinterpret_cast<const uint16_t*>(scs[wave]);
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const int k = j * 1024 + lane * 16;
+            const int b = (k < D ? k : D - 16) >> 5;
+#pragma unroll
+            for (int r = 0; r < kGuRpw; ++r) {
+                dg[r][j] = sc16[r * nblk + b];
+                du[r][j] = sc16[(2 + r) * nblk + b];
+            }
         }
     }
     int first_w = 0;                                    // the word holding the first entry
@@ -817,6 +850,7 @@ int launch_moe_routed(const int8_t* xq, const uint16_t* xd, const uint16_t* xb, 
                       int topk, int E, int D, int F, bool hq, bool tl, void* ws, hipStream_t st) {
     if ((hq || tl) && ((F != 256 && F != 512 && F != 1024) || topk > kMoeMaxTopk)) return GQ8_ESHAPE;
     if (tl && D % 16 != 0) return GQ8_ESHAPE;
+    if (F % 8 != 0) return GQ8_ESHAPE;     // the gate/up rows kernel's waves take whole row pairs
     MoeArgs a{};
     a.xq = xq; a.xd = xd; a.xb = xb; a.w = w;
     a.wgu = static_cast<const int8_t*>(wgu);
