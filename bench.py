@@ -199,6 +199,15 @@ def hc_pair_fn(gq8, h, T, i):
                                         T, N_LR, K_HC, p["wsd"], p["nbd"], s)
 
 
+def hc_pair_tiled_fn(gq8, h, wus_t, T, i):
+    """The pair call with the up weights in the tiled layout (gq8_q8_0_tile16 copies of h's)."""
+    p = h["per_t"][T]
+    wd = h["wds"][i % h["n_sets"]]
+    wu = wus_t[i % h["n_sets"]]
+    return lambda s: gq8.gq8_hc_q8_pair_tiled(wd, p["R"], p["wn"], 1e-6, wu, p["lo"], p["rs"],
+                                              p["out"], T, N_LR, K_HC, p["wsd"], p["nbd"], s)
+
+
 def hc_step_fns(gq8, h):
     def fns(step):
         return [hc_pair_fn(gq8, h, T, step * len(TS) + j) for j, T in enumerate(TS)]
@@ -680,7 +689,7 @@ def tiled_down_arenas(torch, gq8, m):
     return out
 
 
-def bench_configs(torch, gq8, synth, dev, stream, hc_dist, reps, with_oracle=True,
+def bench_configs(torch, gq8, synth, dev, stream, hc_dist, reps, hc_dist_tiled=None, with_oracle=True,
                   gemv_ts=(1, 2, 4, 8, 16)):
     """One record per workload shape of the five configurations: median / p90 / mean us per call
     (graphs of back-to-back calls over rotated weight copies, inputs in HBM), weight GB/s, the
@@ -732,6 +741,11 @@ def bench_configs(torch, gq8, synth, dev, stream, hc_dist, reps, with_oracle=Tru
         emit(config_record(2, "HC pair: RMSNorm + Q8_0 down [320 x 16384], Q8_0 up [16384 x 320]",
                            {"T": T}, hc_dist[T], pair_w, probe.us([pair_w // 2, pair_w // 2]), orc,
                            "the whole call: down then up read (C++ oracle, float64)"))
+    for T in sorted(hc_dist_tiled or {}):
+        emit(config_record(2, "HC pair, up weights tiled (gq8_hc_q8_pair_tiled): RMSNorm + Q8_0 down "
+                              "[320 x 16384], Q8_0 up [16384 x 320]",
+                           {"T": T}, hc_dist_tiled[T], pair_w, probe.us([pair_w // 2, pair_w // 2]), None,
+                           ""))
 
     # 3 and 4: W8A8
     for cfg, (M, N, K) in [(3, (16, 1536, 4096))] + [(4, (m, 2560, 4096)) for m in (1, 4, 8, 16, 32)] + \
@@ -883,6 +897,18 @@ def main():
         g = GraphSteps(torch, stream, lambda i, T=T: [hc_pair_fn(gq8, h, T, 0)], n)
         g.run(n)
         hot[f"T{T}"] = round(time_region(torch, stream, lambda: g.run(n * reps)) / (n * reps) * 1e6, 3)
+    # the same pair with the up weights tiled (gq8_q8_0_tile16): a configuration record of its own
+    hc_dist_tiled = {}
+    if not args.no_configs:
+        wus_t = []
+        for w in h["wus"]:
+            wt = torch.empty_like(w)
+            gq8.gq8_q8_0_tile16(w, K_HC, N_LR, 1, wt)
+            wus_t.append(wt)
+        for T in TS:
+            hc_dist_tiled[T] = timed_dist(torch, stream,
+                                          lambda i, T=T: hc_pair_tiled_fn(gq8, h, wus_t, T, i), n, reps)
+        del wus_t
     dom = "pair"
     # the roofline unit is the pair call, timed over the timed region itself: K steps of one
     # call per T, so the average call is t / (K * len(TS)) and its algorithmic bytes are the mean
@@ -961,7 +987,7 @@ def main():
         },
     }
     if not args.no_configs:
-        result["configs"] = bench_configs(torch, gq8, synth, dev, stream, hc_dist, reps,
+        result["configs"] = bench_configs(torch, gq8, synth, dev, stream, hc_dist, reps, hc_dist_tiled,
                                           with_oracle=not args.no_cpu_baseline,
                                           gemv_ts=[int(t) for t in args.gemv_ts.split(",")])
     if not args.no_cpu_baseline:

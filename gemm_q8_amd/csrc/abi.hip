@@ -295,34 +295,47 @@ GQ8_EXPORT int gq8_hc_q8_down(const void* w_split, const uint16_t* R, const uint
     return launch_hc_down(a, ws, S(stream));
 }
 
-GQ8_EXPORT int gq8_hc_q8_up(const void* w_split, const uint16_t* lo, uint16_t* out, int T, int N,
-                            int K, void* ws, size_t ws_bytes, void* stream) {
-    (void)ws; (void)ws_bytes;
+// tiled: the up weights in the tiled layout (gq8_q8_0_tile16), N % 16 == 0 and K % 320 == 0
+static int hc_up_common(const void* w, const uint16_t* lo, uint16_t* out, int T, int N, int K,
+                        bool tiled, void* stream) {
     if (T < 0 || N < 0 || K < 0) return GQ8_EINVAL;
     if (!q8_shape_ok(T, N, K) || K > 1024) return GQ8_ESHAPE;
+    if (tiled && (N % 16 != 0 || K % 320 != 0)) return GQ8_ESHAPE;
     if (T == 0 || N == 0) return GQ8_OK;
     if (out == nullptr) return GQ8_EINVAL;
     if (K == 0) {
         if (device_cus() == 0) return GQ8_ENODEV;
         return launch_fill_zero(out, (size_t)T * N * sizeof(uint16_t), S(stream));
     }
-    if (w_split == nullptr || lo == nullptr) return GQ8_EINVAL;
-    if (!aligned16(w_split) || !aligned16(lo)) return GQ8_EALIGN;
+    if (w == nullptr || lo == nullptr) return GQ8_EINVAL;
+    if (!aligned16(w) || !aligned16(lo)) return GQ8_EALIGN;
     if (device_cus() == 0) return GQ8_ENODEV;
     GemvArgs a{};
-    a.q = static_cast<const int8_t*>(w_split);
+    a.q = static_cast<const int8_t*>(w);
     a.d = reinterpret_cast<const uint16_t*>(a.q + (size_t)N * K);
-    a.x = lo; a.T = T; a.N = N; a.K = K; a.out = out;
+    a.x = lo; a.T = T; a.N = N; a.K = K; a.out = out; a.wt = tiled;
     return launch_hc_up(a, S(stream));
 }
 
-GQ8_EXPORT int gq8_hc_q8_pair(const void* w_down, const uint16_t* R, const uint16_t* w_norm,
-                              float eps, const void* w_up, uint16_t* lo, float* rs_out,
-                              uint16_t* out, int T, int Nlr, int Khc, void* ws, size_t ws_bytes,
-                              void* stream) {
+GQ8_EXPORT int gq8_hc_q8_up(const void* w_split, const uint16_t* lo, uint16_t* out, int T, int N,
+                            int K, void* ws, size_t ws_bytes, void* stream) {
+    (void)ws; (void)ws_bytes;
+    return hc_up_common(w_split, lo, out, T, N, K, false, stream);
+}
+
+GQ8_EXPORT int gq8_hc_q8_up_tiled(const void* w_tiled, const uint16_t* lo, uint16_t* out, int T,
+                                  int N, int K, void* ws, size_t ws_bytes, void* stream) {
+    (void)ws; (void)ws_bytes;
+    return hc_up_common(w_tiled, lo, out, T, N, K, true, stream);
+}
+
+static int hc_pair_common(const void* w_down, const uint16_t* R, const uint16_t* w_norm, float eps,
+                          const void* w_up, uint16_t* lo, float* rs_out, uint16_t* out, int T,
+                          int Nlr, int Khc, bool tiled, void* ws, size_t ws_bytes, void* stream) {
     if (T < 0 || Nlr < 0 || Khc < 0) return GQ8_EINVAL;
     if (!q8_shape_ok(T, Nlr, Khc) || Nlr % 32 != 0 || Nlr > 1024 || Khc == 0 || Nlr == 0)
         return GQ8_ESHAPE;
+    if (tiled && (Khc % 16 != 0 || Nlr % 320 != 0)) return GQ8_ESHAPE;
     if (T == 0) return GQ8_OK;
     if (w_down == nullptr || R == nullptr || w_norm == nullptr || w_up == nullptr ||
         lo == nullptr || out == nullptr)
@@ -342,8 +355,24 @@ GQ8_EXPORT int gq8_hc_q8_pair(const void* w_down, const uint16_t* R, const uint1
     GemvArgs up{};
     up.q = static_cast<const int8_t*>(w_up);
     up.d = reinterpret_cast<const uint16_t*>(up.q + (size_t)Khc * Nlr);
-    up.x = lo; up.T = T; up.N = Khc; up.K = Nlr; up.out = out;
+    up.x = lo; up.T = T; up.N = Khc; up.K = Nlr; up.out = out; up.wt = tiled;
     return launch_hc_pair(dn, up, ws, S(stream));
+}
+
+GQ8_EXPORT int gq8_hc_q8_pair(const void* w_down, const uint16_t* R, const uint16_t* w_norm,
+                              float eps, const void* w_up, uint16_t* lo, float* rs_out,
+                              uint16_t* out, int T, int Nlr, int Khc, void* ws, size_t ws_bytes,
+                              void* stream) {
+    return hc_pair_common(w_down, R, w_norm, eps, w_up, lo, rs_out, out, T, Nlr, Khc, false, ws,
+                          ws_bytes, stream);
+}
+
+GQ8_EXPORT int gq8_hc_q8_pair_tiled(const void* w_down, const uint16_t* R, const uint16_t* w_norm,
+                                    float eps, const void* w_up_tiled, uint16_t* lo, float* rs_out,
+                                    uint16_t* out, int T, int Nlr, int Khc, void* ws,
+                                    size_t ws_bytes, void* stream) {
+    return hc_pair_common(w_down, R, w_norm, eps, w_up_tiled, lo, rs_out, out, T, Nlr, Khc, true,
+                          ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------------- pending write

@@ -1041,7 +1041,9 @@ __global__ void __launch_bounds__(256) hc_up_kernel(GemvArgs a) {
 // waits only for its own load, so the work of early loads overlaps the arrival of later ones.
 GQ8_DEV int up_koff(int g) { return 16 * (g & 1) + 8 * (g >> 1); }
 
-template <int T>
+// TL: quants in the tiled layout: the wave's 16 rows x 64 columns of load i are one 1 KiB tile,
+// lane l's 16 bytes at byte 16 l of it (the same bytes a lane as the split layout's row pieces).
+template <int T, bool TL = false>
 __global__ void __launch_bounds__(256) hc_up_direct_kernel(GemvArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t xl[kMaxT][kUpLoStride];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1070,9 +1072,10 @@ __global__ void __launch_bounds__(256) hc_up_direct_kernel(GemvArgs a) {
 #pragma unroll
         for (int i = 0; i < kUpCB / 2; ++i) sc[i] = dp[i];
         u32x4 wv[kUpLoads];
-        const int8_t* wp = a.q + (size_t)row * K + c0 + 16 * g;
+        const int8_t* wp = TL ? a.q + ((size_t)(r0 >> 4) * (K >> 6) + (c0 >> 6)) * 1024 + 16 * lane
+                              : a.q + (size_t)row * K + c0 + 16 * g;
 #pragma unroll
-        for (int i = 0; i < kUpLoads; ++i) wv[i] = ld_nt16(wp + 64 * i);
+        for (int i = 0; i < kUpLoads; ++i) wv[i] = ld_nt16(wp + (TL ? 1024 : 64) * i);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < 3; ++i) {
@@ -1170,6 +1173,11 @@ __global__ void __launch_bounds__(256) hc_up_bf16_kernel(GemvArgs a) {
 template <int T>
 static int launch_up_t(GemvArgs a, hipStream_t st) {
     const int ntile = (a.N + 15) / 16;
+    if (a.wt) {                            // tiled weights: the direct kernel only
+        if (a.K % kUpCW != 0 || a.N % 16 != 0) return GQ8_ESHAPE;
+        hipLaunchKernelGGL((hc_up_direct_kernel<T, true>), dim3((ntile + 3) / 4), dim3(256), 0, st, a);
+        return launch_status();
+    }
     if (a.K % kUpCW == 0 && !force_general()) {
         hipLaunchKernelGGL((hc_up_direct_kernel<T>), dim3((ntile + 3) / 4), dim3(256), 0, st, a);
     } else {
@@ -1203,7 +1211,7 @@ constexpr int kPairQuads = kUpCW / 4;       // float4 quads of a 320-wide row
 constexpr int kPairNup = 4;
 constexpr int kPairNcw = 4;
 
-template <int T, bool WB = false>
+template <int T, bool WB = false, bool TL = false>
 __global__ void __launch_bounds__(64 * (kPairNup + kPairNcw)) hc_pair_up_kernel(GemvArgs a) {
     constexpr int NQ = T * kPairQuads;                            // float4 quads of lo
     constexpr int NTC = 64 * kPairNcw;                            // combine threads
@@ -1242,9 +1250,10 @@ __global__ void __launch_bounds__(64 * (kPairNup + kPairNcw)) hc_pair_up_kernel(
             const uint32_t* dp = reinterpret_cast<const uint32_t*>(a.d + (size_t)row * (K >> 5));
 #pragma unroll
             for (int i = 0; i < kUpCB / 2; ++i) sc[i] = dp[i];
-            const int8_t* wp = a.q + (size_t)row * K + 16 * g;
+            const int8_t* wp = TL ? a.q + (size_t)(r0 >> 4) * (K >> 6) * 1024 + 16 * lane
+                                  : a.q + (size_t)row * K + 16 * g;
 #pragma unroll
-            for (int i = 0; i < kUpLoads; ++i) wv[i] = ld_nt16(wp + 64 * i);
+            for (int i = 0; i < kUpLoads; ++i) wv[i] = ld_nt16(wp + (TL ? 1024 : 64) * i);
             __syncthreads();                                      // slab-group sums in LDS
             __syncthreads();                                      // lo in LDS
         }
@@ -1398,7 +1407,12 @@ static int launch_pair_t(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st) {
         up.S = S; up.part = dn.part; up.ssq = dn.ssq; up.eps = dn.eps; up.kd = dn.K;
         up.rs_out = dn.rs_out; up.lo_out = dn.out;
         const int ntile = (up.N + 15) / 16;
-        hipLaunchKernelGGL((hc_pair_up_kernel<T>), dim3((ntile + kPairNup - 1) / kPairNup), dim3(64 * (kPairNup + kPairNcw)), 0, st, up);
+        if (up.wt) {
+            if (up.N % 16 != 0) return GQ8_ESHAPE;
+            hipLaunchKernelGGL((hc_pair_up_kernel<T, false, true>), dim3((ntile + kPairNup - 1) / kPairNup), dim3(64 * (kPairNup + kPairNcw)), 0, st, up);
+        } else {
+            hipLaunchKernelGGL((hc_pair_up_kernel<T>), dim3((ntile + kPairNup - 1) / kPairNup), dim3(64 * (kPairNup + kPairNcw)), 0, st, up);
+        }
         return launch_status();
     }
 }

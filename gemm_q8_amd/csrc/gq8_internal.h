@@ -60,6 +60,8 @@ struct GemvArgs {
     unsigned* cnt;          // last-arriver combine: one arrival counter per 64-row group
     const uint16_t* pw;     // down read with the pending write: bf16 P [T][K] ...
     uint16_t* r_out;        //   ... and R_out = bf16(R + P) [T][K], the stream the read takes
+    bool wt;                // up read: quants in the tiled layout (launch_q8_0_tile16; N % 16 == 0,
+                            //   K % 320 == 0: the direct and fused up kernels only)
 };
 
 // Combine of split partial sums: a kernel of its own (default), or the last-arriving work-group

@@ -48,6 +48,8 @@ _SIGS = {
     "gq8_hc_q8_down": (_I, [_P, _P, _P, _F, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_hc_q8_up": (_I, [_P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_hc_q8_pair": (_I, [_P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "gq8_hc_q8_pair_tiled": (_I, [_P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "gq8_hc_q8_up_tiled": (_I, [_P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_hc_q8_down_pending": (_I, [_P, _P, _P, _P, _F, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_hc_q8_pair_pending": (_I, [_P, _P, _P, _P, _F, _P, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "gq8_hc_q8_pair_noalloc": (_I, [_P, _P, _P, _F, _P, _P, _P, _P, _I, _I, _I, _P]),
@@ -200,6 +202,18 @@ def gq8_hc_q8_pair(w_down, R, w_norm, eps, w_up, lo, rs_out, out, T, Nlr, Khc, w
     return _check("gq8_hc_q8_pair", _lib.gq8_hc_q8_pair(
         _dev(w_down), _dev(R), _dev(w_norm), eps, _dev(w_up), _dev(lo), _dev(rs_out), _dev(out),
         T, Nlr, Khc, _dev(ws), ws_bytes, _stream(stream)))
+
+
+def gq8_hc_q8_up_tiled(w_tiled, lo, out, T, N, K, ws, ws_bytes, stream=None):
+    return _check("gq8_hc_q8_up_tiled", _lib.gq8_hc_q8_up_tiled(
+        _dev(w_tiled), _dev(lo), _dev(out), T, N, K, _dev(ws), ws_bytes, _stream(stream)))
+
+
+def gq8_hc_q8_pair_tiled(w_down, R, w_norm, eps, w_up_tiled, lo, rs_out, out, T, Nlr, Khc, ws,
+                         ws_bytes, stream=None):
+    return _check("gq8_hc_q8_pair_tiled", _lib.gq8_hc_q8_pair_tiled(
+        _dev(w_down), _dev(R), _dev(w_norm), eps, _dev(w_up_tiled), _dev(lo), _dev(rs_out),
+        _dev(out), T, Nlr, Khc, _dev(ws), ws_bytes, _stream(stream)))
 
 
 def gq8_hc_bf16_pair(w_down, R, w_norm, eps, w_up, lo, rs_out, out, T, Nlr, Khc, ws, ws_bytes,

@@ -98,7 +98,8 @@ int gq8_q8_0_quantize(const float* w, int rows, int K, void* w_split, void* stre
  * split layout: the same bytes, reordered (HC-Q8 page, "What changed"). */
 int gq8_q8_0_split_from_blocks(const void* blocks34, int rows, int K, void* w_split, void* stream);
 
-/* Tiled layout, for the routed down weights (gq8_moe_q8_0_routed_flags, GQ8_MOE_DOWN_TILED):
+/* Tiled layout, for the routed down weights (gq8_moe_q8_0_routed_flags, GQ8_MOE_DOWN_TILED) and
+ * the up read's weights:
  * `count` split-layout matrices [rows][K] stored back to back (each gq8_q8_0_bytes(rows, K)
  * bytes, e.g. an expert arena) are copied to w_tiled, each matrix at the same offset and of the
  * same size, with its scales unchanged and its quants reordered into 1 KiB tiles: tile (G, c)
@@ -109,7 +110,7 @@ int gq8_q8_0_split_from_blocks(const void* blocks34, int rows, int K, void* w_sp
  * preparation, not a hot-path call (the layout is a choice for MI355X; the pages' blocks hold
  * the same bytes). rows % 16 == 0, K % 64 == 0 (else GQ8_ESHAPE); both buffers 16-byte
  * aligned (GQ8_EALIGN) and not overlapping (GQ8_EINVAL); count == 0, rows == 0 or K == 0: no
- * work. */
+ * work. The up read takes the same layout (gq8_hc_q8_up_tiled, gq8_hc_q8_pair_tiled). */
 int gq8_q8_0_tile16(const void* w_split, int rows, int K, int count, void* w_tiled, void* stream);
 
 /* q8_1 quantization of bf16 rows x[rows][K] (EP page, "What changed": the q8_1 MoE input).
@@ -221,6 +222,19 @@ int gq8_hc_q8_up(const void* w_split, const uint16_t* lo, uint16_t* out, int T, 
 int gq8_hc_q8_pair(const void* w_down, const uint16_t* R, const uint16_t* w_norm, float eps,
                    const void* w_up, uint16_t* lo, float* rs_out, uint16_t* out,
                    int T, int Nlr, int Khc, void* ws, size_t ws_bytes, void* stream);
+
+/* gq8_hc_q8_up and gq8_hc_q8_pair with the up weights in the tiled layout (gq8_q8_0_tile16 with
+ * rows = N (Khc for the pair), K = the up depth (Nlr), count = 1): the up read's 16-row tiles are
+ * then contiguous 1 KiB loads instead of sixteen 64-byte row pieces each. The results are bitwise
+ * those of the calls on the split layout. Needs N % 16 == 0 and an up depth that is a multiple
+ * of 320 (the up kernels that read whole 320-column chunks), else GQ8_ESHAPE; everything else
+ * (shapes, workspace, errors) as the split-layout calls. Weight preparation (the tiling) is
+ * outside the hot path; the layout is a choice for MI355X. */
+int gq8_hc_q8_up_tiled(const void* w_tiled, const uint16_t* lo, uint16_t* out, int T, int N, int K,
+                       void* ws, size_t ws_bytes, void* stream);
+int gq8_hc_q8_pair_tiled(const void* w_down, const uint16_t* R, const uint16_t* w_norm, float eps,
+                         const void* w_up_tiled, uint16_t* lo, float* rs_out, uint16_t* out,
+                         int T, int Nlr, int Khc, void* ws, size_t ws_bytes, void* stream);
 
 /* The down read and the pair with the pending write folded in (HC-Q8 page, "Summary": R_out, the
  * pending write between the two reads, bitwise the default read's; the page does not define it

@@ -216,6 +216,22 @@ def test_tile16_argument_checks(lib):
     assert raw.gq8_q8_0_tile16(a, 16, 64, 2, a + 1088, None) == lib.EINVAL
 
 
+def test_tiled_up_argument_checks(lib):
+    """The tiled up read and pair need whole 16-row tiles and an up depth that is a multiple of
+    320, checked before any device work."""
+    raw = lib.raw()
+    d = 1 << 20      # never dereferenced
+    assert raw.gq8_hc_q8_up_tiled(d, d, d, 1, 24, 320, None, 0, None) == lib.ESHAPE     # N % 16
+    assert raw.gq8_hc_q8_up_tiled(d, d, d, 1, 32, 64, None, 0, None) == lib.ESHAPE      # K % 320
+    assert raw.gq8_hc_q8_up_tiled(d, d, d, -1, 32, 320, None, 0, None) == lib.EINVAL
+    assert raw.gq8_hc_q8_up_tiled(None, d, d, 1, 32, 320, None, 0, None) == lib.EINVAL
+    assert raw.gq8_hc_q8_up_tiled(d + 8, d, d, 1, 32, 320, None, 0, None) == lib.EALIGN
+    assert raw.gq8_hc_q8_pair_tiled(d, d, d, 1e-6, d, d, None, d, 1, 64, 1024, None, 0,
+                                    None) == lib.ESHAPE                                  # Nlr % 320
+    assert raw.gq8_hc_q8_pair_tiled(d, d, d, 1e-6, d, d, None, d, 1, 320, 1024, None, 0,
+                                    None) == lib.EWORKSPACE
+
+
 def test_per_token_argument_checks(lib):
     raw = lib.raw()
     dummy = 1 << 20  # never dereferenced

@@ -302,6 +302,46 @@ def test_pair_is_the_two_calls(gpu, T, Nlr, Khc):
     check_bf16(to_host(out_p, np.uint16), out_ref, S_up, f"pair up T={T} Nlr={Nlr} Khc={Khc}")
 
 
+def _tiled(gpu, w_split, rows, K):
+    wt = torch.empty_like(w_split)
+    gpu.gq8_q8_0_tile16(w_split, rows, K, 1, wt)
+    return wt
+
+
+@pytest.mark.parametrize("T,N,K", [(1, 16384, 320), (6, 16384, 320), (16, 48, 960), (3, 64, 640)])
+def test_up_tiled_is_the_split_read(gpu, T, N, K):
+    """gq8_hc_q8_up_tiled on the weights tiled by gq8_q8_0_tile16: bitwise the split-layout up
+    read."""
+    d = synth.hc_inputs(T, K=N, N=K, seed=42)          # up weight [N][K] = the pair's w_up
+    wu = q8_0_from_f32(to_dev(d["w_up"]))
+    lo = to_dev(synth.bf16_normal(42, "gpu.up.tiled.lo", (T, K), 0.0, 1.0))
+    out_s = _up(gpu, wu, lo, T, N, K)
+    out_t = torch.full_like(out_s, 0x5555)
+    gpu.gq8_hc_q8_up_tiled(_tiled(gpu, wu, N, K), lo, out_t, T, N, K, None, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(out_t, out_s), f"T={T} N={N} K={K}"
+
+
+@pytest.mark.parametrize("T,Nlr,Khc", [(1, 320, 16384), (2, 320, 16384), (4, 320, 16384),
+                                       (6, 320, 16384), (16, 320, 16384), (3, 640, 2048)])
+def test_pair_tiled_is_the_pair(gpu, T, Nlr, Khc):
+    """gq8_hc_q8_pair_tiled (up weights tiled): lo, rs and out bitwise those of gq8_hc_q8_pair,
+    on every path (whole-row down read at T = 1, the up kernel with the combine for T <= 4,
+    three kernels above, and an up depth of 640)."""
+    d = synth.hc_inputs(T, K=Khc, N=Nlr, seed=43)
+    wd, wu = q8_0_from_f32(to_dev(d["w_down"])), q8_0_from_f32(to_dev(d["w_up"]))
+    R, wn = to_dev(d["R"]), to_dev(d["w_norm"])
+    lo_s, rs_s, out_s = _pair(gpu, wd, R, wn, wu, T, Nlr, Khc)
+    nb = gpu.gq8_workspace_bytes(gpu.OP_HC_PAIR, T, Nlr, Khc)
+    lo_t = torch.full_like(lo_s, 0x5555)
+    rs_t = torch.full_like(rs_s, -1.0)
+    out_t = torch.full_like(out_s, 0x5555)
+    gpu.gq8_hc_q8_pair_tiled(wd, R, wn, 1e-6, _tiled(gpu, wu, Khc, Nlr), lo_t, rs_t, out_t, T, Nlr,
+                             Khc, workspace(nb), nb)
+    torch.cuda.synchronize()
+    assert torch.equal(lo_t, lo_s) and torch.equal(rs_t, rs_s) and torch.equal(out_t, out_s), f"T={T}"
+
+
 def test_pair_graph_replay_and_poison(gpu):
     T, Nlr, Khc = 6, 320, 16384
     d = synth.hc_inputs(T, seed=41)
