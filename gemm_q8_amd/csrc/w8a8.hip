@@ -370,11 +370,13 @@ int launch_w8a8(const W8Plan& p, const int8_t* xq, const float* xs, const int8_t
         case 2: return launch_w8a8_kpw<2>(p, a, st);
         case 3: return launch_w8a8_kpw<3>(p, a, st);
         case 4: return launch_w8a8_kpw<4>(p, a, st);
-        default: {
-            // K > 4096: more k-steps per wave than the unrolled variants hold
-            if (p.kpw <= 8) return launch_w8a8_kpw<8>(p, a, st);
-            return GQ8_ESHAPE;
-        }
+        // K > 4096: one variant per step count, since every wave issues KPW loads of each kind
+        // (clamped past the last step), so a larger KPW than needed multiplies the loads
+        case 5: return launch_w8a8_kpw<5>(p, a, st);
+        case 6: return launch_w8a8_kpw<6>(p, a, st);
+        case 7: return launch_w8a8_kpw<7>(p, a, st);
+        case 8: return launch_w8a8_kpw<8>(p, a, st);
+        default: return GQ8_ESHAPE;
     }
 }
 

@@ -127,6 +127,29 @@ def test_w8a8_max_depth(gpu, M):
     assert np.array_equal(_run(gpu, d, M, N, K), out_ref)
 
 
+@pytest.mark.parametrize("K", [4160, 4352, 5120, 6096, 6720, 7232, 8128])
+@pytest.mark.parametrize("M,N", [(1, 40), (16, 48), (32, 40), (9, 2064)])
+def test_w8a8_deep_ragged_steps(gpu, M, N, K):
+    """Depths past 4096 whose k-step count (K / 64, rounded up) leaves 5 to 8 steps per wave,
+    with the last steps of some waves masked, exact against the oracle: the two-tile MFMA kernel
+    (M = 32), the half-tile one (N = 40, 48), and with N = 2064 the whole-tile one."""
+    d = synth.w8a8_inputs(M, N, K, seed=7 + K % 97)
+    acc_ref, out_ref = w8a8_gemm(d["xq"], d["x_scale"], d["W"], d["w_scale"])
+    assert np.array_equal(_run(gpu, d, M, N, K, i32=True), acc_ref)
+    assert np.array_equal(_run(gpu, d, M, N, K), out_ref)
+
+
+@pytest.mark.parametrize("K", [4352, 7232])
+@pytest.mark.parametrize("M", [1, 8, 15])
+def test_w8a8_dot_kernel_deep_ragged_steps(gpu, monkeypatch, M, K):
+    """The VALU dot kernel (forced) at 5 and 8 k-steps per wave, exact against the oracle."""
+    monkeypatch.setenv("GQ8_W8A8_KERNEL", "dot")
+    N = 40
+    d = synth.w8a8_inputs(M, N, K, seed=11 + M)
+    acc_ref, _ = w8a8_gemm(d["xq"], d["x_scale"], d["W"], d["w_scale"])
+    assert np.array_equal(_run(gpu, d, M, N, K, i32=True), acc_ref)
+
+
 @pytest.mark.parametrize("M,N,K", [(16, 1536, 4096), (5, 37, 80)])
 def test_w8a8_host_pack_equals_device_pack(gpu, M, N, K):
     """gq8_w8a8_pack_host writes the bytes gq8_w8a8_pack writes; the product on them is exact."""

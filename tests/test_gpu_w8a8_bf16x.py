@@ -59,7 +59,7 @@ def _check(gpu, d, M, N, K, tag):
 
 @pytest.mark.parametrize("M", [1, 2, 5, 8, 9, 16, 17, 32])
 @pytest.mark.parametrize("N,K", [(48, 256), (37, 80), (160, 2048), (40, 2048 + 48), (160, 4096),
-                                 (24, 8192)])
+                                 (24, 8192), (40, 4352), (24, 6720)])
 def test_bf16x_exact_small(gpu, M, N, K):
     d = synth.w8a8_bf16_inputs(M, N, K, seed=70 + M)
     _check(gpu, d, M, N, K, f"M={M} N={N} K={K}")
