@@ -17,7 +17,8 @@
 //    kernel without rs.
 //  * down read at T = 1 (hc_down_rows_kernel): a work-group owns two whole rows and all of K,
 //    VALU dots on u = R * w_norm formed in fp32, its own sum of squares for rs: one kernel, no
-//    partial sums; the pair then takes the direct up kernel (two launches).
+//    partial sums; the pair then takes the direct up kernel (two launches), and its launch of
+//    the down read carries extra work-groups that fetch the up read's weights ahead.
 //  * down read, T >= 2 (hc_down_partial_kernel): a work-group takes a 512-column slab x 64 rows, one
 //    16-row 16x16x32 bf16 MFMA tile per wave (from T = 9 two waves per tile, one per column
 //    half). u = R * w_norm is exact in fp32 (8-bit x 8-bit
@@ -676,6 +677,64 @@ __global__ void __launch_bounds__(256) hc_down_combine_kernel(GemvArgs a) {
     }
 }
 
+// The up read's weights fetched ahead (the pair at T = 1). The whole-row down read below keeps
+// its SIMDs busy with VALU work and leaves HBM bandwidth unused, while the up read that follows
+// it starts with its own weights cold. So the pair's down launch carries one extra work-group
+// per up work-group (64 rows each): extra work-group i reads up work-group i's quant rows and
+// block scales with cache-allocating loads, all issued before the first use (addresses past
+// the rows clamp to their first piece), and folds them into a value stored only under an
+// impossible condition, so no load can be dropped. Work-groups are dealt to the 8 XCDs in turn,
+// so with the extra work-groups starting at a multiple of 8, extra work-group i and up
+// work-group i run on the same XCD and the up read finds its rows in that XCD's L2 or the
+// memory-side cache. No result depends on it.
+constexpr int kUpAheadRows = 64;           // rows of an up work-group (four waves of 16)
+constexpr int kUpAheadMaxWG = 1024;        // up reads of more rows than this many work-groups: no fetch
+
+template <int NPT>
+GQ8_DEV uint32_t fetch_rows_ahead(const GemvArgs& a, size_t qb, size_t qe, size_t sb, size_t se) {
+    const size_t nt = blockDim.x, tid = threadIdx.x;
+    u32x4 v[NPT];
+    uint32_t w[2];
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+        const size_t o = qb + 16 * (tid + (size_t)j * nt);
+        v[j] = *reinterpret_cast<const u32x4*>(a.pfq + (o < qe ? o : qb));
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const size_t o = sb + 2 * (tid + (size_t)j * nt);          // two scales a load
+        w[j] = *reinterpret_cast<const uint32_t*>(a.pfd + (o + 1 < se ? o : sb));
+    }
+    uint32_t acc = w[0] ^ w[1];
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+    // what the batch does not cover (deep rows, small work-groups): further rounds
+    for (size_t o = qb + 16 * (tid + (size_t)NPT * nt); o < qe; o += 16 * nt) {
+        const u32x4 u = *reinterpret_cast<const u32x4*>(a.pfq + o);
+        acc ^= u.x ^ u.y ^ u.z ^ u.w;
+    }
+    for (size_t o = sb + 2 * (tid + 2 * nt); o + 1 < se; o += 2 * nt)
+        acc ^= *reinterpret_cast<const uint32_t*>(a.pfd + o);
+    return acc;
+}
+
+GQ8_DEV void fetch_up_rows_ahead(const GemvArgs& a, int i) {
+    const int rlo = kUpAheadRows * i, rhi = imin(a.pf_n, rlo + kUpAheadRows);
+    const size_t qb = (size_t)rlo * a.pf_k, qe = (size_t)rhi * a.pf_k;
+    const size_t sb = (size_t)rlo * (a.pf_k / 32), se = (size_t)rhi * (a.pf_k / 32);
+    const size_t npt = ((qe - qb) / 16 + blockDim.x - 1) / blockDim.x;
+    uint32_t acc;
+    switch (npt) {
+        case 0: case 1: acc = fetch_rows_ahead<1>(a, qb, qe, sb, se); break;
+        case 2: acc = fetch_rows_ahead<2>(a, qb, qe, sb, se); break;
+        case 3: acc = fetch_rows_ahead<3>(a, qb, qe, sb, se); break;
+        case 4: acc = fetch_rows_ahead<4>(a, qb, qe, sb, se); break;
+        case 5: acc = fetch_rows_ahead<5>(a, qb, qe, sb, se); break;
+        default: acc = fetch_rows_ahead<6>(a, qb, qe, sb, se); break;
+    }
+    if (acc == 0x9e3779b9u && a.N < 0) reinterpret_cast<uint16_t*>(a.out)[0] = 0;
+}
+
 // Down read on whole rows (small T): a work-group owns RW rows and all of K, so no partial sums
 // and no combine. Wave w takes the 1024-column chunks w, w + NW, ... (CPW of them per pass, all
 // loaded before the first arithmetic: activations first, then the weights, as the GEMV's
@@ -693,6 +752,14 @@ __global__ void __launch_bounds__(1024) hc_down_rows_kernel(GemvArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int NW = blockDim.x >> 6;
     const int N = a.N, K = a.K, nblk = K >> 5;
+    {
+        const int nrg = (N + RW - 1) / RW;                 // row work-groups; then the fetch-ahead
+        if ((int)blockIdx.x >= nrg) {                      // ones from the next multiple of 8
+            const int nrg8 = (nrg + 7) & ~7;
+            if ((int)blockIdx.x >= nrg8) fetch_up_rows_ahead(a, (int)blockIdx.x - nrg8);
+            return;
+        }
+    }
     const int row0 = blockIdx.x * RW;
     const int nchunk = (K + 1023) >> 10;
     const uint16_t* R = reinterpret_cast<const uint16_t*>(a.x);
@@ -821,7 +888,9 @@ static int launch_down_rows_t(GemvArgs a, hipStream_t st) {
     constexpr int RW = kDownRowsRW;
     const int nchunk = (a.K + 1023) / 1024;
     const int nw = nchunk > 16 ? 16 : nchunk;
-    hipLaunchKernelGGL((hc_down_rows_kernel<T, RW, 1, PW>), dim3((a.N + RW - 1) / RW), dim3(64 * nw), 0, st, a);
+    const int nrg = (a.N + RW - 1) / RW;
+    const int grid = a.pfq != nullptr ? ((nrg + 7) & ~7) + (a.pf_n + kUpAheadRows - 1) / kUpAheadRows : nrg;
+    hipLaunchKernelGGL((hc_down_rows_kernel<T, RW, 1, PW>), dim3(grid), dim3(64 * nw), 0, st, a);
     return launch_status();
 }
 
@@ -1389,6 +1458,12 @@ __global__ void __launch_bounds__(64 * (kPairNup + kPairNcw)) hc_pair_up_kernel(
 // MI355X at K = 16384 (S = 32), folding wins up to T = 4 (T = 4: 9.9 us vs 10.8 us).
 constexpr int kPairMaxT = 4;
 
+// the pair's whole-row down read fetches the up read's weights ahead (hc_down_rows_kernel)
+static void fetch_up_ahead(GemvArgs& dn, const GemvArgs& up) {
+    if ((up.N + kUpAheadRows - 1) / kUpAheadRows > kUpAheadMaxWG) return;
+    dn.pfq = up.q; dn.pfd = up.d; dn.pf_n = up.N; dn.pf_k = up.K;
+}
+
 template <int T>
 static int launch_pair_t(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st) {
     if constexpr (T > kPairMaxT) {
@@ -1396,6 +1471,7 @@ static int launch_pair_t(GemvArgs dn, GemvArgs up, void* ws, hipStream_t st) {
         return rc != GQ8_OK ? rc : launch_up_t<T>(up, st);
     } else {
         if (down_rows<T>() || dn_last_arriver<T>()) {   // the down call, then the up read
+            if (down_rows<T>()) fetch_up_ahead(dn, up);
             const int rc = launch_down_t<T>(dn, ws, st);
             return rc != GQ8_OK ? rc : launch_up_t<T>(up, st);
         }
@@ -1425,6 +1501,7 @@ static int launch_pair_pending_t(GemvArgs dn, GemvArgs up, void* ws, hipStream_t
         return rc != GQ8_OK ? rc : launch_up_t<T>(up, st);
     } else {
         if (up.K != kUpCW || force_general() || down_rows<T>()) {
+            if (down_rows<T>()) fetch_up_ahead(dn, up);
             const int rc = launch_down_pending_t<T>(dn, ws, st);
             return rc != GQ8_OK ? rc : launch_up_t<T>(up, st);
         }

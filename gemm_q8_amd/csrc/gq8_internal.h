@@ -60,6 +60,9 @@ struct GemvArgs {
     unsigned* cnt;          // last-arriver combine: one arrival counter per 64-row group
     const uint16_t* pw;     // down read with the pending write: bf16 P [T][K] ...
     uint16_t* r_out;        //   ... and R_out = bf16(R + P) [T][K], the stream the read takes
+    const int8_t* pfq;      // pair, whole-row down read: the up read's quants and scales, pf_n
+    const uint16_t* pfd;    //   rows of pf_k columns, which extra work-groups of the down read
+    int pf_n, pf_k;         //   fetch ahead into the caches (hc_down_rows_kernel)
     bool wt;                // up read: quants in the tiled layout (launch_q8_0_tile16; N % 16 == 0,
                             //   K % 320 == 0: the direct and fused up kernels only)
 };
