@@ -136,16 +136,18 @@ def code_digest(root, files):
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """HBM bytes per pair call from the committed FETCH_SIZE / WRITE_SIZE summary, or None when
-    the kernel code has changed since those counters were taken."""
+def recorded_traffic(per_t=False):
+    """HBM bytes per pair call from the committed FETCH_SIZE / WRITE_SIZE summary (per T with
+    per_t), or None when the kernel code has changed since those counters were taken."""
     root = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(root, "profiles", "hc_pair_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     ok = code_digest(root, rec["sources"]) == rec["kernel_code_sha256"]
-    return rec["traffic_bytes_per_pair_call"] if ok else None
+    if not ok:
+        return None
+    return rec.get("per_T_bytes") if per_t else rec["traffic_bytes_per_pair_call"]
 
 
 def n_sets_for(nbytes, multiple=1):
@@ -973,6 +975,11 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": recorded_traffic(),
             "traffic_unit": "bytes per pair call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
+            "traffic_per_T": recorded_traffic(per_t=True),
+            "traffic_note": "FETCH_SIZE counts every L2 fill from the memory side. At T = 1 the up "
+                            "read's weights are filled twice: by the down launch's fetch-ahead "
+                            "work-groups, then by the up read itself; the pair is faster for it, "
+                            "which points to the second fill coming from the memory-side cache",
             "avg_call_us": round(avg_us, 3),
             "measured_over": f"the timed region: {args.steps} steps x {len(TS)} pair calls",
             # the same fraction per T (graphs of back-to-back calls of one T after the timed
