@@ -281,9 +281,11 @@ def _pair(gpu, wd, R, wn, wu, T, Nlr, Khc, ws=None, stream=None, lo=None, rs=Non
     return lo, rs, out
 
 
+# T = 1 at depths 1056, 544 and 32: up reads of 16.5, 8.5 and 0.5 work-groups of 64 rows, so the
+# down launch's fetch-ahead work-groups cover a partial last one
 @pytest.mark.parametrize("T,Nlr,Khc", [(1, 320, 16384), (4, 320, 16384), (6, 320, 16384),
                                        (16, 320, 16384), (3, 320, 1056), (8, 64, 2048),
-                                       (5, 96, 544)])
+                                       (5, 96, 544), (1, 320, 1056), (1, 320, 544), (1, 320, 32)])
 def test_pair_is_the_two_calls(gpu, T, Nlr, Khc):
     """The pair entry (two kernels for Nlr = 320, the combine inside the up read) gives bitwise the
     down call's lo and rs and the up call's output on that lo."""
