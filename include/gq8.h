@@ -216,7 +216,9 @@ int gq8_hc_q8_up(const void* w_split, const uint16_t* lo, uint16_t* out, int T, 
  * lo, rs_out and out are bitwise what the two separate calls produce. For Nlr == 320 and
  * 2 <= T <= 4 the down read's combine of its split partial sums runs inside the up kernel (two
  * kernel launches instead of three); otherwise (T = 1: the whole-row down kernel, no combine)
- * the two calls' kernels run in sequence. lo is written (bf16
+ * the two calls' kernels run in sequence. For Nlr == 320 and T = 1 the down kernel's launch
+ * also reads w_up once into the caches ahead of the up read (up to 65536 rows of w_up); no
+ * result depends on it. lo is written (bf16
  * [T][Nlr], 16-byte aligned, required); rs_out fp32 [T] is nullable. T = 1..16, Khc % 32 == 0,
  * Nlr % 32 == 0, 0 < Nlr <= 1024. Workspace: gq8_workspace_bytes(GQ8_OP_HC_PAIR, T, Nlr, Khc). */
 int gq8_hc_q8_pair(const void* w_down, const uint16_t* R, const uint16_t* w_norm, float eps,
