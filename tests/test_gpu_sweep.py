@@ -26,6 +26,10 @@ GEMV = _shapes("gemv", 10, lambda g: (int(g.integers(1, 17)), int(g.integers(1, 
                                       32 * int(g.integers(1, 200))))
 HC = _shapes("hc", 8, lambda g: (int(g.integers(1, 17)), 32 * int(g.integers(1, 33)),
                                  32 * int(g.integers(1, 400))))
+# the tuned pair shapes (Nlr = 320: the whole-row down read with the fetch-ahead at T = 1, the
+# combine inside the up read at T = 2..4, three kernels above) at random T and depth
+HC320 = [(1, 320, 32 * 17), (1, 320, 32 * 389)] + _shapes(
+    "hc320", 6, lambda g: (int(g.integers(1, 17)), 320, 32 * int(g.integers(1, 600))))
 W8 = _shapes("w8a8", 10, lambda g: (int(g.integers(1, 33)), int(g.integers(1, 500)),
                                     16 * int(g.integers(1, 513))))
 
@@ -60,7 +64,7 @@ def test_sweep_gemv(gpu, T, N, K):
     check_f32(to_host(y), y_ref, S, f"sweep gemv T={T} N={N} K={K}")
 
 
-@pytest.mark.parametrize("T,Nlr,Khc", HC)
+@pytest.mark.parametrize("T,Nlr,Khc", HC + HC320)
 def test_sweep_hc_pair(gpu, T, Nlr, Khc):
     d = synth.hc_inputs(T, K=Khc, N=Nlr, seed=61)
     wd, wu = q8_0_from_f32(to_dev(d["w_down"])), q8_0_from_f32(to_dev(d["w_up"]))
