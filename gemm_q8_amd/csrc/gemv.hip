@@ -1460,6 +1460,9 @@ constexpr int kPairMaxT = 4;
 
 // the pair's whole-row down read fetches the up read's weights ahead (hc_down_rows_kernel)
 static void fetch_up_ahead(GemvArgs& dn, const GemvArgs& up) {
+    // rows and depth in multiples of 32 (as every pair has them): each extra work-group then has
+    // at least 32 block scales, so its two-scale loads never pass its rows
+    if (up.N % 32 != 0 || up.K % 32 != 0) return;
     if ((up.N + kUpAheadRows - 1) / kUpAheadRows > kUpAheadMaxWG) return;
     dn.pfq = up.q; dn.pfd = up.d; dn.pf_n = up.N; dn.pf_k = up.K;
 }
