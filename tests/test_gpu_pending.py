@@ -47,7 +47,9 @@ def test_down_pending(gpu, T, N, K):
     assert np.allclose(to_host(rs), rs_ref, rtol=1e-5, atol=0)
 
 
-@pytest.mark.parametrize("T,Nlr,Khc", [(1, 320, 16384), (4, 320, 16384), (6, 320, 16384), (2, 64, 1056)])
+# (1, 64, 1056): the whole-row down read with its fetch-ahead, then the general (LDS-staged) up read
+@pytest.mark.parametrize("T,Nlr,Khc", [(1, 320, 16384), (4, 320, 16384), (6, 320, 16384), (2, 64, 1056),
+                                       (1, 64, 1056)])
 def test_pair_pending(gpu, T, Nlr, Khc):
     d, P = _inputs(T, Nlr, Khc, 81)
     wd, wu = q8_0_from_f32(to_dev(d["w_down"])), q8_0_from_f32(to_dev(d["w_up"]))
